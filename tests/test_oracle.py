@@ -1,0 +1,402 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks one oracle function against the pages' stated arithmetic, a
+closed form, a library routine computing the same quantity another way,
+an invariant, or exhaustive search on tiny inputs. None of them re-types the
+oracle's own formula.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg as sla
+
+from oracle import brute
+from oracle import lbadmm as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(s):
+    return np.random.default_rng(s)
+
+
+# --------------------------------------------------------------------- a1
+def test_precondition_golden_2x3():
+    g = json.load(open(os.path.join(GOLD, "precondition_2x3.json")))
+    for dt in (np.float64, np.float32):
+        Wt = O.precondition(g["W"], g["d_out"], g["d_in"], dt)
+        assert Wt.dtype == dt
+        np.testing.assert_array_equal(Wt, np.array(g["Wt"], dt))
+
+
+def test_precondition_is_diag_matrix_product():
+    rng = _rng(0)
+    W = rng.standard_normal((7, 5))
+    do, di = rng.lognormal(0, .5, 7), rng.lognormal(0, .5, 5)
+    ref = np.diag(do) @ W @ np.diag(di)          # matrix form of D_out W D_in
+    np.testing.assert_allclose(O.precondition(W, do, di), ref, rtol=1e-15, atol=0)
+    # identity preconditioners leave W unchanged, bit for bit, also in fp32
+    W32 = W.astype(np.float32)
+    np.testing.assert_array_equal(
+        O.precondition(W32, np.ones(7, np.float32), np.ones(5, np.float32), np.float32), W32)
+
+
+def test_precondition_fp32_rounds_each_product_once():
+    # the fp32 result must equal the exact product rounded twice in the stated order:
+    # fp64 holds the exact product of two fp32 numbers (48 significant bits < 53).
+    rng = _rng(1)
+    W = rng.standard_normal((33, 17)).astype(np.float32)
+    do = rng.lognormal(0, .5, 33).astype(np.float32)
+    di = rng.lognormal(0, .5, 17).astype(np.float32)
+    first = (W.astype(np.float64) * di.astype(np.float64)[None, :]).astype(np.float32)
+    second = (first.astype(np.float64) * do.astype(np.float64)[:, None]).astype(np.float32)
+    np.testing.assert_array_equal(O.precondition(W, do, di, np.float32), second)
+
+
+# --------------------------------------------------------------------- a2
+def test_init_scale_matches_second_moment():
+    # closed form: for i.i.d. N(0, s^2) U (m x r), V (n x r), E||U V^T||_F^2 = m n r s^4
+    rng = _rng(2)
+    m, n, r = 96, 64, 48
+    Wt = rng.standard_normal((m, n)) * 0.3
+    s0 = O.init_scale(Wt, r)
+    vals = []
+    for k in range(20):
+        U = s0 * rng.standard_normal((m, r))
+        V = s0 * rng.standard_normal((n, r))
+        vals.append(np.sum((U @ V.T) ** 2))
+    ratio = np.mean(vals) / np.sum(Wt ** 2)
+    assert abs(ratio - 1.0) < 0.08, ratio
+
+
+# --------------------------------------------------------------------- a3-a6
+def test_gram_equals_sum_of_row_outer_products():
+    rng = _rng(3)
+    V = rng.standard_normal((9, 4))
+    rho = 0.7
+    G = np.zeros((4, 4))
+    for i in range(9):
+        for p in range(4):
+            for q in range(4):
+                G[p, q] += V[i, p] * V[i, q]
+    for p in range(4):
+        G[p, p] += rho
+    np.testing.assert_allclose(O.gram(V, rho), G, rtol=1e-14, atol=1e-14)
+    w = np.linalg.eigvalsh(O.gram(V, rho))
+    assert w.min() >= rho - 1e-12
+
+
+def test_cholesky_unique_factor():
+    rng = _rng(4)
+    V = rng.standard_normal((50, 12))
+    G = O.gram(V, 1.0)
+    L = O.cholesky(G)
+    assert np.allclose(np.triu(L, 1), 0)
+    assert np.all(np.diag(L) > 0)
+    assert np.linalg.norm(L @ L.T - G) / np.linalg.norm(G) < 1e-14
+    np.testing.assert_allclose(L, sla.cholesky(G, lower=True), rtol=1e-12, atol=1e-13)
+
+
+def test_solve_normal_equations_and_lstsq():
+    """U from the Cholesky route minimises 1/2||Wt - U V^T||^2 + rho/2||U - (Z - Lam)||^2.
+
+    The same minimiser comes from an augmented least-squares problem solved by
+    numpy.linalg.lstsq (an SVD route sharing nothing with the Cholesky route):
+        min_U || [Wt, sqrt(rho)(Z - Lam)] - U [V^T, sqrt(rho) I] ||_F.
+    """
+    rng = _rng(5)
+    m, n, r, rho = 40, 30, 8, 0.5
+    Wt = rng.standard_normal((m, n))
+    V = rng.standard_normal((n, r))
+    Z = rng.standard_normal((m, r))
+    Lam = rng.standard_normal((m, r)) * 0.1
+    G = O.gram(V, rho)
+    R = O.rhs(Wt, V, Z, Lam, rho)
+    U = O.chol_solve(R, O.cholesky(G))
+    res = np.linalg.norm(U @ G - R) / np.linalg.norm(R)
+    assert res < 1e-12, res
+    A = np.vstack([V, np.sqrt(rho) * np.eye(r)])            # (n + r) x r
+    B = np.hstack([Wt, np.sqrt(rho) * (Z - Lam)]).T          # (n + r) x m
+    Ut, *_ = np.linalg.lstsq(A, B, rcond=None)
+    np.testing.assert_allclose(U, Ut.T, rtol=1e-9, atol=1e-11)
+
+
+def test_half_step_is_stationary_point():
+    # gradient of the U sub-problem vanishes at the returned U; dual is Lam + U - Z.
+    rng = _rng(6)
+    m, n, r, rho = 24, 20, 6, 1.3
+    Wt = rng.standard_normal((m, n))
+    V = rng.standard_normal((n, r))
+    Z = rng.standard_normal((m, r))
+    Lam = rng.standard_normal((m, r)) * 0.2
+    U, Znew, Lnew, a, b = O.admm_half(Wt, V, Z, Lam, rho, 5)
+    grad = -(Wt - U @ V.T) @ V + rho * (U - Z + Lam)
+    assert np.linalg.norm(grad) / np.linalg.norm(Wt @ V) < 1e-12
+    np.testing.assert_allclose(Lnew, Lam + U - Znew, rtol=0, atol=1e-13)
+    # the new proxy lies in C: sign times non-negative rank-1
+    assert np.all(a >= 0) and np.all(b >= 0)
+    np.testing.assert_allclose(np.abs(Znew), np.outer(a, b), rtol=1e-14, atol=0)
+
+
+# --------------------------------------------------------------------- a7
+def test_svid_recovers_exact_sign_rank1():
+    rng = _rng(7)
+    for (m, r) in [(5, 3), (64, 17), (130, 64)]:
+        a = rng.uniform(0.1, 2.0, m)
+        b = rng.uniform(0.1, 2.0, r)
+        S = np.where(rng.random((m, r)) < 0.5, -1.0, 1.0)
+        X = S * np.outer(a, b)
+        Z, aa, bb = O.svid(X, 1)
+        assert np.linalg.norm(Z - X) / np.linalg.norm(X) < 1e-13
+        Z32, _, _ = O.svid(X.astype(np.float32), 1)
+        assert Z32.dtype == np.float32
+        assert np.linalg.norm(Z32 - X) / np.linalg.norm(X) < 1e-6
+
+
+def test_svid_converges_to_top_singular_pair():
+    rng = _rng(8)
+    X = rng.standard_normal((40, 25))
+    Z, a, b = O.svid(X, 500)
+    Uu, s, Vt = np.linalg.svd(np.abs(X))
+    top = s[0] * np.outer(np.abs(Uu[:, 0]), np.abs(Vt[0]))
+    np.testing.assert_allclose(np.outer(a, b), top, rtol=1e-9, atol=1e-12)
+    np.testing.assert_array_equal(np.sign(Z) * np.sign(X) >= 0, True)
+
+
+def test_svid_is_projection_onto_sign_rank1_set():
+    # For the converged fit, no other member of C is closer to X: check against
+    # random members and against perturbations of (a, b).
+    rng = _rng(9)
+    X = rng.standard_normal((12, 7))
+    Z, a, b = O.svid(X, 800)
+    d0 = np.linalg.norm(X - Z)
+    for _ in range(300):
+        S = np.where(rng.random(X.shape) < 0.5, -1.0, 1.0)
+        S = np.where(rng.random(X.shape) < 0.9, np.sign(X) + (X == 0), S)
+        aa = np.abs(a * (1 + 0.05 * rng.standard_normal(a.shape)))
+        bb = np.abs(b * (1 + 0.05 * rng.standard_normal(b.shape)))
+        assert np.linalg.norm(X - S * np.outer(aa, bb)) >= d0 - 1e-12
+
+
+def test_svid_als_objective_monotone():
+    rng = _rng(10)
+    X = rng.standard_normal((30, 20)) ** 3
+    A = np.abs(X)
+    prev = np.inf
+    for T in range(1, 12):
+        _, a, b = O.svid(X, T)
+        f = np.linalg.norm(A - np.outer(a, b))
+        assert f <= prev + 1e-12
+        prev = f
+
+
+def test_svid_zero_and_sign_conventions():
+    Z, a, b = O.svid(np.zeros((4, 3)), 5)
+    assert np.all(Z == 0)
+    X = np.array([[0.0, -0.0, 1.0], [2.0, -3.0, 0.0]])
+    Z, a, b = O.svid(X, 3)
+    # sign(+0) = sign(-0) = +1, so zeros map to +a_i b_j
+    assert Z[0, 0] >= 0 and Z[0, 1] >= 0 and Z[1, 2] >= 0 and Z[1, 1] < 0
+    # a zero row / column of |X| gets a zero magnitude
+    X = np.array([[1.0, 0.0], [0.0, 0.0], [2.0, 0.0]])
+    Z, a, b = O.svid(X, 4)
+    assert a[1] == 0 and b[1] == 0
+    assert np.allclose(np.abs(Z[[0, 2], 0]), [1.0, 2.0])
+
+
+# --------------------------------------------------------------------- fixed point
+def _planted(m, n, r, seed):
+    rng = _rng(seed)
+    s1 = rng.uniform(0.5, 2.0, m)
+    s2 = rng.uniform(0.5, 2.0, n)
+    SU = np.where(rng.random((m, r)) < 0.5, -1.0, 1.0)
+    SV = np.where(rng.random((n, r)) < 0.5, -1.0, 1.0)
+    return s1, s2, SU, SV
+
+
+@pytest.mark.parametrize("m,n,r,c", [(16, 24, 4, 1.0), (33, 20, 7, 2.5), (64, 96, 16, 0.3)])
+def test_planted_exact_fixed_point(m, n, r, c):
+    """A planted Wt = diag(s1) SU SV^T diag(s2), started at U0 = diag(s1) SU c,
+    V0 = diag(s2) SV / c, is a fixed point: the solve returns U0 (U0 G = Wt V0 +
+    rho U0), SVID of a sign x rank-1 matrix returns it, and Lambda stays 0.
+    The reconstruction after balancing is exact."""
+    s1, s2, SU, SV = _planted(m, n, r, 11 + m)
+    Wt = O.reconstruct(s1, SU, SV, s2)
+    U0 = s1[:, None] * SU * c
+    V0 = s2[:, None] * SV / c
+    st = O.init_state(Wt, r, 5, U0=U0, V0=V0)
+    st2 = O.iterate(Wt, st, 1.0, 5, 3)
+    for x0, x1 in [(U0, st2.U), (V0, st2.V)]:
+        assert np.linalg.norm(x1 - x0) / np.linalg.norm(x0) < 1e-12
+    assert np.max(np.abs(st2.Lam_U)) < 1e-12 and np.max(np.abs(st2.Lam_V)) < 1e-12
+    Ub, Vb, s1b, s2b, s1w, s2w, ub, vb, e_wt, e_w = O.finish(
+        Wt, Wt, np.ones(m), np.ones(n), st2.U, st2.V)
+    assert e_wt < 1e-12, e_wt
+    np.testing.assert_array_equal(O.unpack_signs(ub, r), SU)
+    np.testing.assert_array_equal(O.unpack_signs(vb, r), SV)
+
+
+def test_planted_recovery_from_perturbed_start():
+    m, n, r = 48, 40, 4
+    s1, s2, SU, SV = _planted(m, n, r, 12)
+    Wt = O.reconstruct(s1, SU, SV, s2)
+    rng = _rng(13)
+    U0 = s1[:, None] * SU * (1 + 0.01 * rng.standard_normal((m, r)))
+    V0 = s2[:, None] * SV * (1 + 0.01 * rng.standard_normal((n, r)))
+    st = O.init_state(Wt, r, 5, U0=U0, V0=V0)
+    e0 = O.finish(Wt, Wt, np.ones(m), np.ones(n), st.U, st.V)[8]
+    st = O.iterate(Wt, st, 1.0, 5, 100)
+    out = O.finish(Wt, Wt, np.ones(m), np.ones(n), st.U, st.V)
+    # the signs stay exact and the scale error shrinks; convergence to 1e-5 takes
+    # ~300 iterations here, so the gate is a 10x reduction within 100 iterations
+    np.testing.assert_array_equal(O.unpack_signs(out[6], r), SU)
+    assert out[8] < 0.1 * e0, (out[8], e0)
+
+
+# --------------------------------------------------------------------- brute force
+@pytest.mark.parametrize("m,n,r,seed", [(3, 4, 1, 0), (4, 3, 2, 1), (4, 4, 2, 2)])
+def test_method_objective_bounded_by_exhaustive_search(m, n, r, seed):
+    rng = _rng(100 + seed)
+    Wt = rng.standard_normal((m, n))
+    res = O.lbadmm(Wt, np.ones(m), np.ones(n), r, rho=1.0, iters=30, svid_steps=5,
+                   EU=rng.standard_normal((m, r)), EV=rng.standard_normal((n, r)))
+    SU, SV = O.unpack_signs(res.U_bits, r), O.unpack_signs(res.V_bits, r)
+    f_method = brute.objective(Wt, res.s1_wt, SU, SV, res.s2_wt)
+    # the oracle's reported error is the same objective, computed densely
+    assert abs(res.rel_err_wt ** 2 * np.sum(Wt ** 2) - f_method) < 1e-10
+    f_min, *_ = brute.brute_force_min(Wt, r)
+    assert f_method >= f_min - 1e-9
+    assert f_min >= 0
+
+
+def test_brute_force_finds_planted_zero_and_method_reaches_it():
+    m, n, r = 4, 4, 2
+    s1, s2, SU, SV = _planted(m, n, r, 14)
+    Wt = O.reconstruct(s1, SU, SV, s2)
+    f_min, *_ = brute.brute_force_min(Wt, r)
+    assert f_min < 1e-16
+    res = O.lbadmm(Wt, np.ones(m), np.ones(n), r, iters=5,
+                   U0=s1[:, None] * SU, V0=s2[:, None] * SV)
+    assert res.rel_err_wt < 1e-12
+
+
+# --------------------------------------------------------------------- a8 / a9
+def test_balance_invariants():
+    rng = _rng(15)
+    U = rng.standard_normal((20, 6)) * rng.uniform(0.1, 10, 6)
+    V = rng.standard_normal((15, 6)) * rng.uniform(0.1, 10, 6)
+    U[:, 2] = 0.0
+    Ub, Vb, c = O.balance(U, V)
+    assert np.linalg.norm(Ub @ Vb.T - U @ V.T) / np.linalg.norm(U @ V.T) < 1e-13
+    nu, nv = np.linalg.norm(Ub, axis=0), np.linalg.norm(Vb, axis=0)
+    ok = np.arange(6) != 2
+    np.testing.assert_allclose(nu[ok], nv[ok], rtol=1e-13)
+    np.testing.assert_array_equal(Vb[:, 2], V[:, 2])
+    assert np.all(c > 0)
+
+
+def test_row_scale_is_least_squares_scalar():
+    rng = _rng(16)
+    F = rng.standard_normal((10, 9))
+    s = O.row_scales(F)
+    for i in range(10):
+        x, *_ = np.linalg.lstsq(np.sign(F[i])[:, None], F[i], rcond=None)
+        assert abs(x[0] - s[i]) < 1e-14
+
+
+# --------------------------------------------------------------------- a10
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 31), (5, 32), (4, 33), (7, 64), (2, 100), (9, 2970)])
+def test_pack_matches_numpy_packbits(rows, cols):
+    rng = _rng(rows * 1000 + cols)
+    X = rng.standard_normal((rows, cols)).astype(np.float32)
+    X[rng.random(X.shape) < 0.05] = 0.0
+    X[rng.random(X.shape) < 0.05] = -0.0
+    bits = O.pack_signs(X)
+    nw = (cols + 31) // 32
+    pad = np.zeros((rows, nw * 32), bool)
+    pad[:, :cols] = X >= 0
+    ref = np.packbits(pad, axis=1, bitorder="little").view("<u4").reshape(rows, nw)
+    np.testing.assert_array_equal(bits, ref)
+    np.testing.assert_array_equal(O.unpack_signs(bits, cols), np.where(X >= 0, 1.0, -1.0))
+
+
+# --------------------------------------------------------------------- a11
+def test_error_dense_equals_entrywise():
+    rng = _rng(17)
+    m, n, r = 4, 3, 2
+    T = rng.standard_normal((m, n))
+    SU = np.where(rng.random((m, r)) < .5, -1.0, 1.0)
+    SV = np.where(rng.random((n, r)) < .5, -1.0, 1.0)
+    s1, s2 = rng.uniform(.1, 1, m), rng.uniform(.1, 1, n)
+    e = O.rel_error(T, s1, SU, SV, s2)
+    f = brute.objective(T, s1, SU, SV, s2)
+    assert abs(e * e * np.sum(T * T) - f) < 1e-12
+
+
+def test_bpw_pages_arithmetic():
+    g = json.load(open(os.path.join(GOLD, "bpw_pages.json")))
+    ex = g["blog_example"]
+    m, n = ex["m"], ex["n"]
+    # parameters of U and V are r (m + n); the page's 5000 for r = 20 is an
+    # arithmetic slip (100*20 + 200*20 = 6000, ratio 3.33x)
+    assert O.bpw(m, n, ex["r_small"]) * m * n == 6000 != ex["page_claim_params_r_small"]
+    assert abs(m * n / (O.bpw(m, n, ex["r_small"]) * m * n) - 10 / 3) < 1e-12
+    # rank 66 in 16-bit factors is ~1x; binary factors are 16x smaller
+    assert abs(m * n / (O.bpw(m, n, ex["r_one"]) * m * n) - ex["page_claim_ratio_r_one"]) < 0.02
+    assert abs(16.0 / O.bpw(m, n, ex["r_one"]) - ex["page_claim_binary_vs_f16"]) < 0.2
+
+    def linear_shapes(c):
+        h, f, kv = c["hidden"], c["mlp"], c["kv"]
+        return [(h, h), (kv, h), (kv, h), (h, h), (f, h), (f, h), (h, f)]
+
+    c = g["llama2_7b"]
+    bits = 0.0
+    for (mm, nn) in linear_shapes(c):
+        r1 = mm * nn / (mm + nn)                         # 1.00 bit per weight
+        bits += O.bpw(mm, nn, r1) * mm * nn
+    bits *= c["layers"]
+    emb_bytes = 2 * c["vocab"] * c["hidden"] * 2         # fp16 input + output embeddings
+    gb = bits / 8 / 1e9 + emb_bytes / 1e9
+    assert abs(gb - c["page_size_gb"]) < 0.006, gb
+
+    c = g["llama2_70b"]
+    params = c["layers"] * sum(mm * nn for mm, nn in linear_shapes(c))
+    emb = 2 * c["vocab"] * c["hidden"]
+    assert abs((params + emb) * 2 / 1e9 - c["bf16_gb"]) < 0.01
+    r055 = [0.55 * mm * nn / (mm + nn) for mm, nn in linear_shapes(c)]
+    bits = c["layers"] * sum(O.bpw(mm, nn, rr) * mm * nn
+                             for (mm, nn), rr in zip(linear_shapes(c), r055))
+    gb = bits / 8 / 1e9 + emb * 2 / 1e9
+    assert abs(gb - c["page_size_gb"]) < 0.01, gb
+    assert abs(c["bf16_gb"] / gb - c["page_ratio"]) < 0.05
+    # the abstracts' 25.8x corresponds to about 0.50 bit per weight, not 0.55
+    lin_gb = c["bf16_gb"] / c["abstract_ratio"] - emb * 2 / 1e9
+    assert abs(lin_gb * 8e9 / params - 0.50) < 0.01
+
+
+# --------------------------------------------------------------------- whole path
+def test_full_path_tiny_runs_and_improves_on_init():
+    from synth import make_tiny
+    L = make_tiny(32, 48, 8, seed=3, iters=10)
+    res = O.lbadmm(L.W, L.d_out, L.d_in, 8, iters=10, EU=L.EU, EV=L.EV)
+    assert np.isfinite(res.rel_err_wt) and 0 < res.rel_err_wt < 1.0
+    assert res.U_bits.shape == (32, 1) and res.V_bits.shape == (48, 1)
+    # W-space error is the same reconstruction mapped back through the preconditioners
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    E = O.reconstruct(res.s1_wt, O.sgn(res.U), O.sgn(res.V), res.s2_wt)
+    Ew = E / L.d_out.astype(np.float64)[:, None] / L.d_in.astype(np.float64)[None, :]
+    e_w = np.linalg.norm(L.W - Ew) / np.linalg.norm(L.W.astype(np.float64))
+    assert abs(e_w - res.rel_err_w) < 1e-12
+    assert abs(np.linalg.norm(Wt - E) / np.linalg.norm(Wt) - res.rel_err_wt) < 1e-12
+
+
+def test_fp32_mode_tracks_fp64():
+    from synth import make_tiny
+    L = make_tiny(64, 80, 16, seed=5, iters=1)
+    r64 = O.lbadmm(L.W, L.d_out, L.d_in, 16, iters=1, EU=L.EU, EV=L.EV)
+    r32 = O.lbadmm(L.W, L.d_out, L.d_in, 16, iters=1, EU=L.EU, EV=L.EV, dtype=np.float32)
+    assert r32.state.U.dtype == np.float32
+    d = np.linalg.norm(r32.state.U - r64.state.U) / np.linalg.norm(r64.state.U)
+    assert d < 1e-4, d
