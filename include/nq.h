@@ -1,0 +1,209 @@
+/*
+ * nq.h -- C ABI of the LB-ADMM low-rank binary factorisation library (gfx950).
+ *
+ * The library computes, for one linear layer, NanoQuant's Latent Binary ADMM
+ * ("NanoQuant: Efficient Sub-1-Bit Quantization of Large Language Models",
+ * digest at paper.rainbus.top):
+ *   - section 方法步骤详情 (method steps), stage 2 step (2): precondition the
+ *     target, Wt = D_out * W * D_in; run LB-ADMM; after convergence balance
+ *     the magnitudes of the two factors and extract channel scales s1, s2;
+ *     step (3): take signs and pack them into an integer format;
+ *   - section 核心方法 (core method): each iteration (a) fixes V and solves
+ *     the regularised linear system for U through a Cholesky factorisation,
+ *     (b) maps the continuous U to the binary proxy Z with SVID, (c) updates
+ *     the dual variable; then the same for V;
+ *   - section 研究动机 (motivation): the representation
+ *     W ~ s1 * U_{+-1} * V_{+-1}^T * s2.
+ * The pages give names, not formulas; the formulas implemented are:
+ *   G = V^T V + rho I,  U = (Wt V + rho (Z_U - Lam_U)) G^{-1},
+ *   X = U + Lam_U,  Z_U = SVID_T(X) = sign(X) .* (a b^T)  with (a, b) from T
+ *   alternating rank-1 least-squares steps on |X| starting at b = 1,
+ *   Lam_U = X - Z_U;  then the V-half with Wt^T and the new U.
+ *   Finish: c_k = sqrt(||v_k|| / ||u_k||), u_k *= c_k, v_k /= c_k;
+ *   s1_i = mean_k |U_ik|, s2_j = mean_k |V_jk| (Wt space), returned divided
+ *   by d_out, d_in (W space); bits = [x >= 0] of the balanced latents.
+ *
+ * Conventions for every entry point:
+ *   - Matrices are row-major float32 with an explicit leading dimension in
+ *     elements (ld >= number of columns). W is m x n = [out, in].
+ *   - Pointers marked "device" must be device memory of the current HIP
+ *     device, 4-byte aligned (uint32 / float). Host pointers are marked.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued on it; calls return before it finishes
+ *     unless stated otherwise.
+ *   - Nothing throws or aborts across this boundary; errors are status codes.
+ *     Argument errors are detected before any device work is enqueued.
+ *     nq_last_error_message() gives text for the last failure on the calling
+ *     thread.
+ *   - Outputs are owned by the caller; handles own their device workspace.
+ */
+#ifndef NQ_H_
+#define NQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nq_status {
+  NQ_OK = 0,
+  NQ_ERR_INVALID_ARG = 1,           /* bad size, pointer, ld, rho, iters, flags    */
+  NQ_ERR_UNSUPPORTED = 2,           /* no usable gfx950 device / shape not allowed */
+  NQ_ERR_OUT_OF_MEMORY = 3,         /* device allocation failed                    */
+  NQ_ERR_HIP = 4,                   /* a HIP runtime call failed                   */
+  NQ_ERR_NOT_POSITIVE_DEFINITE = 5, /* a Cholesky pivot was <= 0 or not finite     */
+  NQ_ERR_NONFINITE = 6,             /* NaN/Inf in the input or produced on device  */
+  NQ_ERR_BAD_PRECONDITIONER = 7     /* an entry of d_out or d_in is not > 0        */
+} nq_status;
+
+/* Flags of nq_lbadmm_desc.flags. */
+#define NQ_FLAG_COMPUTE_ERROR 0x1u  /* compute rel. reconstruction errors into stats     */
+#define NQ_FLAG_INIT_EXACT    0x2u  /* U0/V0 are the starting latents themselves, not
+                                       standard-normal draws to be scaled by sigma0      */
+#define NQ_FLAG_NO_BALANCE    0x4u  /* skip magnitude balancing (U, V, scales and bits
+                                       then come from the raw latents)                   */
+#define NQ_FLAG_SINGLE_STREAM 0x8u  /* no internal second stream: the r x r chain runs
+                                       on `stream` after the right-hand-side GEMM        */
+
+typedef struct nq_lbadmm_desc {
+  int64_t m;          /* rows of W (output features), >= 1                         */
+  int64_t n;          /* columns of W (input features), >= 1                       */
+  int64_t r;          /* rank of the binary factors, >= 1                          */
+  float rho;          /* ADMM penalty, > 0 and finite                              */
+  int32_t iters;      /* ADMM iterations (each: U-half then V-half), >= 0          */
+  int32_t svid_steps; /* alternating rank-1 steps inside SVID, >= 1                */
+  uint64_t seed;      /* seed of the built-in initialiser (used when U0/V0 are
+                         NULL): Philox4x32-10 counter-based normals               */
+  uint32_t flags;     /* NQ_FLAG_*                                                 */
+} nq_lbadmm_desc;
+
+typedef struct nq_lbadmm_stats {
+  double rel_err_wtilde; /* ||Wt - diag(s1w) S_U S_V^T diag(s2w)||_F / ||Wt||_F
+                            (NaN unless NQ_FLAG_COMPUTE_ERROR)                       */
+  double rel_err_w;      /* same in W space with the returned s1, s2               */
+  double sumsq_wtilde;   /* ||Wt||_F^2                                              */
+  double sigma0;         /* init scale (||Wt||_F^2 / (m n r))^(1/4)                 */
+  int64_t potrf_info;    /* 0, or 1 + the first column whose Cholesky pivot was
+                            <= 0 / not finite (over all factorisations of the run) */
+  int32_t nonfinite;     /* nonzero if NaN/Inf was seen in W, the preconditioned
+                            target or the final latents                            */
+  int32_t bad_precond;   /* nonzero if some d_out / d_in entry was not > 0          */
+  float elapsed_ms;      /* device time of the whole run (HIP events)               */
+  int32_t iters_done;
+  int32_t reserved;
+} nq_lbadmm_stats;
+
+typedef struct nq_lbadmm* nq_lbadmm_t;
+
+/* Create a factorisation handle and allocate all of its device workspace on
+ * the current HIP device. Sizes are rounded up internally to tile multiples
+ * (256 for m and n, 128 for r); padding is zero and never visible to callers.
+ * Returns NQ_ERR_INVALID_ARG for a NULL argument or a desc field out of
+ * range, NQ_ERR_UNSUPPORTED when the current device is not gfx950,
+ * NQ_ERR_OUT_OF_MEMORY / NQ_ERR_HIP on allocation failure (*out = NULL). */
+nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out);
+
+/* Device bytes the handle for `desc` allocates (host output). */
+nq_status nq_lbadmm_workspace_bytes(const nq_lbadmm_desc* desc, size_t* bytes);
+
+/* Run the whole per-layer path on `stream`:
+ *   precondition -> init -> `iters` ADMM iterations -> balance -> scales ->
+ *   sign packing (-> errors if NQ_FLAG_COMPUTE_ERROR).
+ * Inputs (device): W m x n (ld ldw >= n), d_out (m), d_in (n), all > 0.
+ *   U0 (m x r, ld r) and V0 (n x r, ld r): standard-normal draws scaled by
+ *   sigma0 on device, or with NQ_FLAG_INIT_EXACT the starting latents as is.
+ *   Both NULL: draws come from the built-in Philox generator and desc.seed.
+ *   Exactly one NULL is NQ_ERR_INVALID_ARG.
+ * Outputs (device, caller-owned, contiguous):
+ *   U (m x r) and V (n x r): the balanced latents;
+ *   s1 (m), s2 (n): W-space scales, so W ~ diag(s1) sign(U) sign(V)^T diag(s2);
+ *   U_bits (m x ceil(r/32)) and V_bits (n x ceil(r/32)) uint32 words, bit k of
+ *   word w of row i = [latent(i, 32 w + k) >= 0], unused high bits zero.
+ *   Any output pointer may be NULL to skip it.
+ * stats (host, nullable): if non-NULL the call waits for `stream`, fills it
+ *   and returns NQ_ERR_NONFINITE / NQ_ERR_BAD_PRECONDITIONER /
+ *   NQ_ERR_NOT_POSITIVE_DEFINITE when the device saw such data. With
+ *   stats == NULL the call is asynchronous and nq_lbadmm_query() reports.
+ * The call allocates nothing. A handle is not thread-safe and must not run
+ * twice concurrently; distinct handles may run concurrently on distinct
+ * streams. */
+nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw,
+                        const float* d_out, const float* d_in,
+                        const float* U0, const float* V0,
+                        float* U, float* V, float* s1, float* s2,
+                        uint32_t* U_bits, uint32_t* V_bits,
+                        nq_lbadmm_stats* stats, void* stream);
+
+/* Wait for the handle's last run on its stream and fill `stats` (host);
+ * returns the same data-dependent status as a run with stats != NULL. */
+nq_status nq_lbadmm_query(nq_lbadmm_t h, nq_lbadmm_stats* stats);
+
+/* Copy the ADMM state left by the last run (before balancing) into caller
+ * buffers (device, contiguous, each nullable): U (m x r), V (n x r), and the
+ * proxies and scaled duals Z_U, Lam_U (m x r), Z_V, Lam_V (n x r).
+ * Enqueued on `stream`. */
+nq_status nq_lbadmm_get_state(nq_lbadmm_t h, float* U, float* V,
+                              float* Z_U, float* Lam_U, float* Z_V, float* Lam_V,
+                              void* stream);
+
+/* Free the handle and its workspace (NULL is ignored). Waits for its work. */
+void nq_lbadmm_destroy(nq_lbadmm_t h);
+
+/* Pack sign bits ("方法步骤详情" step (3): signs packed to an integer format).
+ * X (device) rows x cols, ld ldx >= cols; bits (device) rows x ld_words uint32,
+ * ld_words >= ceil(cols/32). bit k of word w of row i = [X(i, 32 w + k) >= 0]
+ * (so +0 and -0 give 1, NaN gives 0); bits beyond cols in the last word are 0;
+ * words beyond ceil(cols/32) are not written. rows == 0 or cols == 0 is a
+ * no-op. One kernel, no allocation. */
+nq_status nq_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                        uint32_t* bits, int64_t ld_words, void* stream);
+
+/* ---- building blocks (the same kernels the run uses; for tests and tools) ----
+ * These take caller buffers of any shape, copy into zero-padded temporaries
+ * allocated with hipMallocAsync on `stream` (freed on the same stream), run
+ * the kernels, and copy results out. They are not meant for the hot path. */
+
+/* Wt = d_out_i * (W_ij * d_in_j) in float32, the two products rounded in that
+ * order ("方法步骤详情": Wt = D_out W D_in). Wt (device) m x n, ld ldwt. */
+nq_status nq_op_precondition(const float* W, int64_t ldw, int64_t m, int64_t n,
+                             const float* d_out, const float* d_in,
+                             float* Wt, int64_t ldwt, void* stream);
+
+/* G = A^T A + rho I for A (device) rows x cols (ld lda); G (device) cols x cols
+ * (ld ldg), full symmetric ("核心方法" (a): the regularised system matrix). */
+nq_status nq_op_gram(const float* A, int64_t rows, int64_t cols, int64_t lda,
+                     float rho, float* G, int64_t ldg, void* stream);
+
+/* C = A B + rho P for A rows x k (lda), B k x cols (ldb), P rows x cols (ldp,
+ * nullable = 0); C rows x cols (ldc). The right-hand side of "核心方法" (a). */
+nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ldb,
+                         const float* P, int64_t ldp, float rho,
+                         float* C, int64_t ldc,
+                         int64_t rows, int64_t cols, int64_t k, void* stream);
+
+/* Cholesky factorisation G = L L^T of an SPD r x r matrix (lower triangle of
+ * G read) and the inverse Ginv = L^-T L^-1 (full symmetric). L (device,
+ * nullable) receives the factor with zeros above the diagonal. *info (host)
+ * is 0 or 1 + the first failing column; the call waits for `stream`. */
+nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg,
+                                 float* L, int64_t ldl, float* Ginv, int64_t ldgi,
+                                 int64_t* info, void* stream);
+
+/* SVID ("核心方法" (b), "技术新颖性"): Z = sign(X) .* (a b^T) with T rank-1
+ * alternating steps on |X| from b = 1. X, Z (device) rows x cols (ld ldx,
+ * ldz); a (rows) and b (cols) device, nullable. */
+nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                     int32_t T, float* Z, int64_t ldz, float* a, float* b,
+                     void* stream);
+
+const char* nq_status_string(nq_status s);
+const char* nq_last_error_message(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t nq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NQ_H_ */

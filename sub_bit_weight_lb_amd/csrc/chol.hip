@@ -1,0 +1,201 @@
+// Blocked Cholesky factorisation with the inverse factor: G = L L^T and
+// M = L^-1, for the ridge-regularised system matrix G = V^T V + rho I of the
+// regularised solve (NanoQuant digest, section 核心方法, step (a): the linear
+// system is solved through a Cholesky factorisation; the implementation blog,
+// section 待办事项, names this factorisation as where LB-ADMM spends its time).
+//
+// Right-looking, block size 64, three launches per block column k:
+//   diag(k):   one workgroup factors the 64 x 64 diagonal block in LDS by
+//              outer-product elimination, applying the same row operations to
+//              an identity block, which yields both L_kk and M_kk = L_kk^-1
+//              with one barrier per column.
+//   panel(k):  L_ik = A_ik M_kk^T for i > k, and row k of M:
+//              M_kj = -M_kk S_kj for j < k (S_kj accumulated in M's block).
+//   update(k): trailing update A_ij -= L_ik L_jk^T (i >= j > k) and the
+//              inverse accumulators S_ij += L_ik M_kj (i > k >= j).
+// The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
+// M_ij = -M_ii sum_{l = j..i-1} L_il M_lj, which the S accumulators hold.
+// All 64 x 64 x 64 block products run on the 32x32x2 fp32 MFMA with both
+// operands staged k-contiguous in LDS.
+#include "common.h"
+#include <climits>
+
+namespace nq {
+namespace {
+
+constexpr int NB = kNB;   // 64
+constexpr int NT = 256;
+constexpr int LS = NB + 4;  // LDS row stride for MFMA tiles
+
+// out = alpha * X op(Y) + beta * out on 64 x 64 blocks (ld = rp for all).
+// op(Y) = Y^T if TRANS else Y.
+template <bool TRANS>
+__device__ void block_mm(const float* __restrict__ X, const float* __restrict__ Y, float* out,
+                         int rp, float alpha, float beta, float* Xs, float* Ys) {
+  const int tid = threadIdx.x;
+  // X: 64 rows x 16 float4 = 1024 float4, 4 per thread, stored as is ([p][c]).
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = tid + NT * q;
+    const int row = idx >> 4, c4 = idx & 15;
+    *(f32x4*)&Xs[row * LS + c4 * 4] = *(const f32x4*)&X[(int64_t)row * rp + c4 * 4];
+  }
+  if (TRANS) {
+    // B operand (k = c, n = q) = Y[q][c]: Y as is, [q][c].
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + NT * q;
+      const int row = idx >> 4, c4 = idx & 15;
+      *(f32x4*)&Ys[row * LS + c4 * 4] = *(const f32x4*)&Y[(int64_t)row * rp + c4 * 4];
+    }
+  } else {
+    // B operand (k = c, n = q) = Y[c][q]: transpose to [q][c] while staging.
+    const int col = tid & 63, cq = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c0 = (cq + 4 * j) * 4;
+      f32x4 v = {Y[(int64_t)(c0 + 0) * rp + col], Y[(int64_t)(c0 + 1) * rp + col],
+                 Y[(int64_t)(c0 + 2) * rp + col], Y[(int64_t)(c0 + 3) * rp + col]};
+      *(f32x4*)&Ys[col * LS + c0] = v;
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int half = lane >> 5, l32 = lane & 31;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  const float* xs = Xs + (wm * 32 + l32) * LS + 4 * half;
+  const float* ys = Ys + (wn * 32 + l32) * LS + 4 * half;
+#pragma unroll
+  for (int kc = 0; kc < NB; kc += 8) {
+    const f32x4 a = *(const f32x4*)&xs[kc];
+    const f32x4 b = *(const f32x4*)&ys[kc];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = wm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+    const int col = wn * 32 + l32;
+    float* o = out + (int64_t)row * rp + col;
+    const float prev = beta != 0.0f ? *o : 0.0f;
+    *o = alpha * acc[v] + beta * prev;
+  }
+}
+
+__global__ __launch_bounds__(NT) void chol_diag_kernel(float* A, float* M, int rp, int k,
+                                                       int r_real, DevStats* st) {
+  __shared__ float T[NB][NB + 1];
+  __shared__ float E[NB][NB + 1];
+  const int tid = threadIdx.x;
+  const int base = k * NB;
+  for (int idx = tid; idx < NB * NB; idx += NT) {
+    const int i = idx >> 6, c = idx & 63;
+    T[i][c] = A[(int64_t)(base + i) * rp + base + c];
+    E[i][c] = (i == c) ? 1.0f : 0.0f;
+  }
+  __syncthreads();
+  for (int j = 0; j < NB; ++j) {
+    const float d = T[j][j];
+    if (tid == 0 && !(d > 0.0f && isfinite(d)) && base + j < r_real)
+      atomicMin(&st->potrf_info, base + j + 1);
+    const float inv = 1.0f / d;
+    for (int idx = (j + 1) * NB + tid; idx < NB * NB; idx += NT) {
+      const int i = idx >> 6, c = idx & 63;
+      if (c <= i) {
+        const float l = T[i][j] * inv;
+        if (c <= j) E[i][c] -= l * E[j][c];
+        else T[i][c] -= l * T[j][c];
+      }
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < NB * NB; idx += NT) {
+    const int i = idx >> 6, c = idx & 63;
+    float lv = 0.0f, mv = 0.0f;
+    if (c <= i) {
+      lv = T[i][c] / sqrtf(T[c][c]);
+      mv = E[i][c] / sqrtf(T[i][i]);
+    }
+    A[(int64_t)(base + i) * rp + base + c] = lv;
+    M[(int64_t)(base + i) * rp + base + c] = mv;
+  }
+}
+
+__global__ __launch_bounds__(NT) void chol_panel_kernel(float* A, float* M, int rp, int k) {
+  __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
+  __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
+  const int R = rp / NB;
+  const int nL = R - k - 1;
+  const int b = blockIdx.x;
+  const int64_t kk = (int64_t)k * NB;
+  if (b < nL) {
+    const int64_t i0 = (int64_t)(k + 1 + b) * NB;
+    float* Aik = A + i0 * rp + kk;
+    // L_ik = A_ik M_kk^T (written in place; the products read Aik into LDS first)
+    block_mm<true>(Aik, M + kk * rp + kk, Aik, rp, 1.0f, 0.0f, Xs, Ys);
+  } else {
+    const int64_t j0 = (int64_t)(b - nL) * NB;
+    float* Mkj = M + kk * rp + j0;
+    // M_kj = -M_kk S_kj
+    block_mm<false>(M + kk * rp + kk, Mkj, Mkj, rp, -1.0f, 0.0f, Xs, Ys);
+  }
+}
+
+__global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, int rp, int k) {
+  __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
+  __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
+  const int R = rp / NB;
+  const int n = R - k - 1;
+  const int nA = n * (n + 1) / 2;
+  const int b = blockIdx.x;
+  const int64_t kk = (int64_t)k * NB;
+  if (b < nA) {
+    int ii = (int)((sqrtf(8.0f * b + 1.0f) - 1.0f) * 0.5f);
+    while ((ii + 1) * (ii + 2) / 2 <= b) ++ii;
+    while (ii * (ii + 1) / 2 > b) --ii;
+    const int jj = b - ii * (ii + 1) / 2;
+    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
+    // A_ij -= L_ik L_jk^T
+    block_mm<true>(A + i0 * rp + kk, A + j0 * rp + kk, A + i0 * rp + j0, rp, -1.0f, 1.0f, Xs, Ys);
+  } else {
+    const int s = b - nA;
+    const int ii = s / (k + 1), jj = s % (k + 1);
+    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)jj * NB;
+    // S_ij += L_ik M_kj
+    block_mm<false>(A + i0 * rp + kk, M + kk * rp + j0, M + i0 * rp + j0, rp, 1.0f, 1.0f, Xs, Ys);
+  }
+}
+
+__global__ void zero_upper_kernel(float* A, int rp) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rp * rp) return;
+  const int i = (int)(idx / rp), j = (int)(idx % rp);
+  if (j > i) A[idx] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real, DevStats* st,
+                                   bool zero_upper_L, hipStream_t s) {
+  if (rp % NB) return hipErrorInvalidValue;
+  const int R = rp / NB;
+  hipError_t e = launch_zero(M, (size_t)rp * rp, s);
+  if (e != hipSuccess) return e;
+  for (int k = 0; k < R; ++k) {
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(1), dim3(NT), 0, s, A, M, rp, k, r_real, st);
+    const int np = (R - k - 1) + k;
+    if (np > 0) hipLaunchKernelGGL(chol_panel_kernel, dim3(np), dim3(NT), 0, s, A, M, rp, k);
+    const int n = R - k - 1;
+    const int nu = n * (n + 1) / 2 + n * (k + 1);
+    if (nu > 0) hipLaunchKernelGGL(chol_update_kernel, dim3(nu), dim3(NT), 0, s, A, M, rp, k);
+  }
+  if (!zero_upper_L) return hipGetLastError();
+  const int64_t tot = (int64_t)rp * rp;
+  hipLaunchKernelGGL(zero_upper_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, A, rp);
+  return hipGetLastError();
+}
+
+}  // namespace nq

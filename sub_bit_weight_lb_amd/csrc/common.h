@@ -1,0 +1,139 @@
+// Internal declarations shared by the LB-ADMM kernels and the host driver.
+// gfx950 only: wave64, fp32 MFMA (v_mfma_f32_32x32x2_f32), 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nq {
+
+// Padded sizes: every workspace matrix is stored zero-padded to these
+// multiples so that the tiled kernels need no bounds checks.
+constexpr int kPadMN = 256;  // m and n (rows of Wt / Wt^T / U / V)
+constexpr int kPadR = 128;   // r (rank)
+
+inline int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+// Device-side status shared by all kernels of one run.
+struct DevStats {
+  double sumsq_wt;      // ||Wt||_F^2
+  double sumsq_w;       // ||W||_F^2
+  double sigma0;        // init scale
+  double err2_wt;       // squared reconstruction error, Wt space
+  double err2_w;        // squared reconstruction error, W space
+  int nonfinite;        // NaN/Inf seen
+  int bad_precond;      // some d <= 0
+  int potrf_info;       // 0 or 1 + first failing pivot column (min over runs)
+  int pad;
+};
+
+// ---------------------------------------------------------------- GEMM
+enum GemmEpilogue : int {
+  kEpiPlain = 0,   // C = A B
+  kEpiRhs = 1,     // C = A B + rho P                (P ld = ldc)
+  kEpiSolve = 2,   // C = A B;  X = C + X  (X holds Lambda on entry, ld = ldc)
+};
+struct GemmArgs {
+  const float* A; int64_t lda;   // M x K
+  const float* B; int64_t ldb;   // K x N
+  float* C; int64_t ldc;         // M x N
+  const float* P;                // kEpiRhs
+  float* X;                      // kEpiSolve
+  float rho;
+  int M, N, K;
+};
+// M % 256 == 0, N % 128 == 0, K % 32 == 0, ld multiples of 4, 16-byte aligned.
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
+
+// ---------------------------------------------------------------- SYRK / LAUUM
+// Partial Gram tiles: part[c] (rp x rp, ld rp), lower 128 x 128 tiles only,
+// chunk c covering k in [c*kchunk, (c+1)*kchunk) of A (K x rp, ld lda).
+// If tri_kstart, tile row I only uses k >= 128*I (A lower triangular).
+hipError_t launch_syrk_partial(const float* A, int64_t lda, int K, int rp, int kchunk,
+                               bool tri_kstart, float* part, hipStream_t s);
+// G = sum_c part[c] + rho I, written full-symmetric (ld ldg).
+hipError_t launch_gram_reduce(const float* part, int nchunks, int rp, float rho,
+                              float* G, int64_t ldg, hipStream_t s);
+
+// ---------------------------------------------------------------- Cholesky / inverse
+constexpr int kNB = 64;  // block size of the blocked Cholesky
+// In place on A (rp x rp, ld rp, full symmetric on entry): lower triangle becomes
+// L (upper triangle zeroed only if zero_upper_L); M (rp x rp) becomes L^-1
+// (lower, zero upper). st->potrf_info gets min(1 + failing column).
+hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
+                                   DevStats* st, bool zero_upper_L, hipStream_t s);
+
+// ---------------------------------------------------------------- SVID
+struct SvidWork {
+  float* a;        // rows_pad
+  float* b;        // rp
+  float* colpart;  // nchunks x rp
+  float* aapart;   // nchunks
+  float* bbpart;   // rp / 128
+};
+int svid_nchunks(int rows_pad);
+// mode 0: init (P = Z, X left as is), mode 1: update (X <- X - Z, P = 2Z - X_old),
+// mode 2: plain (Z written to P; X untouched).
+hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int T,
+                       int mode, const SvidWork& w, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise
+hipError_t launch_stats_init(DevStats* st, hipStream_t s);
+hipError_t launch_check_precond(const float* d_out, int64_t m, const float* d_in, int64_t n,
+                                DevStats* st, hipStream_t s);
+// Wt (mp x np, ld np) and optionally WtT (np x mp, ld mp); partial sums of squares.
+int precondition_nblocks(int mp, int np_);
+hipError_t launch_precondition(const float* W, int64_t ldw, int64_t m, int64_t n,
+                               const float* d_out, const float* d_in, float* Wt, float* WtT,
+                               int mp, int np_, double* part_wt, double* part_w,
+                               DevStats* st, hipStream_t s);
+hipError_t launch_finalize_norms(const double* part_wt, const double* part_w, int nparts,
+                                 int64_t m, int64_t n, int64_t r, DevStats* st, hipStream_t s);
+// Dst (rows_pad x rp) = scale * Src (rows x r, ld lds) zero padded; scale = sigma0
+// (from st) when use_sigma, else 1. Dst2 (nullable) gets the same values.
+hipError_t launch_init_copy(const float* src, int64_t rows, int64_t r, int64_t lds,
+                            float* dst, float* dst2, int rows_pad, int rp, bool use_sigma,
+                            const DevStats* st, hipStream_t s);
+// Philox4x32-10 standard normals scaled by sigma0 into dst/dst2 (rows x r real part).
+hipError_t launch_init_philox(uint64_t seed, uint32_t stream_id, int64_t rows, int64_t r,
+                              float* dst, float* dst2, int rows_pad, int rp,
+                              const DevStats* st, hipStream_t s);
+hipError_t launch_zero(float* p, size_t n, hipStream_t s);
+// out (rows x r, ld r) = A + B for padded A, B (ld rp).
+hipError_t launch_add_compact(const float* A, const float* B, int64_t rows, int64_t r, int rp,
+                              float* out, hipStream_t s);
+// A[i][i] = val for from <= i < to (ld lda).
+hipError_t launch_set_diag(float* A, int64_t lda, int from, int to, float val, hipStream_t s);
+
+// ---------------------------------------------------------------- finish
+// column sums of squares of F (rows_pad x rp) -> colpart (nchunks x rp)
+hipError_t launch_colsumsq(const float* F, int rows_pad, int rp, float* colpart, hipStream_t s);
+// c_k = sqrt(nv_k / nu_k) (1 if either is 0, or if !balance)
+hipError_t launch_balance_coef(const float* partU, int nchU, const float* partV, int nchV,
+                               int rp, bool balance, float* c, hipStream_t s);
+// F' = F * c_k (or F / c_k when divide): writes out (rows x r, ld r, nullable),
+// scale_out_i = mean_k |F'_ik| / d_i (nullable), scale_wt_i = mean_k |F'_ik|,
+// bits (rows x ceil(r/32), nullable), sign8 (rows_pad x rp int8, zero padded).
+hipError_t launch_apply_finish(const float* F, int64_t rows, int rows_pad, int rp, int64_t r,
+                               const float* c, bool divide, const float* d,
+                               float* out, float* scale_out, float* scale_wt,
+                               uint32_t* bits, int8_t* sign8, DevStats* st, hipStream_t s);
+// Squared errors into st->err2_wt / st->err2_w (deterministic).
+int error_nparts(int mp, int np_);
+// s1w/s2w: Wt-space scales (padded, zero beyond m/n); s1/s2: W-space scales (m, n).
+// parts: 2 * error_nparts doubles.
+hipError_t launch_error(const int8_t* SU, const int8_t* SV, int mp, int np_, int rp,
+                        const float* s1w, const float* s2w, const float* Wt,
+                        const float* W, int64_t ldw, int64_t m, int64_t n,
+                        const float* s1, const float* s2, double* parts,
+                        DevStats* st, hipStream_t s);
+
+// ---------------------------------------------------------------- packing
+hipError_t launch_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
+                             uint32_t* bits, int64_t ld_words, hipStream_t s);
+
+}  // namespace nq

@@ -1,0 +1,428 @@
+// Host driver and C ABI of the LB-ADMM library (declared in include/nq.h).
+//
+// One handle = one layer shape. create() allocates every workspace buffer
+// once (one device allocation, zero-padded layouts); run() only enqueues
+// kernels and never allocates. Per half-iteration the r x r chain
+// (Gram -> Cholesky + inverse factor -> L^-T L^-1) depends only on the other
+// factor, as does the right-hand-side GEMM, so the chain runs on an internal
+// second stream while the GEMM runs on the caller's stream; the solve GEMM
+// joins them. SVID of one half overlaps the next half's chain.
+#include "nq.h"
+#include "abi.h"
+#include "common.h"
+
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <string>
+
+using namespace nq;
+
+namespace {
+
+thread_local std::string g_err;
+
+nq_status fail(nq_status s, const std::string& msg) { return set_error(s, msg); }
+nq_status hip_fail(hipError_t e, const char* what) { return hip_error(e, what); }
+
+#define HIPCHK(expr) NQ_HIPCHK(expr)
+
+constexpr uint32_t kKnownFlags =
+    NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT | NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM;
+
+nq_status check_desc(const nq_lbadmm_desc* d) {
+  if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
+  if (d->m < 1 || d->n < 1 || d->r < 1) return fail(NQ_ERR_INVALID_ARG, "m, n, r must be >= 1");
+  if (d->m > (1 << 22) || d->n > (1 << 22) || d->r > (1 << 16))
+    return fail(NQ_ERR_INVALID_ARG, "m, n must be <= 2^22 and r <= 2^16");
+  if (!(d->rho > 0.0f) || !std::isfinite(d->rho))
+    return fail(NQ_ERR_INVALID_ARG, "rho must be finite and > 0");
+  if (d->iters < 0) return fail(NQ_ERR_INVALID_ARG, "iters must be >= 0");
+  if (d->svid_steps < 1 || d->svid_steps > 10000)
+    return fail(NQ_ERR_INVALID_ARG, "svid_steps must be in [1, 10000]");
+  if (d->flags & ~kKnownFlags) return fail(NQ_ERR_INVALID_ARG, "unknown flag bits");
+  return NQ_OK;
+}
+
+nq_status check_device(int* dev) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count < 1) {
+    g_err = "no HIP device available";
+    return NQ_ERR_UNSUPPORTED;
+  }
+  HIPCHK(hipGetDevice(dev));
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, *dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(NQ_ERR_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", need gfx950");
+  return NQ_OK;
+}
+
+// Split-K choice for the Gram kernel: enough workgroups to cover the chip,
+// chunks of at least 256 rows, at most 4 chunks.
+void gram_split(int K, int rp, int* nch, int* kchunk) {
+  const int R = rp / 128;
+  const int tiles = R * (R + 1) / 2;
+  int c = (512 + tiles - 1) / tiles;
+  c = std::max(1, std::min(c, std::min(4, K / 256)));
+  int kc = (int)round_up((K + c - 1) / c, 32);
+  *kchunk = kc;
+  *nch = (K + kc - 1) / kc;
+}
+
+void lauum_split(int rp, int* nch, int* kchunk) {
+  int c = std::max(1, std::min(4, rp / 128));
+  int kc = (int)round_up((rp + c - 1) / c, 32);
+  *kchunk = kc;
+  *nch = (rp + kc - 1) / kc;
+}
+
+struct Arena {
+  size_t off = 0;
+  template <class T>
+  size_t take(size_t count) {
+    const size_t o = off;
+    off += round_up((int64_t)(count * sizeof(T)), 256);
+    return o;
+  }
+};
+
+}  // namespace
+
+namespace nq {
+nq_status set_error(nq_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+nq_status hip_error(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return e == hipErrorOutOfMemory ? NQ_ERR_OUT_OF_MEMORY : NQ_ERR_HIP;
+}
+}  // namespace nq
+
+struct nq_lbadmm {
+  nq_lbadmm_desc d{};
+  int device = 0;
+  int mp = 0, np_ = 0, rp = 0;
+  int gU_nch = 1, gU_kc = 32, gV_nch = 1, gV_kc = 32, l_nch = 1, l_kc = 32;
+  char* base = nullptr;
+  size_t bytes = 0;
+  float *Wt, *WtT, *U, *V, *LamU, *PU, *LamV, *PV, *R, *G, *Minv, *Ginv, *gpart;
+  SvidWork svU, svV;
+  double *part_wt, *part_w, *err_parts;
+  float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
+  int8_t *SU, *SV;
+  DevStats* st;
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool has_run = false;
+};
+
+namespace {
+
+// Lay out (or just size, when h->base is null) every workspace buffer.
+size_t layout(nq_lbadmm* h) {
+  const int64_t mp = h->mp, np_ = h->np_, rp = h->rp;
+  const int64_t mx = std::max(mp, np_);
+  const int gch = std::max(std::max(h->gU_nch, h->gV_nch), h->l_nch);
+  Arena a;
+  size_t o_Wt = a.take<float>(mp * np_), o_WtT = a.take<float>(np_ * mp);
+  size_t o_U = a.take<float>(mp * rp), o_V = a.take<float>(np_ * rp);
+  size_t o_LamU = a.take<float>(mp * rp), o_PU = a.take<float>(mp * rp);
+  size_t o_LamV = a.take<float>(np_ * rp), o_PV = a.take<float>(np_ * rp);
+  size_t o_R = a.take<float>(mx * rp);
+  size_t o_G = a.take<float>(rp * rp), o_M = a.take<float>(rp * rp), o_Gi = a.take<float>(rp * rp);
+  size_t o_gp = a.take<float>((size_t)gch * rp * rp);
+  const int nchU = svid_nchunks((int)mp), nchV = svid_nchunks((int)np_);
+  size_t o_sUa = a.take<float>(mp), o_sUb = a.take<float>(rp),
+         o_sUc = a.take<float>((size_t)nchU * rp), o_sUaa = a.take<float>(nchU),
+         o_sUbb = a.take<float>(rp / 128);
+  size_t o_sVa = a.take<float>(np_), o_sVb = a.take<float>(rp),
+         o_sVc = a.take<float>((size_t)nchV * rp), o_sVaa = a.take<float>(nchV),
+         o_sVbb = a.take<float>(rp / 128);
+  const int npre = precondition_nblocks((int)mp, (int)np_);
+  size_t o_pwt = a.take<double>(npre), o_pw = a.take<double>(npre);
+  size_t o_err = a.take<double>(2 * (size_t)error_nparts((int)mp, (int)np_));
+  size_t o_cpU = a.take<float>((size_t)nchU * rp), o_cpV = a.take<float>((size_t)nchV * rp);
+  size_t o_cb = a.take<float>(rp), o_s1w = a.take<float>(mp), o_s2w = a.take<float>(np_);
+  size_t o_s1c = a.take<float>(mp), o_s2c = a.take<float>(np_);
+  size_t o_SU = a.take<int8_t>(mp * rp), o_SV = a.take<int8_t>(np_ * rp);
+  size_t o_st = a.take<DevStats>(1);
+  if (h->base) {
+    char* b = h->base;
+    h->Wt = (float*)(b + o_Wt); h->WtT = (float*)(b + o_WtT);
+    h->U = (float*)(b + o_U); h->V = (float*)(b + o_V);
+    h->LamU = (float*)(b + o_LamU); h->PU = (float*)(b + o_PU);
+    h->LamV = (float*)(b + o_LamV); h->PV = (float*)(b + o_PV);
+    h->R = (float*)(b + o_R);
+    h->G = (float*)(b + o_G); h->Minv = (float*)(b + o_M); h->Ginv = (float*)(b + o_Gi);
+    h->gpart = (float*)(b + o_gp);
+    h->svU = SvidWork{(float*)(b + o_sUa), (float*)(b + o_sUb), (float*)(b + o_sUc),
+                      (float*)(b + o_sUaa), (float*)(b + o_sUbb)};
+    h->svV = SvidWork{(float*)(b + o_sVa), (float*)(b + o_sVb), (float*)(b + o_sVc),
+                      (float*)(b + o_sVaa), (float*)(b + o_sVbb)};
+    h->part_wt = (double*)(b + o_pwt); h->part_w = (double*)(b + o_pw);
+    h->err_parts = (double*)(b + o_err);
+    h->colpartU = (float*)(b + o_cpU); h->colpartV = (float*)(b + o_cpV);
+    h->cbal = (float*)(b + o_cb); h->s1w = (float*)(b + o_s1w); h->s2w = (float*)(b + o_s2w);
+    h->s1c = (float*)(b + o_s1c); h->s2c = (float*)(b + o_s2c);
+    h->SU = (int8_t*)(b + o_SU); h->SV = (int8_t*)(b + o_SV);
+    h->st = (DevStats*)(b + o_st);
+  }
+  return a.off;
+}
+
+void plan(nq_lbadmm* h) {
+  h->mp = (int)round_up(h->d.m, kPadMN);
+  h->np_ = (int)round_up(h->d.n, kPadMN);
+  h->rp = (int)round_up(h->d.r, kPadR);
+  gram_split(h->np_, h->rp, &h->gU_nch, &h->gU_kc);  // U-half: Gram of V, K = n
+  gram_split(h->mp, h->rp, &h->gV_nch, &h->gV_kc);   // V-half: Gram of U, K = m
+  lauum_split(h->rp, &h->l_nch, &h->l_kc);
+}
+
+struct Half {
+  const float* Wside;  // M x K (padded, ld K)
+  int M, K;            // rows of the factor being solved, rows of the other factor
+  const float* other;  // K x rp
+  float* out;          // M x rp
+  float* Lam;          // M x rp
+  float* P;            // M x rp
+  const SvidWork* sv;
+  int g_nch, g_kc;
+};
+
+nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
+  const int rp = h->rp;
+  hipStream_t cs = overlap ? h->aux : s;
+  if (overlap) HIPCHK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
+  // r x r chain: G = other^T other + rho I, L and L^-1, G^-1 = L^-T L^-1
+  HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, cs));
+  HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, cs));
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, cs));
+  HIPCHK(launch_syrk_partial(h->Minv, rp, rp, rp, h->l_kc, true, h->gpart, cs));
+  HIPCHK(launch_gram_reduce(h->gpart, h->l_nch, rp, 0.0f, h->Ginv, rp, cs));
+  if (overlap) HIPCHK(hipEventRecord(h->ev_join, h->aux));
+  // R = Wside other + rho (Z - Lam)
+  GemmArgs g{};
+  g.A = x.Wside; g.lda = x.K; g.B = x.other; g.ldb = rp; g.C = h->R; g.ldc = rp;
+  g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
+  HIPCHK(launch_gemm(g, kEpiRhs, s));
+  if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
+  // out = R G^-1, X = out + Lam (into Lam)
+  GemmArgs q{};
+  q.A = h->R; q.lda = rp; q.B = h->Ginv; q.ldb = rp; q.C = x.out; q.ldc = rp;
+  q.X = x.Lam; q.M = x.M; q.N = rp; q.K = rp;
+  HIPCHK(launch_gemm(q, kEpiSolve, s));
+  if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
+  // Z = SVID(X); Lam = X - Z; P = Z - Lam
+  HIPCHK(launch_svid(x.Lam, x.P, x.M, rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, s));
+  return NQ_OK;
+}
+
+nq_status status_from(const DevStats& hs) {
+  if (hs.bad_precond) return fail(NQ_ERR_BAD_PRECONDITIONER, "an entry of d_out or d_in is not > 0");
+  if (hs.nonfinite) return fail(NQ_ERR_NONFINITE, "NaN or Inf in the input or the result");
+  if (hs.potrf_info != 0x7fffffff)
+    return fail(NQ_ERR_NOT_POSITIVE_DEFINITE,
+                "Cholesky pivot <= 0 at column " + std::to_string(hs.potrf_info - 1));
+  return NQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nq_status_string(nq_status s) {
+  switch (s) {
+    case NQ_OK: return "NQ_OK";
+    case NQ_ERR_INVALID_ARG: return "NQ_ERR_INVALID_ARG";
+    case NQ_ERR_UNSUPPORTED: return "NQ_ERR_UNSUPPORTED";
+    case NQ_ERR_OUT_OF_MEMORY: return "NQ_ERR_OUT_OF_MEMORY";
+    case NQ_ERR_HIP: return "NQ_ERR_HIP";
+    case NQ_ERR_NOT_POSITIVE_DEFINITE: return "NQ_ERR_NOT_POSITIVE_DEFINITE";
+    case NQ_ERR_NONFINITE: return "NQ_ERR_NONFINITE";
+    case NQ_ERR_BAD_PRECONDITIONER: return "NQ_ERR_BAD_PRECONDITIONER";
+  }
+  return "NQ_ERR_UNKNOWN";
+}
+
+const char* nq_last_error_message(void) { return g_err.c_str(); }
+
+int32_t nq_version(void) { return 100; }
+
+nq_status nq_lbadmm_workspace_bytes(const nq_lbadmm_desc* desc, size_t* bytes) {
+  nq_status st = check_desc(desc);
+  if (st != NQ_OK) return st;
+  if (!bytes) return fail(NQ_ERR_INVALID_ARG, "bytes is NULL");
+  nq_lbadmm tmp;
+  tmp.d = *desc;
+  plan(&tmp);
+  *bytes = layout(&tmp);
+  return NQ_OK;
+}
+
+nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
+  if (!out) return fail(NQ_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  nq_status st = check_desc(desc);
+  if (st != NQ_OK) return st;
+  int dev = 0;
+  st = check_device(&dev);
+  if (st != NQ_OK) return st;
+  nq_lbadmm* h = new nq_lbadmm();
+  h->d = *desc;
+  h->device = dev;
+  plan(h);
+  h->bytes = layout(h);
+  hipError_t e = hipMalloc((void**)&h->base, h->bytes);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "hipMalloc(workspace)");
+  }
+  layout(h);
+  e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreate(&h->ev_t0);
+  if (e == hipSuccess) e = hipEventCreate(&h->ev_t1);
+  // Padding must read as zero from the start (the run rewrites every live
+  // region it reads, but the finish kernels read padded rows).
+  if (e == hipSuccess) e = hipMemset(h->base, 0, h->bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    nq_status s = hip_fail(e, "create");
+    nq_lbadmm_destroy(h);
+    return s;
+  }
+  *out = h;
+  return NQ_OK;
+}
+
+void nq_lbadmm_destroy(nq_lbadmm_t h) {
+  if (!h) return;
+  int cur = 0;
+  if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
+  if (h->last_stream || h->has_run) (void)hipStreamSynchronize(h->last_stream);
+  if (h->aux) (void)hipStreamSynchronize(h->aux);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
+  if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
+  if (h->aux) (void)hipStreamDestroy(h->aux);
+  if (h->base) (void)hipFree(h->base);
+  if (cur != h->device) (void)hipSetDevice(cur);
+  delete h;
+}
+
+nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float* d_out,
+                        const float* d_in, const float* U0, const float* V0, float* U, float* V,
+                        float* s1, float* s2, uint32_t* U_bits, uint32_t* V_bits,
+                        nq_lbadmm_stats* stats, void* stream) {
+  if (!h) return fail(NQ_ERR_INVALID_ARG, "handle is NULL");
+  if (!W || !d_out || !d_in) return fail(NQ_ERR_INVALID_ARG, "W, d_out and d_in are required");
+  if (ldw < h->d.n) return fail(NQ_ERR_INVALID_ARG, "ldw < n");
+  if ((U0 == nullptr) != (V0 == nullptr))
+    return fail(NQ_ERR_INVALID_ARG, "U0 and V0 must be both given or both NULL");
+  if ((h->d.flags & NQ_FLAG_INIT_EXACT) && !U0)
+    return fail(NQ_ERR_INVALID_ARG, "NQ_FLAG_INIT_EXACT needs U0 and V0");
+  int cur = 0;
+  HIPCHK(hipGetDevice(&cur));
+  if (cur != h->device) return fail(NQ_ERR_INVALID_ARG, "handle belongs to another device");
+
+  hipStream_t s = (hipStream_t)stream;
+  const nq_lbadmm_desc& d = h->d;
+  const int mp = h->mp, np_ = h->np_, rp = h->rp;
+  const bool overlap = !(d.flags & NQ_FLAG_SINGLE_STREAM);
+
+  HIPCHK(hipEventRecord(h->ev_t0, s));
+  HIPCHK(launch_stats_init(h->st, s));
+  HIPCHK(launch_check_precond(d_out, d.m, d_in, d.n, h->st, s));
+  HIPCHK(launch_precondition(W, ldw, d.m, d.n, d_out, d_in, h->Wt, h->WtT, mp, np_, h->part_wt,
+                             h->part_w, h->st, s));
+  HIPCHK(launch_finalize_norms(h->part_wt, h->part_w, precondition_nblocks(mp, np_), d.m, d.n,
+                               d.r, h->st, s));
+  // init: U0 (the latent) into U, and X = U0 into the Lam buffer for SVID
+  if (U0) {
+    const bool scale = !(d.flags & NQ_FLAG_INIT_EXACT);
+    HIPCHK(launch_init_copy(U0, d.m, d.r, d.r, h->U, h->LamU, mp, rp, scale, h->st, s));
+    HIPCHK(launch_init_copy(V0, d.n, d.r, d.r, h->V, h->LamV, np_, rp, scale, h->st, s));
+  } else {
+    HIPCHK(launch_init_philox(d.seed, 0u, d.m, d.r, h->U, h->LamU, mp, rp, h->st, s));
+    HIPCHK(launch_init_philox(d.seed, 1u, d.n, d.r, h->V, h->LamV, np_, rp, h->st, s));
+  }
+  HIPCHK(launch_svid(h->LamU, h->PU, mp, rp, (int)d.r, d.svid_steps, 0, h->svU, s));
+  HIPCHK(launch_svid(h->LamV, h->PV, np_, rp, (int)d.r, d.svid_steps, 0, h->svV, s));
+  if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
+
+  Half hu{h->Wt, mp, np_, h->V, h->U, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc};
+  Half hv{h->WtT, np_, mp, h->U, h->V, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc};
+  for (int it = 0; it < d.iters; ++it) {
+    nq_status st = run_half(h, hu, s, overlap);
+    if (st != NQ_OK) return st;
+    st = run_half(h, hv, s, overlap);
+    if (st != NQ_OK) return st;
+  }
+
+  // finish: balance, scales, signs, bits, errors
+  const int nchU = svid_nchunks(mp), nchV = svid_nchunks(np_);
+  HIPCHK(launch_colsumsq(h->U, mp, rp, h->colpartU, s));
+  HIPCHK(launch_colsumsq(h->V, np_, rp, h->colpartV, s));
+  HIPCHK(launch_balance_coef(h->colpartU, nchU, h->colpartV, nchV, rp,
+                             !(d.flags & NQ_FLAG_NO_BALANCE), h->cbal, s));
+  HIPCHK(launch_apply_finish(h->U, d.m, mp, rp, d.r, h->cbal, false, d_out, U, h->s1c, h->s1w,
+                             U_bits, h->SU, h->st, s));
+  HIPCHK(launch_apply_finish(h->V, d.n, np_, rp, d.r, h->cbal, true, d_in, V, h->s2c, h->s2w,
+                             V_bits, h->SV, h->st, s));
+  if (s1) HIPCHK(hipMemcpyAsync(s1, h->s1c, sizeof(float) * d.m, hipMemcpyDeviceToDevice, s));
+  if (s2) HIPCHK(hipMemcpyAsync(s2, h->s2c, sizeof(float) * d.n, hipMemcpyDeviceToDevice, s));
+  if (d.flags & NQ_FLAG_COMPUTE_ERROR)
+    HIPCHK(launch_error(h->SU, h->SV, mp, np_, rp, h->s1w, h->s2w, h->Wt, W, ldw, d.m, d.n,
+                        h->s1c, h->s2c, h->err_parts, h->st, s));
+  HIPCHK(hipEventRecord(h->ev_t1, s));
+  h->last_stream = s;
+  h->has_run = true;
+  if (stats) return nq_lbadmm_query(h, stats);
+  return NQ_OK;
+}
+
+nq_status nq_lbadmm_query(nq_lbadmm_t h, nq_lbadmm_stats* stats) {
+  if (!h || !stats) return fail(NQ_ERR_INVALID_ARG, "handle and stats are required");
+  if (!h->has_run) return fail(NQ_ERR_INVALID_ARG, "handle has not run");
+  HIPCHK(hipEventSynchronize(h->ev_t1));
+  DevStats hs;
+  HIPCHK(hipMemcpy(&hs, h->st, sizeof(DevStats), hipMemcpyDeviceToHost));
+  float ms = 0.0f;
+  HIPCHK(hipEventElapsedTime(&ms, h->ev_t0, h->ev_t1));
+  std::memset(stats, 0, sizeof(*stats));
+  const bool err = (h->d.flags & NQ_FLAG_COMPUTE_ERROR) != 0;
+  stats->rel_err_wtilde = err ? std::sqrt(hs.err2_wt / hs.sumsq_wt) : NAN;
+  stats->rel_err_w = err ? std::sqrt(hs.err2_w / hs.sumsq_w) : NAN;
+  stats->sumsq_wtilde = hs.sumsq_wt;
+  stats->sigma0 = hs.sigma0;
+  stats->potrf_info = hs.potrf_info == 0x7fffffff ? 0 : hs.potrf_info;
+  stats->nonfinite = hs.nonfinite;
+  stats->bad_precond = hs.bad_precond;
+  stats->elapsed_ms = ms;
+  stats->iters_done = h->d.iters;
+  return status_from(hs);
+}
+
+}  // extern "C"
+
+extern "C" nq_status nq_lbadmm_get_state(nq_lbadmm_t h, float* U, float* V, float* Z_U,
+                                         float* Lam_U, float* Z_V, float* Lam_V, void* stream) {
+  if (!h) return fail(NQ_ERR_INVALID_ARG, "handle is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t m = h->d.m, n = h->d.n, r = h->d.r, rp = h->rp;
+  const size_t sp = sizeof(float) * rp, dp = sizeof(float) * r;
+  if (U) HIPCHK(hipMemcpy2DAsync(U, dp, h->U, sp, dp, m, hipMemcpyDeviceToDevice, s));
+  if (V) HIPCHK(hipMemcpy2DAsync(V, dp, h->V, sp, dp, n, hipMemcpyDeviceToDevice, s));
+  if (Lam_U) HIPCHK(hipMemcpy2DAsync(Lam_U, dp, h->LamU, sp, dp, m, hipMemcpyDeviceToDevice, s));
+  if (Lam_V) HIPCHK(hipMemcpy2DAsync(Lam_V, dp, h->LamV, sp, dp, n, hipMemcpyDeviceToDevice, s));
+  if (Z_U) HIPCHK(launch_add_compact(h->PU, h->LamU, m, r, (int)rp, Z_U, s));
+  if (Z_V) HIPCHK(launch_add_compact(h->PV, h->LamV, n, r, (int)rp, Z_V, s));
+  return NQ_OK;
+}

@@ -1,0 +1,185 @@
+// Building-block entry points: each runs one step of the per-layer path on
+// caller buffers of any shape by staging them into zero-padded temporaries
+// (the kernels themselves assume tile-multiple shapes). Synchronous; they
+// allocate, so they are for tests and tools, not for the hot path.
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "abi.h"
+#include "common.h"
+
+using namespace nq;
+
+namespace {
+
+struct DevBuf {
+  void* p = nullptr;
+  ~DevBuf() {
+    if (p) (void)hipFree(p);
+  }
+  hipError_t alloc(size_t bytes) { return hipMalloc(&p, std::max<size_t>(bytes, 256)); }
+  float* f() const { return (float*)p; }
+  double* d() const { return (double*)p; }
+};
+
+// dst (rows_pad x cols_pad, zero padded) <- src (rows x cols, ld lds)
+hipError_t stage_in(const float* src, int64_t rows, int64_t cols, int64_t lds, float* dst,
+                    int64_t rows_pad, int64_t cols_pad, hipStream_t s) {
+  hipError_t e = launch_zero(dst, (size_t)(rows_pad * cols_pad), s);
+  if (e != hipSuccess) return e;
+  return hipMemcpy2DAsync(dst, sizeof(float) * cols_pad, src, sizeof(float) * lds,
+                          sizeof(float) * cols, rows, hipMemcpyDeviceToDevice, s);
+}
+
+hipError_t stage_out(const float* src, int64_t lds, float* dst, int64_t ldd, int64_t rows,
+                     int64_t cols, hipStream_t s) {
+  return hipMemcpy2DAsync(dst, sizeof(float) * ldd, src, sizeof(float) * lds,
+                          sizeof(float) * cols, rows, hipMemcpyDeviceToDevice, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+nq_status nq_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx, uint32_t* bits,
+                        int64_t ld_words, void* stream) {
+  if (rows < 0 || cols < 0) return set_error(NQ_ERR_INVALID_ARG, "rows and cols must be >= 0");
+  if (rows == 0 || cols == 0) return NQ_OK;
+  if (!X || !bits) return set_error(NQ_ERR_INVALID_ARG, "X and bits are required");
+  if (ldx < cols) return set_error(NQ_ERR_INVALID_ARG, "ldx < cols");
+  if (ld_words < (cols + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ld_words < ceil(cols/32)");
+  NQ_HIPCHK(launch_pack_signs(X, rows, cols, ldx, bits, ld_words, (hipStream_t)stream));
+  return NQ_OK;
+}
+
+nq_status nq_op_precondition(const float* W, int64_t ldw, int64_t m, int64_t n,
+                             const float* d_out, const float* d_in, float* Wt, int64_t ldwt,
+                             void* stream) {
+  if (m < 1 || n < 1 || ldw < n || ldwt < n || !W || !d_out || !d_in || !Wt)
+    return set_error(NQ_ERR_INVALID_ARG, "bad precondition arguments");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t mp = round_up(m, 64), np_ = round_up(n, 64);
+  DevBuf t, parts, st;
+  NQ_HIPCHK(t.alloc(sizeof(float) * mp * np_));
+  const int nb = precondition_nblocks((int)mp, (int)np_);
+  NQ_HIPCHK(parts.alloc(sizeof(double) * 2 * nb));
+  NQ_HIPCHK(st.alloc(sizeof(DevStats)));
+  NQ_HIPCHK(launch_stats_init((DevStats*)st.p, s));
+  NQ_HIPCHK(launch_precondition(W, ldw, m, n, d_out, d_in, t.f(), nullptr, (int)mp, (int)np_,
+                                parts.d(), parts.d() + nb, (DevStats*)st.p, s));
+  NQ_HIPCHK(stage_out(t.f(), np_, Wt, ldwt, m, n, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  return NQ_OK;
+}
+
+nq_status nq_op_gram(const float* A, int64_t rows, int64_t cols, int64_t lda, float rho, float* G,
+                     int64_t ldg, void* stream) {
+  if (rows < 1 || cols < 1 || lda < cols || ldg < cols || !A || !G)
+    return set_error(NQ_ERR_INVALID_ARG, "bad gram arguments");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t K = round_up(rows, 32), rp = round_up(cols, 128);
+  const int R = (int)(rp / 128);
+  const int tiles = R * (R + 1) / 2;
+  int nch = std::max<int64_t>(1, std::min<int64_t>({(512 + tiles - 1) / tiles, 4, K / 256}));
+  const int kc = (int)round_up((K + nch - 1) / nch, 32);
+  nch = (int)((K + kc - 1) / kc);
+  DevBuf a, part, g;
+  NQ_HIPCHK(a.alloc(sizeof(float) * K * rp));
+  NQ_HIPCHK(part.alloc(sizeof(float) * nch * rp * rp));
+  NQ_HIPCHK(g.alloc(sizeof(float) * rp * rp));
+  NQ_HIPCHK(stage_in(A, rows, cols, lda, a.f(), K, rp, s));
+  NQ_HIPCHK(launch_syrk_partial(a.f(), rp, (int)K, (int)rp, kc, false, part.f(), s));
+  NQ_HIPCHK(launch_gram_reduce(part.f(), nch, (int)rp, rho, g.f(), rp, s));
+  NQ_HIPCHK(stage_out(g.f(), rp, G, ldg, cols, cols, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  return NQ_OK;
+}
+
+nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ldb, const float* P,
+                         int64_t ldp, float rho, float* C, int64_t ldc, int64_t rows, int64_t cols,
+                         int64_t k, void* stream) {
+  if (rows < 1 || cols < 1 || k < 1 || !A || !B || !C || lda < k || ldb < cols || ldc < cols ||
+      (P && ldp < cols))
+    return set_error(NQ_ERR_INVALID_ARG, "bad gemm arguments");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t Mp = round_up(rows, 256), Np = round_up(cols, 128), Kp = round_up(k, 32);
+  DevBuf a, b, p, c;
+  NQ_HIPCHK(a.alloc(sizeof(float) * Mp * Kp));
+  NQ_HIPCHK(b.alloc(sizeof(float) * Kp * Np));
+  NQ_HIPCHK(p.alloc(sizeof(float) * Mp * Np));
+  NQ_HIPCHK(c.alloc(sizeof(float) * Mp * Np));
+  NQ_HIPCHK(stage_in(A, rows, k, lda, a.f(), Mp, Kp, s));
+  NQ_HIPCHK(stage_in(B, k, cols, ldb, b.f(), Kp, Np, s));
+  if (P) NQ_HIPCHK(stage_in(P, rows, cols, ldp, p.f(), Mp, Np, s));
+  else NQ_HIPCHK(launch_zero(p.f(), (size_t)(Mp * Np), s));
+  GemmArgs g{};
+  g.A = a.f(); g.lda = Kp; g.B = b.f(); g.ldb = Np; g.C = c.f(); g.ldc = Np;
+  g.P = p.f(); g.rho = rho; g.M = (int)Mp; g.N = (int)Np; g.K = (int)Kp;
+  NQ_HIPCHK(launch_gemm(g, kEpiRhs, s));
+  NQ_HIPCHK(stage_out(c.f(), Np, C, ldc, rows, cols, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  return NQ_OK;
+}
+
+nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* L, int64_t ldl,
+                                 float* Ginv, int64_t ldgi, int64_t* info, void* stream) {
+  if (r < 1 || ldg < r || !G || !info || (L && ldl < r) || (Ginv && ldgi < r))
+    return set_error(NQ_ERR_INVALID_ARG, "bad cholesky arguments");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rp = round_up(r, 128);
+  int nch = (int)std::max<int64_t>(1, std::min<int64_t>(4, rp / 128));
+  const int kc = (int)round_up((rp + nch - 1) / nch, 32);
+  nch = (int)((rp + kc - 1) / kc);
+  DevBuf a, m, part, gi, st;
+  NQ_HIPCHK(a.alloc(sizeof(float) * rp * rp));
+  NQ_HIPCHK(m.alloc(sizeof(float) * rp * rp));
+  NQ_HIPCHK(part.alloc(sizeof(float) * nch * rp * rp));
+  NQ_HIPCHK(gi.alloc(sizeof(float) * rp * rp));
+  NQ_HIPCHK(st.alloc(sizeof(DevStats)));
+  DevStats* dst = (DevStats*)st.p;
+  NQ_HIPCHK(launch_stats_init(dst, s));
+  // [G 0; 0 I]: the identity keeps the padded system positive definite
+  NQ_HIPCHK(stage_in(G, r, r, ldg, a.f(), rp, rp, s));
+  NQ_HIPCHK(launch_set_diag(a.f(), rp, (int)r, (int)rp, 1.0f, s));
+  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), (int)rp, (int)r, dst, true, s));
+  if (Ginv) {
+    NQ_HIPCHK(launch_syrk_partial(m.f(), rp, (int)rp, (int)rp, kc, true, part.f(), s));
+    NQ_HIPCHK(launch_gram_reduce(part.f(), nch, (int)rp, 0.0f, gi.f(), rp, s));
+    NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));
+  }
+  if (L) NQ_HIPCHK(stage_out(a.f(), rp, L, ldl, r, r, s));
+  DevStats hs;
+  NQ_HIPCHK(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  *info = hs.potrf_info == 0x7fffffff ? 0 : hs.potrf_info;
+  if (*info) return set_error(NQ_ERR_NOT_POSITIVE_DEFINITE, "Cholesky pivot <= 0");
+  return NQ_OK;
+}
+
+nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx, int32_t T, float* Z,
+                     int64_t ldz, float* a, float* b, void* stream) {
+  if (rows < 1 || cols < 1 || T < 1 || ldx < cols || !X || (Z && ldz < cols))
+    return set_error(NQ_ERR_INVALID_ARG, "bad svid arguments");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rows_pad = round_up(rows, 4), rp = round_up(cols, 128);
+  const int nch = svid_nchunks((int)rows_pad);
+  DevBuf x, p, wa, wb, wc, waa, wbb;
+  NQ_HIPCHK(x.alloc(sizeof(float) * rows_pad * rp));
+  NQ_HIPCHK(p.alloc(sizeof(float) * rows_pad * rp));
+  NQ_HIPCHK(wa.alloc(sizeof(float) * rows_pad));
+  NQ_HIPCHK(wb.alloc(sizeof(float) * rp));
+  NQ_HIPCHK(wc.alloc(sizeof(float) * nch * rp));
+  NQ_HIPCHK(waa.alloc(sizeof(float) * nch));
+  NQ_HIPCHK(wbb.alloc(sizeof(float) * (rp / 128)));
+  SvidWork w{wa.f(), wb.f(), wc.f(), waa.f(), wbb.f()};
+  NQ_HIPCHK(stage_in(X, rows, cols, ldx, x.f(), rows_pad, rp, s));
+  NQ_HIPCHK(launch_svid(x.f(), p.f(), (int)rows_pad, (int)rp, (int)cols, T, 2, w, s));
+  if (Z) NQ_HIPCHK(stage_out(p.f(), rp, Z, ldz, rows, cols, s));
+  if (a) NQ_HIPCHK(hipMemcpyAsync(a, wa.f(), sizeof(float) * rows, hipMemcpyDeviceToDevice, s));
+  if (b) NQ_HIPCHK(hipMemcpyAsync(b, wb.f(), sizeof(float) * cols, hipMemcpyDeviceToDevice, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  return NQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls)."""
+import ctypes as C
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nq.h")
+
+from sub_bit_weight_lb_amd import _lib as L  # noqa: E402
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nq_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libnq.so is not built; run __graft_entry__.build() first")
+    return L.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the binding declares a signature for each of them
+    assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "sz.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "nq.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(nq_lbadmm_desc),"
+        " offsetof(nq_lbadmm_desc, seed), offsetof(nq_lbadmm_desc, flags),"
+        " sizeof(nq_lbadmm_stats), offsetof(nq_lbadmm_stats, potrf_info),"
+        " offsetof(nq_lbadmm_stats, elapsed_ms)); return 0;}\n")
+    exe = tmp_path / "sz"
+    subprocess.check_call(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src),
+                           "-o", str(exe)])
+    vals = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    assert vals == [C.sizeof(L.Desc), L.Desc.seed.offset, L.Desc.flags.offset,
+                    C.sizeof(L.Stats), L.Stats.potrf_info.offset, L.Stats.elapsed_ms.offset]
+
+
+def test_status_strings_and_version(lib):
+    for code in range(8):
+        assert lib.nq_status_string(code).decode().startswith("NQ_")
+    assert lib.nq_status_string(99).decode() == "NQ_ERR_UNKNOWN"
+    assert lib.nq_version() >= 100
+
+
+def _desc(**kw):
+    d = dict(m=256, n=512, r=128, rho=1.0, iters=2, svid_steps=5, seed=0, flags=0)
+    d.update(kw)
+    return L.Desc(**d)
+
+
+@pytest.mark.parametrize("bad", [dict(m=0), dict(n=-1), dict(r=0), dict(rho=0.0),
+                                 dict(rho=float("nan")), dict(rho=float("inf")), dict(iters=-1),
+                                 dict(svid_steps=0), dict(flags=0x100), dict(r=1 << 17)])
+def test_create_rejects_bad_desc_before_device_work(lib, bad):
+    h = C.c_void_p(0)
+    st = lib.nq_lbadmm_create(C.byref(_desc(**bad)), C.byref(h))
+    assert st == L.NQ_ERR_INVALID_ARG
+    assert h.value is None
+    assert lib.nq_last_error_message().decode()
+    sz = C.c_size_t(0)
+    assert lib.nq_lbadmm_workspace_bytes(C.byref(_desc(**bad)), C.byref(sz)) == L.NQ_ERR_INVALID_ARG
+
+
+def test_create_null_arguments(lib):
+    assert lib.nq_lbadmm_create(None, None) == L.NQ_ERR_INVALID_ARG
+    h = C.c_void_p(0)
+    assert lib.nq_lbadmm_create(None, C.byref(h)) == L.NQ_ERR_INVALID_ARG
+
+
+def test_workspace_bytes_accounts_for_padding(lib):
+    def ws(**kw):
+        s = C.c_size_t(0)
+        assert lib.nq_lbadmm_workspace_bytes(C.byref(_desc(**kw)), C.byref(s)) == 0
+        return s.value
+    a = ws(m=256, n=512, r=128)
+    # same padded shapes -> same bytes; bigger shapes -> more
+    assert ws(m=250, n=500, r=100) == a
+    assert ws(m=4096, n=4096, r=2048) > 32 * a
+    # config-sized layer stays far below 288 GB of HBM
+    big = ws(m=8192, n=28672, r=6144)
+    assert 4e9 < big < 20e9
+
+
+@pytest.mark.skipif(os.environ.get("HIP_VISIBLE_DEVICES") is None and
+                    os.path.exists("/dev/kfd"), reason="a GPU may be visible")
+def test_create_without_device_reports_unsupported(lib):
+    h = C.c_void_p(0)
+    st = lib.nq_lbadmm_create(C.byref(_desc()), C.byref(h))
+    assert st in (L.NQ_ERR_UNSUPPORTED, L.NQ_ERR_HIP)
+    assert h.value is None
+
+
+def test_run_and_query_reject_null_handle(lib):
+    assert lib.nq_lbadmm_run(None, None, 0, None, None, None, None, None, None, None, None,
+                             None, None, None, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lbadmm_query(None, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lbadmm_get_state(None, None, None, None, None, None, None, None) == \
+        L.NQ_ERR_INVALID_ARG
+    lib.nq_lbadmm_destroy(None)
+
+
+def test_pack_signs_argument_checks(lib):
+    assert lib.nq_pack_signs(None, 0, 5, 5, None, 1, None) == 0          # empty is a no-op
+    assert lib.nq_pack_signs(None, 3, 0, 0, None, 0, None) == 0
+    assert lib.nq_pack_signs(None, 3, 5, 5, None, 1, None) == L.NQ_ERR_INVALID_ARG
+    fake = C.c_void_p(0x1000)
+    assert lib.nq_pack_signs(fake, 3, 40, 39, fake, 2, None) == L.NQ_ERR_INVALID_ARG  # ldx < cols
+    assert lib.nq_pack_signs(fake, 3, 40, 40, fake, 1, None) == L.NQ_ERR_INVALID_ARG  # words
+    assert lib.nq_pack_signs(fake, -1, 40, 40, fake, 2, None) == L.NQ_ERR_INVALID_ARG
+
+
+def test_ops_argument_checks(lib):
+    f = C.c_void_p(0x1000)
+    info = C.c_int64(0)
+    assert lib.nq_op_precondition(f, 3, 4, 5, f, f, f, 5, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_gram(f, 0, 4, 4, 1.0, f, 4, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_gemm_rhs(f, 2, f, 4, None, 0, 1.0, f, 4, 3, 4, 5, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_cholesky_inverse(f, 4, 3, f, 4, f, 4, C.byref(info), None) == \
+        L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_svid(f, 4, 4, 4, 0, f, 4, None, None, None) == L.NQ_ERR_INVALID_ARG
+
+
+def test_binding_imports_and_missing_library_fails_loudly(tmp_path):
+    code = ("import sub_bit_weight_lb_amd._lib as L\n"
+            "try:\n    L.load('%s')\nexcept ImportError as e:\n    print('IMPORTERROR', e)\n"
+            % str(tmp_path / "nope.so"))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "IMPORTERROR" in out.stdout, out.stderr
+
+
+def test_product_package_never_imports_oracle():
+    pkg = os.path.join(ROOT, "sub_bit_weight_lb_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.replace("oracle is", ""), f

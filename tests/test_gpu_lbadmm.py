@@ -1,0 +1,140 @@
+"""GPU parity of the whole per-layer path (nq_lbadmm_run) against the oracle."""
+import numpy as np
+import pytest
+
+from oracle import lbadmm as O
+from synth import make_layer, make_tiny
+
+pytestmark = pytest.mark.gpu
+
+
+def T(x, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def H(t):
+    return t.detach().cpu().numpy()
+
+
+def relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def run_gpu(L, r, iters, dev, rho=1.0, T_=5, balance=True, init_exact=False, U0=None, V0=None):
+    import sub_bit_weight_lb_amd as nq
+    m, n = L.W.shape
+    h = nq.LBADMM(m, n, r, rho=rho, iters=iters, svid_steps=T_, balance=balance,
+                  init_exact=init_exact)
+    U0 = L.EU if U0 is None else U0
+    V0 = L.EV if V0 is None else V0
+    res = h.run(T(L.W, dev), T(L.d_out, dev), T(L.d_in, dev), T(U0, dev), T(V0, dev))
+    state = {k: H(v) for k, v in h.state().items()}
+    h.close()
+    return res, state
+
+
+def masked_rel(g, o, X):
+    """Relative Frobenius difference over entries with |X| > 1e-3 rms(X)."""
+    rms = np.sqrt(np.mean(X.astype(np.float64) ** 2))
+    mask = np.abs(X) > 1e-3 * rms
+    return relerr(np.where(mask, g, 0), np.where(mask, o, 0))
+
+
+def sign_agreement(g, o):
+    rms = np.sqrt(np.mean(o ** 2))
+    mask = np.abs(o) > 1e-3 * rms
+    return float(np.mean((g[mask] >= 0) == (o[mask] >= 0)))
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 128), (300, 200, 70), (64, 48, 8), (1, 1, 1)])
+def test_init_and_one_iteration_state(gpu, shape):
+    m, n, r = shape
+    L = make_tiny(m, n, r, seed=11 + m)
+    for iters in (0, 1):
+        res, st = run_gpu(L, r, iters, gpu, balance=False)
+        Wt = O.precondition(L.W, L.d_out, L.d_in)
+        ref = O.init_state(Wt, r, 5, EU=L.EU, EV=L.EV)
+        ref = O.iterate(Wt, ref, 1.0, 5, iters)
+        print(f"case {shape} iters={iters}", flush=True)
+        assert relerr(st["U"], ref.U) < 1e-4, relerr(st["U"], ref.U)
+        assert relerr(st["V"], ref.V) < 1e-4, relerr(st["V"], ref.V)
+        XU = ref.Lam_U + ref.Z_U
+        XV = ref.Lam_V + ref.Z_V
+        for k, Xk in (("Z_U", XU), ("Lam_U", XU), ("Z_V", XV), ("Lam_V", XV)):
+            o = getattr(ref, k)
+            if np.linalg.norm(o) == 0:
+                assert np.max(np.abs(st[k])) < 1e-6
+            else:
+                assert masked_rel(st[k], o, Xk) < 1e-4, (k, masked_rel(st[k], o, Xk))
+        assert sign_agreement(st["U"], ref.U) >= 0.999
+        assert sign_agreement(st["V"], ref.V) >= 0.999
+
+
+def test_tiny_workload_full_run(gpu):
+    L = make_layer("tiny-256x512-r128")
+    wl = L.workload
+    res, st = run_gpu(L, wl.r, wl.iters, gpu, rho=wl.rho, T_=wl.svid_steps)
+    ref = O.lbadmm(L.W, L.d_out, L.d_in, wl.r, wl.rho, wl.iters, wl.svid_steps, EU=L.EU, EV=L.EV)
+    s = res.stats
+    print(f"gpu err {s['rel_err_wtilde']:.6f} oracle {ref.rel_err_wt:.6f}", flush=True)
+    assert abs(s["rel_err_wtilde"] - ref.rel_err_wt) < 1e-3
+    assert abs(s["rel_err_w"] - ref.rel_err_w) < 1e-3
+    assert s["potrf_info"] == 0 and s["nonfinite"] == 0
+    assert abs(s["sigma0"] - ref.sigma0) / ref.sigma0 < 1e-6
+    # the GPU's own error report equals the error of its own outputs, recomputed here
+    SU = O.unpack_signs(H(res.U_bits).view(np.uint32), wl.r)
+    SV = O.unpack_signs(H(res.V_bits).view(np.uint32), wl.r)
+    e_w = O.rel_error(L.W, H(res.s1), SU, SV, H(res.s2))
+    assert abs(e_w - s["rel_err_w"]) < 1e-5
+    # the returned bits are the signs of the returned latents, and balancing held
+    np.testing.assert_array_equal(SU, O.sgn(H(res.U)))
+    np.testing.assert_array_equal(SV, O.sgn(H(res.V)))
+    np.testing.assert_allclose(np.linalg.norm(H(res.U), axis=0), np.linalg.norm(H(res.V), axis=0),
+                               rtol=1e-4)
+    assert sign_agreement(H(res.U), ref.U) > 0.95
+
+
+def test_planted_fixed_point(gpu):
+    m, n, r = 256, 384, 32
+    rng = np.random.default_rng(3)
+    s1 = rng.uniform(0.5, 2, m)
+    s2 = rng.uniform(0.5, 2, n)
+    SU = np.where(rng.random((m, r)) < .5, -1.0, 1.0)
+    SV = np.where(rng.random((n, r)) < .5, -1.0, 1.0)
+    W = O.reconstruct(s1, SU, SV, s2).astype(np.float32)
+    import types
+    L = types.SimpleNamespace(W=W, d_out=np.ones(m, np.float32), d_in=np.ones(n, np.float32))
+    U0 = (s1[:, None] * SU).astype(np.float32)
+    V0 = (s2[:, None] * SV).astype(np.float32)
+    res, st = run_gpu(L, r, 10, gpu, init_exact=True, U0=U0, V0=V0)
+    assert res.stats["rel_err_wtilde"] < 1e-5
+    np.testing.assert_array_equal(O.unpack_signs(H(res.U_bits).view(np.uint32), r), SU)
+    np.testing.assert_array_equal(O.unpack_signs(H(res.V_bits).view(np.uint32), r), SV)
+
+
+def test_deterministic_rerun(gpu):
+    import sub_bit_weight_lb_amd as nq
+    L = make_tiny(300, 260, 70, seed=4, iters=3)
+    h = nq.LBADMM(300, 260, 70, iters=3)
+    a = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+    b = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+    h.close()
+    for x, y in ((a.U, b.U), (a.V, b.V), (a.s1, b.s1), (a.U_bits, b.U_bits)):
+        np.testing.assert_array_equal(H(x), H(y))
+    assert a.stats["rel_err_wtilde"] == b.stats["rel_err_wtilde"]
+
+
+def test_bad_inputs_reported(gpu):
+    import sub_bit_weight_lb_amd as nq
+    L = make_tiny(64, 64, 8, seed=2)
+    W = L.W.copy()
+    W[3, 5] = np.nan
+    with pytest.raises(nq.NQError, match="NONFINITE"):
+        run_gpu(type("L", (), dict(W=W, d_out=L.d_out, d_in=L.d_in, EU=L.EU, EV=L.EV)), 8, 1, gpu)
+    d = L.d_in.copy()
+    d[7] = 0.0
+    with pytest.raises(nq.NQError, match="BAD_PRECONDITIONER"):
+        run_gpu(type("L", (), dict(W=L.W, d_out=L.d_out, d_in=d, EU=L.EU, EV=L.EV)), 8, 1, gpu)
