@@ -105,9 +105,11 @@ __global__ __launch_bounds__(NT) void chol_diag_kernel(float* A, float* M, int r
     for (int idx = (j + 1) * NB + tid; idx < NB * NB; idx += NT) {
       const int i = idx >> 6, c = idx & 63;
       if (c <= i) {
+        // only the lower triangle is kept current: the symmetric partner of
+        // T[j][c] (c > j) is T[c][j]
         const float l = T[i][j] * inv;
         if (c <= j) E[i][c] -= l * E[j][c];
-        else T[i][c] -= l * T[j][c];
+        else T[i][c] -= l * T[c][j];
       }
     }
     __syncthreads();
