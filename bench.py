@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""LB-ADMM throughput on one MI355X.
+
+Workload: a Llama-2-7B attention-projection-shaped layer, W 4096 x 4096 fp32
+N(0, 0.02^2) with 1 % of input columns x10, lognormal(0, 0.5)
+preconditioners, rank 2048 (1.0 bit per weight), rho = 1, 50 ADMM
+iterations, 5 SVID steps (synthetic, seeded; see synth/layers.py).
+
+One step = one whole per-layer run through the C ABI (precondition, init,
+50 iterations of U-half + V-half, balance, scales, packing, errors) with the
+inputs already resident in HBM. value = ADMM iterations per second over the
+timed steps (whole runs, so precondition and finish count against it).
+
+Also reported:
+  roofline      the right-hand-side GEMM R = Wt V + rho (Z - Lam), the
+                largest kernel: algorithmic 2 m n r flops per launch over its
+                average launch duration from HIP events recorded by the
+                library on its own stream during the timed steps, against the
+                157.3 TFLOP/s fp32 MFMA peak; traffic from the committed
+                rocprofv3 counter summary when it matches the current kernel
+                source;
+  cpu_baseline  the CPU oracle (NumPy float64) on the same layer: a bounded
+                number of ADMM iterations on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "llama2-7b-attn-4096x4096-r2048"
+FP32_MFMA_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_rhs_4096x4096_r2048_counters.md")
+GEMM_SRC = os.path.join(ROOT, "sub_bit_weight_lb_amd", "csrc", "gemm.hip")
+
+
+def flops_per_iter(m, n, r):
+    """Algorithmic flops of one ADMM iteration (U-half + V-half): two RHS
+    GEMMs 4mnr, two Gram products (m+n)r^2 (symmetric count), the triangular
+    solves 2(m+n)r^2, two Cholesky factorisations 2 r^3/3."""
+    return 4.0 * m * n * r + 3.0 * (m + n) * r * r + 2.0 * r ** 3 / 3.0
+
+
+def gemm_source_hash():
+    return hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(m, n, r, launches_ms):
+    """HBM bytes per RHS-GEMM launch from the committed counter summary, or
+    None when it is missing or was taken on a different gemm.hip."""
+    if not os.path.exists(COUNTER_SUMMARY):
+        return None
+    txt = open(COUNTER_SUMMARY).read()
+    mh = re.search(r"gemm_src_sha256_16:\s*([0-9a-f]{16})", txt)
+    mt = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not mh or not mt or mh.group(1) != gemm_source_hash():
+        return None
+    return float(mt.group(1))
+
+
+def cpu_baseline(L, budget_s=12.0, max_iters=12):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import lbadmm as O
+    wl = L.workload
+    t0 = time.perf_counter()
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    st = O.init_state(Wt, wl.r, wl.svid_steps, EU=L.EU, EV=L.EV)
+    t_prep = time.perf_counter() - t0
+    done = 0
+    t_iter = 0.0
+    while done < max_iters and (done == 0 or t_iter * (done + 1) / done < budget_s):
+        t1 = time.perf_counter()
+        st = O.iterate(Wt, st, wl.rho, wl.svid_steps, 1)
+        t_iter += time.perf_counter() - t1
+        done += 1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": done / t_iter,
+        "unit": "iters/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{done} ADMM iterations (U-half + V-half) of the same {wl.m}x{wl.n} r={wl.r} "
+                   f"layer in NumPy float64 after preconditioning and init ({t_prep:.1f} s, not "
+                   f"counted); {t_iter:.1f} s of iterations"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "s_per_iter": t_iter / done,
+        "finite": bool(np.isfinite(st.U).all()),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=4)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single-stream", action="store_true")
+    ap.add_argument("--iters", type=int, default=None, help="override ADMM iterations per run")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the per-layer path runs on a single GPU)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sub_bit_weight_lb_amd as nq
+    from synth import make_layer
+
+    dev = torch.device("cuda:0")
+    L = make_layer(WORKLOAD)
+    wl = L.workload
+    m, n, r = wl.m, wl.n, wl.r
+    iters = wl.iters if args.iters is None else args.iters
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    W, d_out, d_in, EU, EV = t(L.W), t(L.d_out), t(L.d_in), t(L.EU), t(L.EV)
+    h = nq.LBADMM(m, n, r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
+                  compute_error=True, single_stream=args.single_stream, profile=True)
+    out = h.alloc_outputs(dev)
+    print(f"bench: {WORKLOAD} iters={iters} warmup={args.warmup} steps={args.steps}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
+    torch.cuda.synchronize()
+    h.profile(reset=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = h.profile(reset=True)
+    status, stats = nq.lbadmm_query(h.handle)
+    if status != 0:
+        raise SystemExit(f"run reported {nq.status_string(status)}")
+    h.close()
+
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    value = args.steps * iters / elapsed
+    F = flops_per_iter(m, n, r)
+    rhs_ms, rhs_n = prof["gemm_rhs"]
+    rhs_avg_s = rhs_ms / max(rhs_n, 1) / 1e3
+    rhs_flops = 2.0 * m * n * r
+    achieved = rhs_flops / rhs_avg_s / 1e12
+    traffic = read_traffic(m, n, r, rhs_avg_s)
+    loop_ms = sum(prof[p][0] for p in ("gemm_rhs", "gemm_solve", "svid"))
+    line = {
+        "metric": "LB-ADMM iters/s on 4096x4096 r=2048 fp32 layer; % of fp32 MFMA peak",
+        "value": round(value, 3),
+        "unit": "iters/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "m": m, "n": n, "r": r, "rho": wl.rho,
+                   "admm_iters_per_step": iters, "svid_steps": wl.svid_steps,
+                   "parallelism": "single-gpu"},
+        "fp32_mfma_peak_frac": round(value * F / (FP32_MFMA_PEAK_TFLOPS * 1e12), 4),
+        "factorised_weights_per_s": round(args.steps * m * n / elapsed, 1),
+        "flops_per_iter": F,
+        "roofline": {
+            "kernel": "gemm_nn_kernel<kEpiRhs> (R = Wt V + rho (Z - Lam))",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / FP32_MFMA_PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(rhs_avg_s * 1e3, 4),
+            "launches": rhs_n,
+            "flops_per_launch": rhs_flops,
+        },
+        "phase_ms_per_iter": {p: round(prof[p][0] / max(args.steps * iters, 1), 4)
+                              for p in ("gemm_rhs", "gemm_solve", "chain", "svid")},
+        "phase_ms_per_step": {p: round(prof[p][0] / args.steps, 3) for p in ("prep", "finish")},
+        "rel_err_wtilde": stats["rel_err_wtilde"],
+        "rel_err_w": stats["rel_err_w"],
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(L)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

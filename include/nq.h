@@ -66,6 +66,19 @@ typedef enum nq_status {
                                        then come from the raw latents)                   */
 #define NQ_FLAG_SINGLE_STREAM 0x8u  /* no internal second stream: the r x r chain runs
                                        on `stream` after the right-hand-side GEMM        */
+#define NQ_FLAG_PROFILE       0x10u /* record HIP events around each phase of every run
+                                       (see nq_lbadmm_profile)                           */
+
+/* Phases timed under NQ_FLAG_PROFILE. */
+typedef enum nq_phase {
+  NQ_PHASE_GEMM_RHS = 0,   /* R = Wt V + rho (Z - Lam) (one launch per half-iteration)   */
+  NQ_PHASE_GEMM_SOLVE = 1, /* U = R G^-1, X = U + Lam (one launch per half-iteration)    */
+  NQ_PHASE_CHAIN = 2,      /* Gram + Cholesky/inverse factor + L^-T L^-1 (per half)       */
+  NQ_PHASE_SVID = 3,       /* SVID power steps + dual update (per half)                   */
+  NQ_PHASE_PREP = 4,       /* preconditioning, norms, init latents, initial SVIDs         */
+  NQ_PHASE_FINISH = 5,     /* balancing, scales, packing, errors                          */
+  NQ_NUM_PHASES = 6
+} nq_phase;
 
 typedef struct nq_lbadmm_desc {
   int64_t m;          /* rows of W (output features), >= 1                         */
@@ -147,6 +160,15 @@ nq_status nq_lbadmm_query(nq_lbadmm_t h, nq_lbadmm_stats* stats);
 nq_status nq_lbadmm_get_state(nq_lbadmm_t h, float* U, float* V,
                               float* Z_U, float* Lam_U, float* Z_V, float* Lam_V,
                               void* stream);
+
+/* Under NQ_FLAG_PROFILE: wait for the handle's pending work and return, per
+ * nq_phase, the summed device time in ms (ms[NQ_NUM_PHASES], host) and the
+ * number of timed intervals (count[NQ_NUM_PHASES], host) since the last reset;
+ * reset != 0 clears the totals afterwards. Each interval is bracketed by HIP
+ * events on the stream its kernels run on. Events are kept in a ring sized
+ * for 8 runs; a run that would overflow it first waits for the pending ones.
+ * NQ_ERR_INVALID_ARG if the handle was created without NQ_FLAG_PROFILE. */
+nq_status nq_lbadmm_profile(nq_lbadmm_t h, double* ms, int64_t* count, int32_t reset);
 
 /* Free the handle and its workspace (NULL is ignored). Waits for its work. */
 void nq_lbadmm_destroy(nq_lbadmm_t h);

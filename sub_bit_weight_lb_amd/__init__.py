@@ -20,11 +20,11 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE,  # noqa: F401
-                   NQ_FLAG_SINGLE_STREAM, NQ_OK, Desc, Stats)
+                   NQ_FLAG_PROFILE, NQ_FLAG_SINGLE_STREAM, NQ_OK, PHASES, Desc, Stats)
 
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
-    "lbadmm_destroy", "lbadmm_workspace_bytes", "pack_signs", "op_precondition", "op_gram",
+    "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "op_precondition", "op_gram",
     "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
 ]
@@ -141,6 +141,16 @@ def lbadmm_get_state(h, U=None, V=None, Z_U=None, Lam_U=None, Z_V=None, Lam_V=No
         "nq_lbadmm_get_state")
 
 
+def lbadmm_profile(h, reset=False) -> dict:
+    """Per-phase device time under NQ_FLAG_PROFILE: {phase: (total_ms, intervals)}."""
+    n = len(PHASES)
+    ms = (C.c_double * n)()
+    cnt = (C.c_int64 * n)()
+    _check(_lib.load().nq_lbadmm_profile(C.c_void_p(h), ms, cnt, 1 if reset else 0),
+           "nq_lbadmm_profile")
+    return {p: (float(ms[i]), int(cnt[i])) for i, p in enumerate(PHASES)}
+
+
 def lbadmm_destroy(h):
     if h:
         _lib.load().nq_lbadmm_destroy(C.c_void_p(h))
@@ -242,8 +252,9 @@ class LBADMM:
     """One handle for one layer shape; reusable across runs of that shape."""
 
     def __init__(self, m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0, compute_error=True,
-                 init_exact=False, balance=True, single_stream=False):
+                 init_exact=False, balance=True, single_stream=False, profile=False):
         flags = 0
+        flags |= NQ_FLAG_PROFILE if profile else 0
         flags |= NQ_FLAG_COMPUTE_ERROR if compute_error else 0
         flags |= NQ_FLAG_INIT_EXACT if init_exact else 0
         flags |= 0 if balance else NQ_FLAG_NO_BALANCE
@@ -268,6 +279,9 @@ class LBADMM:
         st = lbadmm_run(self.handle, W, d_out, d_in, U0, V0, out["U"], out["V"], out["s1"],
                         out["s2"], out["U_bits"], out["V_bits"], want_stats, stream)
         return Result(out["U"], out["V"], out["s1"], out["s2"], out["U_bits"], out["V_bits"], st)
+
+    def profile(self, reset=False):
+        return lbadmm_profile(self.handle, reset)
 
     def state(self, stream=None):
         torch = _torch()

@@ -20,6 +20,9 @@ NQ_FLAG_COMPUTE_ERROR = 0x1
 NQ_FLAG_INIT_EXACT = 0x2
 NQ_FLAG_NO_BALANCE = 0x4
 NQ_FLAG_SINGLE_STREAM = 0x8
+NQ_FLAG_PROFILE = 0x10
+
+PHASES = ["gemm_rhs", "gemm_solve", "chain", "svid", "prep", "finish"]
 
 
 class Desc(C.Structure):
@@ -49,6 +52,7 @@ SIGNATURES = {
     "nq_lbadmm_query": (ST, [P, C.POINTER(Stats)]),
     "nq_lbadmm_get_state": (ST, [P, P, P, P, P, P, P, P]),
     "nq_lbadmm_destroy": (None, [P]),
+    "nq_lbadmm_profile": (ST, [P, C.POINTER(C.c_double), C.POINTER(I64), C.c_int32]),
     "nq_pack_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_op_precondition": (ST, [P, I64, I64, I64, P, P, P, I64, P]),
     "nq_op_gram": (ST, [P, I64, I64, I64, F32, P, I64, P]),

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <vector>
 
 using namespace nq;
 
@@ -27,8 +28,9 @@ nq_status hip_fail(hipError_t e, const char* what) { return hip_error(e, what); 
 
 #define HIPCHK(expr) NQ_HIPCHK(expr)
 
-constexpr uint32_t kKnownFlags =
-    NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT | NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM;
+constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
+                                  NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE;
+constexpr int kProfileRuns = 8;
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
@@ -118,6 +120,12 @@ struct nq_lbadmm {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
+  // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
+  std::vector<hipEvent_t> prof_ev;
+  std::vector<int> prof_phase;  // phase of each pending pair
+  size_t prof_next = 0;         // next free pair
+  double prof_ms[NQ_NUM_PHASES] = {0};
+  int64_t prof_cnt[NQ_NUM_PHASES] = {0};
 };
 
 namespace {
@@ -183,6 +191,34 @@ void plan(nq_lbadmm* h) {
   lauum_split(h->rp, &h->l_nch, &h->l_kc);
 }
 
+size_t pairs_per_run(const nq_lbadmm* h) { return 4 + (size_t)h->d.iters * 8; }
+
+// Fold every pending pair into the totals (waits for the last one).
+nq_status prof_harvest(nq_lbadmm* h) {
+  if (h->prof_next == 0) return NQ_OK;
+  for (size_t p = 0; p < h->prof_next; ++p) HIPCHK(hipEventSynchronize(h->prof_ev[2 * p + 1]));
+  for (size_t p = 0; p < h->prof_next; ++p) {
+    float ms = 0.0f;
+    HIPCHK(hipEventElapsedTime(&ms, h->prof_ev[2 * p], h->prof_ev[2 * p + 1]));
+    h->prof_ms[h->prof_phase[p]] += ms;
+    h->prof_cnt[h->prof_phase[p]] += 1;
+  }
+  h->prof_next = 0;
+  return NQ_OK;
+}
+
+// Start / end of a timed interval: returns the pair index (or -1 when off).
+long prof_begin(nq_lbadmm* h, int phase, hipStream_t s) {
+  if (!(h->d.flags & NQ_FLAG_PROFILE)) return -1;
+  const size_t p = h->prof_next++;
+  h->prof_phase[p] = phase;
+  if (hipEventRecord(h->prof_ev[2 * p], s) != hipSuccess) return -1;
+  return (long)p;
+}
+void prof_end(nq_lbadmm* h, long p, hipStream_t s) {
+  if (p >= 0) (void)hipEventRecord(h->prof_ev[2 * p + 1], s);
+}
+
 struct Half {
   const float* Wside;  // M x K (padded, ld K)
   int M, K;            // rows of the factor being solved, rows of the other factor
@@ -199,26 +235,34 @@ nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
   hipStream_t cs = overlap ? h->aux : s;
   if (overlap) HIPCHK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
   // r x r chain: G = other^T other + rho I, L and L^-1, G^-1 = L^-T L^-1
+  long pc = prof_begin(h, NQ_PHASE_CHAIN, cs);
   HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, cs));
   HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, cs));
   HIPCHK(launch_syrk_partial(h->Minv, rp, rp, rp, h->l_kc, true, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, h->l_nch, rp, 0.0f, h->Ginv, rp, cs));
+  prof_end(h, pc, cs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_join, h->aux));
   // R = Wside other + rho (Z - Lam)
   GemmArgs g{};
   g.A = x.Wside; g.lda = x.K; g.B = x.other; g.ldb = rp; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
+  long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, s);
   HIPCHK(launch_gemm(g, kEpiRhs, s));
+  prof_end(h, pr, s);
   if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
   // out = R G^-1, X = out + Lam (into Lam)
   GemmArgs q{};
   q.A = h->R; q.lda = rp; q.B = h->Ginv; q.ldb = rp; q.C = x.out; q.ldc = rp;
   q.X = x.Lam; q.M = x.M; q.N = rp; q.K = rp;
+  long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
+  prof_end(h, ps, s);
   if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
   // Z = SVID(X); Lam = X - Z; P = Z - Lam
+  long pv = prof_begin(h, NQ_PHASE_SVID, s);
   HIPCHK(launch_svid(x.Lam, x.P, x.M, rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, s));
+  prof_end(h, pv, s);
   return NQ_OK;
 }
 
@@ -288,6 +332,12 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t0);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t1);
+  if (e == hipSuccess && (h->d.flags & NQ_FLAG_PROFILE)) {
+    const size_t pairs = pairs_per_run(h) * kProfileRuns;
+    h->prof_ev.assign(2 * pairs, nullptr);
+    h->prof_phase.assign(pairs, 0);
+    for (size_t i = 0; i < 2 * pairs && e == hipSuccess; ++i) e = hipEventCreate(&h->prof_ev[i]);
+  }
   // Padding must read as zero from the start (the run rewrites every live
   // region it reads, but the finish kernels read padded rows).
   if (e == hipSuccess) e = hipMemset(h->base, 0, h->bytes);
@@ -311,6 +361,8 @@ void nq_lbadmm_destroy(nq_lbadmm_t h) {
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
+  for (hipEvent_t ev : h->prof_ev)
+    if (ev) (void)hipEventDestroy(ev);
   if (h->aux) (void)hipStreamDestroy(h->aux);
   if (h->base) (void)hipFree(h->base);
   if (cur != h->device) (void)hipSetDevice(cur);
@@ -337,7 +389,12 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   const int mp = h->mp, np_ = h->np_, rp = h->rp;
   const bool overlap = !(d.flags & NQ_FLAG_SINGLE_STREAM);
 
+  if ((d.flags & NQ_FLAG_PROFILE) && h->prof_next + pairs_per_run(h) > h->prof_phase.size()) {
+    nq_status ps = prof_harvest(h);
+    if (ps != NQ_OK) return ps;
+  }
   HIPCHK(hipEventRecord(h->ev_t0, s));
+  long pp = prof_begin(h, NQ_PHASE_PREP, s);
   HIPCHK(launch_stats_init(h->st, s));
   HIPCHK(launch_check_precond(d_out, d.m, d_in, d.n, h->st, s));
   HIPCHK(launch_precondition(W, ldw, d.m, d.n, d_out, d_in, h->Wt, h->WtT, mp, np_, h->part_wt,
@@ -355,6 +412,7 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   }
   HIPCHK(launch_svid(h->LamU, h->PU, mp, rp, (int)d.r, d.svid_steps, 0, h->svU, s));
   HIPCHK(launch_svid(h->LamV, h->PV, np_, rp, (int)d.r, d.svid_steps, 0, h->svV, s));
+  prof_end(h, pp, s);
   if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
 
   Half hu{h->Wt, mp, np_, h->V, h->U, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc};
@@ -367,6 +425,7 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   }
 
   // finish: balance, scales, signs, bits, errors
+  long pf = prof_begin(h, NQ_PHASE_FINISH, s);
   const int nchU = svid_nchunks(mp), nchV = svid_nchunks(np_);
   HIPCHK(launch_colsumsq(h->U, mp, rp, h->colpartU, s));
   HIPCHK(launch_colsumsq(h->V, np_, rp, h->colpartV, s));
@@ -381,10 +440,28 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   if (d.flags & NQ_FLAG_COMPUTE_ERROR)
     HIPCHK(launch_error(h->SU, h->SV, mp, np_, rp, h->s1w, h->s2w, h->Wt, W, ldw, d.m, d.n,
                         h->s1c, h->s2c, h->err_parts, h->st, s));
+  prof_end(h, pf, s);
   HIPCHK(hipEventRecord(h->ev_t1, s));
   h->last_stream = s;
   h->has_run = true;
   if (stats) return nq_lbadmm_query(h, stats);
+  return NQ_OK;
+}
+
+nq_status nq_lbadmm_profile(nq_lbadmm_t h, double* ms, int64_t* count, int32_t reset) {
+  if (!h || !ms || !count) return fail(NQ_ERR_INVALID_ARG, "handle, ms and count are required");
+  if (!(h->d.flags & NQ_FLAG_PROFILE))
+    return fail(NQ_ERR_INVALID_ARG, "handle was created without NQ_FLAG_PROFILE");
+  nq_status st = prof_harvest(h);
+  if (st != NQ_OK) return st;
+  for (int p = 0; p < NQ_NUM_PHASES; ++p) {
+    ms[p] = h->prof_ms[p];
+    count[p] = h->prof_cnt[p];
+    if (reset) {
+      h->prof_ms[p] = 0.0;
+      h->prof_cnt[p] = 0;
+    }
+  }
   return NQ_OK;
 }
 
