@@ -5,10 +5,10 @@
 // section 待办事项, names this factorisation as where LB-ADMM spends its time).
 //
 // Right-looking, block size 64, three launches per block column k:
-//   diag(k):   one workgroup factors the 64 x 64 diagonal block in LDS by
-//              outer-product elimination, applying the same row operations to
-//              an identity block, which yields both L_kk and M_kk = L_kk^-1
-//              with one barrier per column.
+//   diag(k):   one workgroup factors the 64 x 64 diagonal block by
+//              outer-product elimination with register-resident 4 x 4 blocks,
+//              applying the same row operations to an identity block, which
+//              yields both L_kk and M_kk = L_kk^-1 with one barrier per column.
 //   panel(k):  L_ik = A_ik M_kk^T for i > k, and row k of M:
 //              M_kj = -M_kk S_kj for j < k (S_kj accumulated in M's block).
 //   update(k): trailing update A_ij -= L_ik L_jk^T (i >= j > k) and the
@@ -85,44 +85,96 @@ __device__ void block_mm(const float* __restrict__ X, const float* __restrict__ 
   }
 }
 
+// Diagonal block: L_kk and M_kk = L_kk^-1 of the 64 x 64 block (k, k).
+// Outer-product elimination on the lower triangle with the same row
+// operations applied to an identity block E. Thread t holds the 4 x 4 block
+// (t / 16, t % 16) of T and of E in registers. Step j needs column j of T
+// (multipliers and partners T[c][j]) and row j of E; their owners publish
+// them to LDS after the previous step's update, so each step costs one
+// barrier. At the end L = T D^-1/2 and M = D^-1/2 E with D the pivots.
 __global__ __launch_bounds__(NT) void chol_diag_kernel(float* A, float* M, int rp, int k,
                                                        int r_real, DevStats* st) {
-  __shared__ float T[NB][NB + 1];
-  __shared__ float E[NB][NB + 1];
+  __shared__ __attribute__((aligned(16))) float colbuf[2][NB];
+  __shared__ __attribute__((aligned(16))) float erow[2][NB];
+  __shared__ float dvec[NB];
   const int tid = threadIdx.x;
-  const int base = k * NB;
-  for (int idx = tid; idx < NB * NB; idx += NT) {
-    const int i = idx >> 6, c = idx & 63;
-    T[i][c] = A[(int64_t)(base + i) * rp + base + c];
-    E[i][c] = (i == c) ? 1.0f : 0.0f;
+  const int bi = tid >> 4, bj = tid & 15;
+  const bool lower = bi >= bj;
+  const int64_t base = (int64_t)k * NB;
+  float Tr[4][4], Er[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const f32x4 v = *(const f32x4*)&A[(base + 4 * bi + a) * rp + base + 4 * bj];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      Tr[a][b] = v[b];
+      Er[a][b] = (bi == bj && a == b) ? 1.0f : 0.0f;
+    }
+  }
+  if (bj == 0) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) colbuf[0][4 * bi + a] = Tr[a][0];
+  }
+  if (bi == 0) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) erow[0][4 * bj + b] = Er[0][b];
   }
   __syncthreads();
+#pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const float d = T[j][j];
-    if (tid == 0 && !(d > 0.0f && isfinite(d)) && base + j < r_real)
-      atomicMin(&st->potrf_info, base + j + 1);
+    const int buf = j & 1;
+    const float d = colbuf[buf][j];
+    if (tid == 0) {
+      dvec[j] = d;
+      if (!(d > 0.0f && isfinite(d)) && (int)base + j < r_real)
+        atomicMin(&st->potrf_info, (int)base + j + 1);
+    }
     const float inv = 1.0f / d;
-    for (int idx = (j + 1) * NB + tid; idx < NB * NB; idx += NT) {
-      const int i = idx >> 6, c = idx & 63;
-      if (c <= i) {
-        // only the lower triangle is kept current: the symmetric partner of
-        // T[j][c] (c > j) is T[c][j]
-        const float l = T[i][j] * inv;
-        if (c <= j) E[i][c] -= l * E[j][c];
-        else T[i][c] -= l * T[c][j];
+    if (lower && 4 * bi + 3 > j) {
+      const f32x4 li = *(const f32x4*)&colbuf[buf][4 * bi];
+      const f32x4 cj = *(const f32x4*)&colbuf[buf][4 * bj];
+      const f32x4 ej = *(const f32x4*)&erow[buf][4 * bj];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        if (4 * bi + a > j) {
+          const float l = li[a] * inv;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            if (4 * bj + b > j) Tr[a][b] -= l * cj[b];
+            Er[a][b] -= l * ej[b];
+          }
+        }
+      }
+    }
+    if (j + 1 < NB) {
+      const int jn = j + 1, jb = jn >> 2, jo = jn & 3;
+      if (bj == jb) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) colbuf[buf ^ 1][4 * bi + a] = Tr[a][jo];
+      }
+      if (bi == jb) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) erow[buf ^ 1][4 * bj + b] = Er[jo][b];
       }
     }
     __syncthreads();
   }
-  for (int idx = tid; idx < NB * NB; idx += NT) {
-    const int i = idx >> 6, c = idx & 63;
-    float lv = 0.0f, mv = 0.0f;
-    if (c <= i) {
-      lv = T[i][c] / sqrtf(T[c][c]);
-      mv = E[i][c] / sqrtf(T[i][i]);
+  f32x4 lv[4], mv[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int i = 4 * bi + a;
+    const float si = sqrtf(dvec[i]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int c = 4 * bj + b;
+      lv[a][b] = c <= i ? Tr[a][b] / sqrtf(dvec[c]) : 0.0f;
+      mv[a][b] = c <= i ? Er[a][b] / si : 0.0f;
     }
-    A[(int64_t)(base + i) * rp + base + c] = lv;
-    M[(int64_t)(base + i) * rp + base + c] = mv;
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    *(f32x4*)&A[(base + 4 * bi + a) * rp + base + 4 * bj] = lv[a];
+    *(f32x4*)&M[(base + 4 * bi + a) * rp + base + 4 * bj] = mv[a];
   }
 }
 

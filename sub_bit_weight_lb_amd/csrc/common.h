@@ -71,13 +71,15 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
 struct SvidWork {
   float* a;        // rows_pad
   float* b;        // rp
-  float* colpart;  // nchunks x rp
-  float* aapart;   // nchunks
+  float* colpart;  // svid_partials(rows_pad, rp) x rp
+  float* aapart;   // svid_partials(rows_pad, rp)
   float* bbpart;   // rp / 128
 };
-int svid_nchunks(int rows_pad);
+int svid_nchunks(int rows_pad);            // 64-row chunks of the column pass
+int svid_partials(int rows_pad, int rp);   // partial rows the SVID work arrays hold
 // mode 0: init (P = Z, X left as is), mode 1: update (X <- X - Z, P = 2Z - X_old),
 // mode 2: plain (Z written to P; X untouched).
+// rows_pad % 8 == 0, rp % 128 == 0.
 hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int T,
                        int mode, const SvidWork& w, hipStream_t s);
 

@@ -144,11 +144,13 @@ size_t layout(nq_lbadmm* h) {
   size_t o_G = a.take<float>(rp * rp), o_M = a.take<float>(rp * rp), o_Gi = a.take<float>(rp * rp);
   size_t o_gp = a.take<float>((size_t)gch * rp * rp);
   const int nchU = svid_nchunks((int)mp), nchV = svid_nchunks((int)np_);
+  const int spU = std::max(nchU, svid_partials((int)mp, (int)rp));
+  const int spV = std::max(nchV, svid_partials((int)np_, (int)rp));
   size_t o_sUa = a.take<float>(mp), o_sUb = a.take<float>(rp),
-         o_sUc = a.take<float>((size_t)nchU * rp), o_sUaa = a.take<float>(nchU),
+         o_sUc = a.take<float>((size_t)spU * rp), o_sUaa = a.take<float>(spU),
          o_sUbb = a.take<float>(rp / 128);
   size_t o_sVa = a.take<float>(np_), o_sVb = a.take<float>(rp),
-         o_sVc = a.take<float>((size_t)nchV * rp), o_sVaa = a.take<float>(nchV),
+         o_sVc = a.take<float>((size_t)spV * rp), o_sVaa = a.take<float>(spV),
          o_sVbb = a.take<float>(rp / 128);
   const int npre = precondition_nblocks((int)mp, (int)np_);
   size_t o_pwt = a.take<double>(npre), o_pw = a.take<double>(npre);

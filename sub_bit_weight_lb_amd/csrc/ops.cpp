@@ -162,8 +162,8 @@ nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx, in
   if (rows < 1 || cols < 1 || T < 1 || ldx < cols || !X || (Z && ldz < cols))
     return set_error(NQ_ERR_INVALID_ARG, "bad svid arguments");
   hipStream_t s = (hipStream_t)stream;
-  const int64_t rows_pad = round_up(rows, 4), rp = round_up(cols, 128);
-  const int nch = svid_nchunks((int)rows_pad);
+  const int64_t rows_pad = round_up(rows, 8), rp = round_up(cols, 128);
+  const int nch = std::max(svid_nchunks((int)rows_pad), svid_partials((int)rows_pad, (int)rp));
   DevBuf x, p, wa, wb, wc, waa, wbb;
   NQ_HIPCHK(x.alloc(sizeof(float) * rows_pad * rp));
   NQ_HIPCHK(p.alloc(sizeof(float) * rows_pad * rp));

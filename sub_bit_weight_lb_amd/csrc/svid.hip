@@ -8,10 +8,11 @@
 //   Dual: Lam = X - Z, and the right-hand side of the next solve needs
 //   Z - Lam = 2 Z - X, which is stored instead of Z (one read there).
 //
-// HBM-bound. Per step: a row pass (one wave per row, float4 loads, wave
-// reduction) and a column pass (one thread per column over a 64-row chunk,
-// coalesced along the row), then a small column reduce. All reductions run in
-// a fixed order, so results are bit-reproducible.
+// HBM-bound. Per power step one fused pass: each block holds a slab of full
+// rows in registers, forms a for its rows and then its rows' share of
+// |X|^T a, so X is read once per step; a small reduce then forms b. For
+// r beyond 16384 a row pass and a column pass replace the fused one. All
+// reductions run in a fixed order, so results are bit-reproducible.
 #include "common.h"
 
 namespace nq {
@@ -57,22 +58,39 @@ __global__ __launch_bounds__(256) void svid_row_kernel(const float* __restrict__
 }
 
 // colpart[c][j] = sum_{i in chunk c} w(X_ij, a_i); aapart[c] = sum a_i^2.
-// OP 0: |X_ij| a_i (SVID); OP 1: X_ij^2 (column norms).
+// OP 0: |X_ij| a_i (SVID); OP 1: X_ij^2 (column norms). 32 x 8 threads:
+// float4 columns x row stripes of the 64-row chunk, fixed-order reduction.
 template <int OP>
-__global__ __launch_bounds__(CB) void colsum_kernel(const float* __restrict__ X, int rp,
-                                                    int rows_pad, const float* __restrict__ a,
-                                                    float* __restrict__ colpart,
-                                                    float* __restrict__ aapart) {
-  const int j = blockIdx.x * CB + threadIdx.x;
+__global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X, int rp,
+                                                     int rows_pad, const float* __restrict__ a,
+                                                     float* __restrict__ colpart,
+                                                     float* __restrict__ aapart) {
+  __shared__ f32x4 red[8][32];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int q = blockIdx.x * 32 + tx;
   const int c = blockIdx.y;
   const int i0 = c * CR, i1 = min(rows_pad, i0 + CR);
-  float acc = 0.0f;
-  for (int i = i0; i < i1; ++i) {
-    const float x = X[(int64_t)i * rp + j];
-    if (OP == 0) acc += fabsf(x) * a[i];
-    else acc += x * x;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int i = i0 + ty; i < i1; i += 8) {
+    const f32x4 x = ((const f32x4*)(X + (int64_t)i * rp))[q];
+    if (OP == 0) {
+      const float ai = a[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += fabsf(x[e]) * ai;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += x[e] * x[e];
+    }
   }
-  colpart[(int64_t)c * rp + j] = acc;
+  red[ty][tx] = acc;
+  __syncthreads();
+  if (ty == 0) {
+    f32x4 t = red[0][tx];
+#pragma unroll
+    for (int y = 1; y < 8; ++y) t += red[y][tx];
+    ((f32x4*)(colpart + (int64_t)c * rp))[q] = t;
+  }
   if (OP == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
     float aa = 0.0f;
     for (int i = i0; i < i1; ++i) aa += a[i] * a[i];
@@ -80,27 +98,124 @@ __global__ __launch_bounds__(CB) void colsum_kernel(const float* __restrict__ X,
   }
 }
 
-// b_j = sum_c colpart[c][j] / aa, aa = sum aapart; bbpart[block] = sum b_j^2.
-__global__ __launch_bounds__(CB) void svid_colreduce_kernel(const float* __restrict__ colpart,
-                                                            int nchunks,
-                                                            const float* __restrict__ aapart,
-                                                            int rp, float* __restrict__ b,
-                                                            float* __restrict__ bbpart) {
-  __shared__ float red[CB];
-  const int j = blockIdx.x * CB + threadIdx.x;
-  float aa = 0.0f;
-  for (int c = 0; c < nchunks; ++c) aa += aapart[c];
-  float p = 0.0f;
-  for (int c = 0; c < nchunks; ++c) p += colpart[(int64_t)c * rp + j];
-  const float bj = aa > 0.0f ? p / aa : 0.0f;
-  b[j] = bj;
-  red[threadIdx.x] = bj * bj;
+// One fused power step for a slab of RS full rows held in registers:
+//   a_i = sum_j |X_ij| b_j / bb          (rows of the slab, block reduction)
+//   part[slab][j] = sum_{i in slab} |X_ij| a_i,  aapart[slab] = sum a_i^2
+// so X is read once per step. Thread t owns float4 columns t + 256 u.
+template <int RS, int NU>
+__global__ __launch_bounds__(256) void svid_step_kernel(const float* __restrict__ X, int rp,
+                                                        const float* __restrict__ b,
+                                                        const float* __restrict__ bbpart, int nbb,
+                                                        float* __restrict__ a,
+                                                        float* __restrict__ part,
+                                                        float* __restrict__ aapart) {
+  __shared__ float red[RS][4];
+  __shared__ float arow[RS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rp4 = rp / 4;
+  const int64_t i0 = (int64_t)blockIdx.x * RS;
+  float bb = 0.0f;
+  for (int q = lane; q < nbb; q += 64) bb += bbpart[q];
+  bb = wave_sum(bb);
+  f32x4 x[RS][NU];
+  f32x4 bv[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int q = tid + 256 * u;
+    bv[u] = q < rp4 ? ((const f32x4*)b)[q] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int r = 0; r < RS; ++r)
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int q = tid + 256 * u;
+      x[r][u] = q < rp4 ? ((const f32x4*)(X + (i0 + r) * rp))[q] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+  float s[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += fabsf(x[r][u][e]) * bv[u][e];
+    s[r] = wave_sum(acc);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r) red[r][wave] = s[r];
+  }
   __syncthreads();
-  for (int o = CB / 2; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+  if (tid < RS) {
+    const float tot = red[tid][0] + red[tid][1] + red[tid][2] + red[tid][3];
+    const float ai = bb > 0.0f ? tot / bb : 0.0f;
+    arow[tid] = ai;
+    a[i0 + tid] = ai;
+  }
+  __syncthreads();
+  float av[RS];
+#pragma unroll
+  for (int r = 0; r < RS; ++r) av[r] = arow[r];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int q = tid + 256 * u;
+    if (q < rp4) {
+      f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int r = 0; r < RS; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] += fabsf(x[r][u][e]) * av[r];
+      ((f32x4*)(part + (int64_t)blockIdx.x * rp))[q] = p;
+    }
+  }
+  if (tid == 0) {
+    float aa = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RS; ++r) aa += av[r] * av[r];
+    aapart[blockIdx.x] = aa;
+  }
+}
+
+// b_j = sum_c part[c][j] / aa over nch partial rows; 128 columns per block,
+// 32 x 8 threads (float4 columns x chunk stripes), fixed-order reductions.
+__global__ __launch_bounds__(256) void svid_reduce_wide_kernel(const float* __restrict__ part,
+                                                               int nch,
+                                                               const float* __restrict__ aapart,
+                                                               int rp, float* __restrict__ b,
+                                                               float* __restrict__ bbpart) {
+  __shared__ f32x4 red[8][32];
+  __shared__ float aared[256];
+  __shared__ float bbred[32];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int q = blockIdx.x * 32 + tx;  // float4 column index
+  float aa = 0.0f;
+  for (int c = threadIdx.x; c < nch; c += 256) aa += aapart[c];
+  aared[threadIdx.x] = aa;
+  f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int c = ty; c < nch; c += 8) p += ((const f32x4*)(part + (int64_t)c * rp))[q];
+  red[ty][tx] = p;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) aared[threadIdx.x] += aared[threadIdx.x + o];
     __syncthreads();
   }
-  if (threadIdx.x == 0) bbpart[blockIdx.x] = red[0];
+  if (ty == 0) {
+    f32x4 t = red[0][tx];
+#pragma unroll
+    for (int y = 1; y < 8; ++y) t += red[y][tx];
+    const float tot = aared[0];
+    f32x4 bj;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bj[e] = tot > 0.0f ? t[e] / tot : 0.0f;
+    ((f32x4*)b)[q] = bj;
+    bbred[tx] = bj[0] * bj[0] + bj[1] * bj[1] + bj[2] * bj[2] + bj[3] * bj[3];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+    for (int y = 0; y < 32; ++y) t += bbred[y];
+    bbpart[blockIdx.x] = t;
+  }
 }
 
 // Z = sign(X) a_i b_j; mode 0: P = Z, X = 0; mode 1: X = X - Z, P = Z - X_new;
@@ -139,18 +254,52 @@ __global__ __launch_bounds__(256) void svid_final_kernel(float* __restrict__ X,
 
 int svid_nchunks(int rows_pad) { return (rows_pad + CR - 1) / CR; }
 
+namespace {
+// Slab rows RS and float4s per thread NU for the fused step at this rp.
+template <int RS, int NU>
+void launch_step(float* X, int rows_pad, int rp, int nbb, const SvidWork& w, hipStream_t s) {
+  hipLaunchKernelGGL((svid_step_kernel<RS, NU>), dim3(rows_pad / RS), dim3(256), 0, s, X, rp, w.b,
+                     w.bbpart, nbb, w.a, w.colpart, w.aapart);
+}
+bool fused_step(float* X, int rows_pad, int rp, int nbb, const SvidWork& w, hipStream_t s) {
+  const int nu = (rp / 4 + 255) / 256;
+  if (nu <= 1) launch_step<8, 1>(X, rows_pad, rp, nbb, w, s);
+  else if (nu <= 2) launch_step<8, 2>(X, rows_pad, rp, nbb, w, s);
+  else if (nu <= 4) launch_step<4, 4>(X, rows_pad, rp, nbb, w, s);
+  else if (nu <= 8) launch_step<2, 8>(X, rows_pad, rp, nbb, w, s);
+  else if (nu <= 16) launch_step<1, 16>(X, rows_pad, rp, nbb, w, s);
+  else return false;
+  return true;
+}
+int fused_rows(int rp) {
+  const int nu = (rp / 4 + 255) / 256;
+  return nu <= 2 ? 8 : nu <= 4 ? 4 : nu <= 8 ? 2 : nu <= 16 ? 1 : 0;
+}
+}  // namespace
+
+int svid_partials(int rows_pad, int rp) {
+  const int rs = fused_rows(rp);
+  return rs ? rows_pad / rs : svid_nchunks(rows_pad);
+}
+
 hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int T, int mode,
                        const SvidWork& w, hipStream_t s) {
-  if (rp % CB || rows_pad % 4) return hipErrorInvalidValue;
+  if (rp % CB || rows_pad % 8) return hipErrorInvalidValue;
   const int nbb = rp / CB;
   const int nch = svid_nchunks(rows_pad);
+  const int rs = fused_rows(rp);
   hipLaunchKernelGGL(svid_init_b_kernel, dim3(nbb), dim3(CB), 0, s, w.b, w.bbpart, rp, r_real);
   for (int t = 0; t < T; ++t) {
+    if (rs && fused_step(X, rows_pad, rp, nbb, w, s)) {
+      hipLaunchKernelGGL(svid_reduce_wide_kernel, dim3(rp / 128), dim3(256), 0, s, w.colpart,
+                         rows_pad / rs, w.aapart, rp, w.b, w.bbpart);
+      continue;
+    }
     hipLaunchKernelGGL(svid_row_kernel, dim3(rows_pad / 4), dim3(256), 0, s, X, rp, w.b,
                        w.bbpart, nbb, w.a);
-    hipLaunchKernelGGL(colsum_kernel<0>, dim3(rp / CB, nch), dim3(CB), 0, s, X, rp, rows_pad,
+    hipLaunchKernelGGL(colsum_kernel<0>, dim3(rp / 128, nch), dim3(256), 0, s, X, rp, rows_pad,
                        w.a, w.colpart, w.aapart);
-    hipLaunchKernelGGL(svid_colreduce_kernel, dim3(nbb), dim3(CB), 0, s, w.colpart, nch,
+    hipLaunchKernelGGL(svid_reduce_wide_kernel, dim3(rp / 128), dim3(256), 0, s, w.colpart, nch,
                        w.aapart, rp, w.b, w.bbpart);
   }
   const int64_t n4 = (int64_t)rows_pad * rp / 4;
@@ -163,7 +312,7 @@ hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int
 hipError_t launch_colsumsq(const float* F, int rows_pad, int rp, float* colpart, hipStream_t s) {
   if (rp % CB) return hipErrorInvalidValue;
   const int nch = svid_nchunks(rows_pad);
-  hipLaunchKernelGGL(colsum_kernel<1>, dim3(rp / CB, nch), dim3(CB), 0, s, F, rp, rows_pad,
+  hipLaunchKernelGGL(colsum_kernel<1>, dim3(rp / 128, nch), dim3(256), 0, s, F, rp, rows_pad,
                      (const float*)nullptr, colpart, (float*)nullptr);
   return hipGetLastError();
 }
