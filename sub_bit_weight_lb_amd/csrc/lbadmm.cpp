@@ -9,6 +9,7 @@
 // joins them. SVID of one half overlaps the next half's chain.
 #include "nq.h"
 #include "abi.h"
+#include "chol_schedule.h"
 #include "common.h"
 
 #include <climits>
@@ -116,6 +117,8 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
+  CholDagWork dag{};
+  int ntasks = 0;
   hipStream_t aux = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
@@ -148,10 +151,12 @@ size_t layout(nq_lbadmm* h) {
   const int spV = std::max(nchV, svid_partials((int)np_, (int)rp));
   size_t o_sUa = a.take<float>(mp), o_sUb = a.take<float>(rp),
          o_sUc = a.take<float>((size_t)spU * rp), o_sUaa = a.take<float>(spU),
-         o_sUbb = a.take<float>(rp / 128);
+         o_sUbb = a.take<float>(rp / 128), o_sUp2 = a.take<float>(kSvidReduceRows * rp),
+         o_sUct = a.take<int>(rp / 128);
   size_t o_sVa = a.take<float>(np_), o_sVb = a.take<float>(rp),
          o_sVc = a.take<float>((size_t)spV * rp), o_sVaa = a.take<float>(spV),
-         o_sVbb = a.take<float>(rp / 128);
+         o_sVbb = a.take<float>(rp / 128), o_sVp2 = a.take<float>(kSvidReduceRows * rp),
+         o_sVct = a.take<int>(rp / 128);
   const int npre = precondition_nblocks((int)mp, (int)np_);
   size_t o_pwt = a.take<double>(npre), o_pw = a.take<double>(npre);
   size_t o_err = a.take<double>(2 * (size_t)error_nparts((int)mp, (int)np_));
@@ -160,6 +165,10 @@ size_t layout(nq_lbadmm* h) {
   size_t o_s1c = a.take<float>(mp), o_s2c = a.take<float>(np_);
   size_t o_SU = a.take<int8_t>(mp * rp), o_SV = a.take<int8_t>(np_ * rp);
   size_t o_st = a.take<DevStats>(1);
+  const int R = (int)(rp / kNB);
+  size_t o_tasks = a.take<CholDevTask>((size_t)h->ntasks);
+  size_t o_flags = a.take<uint64_t>((size_t)4 * R * R);
+  size_t o_epoch = a.take<uint64_t>(1), o_ticket = a.take<int>(1);
   if (h->base) {
     char* b = h->base;
     h->Wt = (float*)(b + o_Wt); h->WtT = (float*)(b + o_WtT);
@@ -170,9 +179,11 @@ size_t layout(nq_lbadmm* h) {
     h->G = (float*)(b + o_G); h->Minv = (float*)(b + o_M); h->Ginv = (float*)(b + o_Gi);
     h->gpart = (float*)(b + o_gp);
     h->svU = SvidWork{(float*)(b + o_sUa), (float*)(b + o_sUb), (float*)(b + o_sUc),
-                      (float*)(b + o_sUaa), (float*)(b + o_sUbb)};
+                      (float*)(b + o_sUaa), (float*)(b + o_sUbb), (float*)(b + o_sUp2),
+                      (int*)(b + o_sUct)};
     h->svV = SvidWork{(float*)(b + o_sVa), (float*)(b + o_sVb), (float*)(b + o_sVc),
-                      (float*)(b + o_sVaa), (float*)(b + o_sVbb)};
+                      (float*)(b + o_sVaa), (float*)(b + o_sVbb), (float*)(b + o_sVp2),
+                      (int*)(b + o_sVct)};
     h->part_wt = (double*)(b + o_pwt); h->part_w = (double*)(b + o_pw);
     h->err_parts = (double*)(b + o_err);
     h->colpartU = (float*)(b + o_cpU); h->colpartV = (float*)(b + o_cpV);
@@ -180,6 +191,13 @@ size_t layout(nq_lbadmm* h) {
     h->s1c = (float*)(b + o_s1c); h->s2c = (float*)(b + o_s2c);
     h->SU = (int8_t*)(b + o_SU); h->SV = (int8_t*)(b + o_SV);
     h->st = (DevStats*)(b + o_st);
+    h->dag.R = R;
+    h->dag.tasks = b + o_tasks;
+    h->dag.ntasks = h->ntasks;
+    h->dag.grid = 256;
+    h->dag.flags = (uint64_t*)(b + o_flags);
+    h->dag.epoch = (uint64_t*)(b + o_epoch);
+    h->dag.ticket = (int*)(b + o_ticket);
   }
   return a.off;
 }
@@ -191,6 +209,15 @@ void plan(nq_lbadmm* h) {
   gram_split(h->np_, h->rp, &h->gU_nch, &h->gU_kc);  // U-half: Gram of V, K = n
   gram_split(h->mp, h->rp, &h->gV_nch, &h->gV_kc);   // V-half: Gram of U, K = m
   lauum_split(h->rp, &h->l_nch, &h->l_kc);
+  const int R = h->rp / kNB;
+  // task count of the tile DAG (chol_schedule.h)
+  int64_t nt = 0;
+  for (int k = 0; k < R; ++k) {
+    const int n = R - k - 1;
+    nt += 1 + std::max(0, R - k - 2) + k + (int64_t)n * (n + 1) / 2 - (n > 0 ? 1 : 0) +
+          (int64_t)n * (k + 1);
+  }
+  h->ntasks = (int)nt;
 }
 
 size_t pairs_per_run(const nq_lbadmm* h) { return 4 + (size_t)h->d.iters * 8; }
@@ -240,7 +267,7 @@ nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
   long pc = prof_begin(h, NQ_PHASE_CHAIN, cs);
   HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, cs));
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, cs));
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, h->dag, false, cs));
   HIPCHK(launch_syrk_partial(h->Minv, rp, rp, rp, h->l_kc, true, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, h->l_nch, rp, 0.0f, h->Ginv, rp, cs));
   prof_end(h, pc, cs);
@@ -271,6 +298,8 @@ nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
 nq_status status_from(const DevStats& hs) {
   if (hs.bad_precond) return fail(NQ_ERR_BAD_PRECONDITIONER, "an entry of d_out or d_in is not > 0");
   if (hs.nonfinite) return fail(NQ_ERR_NONFINITE, "NaN or Inf in the input or the result");
+  if (hs.sched_err)
+    return fail(NQ_ERR_HIP, "a tile-DAG Cholesky wait timed out; results are invalid");
   if (hs.potrf_info != 0x7fffffff)
     return fail(NQ_ERR_NOT_POSITIVE_DEFINITE,
                 "Cholesky pivot <= 0 at column " + std::to_string(hs.potrf_info - 1));
@@ -343,6 +372,12 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   // Padding must read as zero from the start (the run rewrites every live
   // region it reads, but the finish kernels read padded rows).
   if (e == hipSuccess) e = hipMemset(h->base, 0, h->bytes);
+  if (e == hipSuccess) {
+    const std::vector<CholDevTask> tasks = build_chol_dev_tasks(h->dag.R);
+    if ((int)tasks.size() != h->ntasks) e = hipErrorInvalidValue;
+    else e = hipMemcpy((void*)h->dag.tasks, tasks.data(), sizeof(CholDevTask) * tasks.size(),
+                       hipMemcpyHostToDevice);
+  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     nq_status s = hip_fail(e, "create");

@@ -176,45 +176,72 @@ __global__ __launch_bounds__(256) void svid_step_kernel(const float* __restrict_
   }
 }
 
-// b_j = sum_c part[c][j] / aa over nch partial rows; 128 columns per block,
-// 32 x 8 threads (float4 columns x chunk stripes), fixed-order reductions.
-__global__ __launch_bounds__(256) void svid_reduce_wide_kernel(const float* __restrict__ part,
-                                                               int nch,
-                                                               const float* __restrict__ aapart,
-                                                               int rp, float* __restrict__ b,
-                                                               float* __restrict__ bbpart) {
+// b_j = sum_c part[c][j] / aa over nch partial rows, in two levels inside one
+// launch: block (g, y) sums its share of the partial rows for the 128 columns
+// of group g into part2[y]; the last block of group g to finish (atomic
+// ticket, counter reset afterwards) adds part2[0..NY) in order, divides by
+// aa and writes b and bbpart[g]. The summation order is fixed, so the result
+// does not depend on which block finishes last.
+constexpr int NY = kSvidReduceRows;  // row groups of the reduce
+__global__ __launch_bounds__(256) void svid_reduce_kernel(const float* __restrict__ part, int nch,
+                                                          const float* __restrict__ aapart,
+                                                          int rp, float* __restrict__ part2,
+                                                          int* __restrict__ counters,
+                                                          float* __restrict__ b,
+                                                          float* __restrict__ bbpart) {
   __shared__ f32x4 red[8][32];
-  __shared__ float aared[256];
-  __shared__ float bbred[32];
+  __shared__ float fred[256];
+  __shared__ int is_last;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int q = blockIdx.x * 32 + tx;  // float4 column index
-  float aa = 0.0f;
-  for (int c = threadIdx.x; c < nch; c += 256) aa += aapart[c];
-  aared[threadIdx.x] = aa;
+  const int g = blockIdx.x, y = blockIdx.y;
+  const int q = g * 32 + tx;  // float4 column index
+  const int c0 = (int)((int64_t)nch * y / NY), c1 = (int)((int64_t)nch * (y + 1) / NY);
   f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c = ty; c < nch; c += 8) p += ((const f32x4*)(part + (int64_t)c * rp))[q];
+#pragma unroll 4
+  for (int c = c0 + ty; c < c1; c += 8) p += ((const f32x4*)(part + (int64_t)c * rp))[q];
   red[ty][tx] = p;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) aared[threadIdx.x] += aared[threadIdx.x + o];
-    __syncthreads();
-  }
   if (ty == 0) {
     f32x4 t = red[0][tx];
 #pragma unroll
-    for (int y = 1; y < 8; ++y) t += red[y][tx];
-    const float tot = aared[0];
+    for (int k = 1; k < 8; ++k) t += red[k][tx];
+    ((f32x4*)(part2 + (int64_t)y * rp))[q] = t;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(&counters[g], 1);
+    is_last = (prev == NY - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+  float aa = 0.0f;
+  for (int c = threadIdx.x; c < nch; c += 256) aa += aapart[c];
+  fred[threadIdx.x] = aa;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) fred[threadIdx.x] += fred[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float tot = fred[0];
+  __syncthreads();
+  if (ty == 0) {
+    f32x4 t = ((const f32x4*)part2)[q];
+#pragma unroll
+    for (int k = 1; k < NY; ++k) t += ((const f32x4*)(part2 + (int64_t)k * rp))[q];
     f32x4 bj;
 #pragma unroll
     for (int e = 0; e < 4; ++e) bj[e] = tot > 0.0f ? t[e] / tot : 0.0f;
     ((f32x4*)b)[q] = bj;
-    bbred[tx] = bj[0] * bj[0] + bj[1] * bj[1] + bj[2] * bj[2] + bj[3] * bj[3];
+    fred[tx] = bj[0] * bj[0] + bj[1] * bj[1] + bj[2] * bj[2] + bj[3] * bj[3];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     float t = 0.0f;
-    for (int y = 0; y < 32; ++y) t += bbred[y];
-    bbpart[blockIdx.x] = t;
+    for (int k = 0; k < 32; ++k) t += fred[k];
+    bbpart[g] = t;
+    counters[g] = 0;
   }
 }
 
@@ -291,16 +318,16 @@ hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int
   hipLaunchKernelGGL(svid_init_b_kernel, dim3(nbb), dim3(CB), 0, s, w.b, w.bbpart, rp, r_real);
   for (int t = 0; t < T; ++t) {
     if (rs && fused_step(X, rows_pad, rp, nbb, w, s)) {
-      hipLaunchKernelGGL(svid_reduce_wide_kernel, dim3(rp / 128), dim3(256), 0, s, w.colpart,
-                         rows_pad / rs, w.aapart, rp, w.b, w.bbpart);
+      hipLaunchKernelGGL(svid_reduce_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart,
+                         rows_pad / rs, w.aapart, rp, w.part2, w.counters, w.b, w.bbpart);
       continue;
     }
     hipLaunchKernelGGL(svid_row_kernel, dim3(rows_pad / 4), dim3(256), 0, s, X, rp, w.b,
                        w.bbpart, nbb, w.a);
     hipLaunchKernelGGL(colsum_kernel<0>, dim3(rp / 128, nch), dim3(256), 0, s, X, rp, rows_pad,
                        w.a, w.colpart, w.aapart);
-    hipLaunchKernelGGL(svid_reduce_wide_kernel, dim3(rp / 128), dim3(256), 0, s, w.colpart, nch,
-                       w.aapart, rp, w.b, w.bbpart);
+    hipLaunchKernelGGL(svid_reduce_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart, nch,
+                       w.aapart, rp, w.part2, w.counters, w.b, w.bbpart);
   }
   const int64_t n4 = (int64_t)rows_pad * rp / 4;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 8192);

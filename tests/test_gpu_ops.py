@@ -60,7 +60,7 @@ def test_gram(gpu, rows, cols):
     np.testing.assert_array_equal(got, got.T)   # exactly symmetric
 
 
-@pytest.mark.parametrize("r", [1, 3, 64, 100, 128, 300, 640])
+@pytest.mark.parametrize("r", [1, 3, 64, 100, 128, 300, 640, 2048])
 def test_cholesky_inverse(gpu, r):
     import sub_bit_weight_lb_amd as nq
     rng = np.random.default_rng(r)
