@@ -4,22 +4,22 @@
 // system is solved through a Cholesky factorisation; the implementation blog,
 // section 待办事项, names this factorisation as where LB-ADMM spends its time).
 //
-// One persistent launch per factorisation: a tile DAG over 64 x 64 tiles
-// (task kinds and their order: chol_schedule.h). Workgroups take tasks in
-// list order from an atomic ticket, wait for the flags of the task's inputs,
-// run the task and set its output flags. Since every input is produced by a
-// task earlier in the list, which some running workgroup has already taken,
-// progress never depends on more than one workgroup being resident. Each
-// wait is bounded in time; on expiry the kernel records an error in the
-// device stats and every workgroup leaves, so the launch always ends.
-//   diagonal tiles: outer-product elimination with register-resident 4 x 4
-//   blocks, the same row operations applied to an identity block, giving
-//   L_kk and M_kk = L_kk^-1 with one barrier per column;
-//   off-diagonal tiles: 64 x 64 x 64 products on the 32x32x2 fp32 MFMA.
+// Right-looking, block size 64, two launches per block column k:
+//   panel(k):  L_ik = A_ik M_kk^T for i > k (in place), and row k of the
+//              inverse factor, M_kj = -M_kk S_kj for j < k;
+//   update(k): trailing update A_ij -= L_ik L_jk^T (i >= j > k) and the
+//              inverse partial sums S_ij += L_ik M_kj (i > k >= j); its first
+//              workgroup instead updates the next diagonal tile and factors
+//              it, so no launch is spent on the diagonal alone.
+// Diagonal tiles: outer-product elimination with register-resident 4 x 4
+// blocks, the same row operations applied to an identity block, giving L_kk
+// and M_kk = L_kk^-1 with one barrier per column. Off-diagonal tiles: 64 x 64
+// x 64 products on the 32x32x2 fp32 MFMA.
 // The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
 // M_ij = -M_ii sum_{l = j..i-1} L_il M_lj; the partial sums S_ij are kept in
 // M's own tiles until row i of M is formed.
-#include "chol_schedule.h"
+// Workgroups of one launch never wait for each other: every dependency
+// crosses a launch boundary.
 #include "common.h"
 #include <climits>
 
@@ -193,132 +193,63 @@ __device__ void diag_factor(float* A, float* M, int rp, int k, int r_real, DevSt
   }
 }
 
-constexpr uint64_t kVerBits = 20;           // flag = epoch << 20 | version
-constexpr uint64_t kTimeoutTicks = 200000000; // wall-clock ticks (2 s at 100 MHz)
+__global__ __launch_bounds__(NT) void chol_diag0_kernel(float* A, float* M, int rp, int r_real,
+                                                        DevStats* st) {
+  __shared__ __attribute__((aligned(16))) DiagSmem dsm;
+  diag_factor(A, M, rp, 0, r_real, st, dsm);
+}
 
-__device__ inline void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-// Thread 0 only: wait until *f >= target; false on timeout or a recorded error.
-__device__ bool wait_flag(const uint64_t* f, uint64_t target, int* err) {
-  const uint64_t t0 = wall_clock64();
-  for (;;) {
-    const uint64_t v = __hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    if (v >= target) return true;
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return false;
-    if (wall_clock64() - t0 > kTimeoutTicks) {
-      atomicOr(err, 1);
-      return false;
-    }
-    __builtin_amdgcn_s_sleep(2);
+__global__ __launch_bounds__(NT) void chol_panel_kernel(float* A, float* M, int rp, int k) {
+  __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
+  __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
+  const int R = rp / NB;
+  const int nL = R - k - 1;
+  const int b = blockIdx.x;
+  const int64_t kk = (int64_t)k * NB;
+  if (b < nL) {
+    const int64_t i0 = (int64_t)(k + 1 + b) * NB;
+    float* Aik = A + i0 * rp + kk;
+    block_mm<true>(Aik, M + kk * rp + kk, Aik, rp, 1.0f, 0.0f, Xs, Ys);
+  } else {
+    const int64_t j0 = (int64_t)(b - nL) * NB;
+    float* Mkj = M + kk * rp + j0;
+    block_mm<false>(M + kk * rp + kk, Mkj, Mkj, rp, -1.0f, 0.0f, Xs, Ys);
   }
 }
 
-// Make this workgroup's global writes visible device-wide, then set flag
-// `idx` (if >= 0) to base | version.
-__device__ void publish(uint64_t* flags, int idx, uint64_t base, int version) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0 && idx >= 0)
-    __hip_atomic_store(flags + idx, base | (uint64_t)version, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-struct CholDagArgs {
-  float* A;
-  float* M;
-  int rp;
-  int r_real;
-  DevStats* st;
-  const CholDevTask* tasks;
-  int ntasks;
-  int* ticket;
-  const uint64_t* epoch;
-  uint64_t* flags;
-};
-
-__global__ __launch_bounds__(NT) void chol_dag_kernel(CholDagArgs p) {
+__global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, int rp, int k,
+                                                         int r_real, DevStats* st) {
   __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
   __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
   __shared__ __attribute__((aligned(16))) DiagSmem dsm;
-  __shared__ int s_ticket, s_ok;
-  const int tid = threadIdx.x;
-  const uint64_t base = (*p.epoch) << kVerBits;
-  float* A = p.A;
-  float* M = p.M;
-  const int rp = p.rp;
-  int* err = &p.st->sched_err;
-  for (;;) {
-    if (tid == 0) s_ticket = atomicAdd(p.ticket, 1);
-    __syncthreads();
-    const int t = s_ticket;
-    if (t >= p.ntasks) break;
-    const CholDevTask tk = p.tasks[t];
-    if (tid == 0) {
-      bool ok = true;
-      for (int q = 0; q < 3 && ok; ++q)
-        if (tk.dep[q] >= 0) ok = wait_flag(p.flags + tk.dep[q], base | (uint64_t)tk.dver[q], err);
-      s_ok = ok;
-    }
-    __syncthreads();
-    if (!s_ok) break;
-    acquire_agent();
-    const int64_t i0 = (int64_t)tk.i * NB, j0 = (int64_t)tk.j * NB, k0 = (int64_t)tk.k * NB;
-    switch (tk.type) {
-      case kTaskDiag: {
-        int o = 0;
-        if (tk.k >= 1) {
-          const int64_t km = k0 - NB;
-          float* Lk = A + k0 * rp + km;
-          // L_{k,k-1} = A_{k,k-1} M_{k-1,k-1}^T, published at once
-          block_mm<true>(Lk, M + km * rp + km, Lk, rp, 1.0f, 0.0f, Xs, Ys);
-          publish(p.flags, tk.out[0], base, tk.over[0]);
-          acquire_agent();
-          // A_kk -= L_{k,k-1} L_{k,k-1}^T
-          block_mm<true>(Lk, Lk, A + k0 * rp + k0, rp, -1.0f, 1.0f, Xs, Ys);
-          __threadfence();
-          __syncthreads();
-          acquire_agent();
-          o = 1;
-        }
-        diag_factor(A, M, rp, tk.k, p.r_real, p.st, dsm);
-        publish(p.flags, tk.out[o], base, tk.over[o]);
-        if (tid == 0 && tk.out[o + 1] >= 0)
-          __hip_atomic_store(p.flags + tk.out[o + 1], base | (uint64_t)tk.over[o + 1],
-                             __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      case kTaskPanelL: {
-        float* Aik = A + i0 * rp + k0;
-        block_mm<true>(Aik, M + k0 * rp + k0, Aik, rp, 1.0f, 0.0f, Xs, Ys);
-        publish(p.flags, tk.out[0], base, tk.over[0]);
-        break;
-      }
-      case kTaskPanelM: {
-        float* Mkj = M + k0 * rp + j0;
-        block_mm<false>(M + k0 * rp + k0, Mkj, Mkj, rp, -1.0f, 0.0f, Xs, Ys);
-        publish(p.flags, tk.out[0], base, tk.over[0]);
-        break;
-      }
-      case kTaskUpdA: {
-        block_mm<true>(A + i0 * rp + k0, A + j0 * rp + k0, A + i0 * rp + j0, rp, -1.0f, 1.0f, Xs,
-                       Ys);
-        publish(p.flags, tk.out[0], base, tk.over[0]);
-        break;
-      }
-      default: {  // kTaskUpdS
-        block_mm<false>(A + i0 * rp + k0, M + k0 * rp + j0, M + i0 * rp + j0, rp, 1.0f, 1.0f, Xs,
-                        Ys);
-        publish(p.flags, tk.out[0], base, tk.over[0]);
-        break;
-      }
-    }
+  const int R = rp / NB;
+  const int n = R - k - 1;
+  const int64_t kk = (int64_t)k * NB;
+  int b = blockIdx.x;
+  if (b == 0) {
+    // next diagonal tile: A_{k+1,k+1} -= L_{k+1,k} L_{k+1,k}^T, then factor it
+    const int64_t d0 = kk + NB;
+    block_mm<true>(A + d0 * rp + kk, A + d0 * rp + kk, A + d0 * rp + d0, rp, -1.0f, 1.0f, Xs, Ys);
+    __threadfence_block();
+    diag_factor(A, M, rp, k + 1, r_real, st, dsm);
+    return;
   }
-}
-
-// Ticket to 0, epoch + 1, before each factorisation (stream-ordered).
-__global__ void chol_dag_prep_kernel(int* ticket, uint64_t* epoch) {
-  *ticket = 0;
-  *epoch = *epoch + 1;
+  b -= 1;
+  const int nA = n * (n + 1) / 2 - 1;  // lower tiles of the trailing block but (k+1, k+1)
+  if (b < nA) {
+    const int t = b + 1;
+    int ii = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+    while (ii * (ii + 1) / 2 > t) --ii;
+    const int jj = t - ii * (ii + 1) / 2;
+    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
+    block_mm<true>(A + i0 * rp + kk, A + j0 * rp + kk, A + i0 * rp + j0, rp, -1.0f, 1.0f, Xs, Ys);
+  } else {
+    const int q = b - nA;
+    const int ii = q / (k + 1), jj = q % (k + 1);
+    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)jj * NB;
+    block_mm<false>(A + i0 * rp + kk, M + kk * rp + j0, M + i0 * rp + j0, rp, 1.0f, 1.0f, Xs, Ys);
+  }
 }
 
 __global__ void zero_upper_kernel(float* A, int rp) {
@@ -331,15 +262,21 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 }  // namespace
 
 hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real, DevStats* st,
-                                   const CholDagWork& w, bool zero_upper_L, hipStream_t s) {
-  if (rp % NB || w.R != rp / NB) return hipErrorInvalidValue;
+                                   bool zero_upper_L, hipStream_t s) {
+  if (rp % NB) return hipErrorInvalidValue;
+  const int R = rp / NB;
   hipError_t e = launch_zero(M, (size_t)rp * rp, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chol_dag_prep_kernel, dim3(1), dim3(1), 0, s, w.ticket, w.epoch);
-  CholDagArgs a{A, M, rp, r_real, st, (const CholDevTask*)w.tasks, w.ntasks, w.ticket, w.epoch,
-                w.flags};
-  const int grid = w.ntasks < w.grid ? w.ntasks : w.grid;
-  hipLaunchKernelGGL(chol_dag_kernel, dim3(grid), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(chol_diag0_kernel, dim3(1), dim3(NT), 0, s, A, M, rp, r_real, st);
+  for (int k = 0; k < R; ++k) {
+    const int np = (R - k - 1) + k;
+    if (np > 0) hipLaunchKernelGGL(chol_panel_kernel, dim3(np), dim3(NT), 0, s, A, M, rp, k);
+    const int n = R - k - 1;
+    if (n > 0) {
+      const int nb = 1 + (n * (n + 1) / 2 - 1) + n * (k + 1);
+      hipLaunchKernelGGL(chol_update_kernel, dim3(nb), dim3(NT), 0, s, A, M, rp, k, r_real, st);
+    }
+  }
   if (!zero_upper_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;
   hipLaunchKernelGGL(zero_upper_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, A, rp);

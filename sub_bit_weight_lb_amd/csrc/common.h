@@ -28,7 +28,7 @@ struct DevStats {
   int nonfinite;        // NaN/Inf seen
   int bad_precond;      // some d <= 0
   int potrf_info;       // 0 or 1 + first failing pivot column (min over runs)
-  int sched_err;        // a tile-DAG wait timed out
+  int pad;
 };
 
 // ---------------------------------------------------------------- GEMM
@@ -61,21 +61,11 @@ hipError_t launch_gram_reduce(const float* part, int nchunks, int rp, float rho,
 
 // ---------------------------------------------------------------- Cholesky / inverse
 constexpr int kNB = 64;  // block size of the blocked Cholesky
-// Device-side state of the tile-DAG factorisation of an rp x rp matrix.
-struct CholDagWork {
-  int R;              // rp / kNB
-  const void* tasks;  // CholDevTask[ntasks] (chol_schedule.h), device
-  int ntasks;
-  int grid;           // persistent workgroups
-  int* ticket;        // device int
-  uint64_t* epoch;    // device counter, zero before the first use
-  uint64_t* flags;    // 4 R R device flags, zero before the first use
-};
 // In place on A (rp x rp, ld rp, full symmetric on entry): lower triangle becomes
 // L (upper triangle zeroed only if zero_upper_L); M (rp x rp) becomes L^-1
 // (lower, zero upper). st->potrf_info gets min(1 + failing column).
 hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real, DevStats* st,
-                                   const CholDagWork& w, bool zero_upper_L, hipStream_t s);
+                                   bool zero_upper_L, hipStream_t s);
 
 // ---------------------------------------------------------------- SVID
 struct SvidWork {
@@ -85,7 +75,6 @@ struct SvidWork {
   float* aapart;   // svid_partials(rows_pad, rp)
   float* bbpart;   // rp / 128
   float* part2;    // kSvidReduceRows x rp
-  int* counters;   // rp / 128, zero between launches
 };
 constexpr int kSvidReduceRows = 16;
 int svid_nchunks(int rows_pad);            // 64-row chunks of the column pass

@@ -2,14 +2,19 @@
 //
 // One handle = one layer shape. create() allocates every workspace buffer
 // once (one device allocation, zero-padded layouts); run() only enqueues
-// kernels and never allocates. Per half-iteration the r x r chain
-// (Gram -> Cholesky + inverse factor -> L^-T L^-1) depends only on the other
-// factor, as does the right-hand-side GEMM, so the chain runs on an internal
-// second stream while the GEMM runs on the caller's stream; the solve GEMM
-// joins them. SVID of one half overlaps the next half's chain.
+// kernels and never allocates. Three streams per half-iteration:
+//   caller's stream: right-hand-side GEMM, then (after the chain) the solve
+//                    GEMM;
+//   chain stream:    Gram -> Cholesky + inverse factor -> L^-T L^-1, which
+//                    depends only on the other factor, like the RHS GEMM;
+//   SVID stream:     SVID + dual update of the factor just solved, which the
+//                    next half (the other factor) does not read, so it runs
+//                    under the next half's chain and RHS GEMM.
+// Events order the shared buffers: the chain of half h+1 starts after the
+// solve of half h (it overwrites G^-1), and the RHS GEMM of a factor waits
+// for that factor's previous SVID (it reads Z - Lam).
 #include "nq.h"
 #include "abi.h"
-#include "chol_schedule.h"
 #include "common.h"
 
 #include <climits>
@@ -117,10 +122,9 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
-  CholDagWork dag{};
-  int ntasks = 0;
-  hipStream_t aux = nullptr;
+  hipStream_t aux = nullptr, svs = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
+  hipEvent_t ev_svid[2] = {nullptr, nullptr};
   hipStream_t last_stream = nullptr;
   bool has_run = false;
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
@@ -151,12 +155,10 @@ size_t layout(nq_lbadmm* h) {
   const int spV = std::max(nchV, svid_partials((int)np_, (int)rp));
   size_t o_sUa = a.take<float>(mp), o_sUb = a.take<float>(rp),
          o_sUc = a.take<float>((size_t)spU * rp), o_sUaa = a.take<float>(spU),
-         o_sUbb = a.take<float>(rp / 128), o_sUp2 = a.take<float>(kSvidReduceRows * rp),
-         o_sUct = a.take<int>(rp / 128);
+         o_sUbb = a.take<float>(rp / 128), o_sUp2 = a.take<float>(kSvidReduceRows * rp);
   size_t o_sVa = a.take<float>(np_), o_sVb = a.take<float>(rp),
          o_sVc = a.take<float>((size_t)spV * rp), o_sVaa = a.take<float>(spV),
-         o_sVbb = a.take<float>(rp / 128), o_sVp2 = a.take<float>(kSvidReduceRows * rp),
-         o_sVct = a.take<int>(rp / 128);
+         o_sVbb = a.take<float>(rp / 128), o_sVp2 = a.take<float>(kSvidReduceRows * rp);
   const int npre = precondition_nblocks((int)mp, (int)np_);
   size_t o_pwt = a.take<double>(npre), o_pw = a.take<double>(npre);
   size_t o_err = a.take<double>(2 * (size_t)error_nparts((int)mp, (int)np_));
@@ -165,10 +167,6 @@ size_t layout(nq_lbadmm* h) {
   size_t o_s1c = a.take<float>(mp), o_s2c = a.take<float>(np_);
   size_t o_SU = a.take<int8_t>(mp * rp), o_SV = a.take<int8_t>(np_ * rp);
   size_t o_st = a.take<DevStats>(1);
-  const int R = (int)(rp / kNB);
-  size_t o_tasks = a.take<CholDevTask>((size_t)h->ntasks);
-  size_t o_flags = a.take<uint64_t>((size_t)4 * R * R);
-  size_t o_epoch = a.take<uint64_t>(1), o_ticket = a.take<int>(1);
   if (h->base) {
     char* b = h->base;
     h->Wt = (float*)(b + o_Wt); h->WtT = (float*)(b + o_WtT);
@@ -179,11 +177,9 @@ size_t layout(nq_lbadmm* h) {
     h->G = (float*)(b + o_G); h->Minv = (float*)(b + o_M); h->Ginv = (float*)(b + o_Gi);
     h->gpart = (float*)(b + o_gp);
     h->svU = SvidWork{(float*)(b + o_sUa), (float*)(b + o_sUb), (float*)(b + o_sUc),
-                      (float*)(b + o_sUaa), (float*)(b + o_sUbb), (float*)(b + o_sUp2),
-                      (int*)(b + o_sUct)};
+                      (float*)(b + o_sUaa), (float*)(b + o_sUbb), (float*)(b + o_sUp2)};
     h->svV = SvidWork{(float*)(b + o_sVa), (float*)(b + o_sVb), (float*)(b + o_sVc),
-                      (float*)(b + o_sVaa), (float*)(b + o_sVbb), (float*)(b + o_sVp2),
-                      (int*)(b + o_sVct)};
+                      (float*)(b + o_sVaa), (float*)(b + o_sVbb), (float*)(b + o_sVp2)};
     h->part_wt = (double*)(b + o_pwt); h->part_w = (double*)(b + o_pw);
     h->err_parts = (double*)(b + o_err);
     h->colpartU = (float*)(b + o_cpU); h->colpartV = (float*)(b + o_cpV);
@@ -191,13 +187,6 @@ size_t layout(nq_lbadmm* h) {
     h->s1c = (float*)(b + o_s1c); h->s2c = (float*)(b + o_s2c);
     h->SU = (int8_t*)(b + o_SU); h->SV = (int8_t*)(b + o_SV);
     h->st = (DevStats*)(b + o_st);
-    h->dag.R = R;
-    h->dag.tasks = b + o_tasks;
-    h->dag.ntasks = h->ntasks;
-    h->dag.grid = 256;
-    h->dag.flags = (uint64_t*)(b + o_flags);
-    h->dag.epoch = (uint64_t*)(b + o_epoch);
-    h->dag.ticket = (int*)(b + o_ticket);
   }
   return a.off;
 }
@@ -209,15 +198,6 @@ void plan(nq_lbadmm* h) {
   gram_split(h->np_, h->rp, &h->gU_nch, &h->gU_kc);  // U-half: Gram of V, K = n
   gram_split(h->mp, h->rp, &h->gV_nch, &h->gV_kc);   // V-half: Gram of U, K = m
   lauum_split(h->rp, &h->l_nch, &h->l_kc);
-  const int R = h->rp / kNB;
-  // task count of the tile DAG (chol_schedule.h)
-  int64_t nt = 0;
-  for (int k = 0; k < R; ++k) {
-    const int n = R - k - 1;
-    nt += 1 + std::max(0, R - k - 2) + k + (int64_t)n * (n + 1) / 2 - (n > 0 ? 1 : 0) +
-          (int64_t)n * (k + 1);
-  }
-  h->ntasks = (int)nt;
 }
 
 size_t pairs_per_run(const nq_lbadmm* h) { return 4 + (size_t)h->d.iters * 8; }
@@ -257,22 +237,25 @@ struct Half {
   float* P;            // M x rp
   const SvidWork* sv;
   int g_nch, g_kc;
+  int factor;  // 0 = U, 1 = V
 };
 
 nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
   const int rp = h->rp;
   hipStream_t cs = overlap ? h->aux : s;
+  hipStream_t vs = overlap ? h->svs : s;
   if (overlap) HIPCHK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
   // r x r chain: G = other^T other + rho I, L and L^-1, G^-1 = L^-T L^-1
   long pc = prof_begin(h, NQ_PHASE_CHAIN, cs);
   HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, cs));
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, h->dag, false, cs));
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, cs));
   HIPCHK(launch_syrk_partial(h->Minv, rp, rp, rp, h->l_kc, true, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, h->l_nch, rp, 0.0f, h->Ginv, rp, cs));
   prof_end(h, pc, cs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_join, h->aux));
-  // R = Wside other + rho (Z - Lam)
+  // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last SVID
+  if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_svid[x.factor], 0));
   GemmArgs g{};
   g.A = x.Wside; g.lda = x.K; g.B = x.other; g.ldb = rp; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
@@ -287,19 +270,21 @@ nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
   long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
   prof_end(h, ps, s);
-  if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
+  if (overlap) {
+    HIPCHK(hipEventRecord(h->ev_fork, s));
+    HIPCHK(hipStreamWaitEvent(h->svs, h->ev_fork, 0));
+  }
   // Z = SVID(X); Lam = X - Z; P = Z - Lam
-  long pv = prof_begin(h, NQ_PHASE_SVID, s);
-  HIPCHK(launch_svid(x.Lam, x.P, x.M, rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, s));
-  prof_end(h, pv, s);
+  long pv = prof_begin(h, NQ_PHASE_SVID, vs);
+  HIPCHK(launch_svid(x.Lam, x.P, x.M, rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, vs));
+  prof_end(h, pv, vs);
+  if (overlap) HIPCHK(hipEventRecord(h->ev_svid[x.factor], h->svs));
   return NQ_OK;
 }
 
 nq_status status_from(const DevStats& hs) {
   if (hs.bad_precond) return fail(NQ_ERR_BAD_PRECONDITIONER, "an entry of d_out or d_in is not > 0");
   if (hs.nonfinite) return fail(NQ_ERR_NONFINITE, "NaN or Inf in the input or the result");
-  if (hs.sched_err)
-    return fail(NQ_ERR_HIP, "a tile-DAG Cholesky wait timed out; results are invalid");
   if (hs.potrf_info != 0x7fffffff)
     return fail(NQ_ERR_NOT_POSITIVE_DEFINITE,
                 "Cholesky pivot <= 0 at column " + std::to_string(hs.potrf_info - 1));
@@ -359,6 +344,9 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   }
   layout(h);
   e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->svs, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_svid[0], hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_svid[1], hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t0);
@@ -372,12 +360,6 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   // Padding must read as zero from the start (the run rewrites every live
   // region it reads, but the finish kernels read padded rows).
   if (e == hipSuccess) e = hipMemset(h->base, 0, h->bytes);
-  if (e == hipSuccess) {
-    const std::vector<CholDevTask> tasks = build_chol_dev_tasks(h->dag.R);
-    if ((int)tasks.size() != h->ntasks) e = hipErrorInvalidValue;
-    else e = hipMemcpy((void*)h->dag.tasks, tasks.data(), sizeof(CholDevTask) * tasks.size(),
-                       hipMemcpyHostToDevice);
-  }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     nq_status s = hip_fail(e, "create");
@@ -394,13 +376,17 @@ void nq_lbadmm_destroy(nq_lbadmm_t h) {
   if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
   if (h->last_stream || h->has_run) (void)hipStreamSynchronize(h->last_stream);
   if (h->aux) (void)hipStreamSynchronize(h->aux);
+  if (h->svs) (void)hipStreamSynchronize(h->svs);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
   for (hipEvent_t ev : h->prof_ev)
     if (ev) (void)hipEventDestroy(ev);
+  for (hipEvent_t ev : h->ev_svid)
+    if (ev) (void)hipEventDestroy(ev);
   if (h->aux) (void)hipStreamDestroy(h->aux);
+  if (h->svs) (void)hipStreamDestroy(h->svs);
   if (h->base) (void)hipFree(h->base);
   if (cur != h->device) (void)hipSetDevice(cur);
   delete h;
@@ -452,13 +438,22 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   prof_end(h, pp, s);
   if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
 
-  Half hu{h->Wt, mp, np_, h->V, h->U, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc};
-  Half hv{h->WtT, np_, mp, h->U, h->V, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc};
+  Half hu{h->Wt, mp, np_, h->V, h->U, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc, 0};
+  Half hv{h->WtT, np_, mp, h->U, h->V, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc, 1};
+  if (overlap) {
+    // the SVID stream starts after the initial SVIDs on the caller's stream
+    HIPCHK(hipStreamWaitEvent(h->svs, h->ev_fork, 0));
+  }
   for (int it = 0; it < d.iters; ++it) {
     nq_status st = run_half(h, hu, s, overlap);
     if (st != NQ_OK) return st;
     st = run_half(h, hv, s, overlap);
     if (st != NQ_OK) return st;
+  }
+  if (overlap) {
+    // join: the last SVIDs (and with them every earlier one) before finishing
+    HIPCHK(hipEventRecord(h->ev_svid[0], h->svs));
+    HIPCHK(hipStreamWaitEvent(s, h->ev_svid[0], 0));
   }
 
   // finish: balance, scales, signs, bits, errors

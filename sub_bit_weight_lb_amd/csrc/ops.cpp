@@ -7,7 +7,6 @@
 #include <vector>
 
 #include "abi.h"
-#include "chol_schedule.h"
 #include "common.h"
 
 using namespace nq;
@@ -132,16 +131,7 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
   int nch = (int)std::max<int64_t>(1, std::min<int64_t>(4, rp / 128));
   const int kc = (int)round_up((rp + nch - 1) / nch, 32);
   nch = (int)((rp + kc - 1) / kc);
-  DevBuf a, m, part, gi, st, tasks, flags;
-  const int R = (int)(rp / kNB);
-  const std::vector<CholDevTask> tl = build_chol_dev_tasks(R);
-  NQ_HIPCHK(tasks.alloc(sizeof(CholDevTask) * tl.size()));
-  NQ_HIPCHK(hipMemcpy(tasks.p, tl.data(), sizeof(CholDevTask) * tl.size(), hipMemcpyHostToDevice));
-  NQ_HIPCHK(flags.alloc(sizeof(uint64_t) * (4 * (size_t)R * R + 2)));
-  NQ_HIPCHK(hipMemset(flags.p, 0, sizeof(uint64_t) * (4 * (size_t)R * R + 2)));
-  uint64_t* fl = (uint64_t*)flags.p;
-  CholDagWork w{R, tasks.p, (int)tl.size(), 256, (int*)(fl + 4 * (size_t)R * R + 1),
-                fl + 4 * (size_t)R * R, fl};
+  DevBuf a, m, part, gi, st;
   NQ_HIPCHK(a.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(m.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(part.alloc(sizeof(float) * nch * rp * rp));
@@ -152,7 +142,7 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
   // [G 0; 0 I]: the identity keeps the padded system positive definite
   NQ_HIPCHK(stage_in(G, r, r, ldg, a.f(), rp, rp, s));
   NQ_HIPCHK(launch_set_diag(a.f(), rp, (int)r, (int)rp, 1.0f, s));
-  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), (int)rp, (int)r, dst, w, true, s));
+  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), (int)rp, (int)r, dst, true, s));
   if (Ginv) {
     NQ_HIPCHK(launch_syrk_partial(m.f(), rp, (int)rp, (int)rp, kc, true, part.f(), s));
     NQ_HIPCHK(launch_gram_reduce(part.f(), nch, (int)rp, 0.0f, gi.f(), rp, s));
@@ -162,7 +152,6 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
   DevStats hs;
   NQ_HIPCHK(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s));
   NQ_HIPCHK(hipStreamSynchronize(s));
-  if (hs.sched_err) return set_error(NQ_ERR_HIP, "a tile-DAG Cholesky wait timed out");
   *info = hs.potrf_info == 0x7fffffff ? 0 : hs.potrf_info;
   if (*info) return set_error(NQ_ERR_NOT_POSITIVE_DEFINITE, "Cholesky pivot <= 0");
   return NQ_OK;
@@ -175,7 +164,7 @@ nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx, in
   hipStream_t s = (hipStream_t)stream;
   const int64_t rows_pad = round_up(rows, 8), rp = round_up(cols, 128);
   const int nch = std::max(svid_nchunks((int)rows_pad), svid_partials((int)rows_pad, (int)rp));
-  DevBuf x, p, wa, wb, wc, waa, wbb, wp2, wct;
+  DevBuf x, p, wa, wb, wc, waa, wbb, wp2;
   NQ_HIPCHK(x.alloc(sizeof(float) * rows_pad * rp));
   NQ_HIPCHK(p.alloc(sizeof(float) * rows_pad * rp));
   NQ_HIPCHK(wa.alloc(sizeof(float) * rows_pad));
@@ -184,9 +173,7 @@ nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx, in
   NQ_HIPCHK(waa.alloc(sizeof(float) * nch));
   NQ_HIPCHK(wbb.alloc(sizeof(float) * (rp / 128)));
   NQ_HIPCHK(wp2.alloc(sizeof(float) * kSvidReduceRows * rp));
-  NQ_HIPCHK(wct.alloc(sizeof(int) * (rp / 128)));
-  NQ_HIPCHK(launch_zero(wct.f(), (size_t)(rp / 128), s));
-  SvidWork w{wa.f(), wb.f(), wc.f(), waa.f(), wbb.f(), wp2.f(), (int*)wct.p};
+  SvidWork w{wa.f(), wb.f(), wc.f(), waa.f(), wbb.f(), wp2.f()};
   NQ_HIPCHK(stage_in(X, rows, cols, ldx, x.f(), rows_pad, rp, s));
   NQ_HIPCHK(launch_svid(x.f(), p.f(), (int)rows_pad, (int)rp, (int)cols, T, 2, w, s));
   if (Z) NQ_HIPCHK(stage_out(p.f(), rp, Z, ldz, rows, cols, s));

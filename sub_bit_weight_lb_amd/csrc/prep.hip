@@ -16,7 +16,7 @@ __global__ void stats_init_kernel(DevStats* st) {
   st->nonfinite = 0;
   st->bad_precond = 0;
   st->potrf_info = 0x7fffffff;
-  st->sched_err = 0;
+  st->pad = 0;
 }
 
 __global__ void check_precond_kernel(const float* __restrict__ d_out, int64_t m,

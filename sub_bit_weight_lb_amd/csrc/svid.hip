@@ -176,25 +176,18 @@ __global__ __launch_bounds__(256) void svid_step_kernel(const float* __restrict_
   }
 }
 
-// b_j = sum_c part[c][j] / aa over nch partial rows, in two levels inside one
-// launch: block (g, y) sums its share of the partial rows for the 128 columns
-// of group g into part2[y]; the last block of group g to finish (atomic
-// ticket, counter reset afterwards) adds part2[0..NY) in order, divides by
-// aa and writes b and bbpart[g]. The summation order is fixed, so the result
-// does not depend on which block finishes last.
+// b_j = sum_c part[c][j] / aa over nch partial rows, in two launches:
+// stage 1, block (g, y): the y-th share of the partial rows for the 128
+// columns of group g -> part2[y]; stage 2, block g: part2[0..NY) in order,
+// aa = sum of aapart, b = sum / aa, bbpart[g] = sum b^2. Fixed order
+// throughout, no inter-block communication inside a launch.
 constexpr int NY = kSvidReduceRows;  // row groups of the reduce
-__global__ __launch_bounds__(256) void svid_reduce_kernel(const float* __restrict__ part, int nch,
-                                                          const float* __restrict__ aapart,
-                                                          int rp, float* __restrict__ part2,
-                                                          int* __restrict__ counters,
-                                                          float* __restrict__ b,
-                                                          float* __restrict__ bbpart) {
+__global__ __launch_bounds__(256) void svid_reduce1_kernel(const float* __restrict__ part, int nch,
+                                                           int rp, float* __restrict__ part2) {
   __shared__ f32x4 red[8][32];
-  __shared__ float fred[256];
-  __shared__ int is_last;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int g = blockIdx.x, y = blockIdx.y;
-  const int q = g * 32 + tx;  // float4 column index
+  const int q = blockIdx.x * 32 + tx;  // float4 column index
+  const int y = blockIdx.y;
   const int c0 = (int)((int64_t)nch * y / NY), c1 = (int)((int64_t)nch * (y + 1) / NY);
   f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
@@ -207,15 +200,15 @@ __global__ __launch_bounds__(256) void svid_reduce_kernel(const float* __restric
     for (int k = 1; k < 8; ++k) t += red[k][tx];
     ((f32x4*)(part2 + (int64_t)y * rp))[q] = t;
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&counters[g], 1);
-    is_last = (prev == NY - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+}
+
+__global__ __launch_bounds__(256) void svid_reduce2_kernel(const float* __restrict__ part2,
+                                                           const float* __restrict__ aapart,
+                                                           int nch, int rp, float* __restrict__ b,
+                                                           float* __restrict__ bbpart) {
+  __shared__ float fred[256];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int q = blockIdx.x * 32 + tx;
   float aa = 0.0f;
   for (int c = threadIdx.x; c < nch; c += 256) aa += aapart[c];
   fred[threadIdx.x] = aa;
@@ -240,8 +233,7 @@ __global__ __launch_bounds__(256) void svid_reduce_kernel(const float* __restric
   if (threadIdx.x == 0) {
     float t = 0.0f;
     for (int k = 0; k < 32; ++k) t += fred[k];
-    bbpart[g] = t;
-    counters[g] = 0;
+    bbpart[blockIdx.x] = t;
   }
 }
 
@@ -318,16 +310,20 @@ hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int
   hipLaunchKernelGGL(svid_init_b_kernel, dim3(nbb), dim3(CB), 0, s, w.b, w.bbpart, rp, r_real);
   for (int t = 0; t < T; ++t) {
     if (rs && fused_step(X, rows_pad, rp, nbb, w, s)) {
-      hipLaunchKernelGGL(svid_reduce_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart,
-                         rows_pad / rs, w.aapart, rp, w.part2, w.counters, w.b, w.bbpart);
+      hipLaunchKernelGGL(svid_reduce1_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart,
+                         rows_pad / rs, rp, w.part2);
+      hipLaunchKernelGGL(svid_reduce2_kernel, dim3(rp / 128), dim3(256), 0, s, w.part2, w.aapart,
+                         rows_pad / rs, rp, w.b, w.bbpart);
       continue;
     }
     hipLaunchKernelGGL(svid_row_kernel, dim3(rows_pad / 4), dim3(256), 0, s, X, rp, w.b,
                        w.bbpart, nbb, w.a);
     hipLaunchKernelGGL(colsum_kernel<0>, dim3(rp / 128, nch), dim3(256), 0, s, X, rp, rows_pad,
                        w.a, w.colpart, w.aapart);
-    hipLaunchKernelGGL(svid_reduce_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart, nch,
-                       w.aapart, rp, w.part2, w.counters, w.b, w.bbpart);
+    hipLaunchKernelGGL(svid_reduce1_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart, nch,
+                       rp, w.part2);
+    hipLaunchKernelGGL(svid_reduce2_kernel, dim3(rp / 128), dim3(256), 0, s, w.part2, w.aapart,
+                       nch, rp, w.b, w.bbpart);
   }
   const int64_t n4 = (int64_t)rows_pad * rp / 4;
   const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
