@@ -102,8 +102,8 @@ struct DiagSmem {
   float dvec[NB];
 };
 
-__device__ void diag_factor(float* A, float* M, int rp, int k, int r_real, DevStats* st,
-                            DiagSmem& sm) {
+__device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, int r_real,
+                                            DevStats* st, DiagSmem& sm) {
   float (&colbuf)[2][NB] = sm.colbuf;
   float (&erow)[2][NB] = sm.erow;
   float (&dvec)[NB] = sm.dvec;
@@ -129,21 +129,20 @@ __device__ void diag_factor(float* A, float* M, int rp, int k, int r_real, DevSt
     for (int b = 0; b < 4; ++b) erow[0][4 * bj + b] = Er[0][b];
   }
   __syncthreads();
-  // Outer loop over 4-wide block columns, inner 4 steps unrolled so that
-  // every register index is a compile-time constant. Rows <= j and columns
-  // <= j are masked arithmetically instead of branching.
+  // Outer loop over 4-wide block columns (not unrolled, to bound register
+  // use), inner 4 steps unrolled so every register index is static. Rows and
+  // columns <= j are masked arithmetically. The entries the next step
+  // broadcasts (column j+1 of T, row j+1 of E) are updated and published
+  // first; the remaining updates overlap the LDS writes.
+#pragma unroll 1
   for (int J = 0; J < NB / 4; ++J) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * J + jj;
-      const int buf = jj & 1;  // NB / 4 steps per J is even, so parity follows jj
+      const int buf = jj & 1;
       const float d = colbuf[buf][j];
-      if (tid == 0) {
-        dvec[j] = d;
-        if (!(d > 0.0f && isfinite(d)) && (int)base + j < r_real)
-          atomicMin(&st->potrf_info, (int)base + j + 1);
-      }
-      const float inv = 1.0f / d;
+      if (tid == 0) dvec[j] = d;
+      const float inv = __builtin_amdgcn_rcpf(d);
       const f32x4 li = *(const f32x4*)&colbuf[buf][4 * bi];
       const f32x4 cj = *(const f32x4*)&colbuf[buf][4 * bj];
       const f32x4 ej = *(const f32x4*)&erow[buf][4 * bj];
@@ -152,26 +151,43 @@ __device__ void diag_factor(float* A, float* M, int rp, int k, int r_real, DevSt
       for (int a = 0; a < 4; ++a) l[a] = (4 * bi + a > j) ? li[a] * inv : 0.0f;
 #pragma unroll
       for (int b = 0; b < 4; ++b) cm[b] = (4 * bj + b > j) ? cj[b] : 0.0f;
+      const int jo = (jj + 1) & 3;               // position of j + 1 in its block
+      const int nb_ = (jj == 3) ? J + 1 : J;     // block index of j + 1
+      if (j + 1 < NB) {
+        if (bj == nb_) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            Tr[a][jo] = fmaf(-l[a], cm[jo], Tr[a][jo]);
+            colbuf[buf ^ 1][4 * bi + a] = Tr[a][jo];
+          }
+        }
+        if (bi == nb_) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            Er[jo][b] = fmaf(-l[jo], ej[b], Er[jo][b]);
+            erow[buf ^ 1][4 * bj + b] = Er[jo][b];
+          }
+        }
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          Tr[a][b] = fmaf(-l[a], cm[b], Tr[a][b]);
-          Er[a][b] = fmaf(-l[a], ej[b], Er[a][b]);
+          const bool doneT = (j + 1 < NB) && bj == nb_ && b == jo;
+          const bool doneE = (j + 1 < NB) && bi == nb_ && a == jo;
+          if (!doneT) Tr[a][b] = fmaf(-l[a], cm[b], Tr[a][b]);
+          if (!doneE) Er[a][b] = fmaf(-l[a], ej[b], Er[a][b]);
         }
-      // publish column j + 1 of T and row j + 1 of E for the next step
-      const int nb_ = (jj == 3) ? J + 1 : J;
-      if (j + 1 < NB) {
-        if (bj == nb_) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) colbuf[buf ^ 1][4 * bi + a] = Tr[a][(jj + 1) & 3];
-        }
-        if (bi == nb_) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) erow[buf ^ 1][4 * bj + b] = Er[(jj + 1) & 3][b];
-        }
-      }
       __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    for (int j = 0; j < NB; ++j) {
+      const float d = dvec[j];
+      if (!(d > 0.0f && isfinite(d)) && (int)base + j < r_real) {
+        atomicMin(&st->potrf_info, (int)base + j + 1);
+        break;
+      }
     }
   }
   f32x4 lv[4], mv[4];

@@ -135,28 +135,44 @@ __global__ __launch_bounds__(NT) void gemm_nn_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // Accumulator layout of the 32x32 fp32 MFMA: lane l, register v holds
-  // row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32 of the block.
+  // Epilogue through LDS, one 32 x 32 block per wave at a time: the block is
+  // written in the MFMA accumulator layout (lane l, register v holds row
+  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32), read back row-major as
+  // float4, and combined with P / Lam by coalesced float4 accesses. This also
+  // keeps the compiler from moving all 128 accumulators and their partner
+  // loads into VGPRs at once. The tiles' LDS is free after the last barrier.
+  constexpr int ES = 36;  // row stride of the per-wave staging block
+  float* stage = &As[0][0] + wave * 32 * ES;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 2; ++ni) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = tm * BM + wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        const int col = tn * BN + wn * 64 + ni * 32 + l32;
+      for (int v = 0; v < 16; ++v)
+        stage[(8 * (v >> 2) + 4 * half + (v & 3)) * ES + l32] = acc[mi][ni][v];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): wave-local LDS round trip
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 8 * t + (lane >> 3), c4 = (lane & 7) * 4;
+        const f32x4 val = *(const f32x4*)&stage[r * ES + c4];
+        const int row = tm * BM + wm * 128 + mi * 32 + r;
+        const int col = tn * BN + wn * 64 + ni * 32 + c4;
         const int64_t idx = (int64_t)row * p.ldc + col;
-        float val = acc[mi][ni][v];
         if (EPI == kEpiRhs) {
-          val = val + p.rho * p.P[idx];
-          p.C[idx] = val;
+          const f32x4 pv = *(const f32x4*)&p.P[idx];
+          *(f32x4*)&p.C[idx] = val + p.rho * pv;
         } else if (EPI == kEpiSolve) {
-          p.C[idx] = val;
-          p.X[idx] = val + p.X[idx];
+          const f32x4 xv = *(const f32x4*)&p.X[idx];
+          *(f32x4*)&p.C[idx] = val;
+          *(f32x4*)&p.X[idx] = val + xv;
         } else {
-          p.C[idx] = val;
+          *(f32x4*)&p.C[idx] = val;
         }
       }
+      __builtin_amdgcn_wave_barrier();
+    }
 }
 
 }  // namespace

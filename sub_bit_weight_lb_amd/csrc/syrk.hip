@@ -14,7 +14,7 @@
 namespace nq {
 namespace {
 
-constexpr int TS = 128, BK = 32, NT = 256;
+constexpr int TS = 128, BK = 16, NT = 256;
 constexpr int LDS_S = BK + 4;
 
 __global__ __launch_bounds__(NT) void syrk_partial_kernel(const float* __restrict__ A, int64_t lda,
@@ -42,10 +42,12 @@ __global__ __launch_bounds__(NT) void syrk_partial_kernel(const float* __restric
 
   const float* __restrict__ Ai = A + (int64_t)I * TS + col;
   const float* __restrict__ Aj = A + (int64_t)J * TS + col;
-  float ri[16], rj[16];
+  // each thread stages column `col`, k quads q0 + 2 j of the BK-row slice
+  constexpr int NQ = BK / 8;  // quads per thread
+  float ri[4 * NQ], rj[4 * NQ];
   auto gload = [&](int kb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NQ; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t k = kb + (q0 + 2 * j) * 4 + e;
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(NT) void syrk_partial_kernel(const float* __restric
   };
   auto sstore = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NQ; ++j) {
       f32x4 vi = {ri[j * 4], ri[j * 4 + 1], ri[j * 4 + 2], ri[j * 4 + 3]};
       f32x4 vj = {rj[j * 4], rj[j * 4 + 1], rj[j * 4 + 2], rj[j * 4 + 3]};
       *(f32x4*)&Si[buf][col * LDS_S + (q0 + 2 * j) * 4] = vi;
