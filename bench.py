@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-stream", action="store_true")
     ap.add_argument("--iters", type=int, default=None, help="override ADMM iterations per run")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -113,6 +115,18 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        # A plain copy of known size: 256 MiB read + 256 MiB written per launch.
+        n = 64 * 1024 * 1024
+        src = torch.rand(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 4 * n, "bytes_written": 4 * n,
+                          "launches": 4}), flush=True)
+        return
 
     import sub_bit_weight_lb_amd as nq
     from synth import make_layer
