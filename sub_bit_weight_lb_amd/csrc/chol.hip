@@ -11,10 +11,10 @@
 //              inverse partial sums S_ij += L_ik M_kj (i > k >= j); its first
 //              workgroup instead updates the next diagonal tile and factors
 //              it, so no launch is spent on the diagonal alone.
-// Diagonal tiles: outer-product elimination with register-resident 4 x 4
-// blocks, the same row operations applied to an identity block, giving L_kk
-// and M_kk = L_kk^-1 with one barrier per column. Off-diagonal tiles: 64 x 64
-// x 64 products on the 32x32x2 fp32 MFMA.
+// Diagonal tiles: one wave factors the tile in registers (one row per lane,
+// column broadcasts through LDS, no barrier per column) while a second wave
+// forms L^-1 from the same broadcasts. Off-diagonal tiles: 64 x 64 x 64
+// products on the 32x32x2 fp32 MFMA.
 // The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
 // M_ij = -M_ii sum_{l = j..i-1} L_il M_lj; the partial sums S_ij are kept in
 // M's own tiles until row i of M is formed.
@@ -89,123 +89,151 @@ __device__ void block_mm(const float* __restrict__ X, const float* __restrict__ 
   __syncthreads();  // Xs / Ys may be refilled by the caller's next product
 }
 
-// Diagonal block: L_kk and M_kk = L_kk^-1 of the 64 x 64 block (k, k).
-// Outer-product elimination on the lower triangle with the same row
-// operations applied to an identity block E. Thread t holds the 4 x 4 block
-// (t / 16, t % 16) of T and of E in registers. Step j needs column j of T
-// (multipliers and partners T[c][j]) and row j of E; their owners publish
-// them to LDS after the previous step's update, so each step costs one
-// barrier. At the end L = T D^-1/2 and M = D^-1/2 E with D the pivots.
+// LDS of the diagonal-tile factorisation (aliases the product buffers of
+// the update kernel, which are idle by then).
 struct DiagSmem {
-  float colbuf[2][NB];
-  float erow[2][NB];
-  float dvec[NB];
+  float col[NB][NB];  // col[j][i]: Schur column j at row i (i >= j), published by wave 0
+  float dpiv[NB];     // pivots d_j
+  float rs[NB];       // 1 / sqrt(d_j)
+  int ready;          // columns 0 .. ready - 1 of col are published
 };
 
+// Upper bound on the sleep iterations of the consumer wave (each s_sleep 1
+// is about 64 clocks, so about 0.1 s): the producer publishes all 64
+// columns within microseconds; the bound only guarantees the wait ends.
+constexpr int kSpinLimit = 1 << 22;
+
+__device__ __forceinline__ float bcast(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Wait until at least n columns are published; false if the bound ran out.
+__device__ __forceinline__ bool wait_ready(const DiagSmem& sm, int n) {
+  int spins = 0;
+  while (__hip_atomic_load(&sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit) return false;
+  }
+  return true;
+}
+
+// Diagonal tile k: A_kk = L L^T and M_kk = L^-1, written to A and M (zeros
+// above the diagonal). Right-looking elimination A = Lt D Lt^T (Lt unit lower
+// triangular, D the pivots), L = Lt D^1/2, L^-1 = D^-1/2 Lt^-1.
+//  - Wave 0 holds the Schur complement in registers, lane i holding row i.
+//    Step j broadcasts column j through LDS (uniform-address reads) and
+//    updates t[c] -= (t[j] / d_j) col_j[c] for c > j. Software pipelined:
+//    column j + 1 is final once its entry of step j is updated, so it is
+//    published, and its reads are in flight, while the rest of step j
+//    issues; the pivot comes by readlane.
+//  - Wave 1 applies the same row operations to the identity in column form
+//    (lane c holds column c of Lt^-1): e[i] -= col_j[i] (e[j] / d_j), i > j,
+//    reading the published columns, which it waits for in groups of 8
+//    through an LDS counter (bounded wait).
+// Pivots <= 0 or non-finite set potrf_info (first such row, 1-based).
 __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, int r_real,
                                             DevStats* st, DiagSmem& sm) {
-  float (&colbuf)[2][NB] = sm.colbuf;
-  float (&erow)[2][NB] = sm.erow;
-  float (&dvec)[NB] = sm.dvec;
-  const int tid = threadIdx.x;
-  const int bi = tid >> 4, bj = tid & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t base = (int64_t)k * NB;
-  float Tr[4][4], Er[4][4];
+  if (tid == 0) sm.ready = 0;
+  __syncthreads();
+  bool waited = true;
+  if (wave == 0) {
+    float t[NB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const f32x4 v = *(const f32x4*)&A[(base + 4 * bi + a) * rp + base + 4 * bj];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      Tr[a][b] = v[b];
-      Er[a][b] = (bi == bj && a == b) ? 1.0f : 0.0f;
+    for (int c4 = 0; c4 < NB / 4; ++c4) {
+      const f32x4 v = *(const f32x4*)&A[(base + lane) * rp + base + 4 * c4];
+      t[4 * c4 + 0] = v[0];
+      t[4 * c4 + 1] = v[1];
+      t[4 * c4 + 2] = v[2];
+      t[4 * c4 + 3] = v[3];
     }
-  }
-  if (bj == 0) {
+    float cv[2][NB];
+    sm.col[0][lane] = t[0];
+    __hip_atomic_store(&sm.ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) colbuf[0][4 * bi + a] = Tr[a][0];
-  }
-  if (bi == 0) {
+    for (int c = 1; c < NB; ++c) cv[0][c] = sm.col[0][c];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) erow[0][4 * bj + b] = Er[0][b];
+    for (int j = 0; j < NB; ++j) {
+      const int b = j & 1;
+      const float d = bcast(t[j], j);
+      sm.dpiv[j] = d;
+      const float l = lane > j ? t[j] * __builtin_amdgcn_rcpf(d) : 0.0f;
+      if (j + 1 < NB) {
+        t[j + 1] = fmaf(-l, cv[b][j + 1], t[j + 1]);
+        sm.col[j + 1][lane] = t[j + 1];
+        __hip_atomic_store(&sm.ready, j + 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+#pragma unroll
+        for (int c = j + 2; c < NB; ++c) cv[b ^ 1][c] = sm.col[j + 1][c];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = j + 2; c < NB; ++c) t[c] = fmaf(-l, cv[b][c], t[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // t[c] (c < lane) = Lt_ic d_c, t[lane] = d_lane; L_ic = t[c] / sqrt(d_c)
+    const float di = sm.dpiv[lane];
+    sm.rs[lane] = 1.0f / sqrtf(di);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c4 = 0; c4 < NB / 4; ++c4) {
+      f32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * c4 + q;
+        v[q] = c < lane ? t[c] * sm.rs[c] : (c == lane ? sqrtf(di) : 0.0f);
+      }
+      *(f32x4*)&A[(base + lane) * rp + base + 4 * c4] = v;
+    }
+  } else if (wave == 1) {
+    float e[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) e[i] = i == lane ? 1.0f : 0.0f;
+    float cw[2][NB];
+    float* mrow = M + base * rp + base + lane;  // row j of the tile at step j
+    waited = wait_ready(sm, 9);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) cw[0][i] = sm.col[0][i];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int b = j & 1;
+      if (j + 1 < NB) {
+        if ((j + 1) % 8 == 0) waited = waited && wait_ready(sm, j + 9 < NB ? j + 9 : NB);
+        // The read address carries an opaque zero that depends on e[j], so
+        // the compiler cannot hoist a later step's reads into this one (all
+        // reads between two waits would otherwise be issued at once and
+        // overflow the register file). The shift keeps 256-byte alignment
+        // visible, so the reads still merge into 16-byte loads.
+        int z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z) : "v"(e[j]));
+        const float* cj = &sm.col[j + 1][0] + (z << 6);
+#pragma unroll
+        for (int i = j + 1; i < NB; ++i) cw[b ^ 1][i] = cj[i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // row j of Lt^-1 is final: M_jc = e[j] / sqrt(d_j), a contiguous row store
+      const float d = cw[b][j];
+      *mrow = e[j] * __builtin_amdgcn_rsqf(d);
+      mrow += rp;
+      const float f = e[j] * __builtin_amdgcn_rcpf(d);
+#pragma unroll
+      for (int i = j + 1; i < NB; ++i) e[i] = fmaf(-cw[b][i], f, e[i]);
+      // pin this step's updates here (no instruction): otherwise the
+      // instruction selector sinks each update towards its last use and keeps
+      // every broadcast value of the group of steps live
+#pragma unroll
+      for (int i = j + 1; i < NB; ++i) asm volatile("" : "+v"(e[i]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __syncthreads();
-  // Outer loop over 4-wide block columns (not unrolled, to bound register
-  // use), inner 4 steps unrolled so every register index is static. Rows and
-  // columns <= j are masked arithmetically. The entries the next step
-  // broadcasts (column j+1 of T, row j+1 of E) are updated and published
-  // first; the remaining updates overlap the LDS writes.
-#pragma unroll 1
-  for (int J = 0; J < NB / 4; ++J) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * J + jj;
-      const int buf = jj & 1;
-      const float d = colbuf[buf][j];
-      if (tid == 0) dvec[j] = d;
-      const float inv = __builtin_amdgcn_rcpf(d);
-      const f32x4 li = *(const f32x4*)&colbuf[buf][4 * bi];
-      const f32x4 cj = *(const f32x4*)&colbuf[buf][4 * bj];
-      const f32x4 ej = *(const f32x4*)&erow[buf][4 * bj];
-      float l[4], cm[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) l[a] = (4 * bi + a > j) ? li[a] * inv : 0.0f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) cm[b] = (4 * bj + b > j) ? cj[b] : 0.0f;
-      const int jo = (jj + 1) & 3;               // position of j + 1 in its block
-      const int nb_ = (jj == 3) ? J + 1 : J;     // block index of j + 1
-      if (j + 1 < NB) {
-        if (bj == nb_) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            Tr[a][jo] = fmaf(-l[a], cm[jo], Tr[a][jo]);
-            colbuf[buf ^ 1][4 * bi + a] = Tr[a][jo];
-          }
-        }
-        if (bi == nb_) {
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            Er[jo][b] = fmaf(-l[jo], ej[b], Er[jo][b]);
-            erow[buf ^ 1][4 * bj + b] = Er[jo][b];
-          }
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const bool doneT = (j + 1 < NB) && bj == nb_ && b == jo;
-          const bool doneE = (j + 1 < NB) && bi == nb_ && a == jo;
-          if (!doneT) Tr[a][b] = fmaf(-l[a], cm[b], Tr[a][b]);
-          if (!doneE) Er[a][b] = fmaf(-l[a], ej[b], Er[a][b]);
-        }
-      __syncthreads();
-    }
-  }
-  if (tid == 0) {
-    for (int j = 0; j < NB; ++j) {
-      const float d = dvec[j];
-      if (!(d > 0.0f && isfinite(d)) && (int)base + j < r_real) {
-        atomicMin(&st->potrf_info, (int)base + j + 1);
-        break;
-      }
-    }
-  }
-  f32x4 lv[4], mv[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = 4 * bi + a;
-    const float si = sqrtf(dvec[i]);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int c = 4 * bj + b;
-      lv[a][b] = c <= i ? Tr[a][b] / sqrtf(dvec[c]) : 0.0f;
-      mv[a][b] = c <= i ? Er[a][b] / si : 0.0f;
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    *(f32x4*)&A[(base + 4 * bi + a) * rp + base + 4 * bj] = lv[a];
-    *(f32x4*)&M[(base + 4 * bi + a) * rp + base + 4 * bj] = mv[a];
+  if (wave == 1) {
+    if (!waited && lane == 0) atomicMin(&st->potrf_info, (int)base + 1);
+  } else if (wave == 0) {
+    const float d = sm.dpiv[lane];
+    const bool bad = !(d > 0.0f && isfinite(d)) && (int)base + lane < r_real;
+    const uint64_t m = __ballot(bad);
+    if (m && lane == 0) atomicMin(&st->potrf_info, (int)base + __ffsll((unsigned long long)m));
   }
 }
 
@@ -235,9 +263,14 @@ __global__ __launch_bounds__(NT) void chol_panel_kernel(float* A, float* M, int 
 
 __global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, int rp, int k,
                                                          int r_real, DevStats* st) {
-  __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
-  __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
-  __shared__ __attribute__((aligned(16))) DiagSmem dsm;
+  // product buffers and the diagonal-tile scratch share one LDS block
+  constexpr int kProdFloats = 2 * NB * LS;
+  constexpr int kDiagFloats = (int)(sizeof(DiagSmem) / sizeof(float));
+  __shared__ __attribute__((aligned(16))) float lds[kProdFloats > kDiagFloats ? kProdFloats
+                                                                             : kDiagFloats];
+  float* Xs = lds;
+  float* Ys = lds + NB * LS;
+  DiagSmem& dsm = *reinterpret_cast<DiagSmem*>(lds);
   const int R = rp / NB;
   const int n = R - k - 1;
   const int64_t kk = (int64_t)k * NB;
@@ -247,6 +280,7 @@ __global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, int
     const int64_t d0 = kk + NB;
     block_mm<true>(A + d0 * rp + kk, A + d0 * rp + kk, A + d0 * rp + d0, rp, -1.0f, 1.0f, Xs, Ys);
     __threadfence_block();
+    __syncthreads();
     diag_factor(A, M, rp, k + 1, r_real, st, dsm);
     return;
   }
