@@ -30,38 +30,46 @@ constexpr int NB = kNB;   // 64
 constexpr int NT = 256;
 constexpr int LS = NB + 4;  // LDS row stride for MFMA tiles
 
-// out = alpha * X op(Y) + beta * out on 64 x 64 blocks (ld = rp for all).
-// op(Y) = Y^T if TRANS else Y.
-template <bool TRANS>
+// Epilogues of the 64 x 64 block product P = op(X) op(Y).
+enum BlockEpi {
+  kBlkAxpby,  // out = alpha P + beta out
+  kBlkSymAcc  // symmetric accumulate into G^-1 (see block_mm)
+};
+
+// 64 x 64 x 64 block product on the 32x32x2 fp32 MFMA (ld = rp for all).
+// op(X) = X^T if TA else X; op(Y) = Y^T if TB else Y.
+// kBlkAxpby:  out = alpha P + beta out.
+// kBlkSymAcc: out is tile (i, j), i >= j, of a symmetric matrix and out2 its
+//   mirror tile (j, i) (out2 == out on the diagonal, where only P's lower
+//   triangle is used). v = P + (beta != 0 ? out : 0) is written to out and,
+//   transposed, to out2, so both halves hold the same sums and the result
+//   is exactly symmetric.
+template <bool TA, bool TB, BlockEpi EPI = kBlkAxpby>
 __device__ void block_mm(const float* __restrict__ X, const float* __restrict__ Y, float* out,
-                         int rp, float alpha, float beta, float* Xs, float* Ys) {
+                         int rp, float alpha, float beta, float* Xs, float* Ys,
+                         float* out2 = nullptr) {
   const int tid = threadIdx.x;
-  // X: 64 rows x 16 float4 = 1024 float4, 4 per thread, stored as is ([p][c]).
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int idx = tid + NT * q;
-    const int row = idx >> 4, c4 = idx & 15;
-    *(f32x4*)&Xs[row * LS + c4 * 4] = *(const f32x4*)&X[(int64_t)row * rp + c4 * 4];
-  }
-  if (TRANS) {
-    // B operand (k = c, n = q) = Y[q][c]: Y as is, [q][c].
+  // Both operands are staged [m or n][k] with k contiguous.
+  auto stage_rows = [&](const float* S, float* D) {  // operand(i, c) = S[i][c]
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + NT * q;
       const int row = idx >> 4, c4 = idx & 15;
-      *(f32x4*)&Ys[row * LS + c4 * 4] = *(const f32x4*)&Y[(int64_t)row * rp + c4 * 4];
+      *(f32x4*)&D[row * LS + c4 * 4] = *(const f32x4*)&S[(int64_t)row * rp + c4 * 4];
     }
-  } else {
-    // B operand (k = c, n = q) = Y[c][q]: transpose to [q][c] while staging.
+  };
+  auto stage_cols = [&](const float* S, float* D) {  // operand(i, c) = S[c][i]
     const int col = tid & 63, cq = tid >> 6;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c0 = (cq + 4 * j) * 4;
-      f32x4 v = {Y[(int64_t)(c0 + 0) * rp + col], Y[(int64_t)(c0 + 1) * rp + col],
-                 Y[(int64_t)(c0 + 2) * rp + col], Y[(int64_t)(c0 + 3) * rp + col]};
-      *(f32x4*)&Ys[col * LS + c0] = v;
+      f32x4 v = {S[(int64_t)(c0 + 0) * rp + col], S[(int64_t)(c0 + 1) * rp + col],
+                 S[(int64_t)(c0 + 2) * rp + col], S[(int64_t)(c0 + 3) * rp + col]};
+      *(f32x4*)&D[col * LS + c0] = v;
     }
-  }
+  };
+  if (TA) stage_cols(X, Xs); else stage_rows(X, Xs);
+  if (TB) stage_rows(Y, Ys); else stage_cols(Y, Ys);
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -83,8 +91,15 @@ __device__ void block_mm(const float* __restrict__ X, const float* __restrict__ 
     const int row = wm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
     const int col = wn * 32 + l32;
     float* o = out + (int64_t)row * rp + col;
-    const float prev = beta != 0.0f ? *o : 0.0f;
-    *o = alpha * acc[v] + beta * prev;
+    if (EPI == kBlkAxpby) {
+      const float prev = beta != 0.0f ? *o : 0.0f;
+      *o = alpha * acc[v] + beta * prev;
+    } else {
+      if (out2 == out && col > row) continue;  // diagonal tile: lower triangle only
+      const float val = acc[v] + (beta != 0.0f ? *o : 0.0f);
+      *o = val;
+      out2[(int64_t)col * rp + row] = val;
+    }
   }
   __syncthreads();  // Xs / Ys may be refilled by the caller's next product
 }
@@ -239,11 +254,13 @@ __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, i
 
 __global__ __launch_bounds__(NT) void chol_diag0_kernel(float* A, float* M, int rp, int r_real,
                                                         DevStats* st) {
+  __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) DiagSmem dsm;
   diag_factor(A, M, rp, 0, r_real, st, dsm);
 }
 
 __global__ __launch_bounds__(NT) void chol_panel_kernel(float* A, float* M, int rp, int k) {
+  __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
   __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
   const int R = rp / NB;
@@ -253,16 +270,33 @@ __global__ __launch_bounds__(NT) void chol_panel_kernel(float* A, float* M, int 
   if (b < nL) {
     const int64_t i0 = (int64_t)(k + 1 + b) * NB;
     float* Aik = A + i0 * rp + kk;
-    block_mm<true>(Aik, M + kk * rp + kk, Aik, rp, 1.0f, 0.0f, Xs, Ys);
+    block_mm<false, true>(Aik, M + kk * rp + kk, Aik, rp, 1.0f, 0.0f, Xs, Ys);
   } else {
     const int64_t j0 = (int64_t)(b - nL) * NB;
     float* Mkj = M + kk * rp + j0;
-    block_mm<false>(M + kk * rp + kk, Mkj, Mkj, rp, -1.0f, 0.0f, Xs, Ys);
+    block_mm<false, false>(M + kk * rp + kk, Mkj, Mkj, rp, -1.0f, 0.0f, Xs, Ys);
   }
 }
 
-__global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, int rp, int k,
-                                                         int r_real, DevStats* st) {
+// Lower-triangle tile index t -> (i, j), i >= j.
+__device__ __forceinline__ void tri_index(int t, int& i, int& j) {
+  int ii = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+  while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+  while (ii * (ii + 1) / 2 > t) --ii;
+  i = ii;
+  j = t - ii * (ii + 1) / 2;
+}
+
+// Workgroups of update(k), in this order:
+//   1 (if k + 1 < R): A_{k+1,k+1} -= L_{k+1,k} L_{k+1,k}^T, then factor it;
+//   the other lower tiles of the trailing block: A_ij -= L_ik L_jk^T;
+//   inverse partial sums: S_ij += L_ik M_kj (i > k >= j), kept in M;
+//   if Ginv: Ginv_ij += M_ki^T M_kj for j <= i <= k (row k of M is final
+//     once panel(k) has run; tile (i, j) starts at k = i), plus mirror.
+// With k = R - 1 only the Ginv group is left (after the last panel).
+__global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, float* Ginv, int rp,
+                                                         int k, int r_real, DevStats* st) {
+  __builtin_amdgcn_s_setprio(3);
   // product buffers and the diagonal-tile scratch share one LDS block
   constexpr int kProdFloats = 2 * NB * LS;
   constexpr int kDiagFloats = (int)(sizeof(DiagSmem) / sizeof(float));
@@ -275,31 +309,42 @@ __global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, int
   const int n = R - k - 1;
   const int64_t kk = (int64_t)k * NB;
   int b = blockIdx.x;
-  if (b == 0) {
-    // next diagonal tile: A_{k+1,k+1} -= L_{k+1,k} L_{k+1,k}^T, then factor it
-    const int64_t d0 = kk + NB;
-    block_mm<true>(A + d0 * rp + kk, A + d0 * rp + kk, A + d0 * rp + d0, rp, -1.0f, 1.0f, Xs, Ys);
-    __threadfence_block();
-    __syncthreads();
-    diag_factor(A, M, rp, k + 1, r_real, st, dsm);
-    return;
+  if (n > 0) {
+    if (b == 0) {
+      const int64_t d0 = kk + NB;
+      block_mm<false, true>(A + d0 * rp + kk, A + d0 * rp + kk, A + d0 * rp + d0, rp, -1.0f, 1.0f,
+                            Xs, Ys);
+      __threadfence_block();
+      __syncthreads();
+      diag_factor(A, M, rp, k + 1, r_real, st, dsm);
+      return;
+    }
+    b -= 1;
+    const int nA = n * (n + 1) / 2 - 1;  // lower tiles of the trailing block but (k+1, k+1)
+    if (b < nA) {
+      int ii, jj;
+      tri_index(b + 1, ii, jj);
+      const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
+      block_mm<false, true>(A + i0 * rp + kk, A + j0 * rp + kk, A + i0 * rp + j0, rp, -1.0f, 1.0f,
+                            Xs, Ys);
+      return;
+    }
+    b -= nA;
+    const int nS = n * (k + 1);
+    if (b < nS) {
+      const int ii = b / (k + 1), jj = b % (k + 1);
+      const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)jj * NB;
+      block_mm<false, false>(A + i0 * rp + kk, M + kk * rp + j0, M + i0 * rp + j0, rp, 1.0f, 1.0f,
+                             Xs, Ys);
+      return;
+    }
+    b -= nS;
   }
-  b -= 1;
-  const int nA = n * (n + 1) / 2 - 1;  // lower tiles of the trailing block but (k+1, k+1)
-  if (b < nA) {
-    const int t = b + 1;
-    int ii = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
-    while (ii * (ii + 1) / 2 > t) --ii;
-    const int jj = t - ii * (ii + 1) / 2;
-    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
-    block_mm<true>(A + i0 * rp + kk, A + j0 * rp + kk, A + i0 * rp + j0, rp, -1.0f, 1.0f, Xs, Ys);
-  } else {
-    const int q = b - nA;
-    const int ii = q / (k + 1), jj = q % (k + 1);
-    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)jj * NB;
-    block_mm<false>(A + i0 * rp + kk, M + kk * rp + j0, M + i0 * rp + j0, rp, 1.0f, 1.0f, Xs, Ys);
-  }
+  int ii, jj;
+  tri_index(b, ii, jj);
+  const int64_t i0 = (int64_t)ii * NB, j0 = (int64_t)jj * NB;
+  block_mm<true, false, kBlkSymAcc>(M + kk * rp + i0, M + kk * rp + j0, Ginv + i0 * rp + j0, rp,
+                                    1.0f, ii == k ? 0.0f : 1.0f, Xs, Ys, Ginv + j0 * rp + i0);
 }
 
 __global__ void zero_upper_kernel(float* A, int rp) {
@@ -311,8 +356,8 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 
 }  // namespace
 
-hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real, DevStats* st,
-                                   bool zero_upper_L, hipStream_t s) {
+hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
+                                   DevStats* st, bool zero_upper_L, hipStream_t s) {
   if (rp % NB) return hipErrorInvalidValue;
   const int R = rp / NB;
   hipError_t e = launch_zero(M, (size_t)rp * rp, s);
@@ -322,10 +367,11 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real, DevSt
     const int np = (R - k - 1) + k;
     if (np > 0) hipLaunchKernelGGL(chol_panel_kernel, dim3(np), dim3(NT), 0, s, A, M, rp, k);
     const int n = R - k - 1;
-    if (n > 0) {
-      const int nb = 1 + (n * (n + 1) / 2 - 1) + n * (k + 1);
-      hipLaunchKernelGGL(chol_update_kernel, dim3(nb), dim3(NT), 0, s, A, M, rp, k, r_real, st);
-    }
+    const int nb = (n > 0 ? 1 + (n * (n + 1) / 2 - 1) + n * (k + 1) : 0) +
+                   (Ginv ? (k + 1) * (k + 2) / 2 : 0);
+    if (nb > 0)
+      hipLaunchKernelGGL(chol_update_kernel, dim3(nb), dim3(NT), 0, s, A, M, Ginv, rp, k, r_real,
+                         st);
   }
   if (!zero_upper_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;

@@ -79,13 +79,6 @@ void gram_split(int K, int rp, int* nch, int* kchunk) {
   *nch = (K + kc - 1) / kc;
 }
 
-void lauum_split(int rp, int* nch, int* kchunk) {
-  int c = std::max(1, std::min(4, rp / 128));
-  int kc = (int)round_up((rp + c - 1) / c, 32);
-  *kchunk = kc;
-  *nch = (rp + kc - 1) / kc;
-}
-
 struct Arena {
   size_t off = 0;
   template <class T>
@@ -113,7 +106,7 @@ struct nq_lbadmm {
   nq_lbadmm_desc d{};
   int device = 0;
   int mp = 0, np_ = 0, rp = 0;
-  int gU_nch = 1, gU_kc = 32, gV_nch = 1, gV_kc = 32, l_nch = 1, l_kc = 32;
+  int gU_nch = 1, gU_kc = 32, gV_nch = 1, gV_kc = 32;
   char* base = nullptr;
   size_t bytes = 0;
   float *Wt, *WtT, *U, *V, *LamU, *PU, *LamV, *PV, *R, *G, *Minv, *Ginv, *gpart;
@@ -141,7 +134,7 @@ namespace {
 size_t layout(nq_lbadmm* h) {
   const int64_t mp = h->mp, np_ = h->np_, rp = h->rp;
   const int64_t mx = std::max(mp, np_);
-  const int gch = std::max(std::max(h->gU_nch, h->gV_nch), h->l_nch);
+  const int gch = std::max(h->gU_nch, h->gV_nch);
   Arena a;
   size_t o_Wt = a.take<float>(mp * np_), o_WtT = a.take<float>(np_ * mp);
   size_t o_U = a.take<float>(mp * rp), o_V = a.take<float>(np_ * rp);
@@ -197,7 +190,6 @@ void plan(nq_lbadmm* h) {
   h->rp = (int)round_up(h->d.r, kPadR);
   gram_split(h->np_, h->rp, &h->gU_nch, &h->gU_kc);  // U-half: Gram of V, K = n
   gram_split(h->mp, h->rp, &h->gV_nch, &h->gV_kc);   // V-half: Gram of U, K = m
-  lauum_split(h->rp, &h->l_nch, &h->l_kc);
 }
 
 size_t pairs_per_run(const nq_lbadmm* h) { return 4 + (size_t)h->d.iters * 8; }
@@ -245,13 +237,12 @@ nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
   hipStream_t cs = overlap ? h->aux : s;
   hipStream_t vs = overlap ? h->svs : s;
   if (overlap) HIPCHK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
-  // r x r chain: G = other^T other + rho I, L and L^-1, G^-1 = L^-T L^-1
+  // r x r chain: G = other^T other + rho I, L and M = L^-1, G^-1 = M^T M
+  // (accumulated block row by block row while the factorisation runs)
   long pc = prof_begin(h, NQ_PHASE_CHAIN, cs);
   HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, cs));
   HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, cs));
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, cs));
-  HIPCHK(launch_syrk_partial(h->Minv, rp, rp, rp, h->l_kc, true, h->gpart, cs));
-  HIPCHK(launch_gram_reduce(h->gpart, h->l_nch, rp, 0.0f, h->Ginv, rp, cs));
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, cs));
   prof_end(h, pc, cs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_join, h->aux));
   // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last SVID

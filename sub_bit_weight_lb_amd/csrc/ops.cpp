@@ -128,26 +128,19 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
     return set_error(NQ_ERR_INVALID_ARG, "bad cholesky arguments");
   hipStream_t s = (hipStream_t)stream;
   const int64_t rp = round_up(r, 128);
-  int nch = (int)std::max<int64_t>(1, std::min<int64_t>(4, rp / 128));
-  const int kc = (int)round_up((rp + nch - 1) / nch, 32);
-  nch = (int)((rp + kc - 1) / kc);
-  DevBuf a, m, part, gi, st;
+  DevBuf a, m, gi, st;
   NQ_HIPCHK(a.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(m.alloc(sizeof(float) * rp * rp));
-  NQ_HIPCHK(part.alloc(sizeof(float) * nch * rp * rp));
-  NQ_HIPCHK(gi.alloc(sizeof(float) * rp * rp));
+  if (Ginv) NQ_HIPCHK(gi.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(st.alloc(sizeof(DevStats)));
   DevStats* dst = (DevStats*)st.p;
   NQ_HIPCHK(launch_stats_init(dst, s));
   // [G 0; 0 I]: the identity keeps the padded system positive definite
   NQ_HIPCHK(stage_in(G, r, r, ldg, a.f(), rp, rp, s));
   NQ_HIPCHK(launch_set_diag(a.f(), rp, (int)r, (int)rp, 1.0f, s));
-  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), (int)rp, (int)r, dst, true, s));
-  if (Ginv) {
-    NQ_HIPCHK(launch_syrk_partial(m.f(), rp, (int)rp, (int)rp, kc, true, part.f(), s));
-    NQ_HIPCHK(launch_gram_reduce(part.f(), nch, (int)rp, 0.0f, gi.f(), rp, s));
-    NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));
-  }
+  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), Ginv ? gi.f() : nullptr, (int)rp, (int)r, dst,
+                                    true, s));
+  if (Ginv) NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));
   if (L) NQ_HIPCHK(stage_out(a.f(), rp, L, ldl, r, r, s));
   DevStats hs;
   NQ_HIPCHK(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s));

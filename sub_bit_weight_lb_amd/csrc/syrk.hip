@@ -20,6 +20,9 @@ constexpr int LDS_S = BK + 4;
 __global__ __launch_bounds__(NT) void syrk_partial_kernel(const float* __restrict__ A, int64_t lda,
                                                           int K, int rp, int kchunk, int tri,
                                                           float* __restrict__ part) {
+  // the Gram heads the r x r chain, the critical path of an ADMM half: its
+  // waves win issue arbitration against co-resident GEMM waves
+  __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) float Si[2][TS * LDS_S];
   __shared__ __attribute__((aligned(16))) float Sj[2][TS * LDS_S];
 
@@ -124,6 +127,7 @@ __global__ __launch_bounds__(NT) void syrk_partial_kernel(const float* __restric
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part,
                                                           int nchunks, int rp, float rho,
                                                           float* __restrict__ G, int64_t ldg) {
+  __builtin_amdgcn_s_setprio(3);
   __shared__ float tile[32][33];
   const int ti = blockIdx.y, tj = blockIdx.x;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
