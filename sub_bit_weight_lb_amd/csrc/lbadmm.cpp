@@ -19,6 +19,7 @@
 
 #include <climits>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -37,6 +38,8 @@ nq_status hip_fail(hipError_t e, const char* what) { return hip_error(e, what); 
 constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
                                   NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE;
 constexpr int kProfileRuns = 8;
+// CUs reserved for the Cholesky chain while the RHS GEMM runs on the rest.
+constexpr int kChainCUs = 0;
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
@@ -115,9 +118,12 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
-  hipStream_t aux = nullptr, svs = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_t0 = nullptr, ev_t1 = nullptr;
-  hipEvent_t ev_svid[2] = {nullptr, nullptr};
+  // chain_s: the Cholesky, on a reserved group of CUs; gemm_s: the RHS GEMM
+  // and the SVIDs, on the other CUs (see run_half)
+  hipStream_t chain_s = nullptr, gemm_s = nullptr;
+  int chain_cus = 0;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_gram = nullptr, ev_rhs = nullptr,
+            ev_t0 = nullptr, ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
@@ -232,28 +238,58 @@ struct Half {
   int factor;  // 0 = U, 1 = V
 };
 
-nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
+// Z = SVID(X); Lam = X - Z; P = Z - Lam for the factor of half x.
+nq_status run_svid(nq_lbadmm* h, const Half& x, hipStream_t vs) {
+  long pv = prof_begin(h, NQ_PHASE_SVID, vs);
+  HIPCHK(launch_svid(x.Lam, x.P, x.M, h->rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, vs));
+  prof_end(h, pv, vs);
+  return NQ_OK;
+}
+
+// One ADMM half for the factor of x. With overlap:
+//   s (the caller's stream, whole chip): the Gram G = other^T other + rho I,
+//        which heads the critical path; later the solve out = R G^-1
+//        (X = out + Lam into Lam);
+//   chain_s (a reserved group of CUs): after the Gram, the blocked Cholesky
+//        with M = L^-1 and G^-1 = M^T M, a chain of latency-bound launches;
+//   gemm_s (the other CUs): after the Gram, R = Wside other + rho (Z - Lam),
+//        then the SVID of the previous half (`pending`), which has until the
+//        next half of its own factor (later on this stream) to finish.
+// The chain runs on CUs of its own because a wave sharing a SIMD with GEMM
+// waves issues several times slower, and the chain is the critical path.
+nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t s,
+                   bool overlap) {
   const int rp = h->rp;
-  hipStream_t cs = overlap ? h->aux : s;
-  hipStream_t vs = overlap ? h->svs : s;
-  if (overlap) HIPCHK(hipStreamWaitEvent(h->aux, h->ev_fork, 0));
-  // r x r chain: G = other^T other + rho I, L and M = L^-1, G^-1 = M^T M
-  // (accumulated block row by block row while the factorisation runs)
-  long pc = prof_begin(h, NQ_PHASE_CHAIN, cs);
-  HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, cs));
-  HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, cs));
+  hipStream_t cs = overlap ? h->chain_s : s;
+  hipStream_t gs = overlap ? h->gemm_s : s;
+  long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
+  HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, s));
+  HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, s));
+  if (overlap) {
+    HIPCHK(hipEventRecord(h->ev_gram, s));
+    HIPCHK(hipStreamWaitEvent(h->chain_s, h->ev_gram, 0));
+    HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
+  }
   HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, cs));
   prof_end(h, pc, cs);
-  if (overlap) HIPCHK(hipEventRecord(h->ev_join, h->aux));
-  // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last SVID
-  if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_svid[x.factor], 0));
+  if (overlap) HIPCHK(hipEventRecord(h->ev_join, cs));
+  // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last
+  // SVID, earlier on the same stream
   GemmArgs g{};
   g.A = x.Wside; g.lda = x.K; g.B = x.other; g.ldb = rp; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
-  long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, s);
-  HIPCHK(launch_gemm(g, kEpiRhs, s));
-  prof_end(h, pr, s);
-  if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
+  long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, gs);
+  HIPCHK(launch_gemm(g, kEpiRhs, gs));
+  prof_end(h, pr, gs);
+  if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
+  if (pending) {
+    nq_status st = run_svid(h, *pending, gs);
+    if (st != NQ_OK) return st;
+  }
+  if (overlap) {
+    HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
+    HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
+  }
   // out = R G^-1, X = out + Lam (into Lam)
   GemmArgs q{};
   q.A = h->R; q.lda = rp; q.B = h->Ginv; q.ldb = rp; q.C = x.out; q.ldc = rp;
@@ -261,15 +297,6 @@ nq_status run_half(nq_lbadmm* h, const Half& x, hipStream_t s, bool overlap) {
   long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
   prof_end(h, ps, s);
-  if (overlap) {
-    HIPCHK(hipEventRecord(h->ev_fork, s));
-    HIPCHK(hipStreamWaitEvent(h->svs, h->ev_fork, 0));
-  }
-  // Z = SVID(X); Lam = X - Z; P = Z - Lam
-  long pv = prof_begin(h, NQ_PHASE_SVID, vs);
-  HIPCHK(launch_svid(x.Lam, x.P, x.M, rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, vs));
-  prof_end(h, pv, vs);
-  if (overlap) HIPCHK(hipEventRecord(h->ev_svid[x.factor], h->svs));
   return NQ_OK;
 }
 
@@ -315,6 +342,36 @@ nq_status nq_lbadmm_workspace_bytes(const nq_lbadmm_desc* desc, size_t* bytes) {
   return NQ_OK;
 }
 
+namespace {
+// The chain stream gets the last `chain_cus` CUs of the device, the GEMM
+// stream all the others. NQ_CHAIN_CUS overrides the count (0 = no masks,
+// both streams on the whole chip).
+hipError_t create_streams(nq_lbadmm* h) {
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, h->device);
+  if (e != hipSuccess) return e;
+  const int ncu = prop.multiProcessorCount;
+  int res = kChainCUs;
+  if (const char* env = std::getenv("NQ_CHAIN_CUS")) res = std::atoi(env);
+  res = std::max(0, std::min(res, ncu / 2));
+  h->chain_cus = res;
+  if (res == 0) {
+    e = hipStreamCreateWithFlags(&h->chain_s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->gemm_s, hipStreamNonBlocking);
+    return e;
+  }
+  const int words = (ncu + 31) / 32;
+  std::vector<uint32_t> chain(words, 0u), gemm(words, 0u);
+  for (int c = 0; c < ncu; ++c) {
+    std::vector<uint32_t>& m = c >= ncu - res ? chain : gemm;
+    m[c / 32] |= 1u << (c % 32);
+  }
+  e = hipExtStreamCreateWithCUMask(&h->chain_s, (uint32_t)words, chain.data());
+  if (e == hipSuccess) e = hipExtStreamCreateWithCUMask(&h->gemm_s, (uint32_t)words, gemm.data());
+  return e;
+}
+}  // namespace
+
 nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   if (!out) return fail(NQ_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
@@ -334,12 +391,11 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
     return hip_fail(e, "hipMalloc(workspace)");
   }
   layout(h);
-  e = hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->svs, hipStreamNonBlocking);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_svid[0], hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_svid[1], hipEventDisableTiming);
+  e = create_streams(h);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_gram, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_rhs, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t0);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t1);
   if (e == hipSuccess && (h->d.flags & NQ_FLAG_PROFILE)) {
@@ -366,18 +422,18 @@ void nq_lbadmm_destroy(nq_lbadmm_t h) {
   int cur = 0;
   if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
   if (h->last_stream || h->has_run) (void)hipStreamSynchronize(h->last_stream);
-  if (h->aux) (void)hipStreamSynchronize(h->aux);
-  if (h->svs) (void)hipStreamSynchronize(h->svs);
+  if (h->chain_s) (void)hipStreamSynchronize(h->chain_s);
+  if (h->gemm_s) (void)hipStreamSynchronize(h->gemm_s);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_join) (void)hipEventDestroy(h->ev_join);
+  if (h->ev_gram) (void)hipEventDestroy(h->ev_gram);
+  if (h->ev_rhs) (void)hipEventDestroy(h->ev_rhs);
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
   for (hipEvent_t ev : h->prof_ev)
     if (ev) (void)hipEventDestroy(ev);
-  for (hipEvent_t ev : h->ev_svid)
-    if (ev) (void)hipEventDestroy(ev);
-  if (h->aux) (void)hipStreamDestroy(h->aux);
-  if (h->svs) (void)hipStreamDestroy(h->svs);
+  if (h->chain_s) (void)hipStreamDestroy(h->chain_s);
+  if (h->gemm_s) (void)hipStreamDestroy(h->gemm_s);
   if (h->base) (void)hipFree(h->base);
   if (cur != h->device) (void)hipSetDevice(cur);
   delete h;
@@ -427,24 +483,25 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   HIPCHK(launch_svid(h->LamU, h->PU, mp, rp, (int)d.r, d.svid_steps, 0, h->svU, s));
   HIPCHK(launch_svid(h->LamV, h->PV, np_, rp, (int)d.r, d.svid_steps, 0, h->svV, s));
   prof_end(h, pp, s);
-  if (overlap) HIPCHK(hipEventRecord(h->ev_fork, s));
 
   Half hu{h->Wt, mp, np_, h->V, h->U, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc, 0};
   Half hv{h->WtT, np_, mp, h->U, h->V, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc, 1};
-  if (overlap) {
-    // the SVID stream starts after the initial SVIDs on the caller's stream
-    HIPCHK(hipStreamWaitEvent(h->svs, h->ev_fork, 0));
-  }
+  const Half* pending = nullptr;
   for (int it = 0; it < d.iters; ++it) {
-    nq_status st = run_half(h, hu, s, overlap);
+    nq_status st = run_half(h, hu, pending, s, overlap);
     if (st != NQ_OK) return st;
-    st = run_half(h, hv, s, overlap);
+    st = run_half(h, hv, &hu, s, overlap);
     if (st != NQ_OK) return st;
+    pending = &hv;
   }
   if (overlap) {
-    // join: the last SVIDs (and with them every earlier one) before finishing
-    HIPCHK(hipEventRecord(h->ev_svid[0], h->svs));
-    HIPCHK(hipStreamWaitEvent(s, h->ev_svid[0], 0));
+    // join: the SVID launched by the last half on the GEMM stream
+    HIPCHK(hipEventRecord(h->ev_fork, h->gemm_s));
+    HIPCHK(hipStreamWaitEvent(s, h->ev_fork, 0));
+  }
+  if (pending) {
+    nq_status st = run_svid(h, *pending, s);
+    if (st != NQ_OK) return st;
   }
 
   // finish: balance, scales, signs, bits, errors

@@ -1,0 +1,189 @@
+"""GPU parity at the full sizes of the synthetic Llama-2-shaped layers, in the
+launch configuration the benchmark times (overlapped streams, profiling
+events and the error computation on).
+
+- 4096 x 4096, r = 2048 and 11008 x 4096, r = 1536: one iteration against the
+  float64 oracle element by element; the whole run against the oracle's
+  end-of-run figures stored under tests/golden/ (written by
+  tests/golden/make_lbadmm_final.py, which calls only oracle/).
+- 8192 x 28672, r = 6144: the oracle cannot run an iteration in seconds here,
+  so the initial SVID projections are compared in full, the first U-half
+  solve through sampled entries of its normal equations U G = R (G and R
+  built from the inputs by the oracle's routines), and the whole run against
+  the stored end-of-run figures when they exist.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lbadmm as O
+from synth import make_layer
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+ATTN = "llama2-7b-attn-4096x4096-r2048"
+MLP = "llama2-7b-mlp-11008x4096-r1536"
+DOWN70 = "llama2-70b-down-8192x28672-r6144"
+
+
+def T(x, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def H(t):
+    return t.detach().cpu().numpy()
+
+
+def relerr(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def masked_rel(g, o, X):
+    """Relative Frobenius difference over entries with |X| > 1e-3 rms(X)."""
+    rms = np.sqrt(np.mean(X.astype(np.float64) ** 2))
+    mask = np.abs(X) > 1e-3 * rms
+    return relerr(np.where(mask, g, 0), np.where(mask, o, 0))
+
+
+def sign_agreement(g, o):
+    rms = np.sqrt(np.mean(o ** 2))
+    mask = np.abs(o) > 1e-3 * rms
+    return float(np.mean((g[mask] >= 0) == (o[mask] >= 0)))
+
+
+def bench_run(L, iters, dev):
+    """One run with the handle settings the benchmark uses; returns the
+    result and the (unbalanced) ADMM state."""
+    import sub_bit_weight_lb_amd as nq
+    wl = L.workload
+    m, n = L.W.shape
+    h = nq.LBADMM(m, n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
+                  compute_error=True, profile=True)
+    res = h.run(T(L.W, dev), T(L.d_out, dev), T(L.d_in, dev), T(L.EU, dev), T(L.EV, dev))
+    st = {k: H(v) for k, v in h.state().items()}
+    h.close()
+    return res, st
+
+
+def check_final_properties(res, r):
+    """Bits are the signs of the returned latents; balancing held."""
+    U, V = H(res.U), H(res.V)
+    SU = O.unpack_signs(H(res.U_bits).view(np.uint32), r)
+    SV = O.unpack_signs(H(res.V_bits).view(np.uint32), r)
+    np.testing.assert_array_equal(SU, O.sgn(U))
+    np.testing.assert_array_equal(SV, O.sgn(V))
+    np.testing.assert_allclose(np.linalg.norm(U, axis=0), np.linalg.norm(V, axis=0), rtol=1e-4)
+    s = res.stats
+    assert s["potrf_info"] == 0 and s["nonfinite"] == 0
+
+
+def load_golden(name):
+    path = os.path.join(GOLDEN, f"lbadmm_final_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("name", [ATTN, MLP])
+def test_one_iteration_full_size(gpu, name):
+    L = make_layer(name)
+    wl = L.workload
+    print(f"case {name}: one iteration", flush=True)
+    _, st = bench_run(L, 1, gpu)
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    ref = O.init_state(Wt, wl.r, wl.svid_steps, EU=L.EU, EV=L.EV)
+    ref = O.iterate(Wt, ref, wl.rho, wl.svid_steps, 1)
+    eu, ev = relerr(st["U"], ref.U), relerr(st["V"], ref.V)
+    print(f"  U {eu:.2e} V {ev:.2e}", flush=True)
+    assert eu < 1e-4 and ev < 1e-4
+    XU = ref.Lam_U + ref.Z_U
+    XV = ref.Lam_V + ref.Z_V
+    for k, Xk in (("Z_U", XU), ("Lam_U", XU), ("Z_V", XV), ("Lam_V", XV)):
+        e = masked_rel(st[k], getattr(ref, k), Xk)
+        assert e < 1e-4, (k, e)
+    assert sign_agreement(st["U"], ref.U) >= 0.999
+    assert sign_agreement(st["V"], ref.V) >= 0.999
+
+
+@pytest.mark.parametrize("name", [ATTN, MLP])
+def test_full_run_vs_stored_oracle(gpu, name):
+    g = load_golden(name)
+    assert g is not None, f"missing tests/golden/lbadmm_final_{name}.json"
+    L = make_layer(name)
+    wl = L.workload
+    assert (g["m"], g["n"], g["r"], g["iters"], g["seed"]) == (wl.m, wl.n, wl.r, wl.iters, wl.seed)
+    print(f"case {name}: {wl.iters} iterations", flush=True)
+    res, _ = bench_run(L, wl.iters, gpu)
+    s = res.stats
+    print(f"  gpu {s['rel_err_wtilde']:.6f} oracle {g['rel_err_wtilde']:.6f}", flush=True)
+    assert abs(s["rel_err_wtilde"] - g["rel_err_wtilde"]) < 1e-3
+    assert abs(s["rel_err_w"] - g["rel_err_w"]) < 1e-3
+    assert abs(s["sigma0"] - g["sigma0"]) / g["sigma0"] < 1e-6
+    check_final_properties(res, wl.r)
+
+
+@pytest.fixture(scope="module")
+def down70():
+    return make_layer(DOWN70)
+
+
+def test_70b_down_initial_projections(gpu, down70):
+    L = down70
+    wl = L.workload
+    print(f"case {DOWN70}: init", flush=True)
+    _, st = bench_run(L, 0, gpu)
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    s0 = O.init_scale(Wt, wl.r)
+    del Wt
+    for k, E in (("U", L.EU), ("V", L.EV)):
+        X = s0 * E.astype(np.float64)
+        assert relerr(st[k], X) < 1e-6
+        Z, _, _ = O.svid(X, wl.svid_steps)
+        assert relerr(st[f"Z_{k}"], Z) < 1e-4, k
+        del X, Z
+
+
+def test_70b_down_first_solve_sampled(gpu, down70):
+    """Sampled entries of U G = R for the first U-half, with G = V0^T V0 + rho I
+    and R = Wt V0 + rho Z_U0 (Lam = 0 at the start) built from the inputs."""
+    L = down70
+    wl = L.workload
+    print(f"case {DOWN70}: first solve", flush=True)
+    _, st = bench_run(L, 1, gpu)
+    U = st["U"]
+    rng = np.random.default_rng(70)
+    rows = rng.choice(wl.m, 12, replace=False)
+    cols = rng.choice(wl.r, 12, replace=False)
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    s0 = O.init_scale(Wt, wl.r)
+    V0 = s0 * L.EV.astype(np.float64)
+    ZU0, _, _ = O.svid(s0 * L.EU.astype(np.float64), wl.svid_steps)
+    Gcols = V0.T @ V0[:, cols]                      # r x 12
+    Gcols[cols, np.arange(len(cols))] += wl.rho
+    R = Wt[rows] @ V0[:, cols] + wl.rho * ZU0[np.ix_(rows, cols)]
+    lhs = U[rows].astype(np.float64) @ Gcols
+    e = relerr(lhs, R)
+    print(f"  normal-equation residual {e:.2e}", flush=True)
+    assert e < 1e-4
+
+
+def test_70b_down_full_run(gpu, down70):
+    g = load_golden(DOWN70)
+    L = down70
+    wl = L.workload
+    print(f"case {DOWN70}: {wl.iters} iterations", flush=True)
+    res, _ = bench_run(L, wl.iters, gpu)
+    check_final_properties(res, wl.r)
+    if g is None:
+        pytest.skip("stored oracle figures for the 8192 x 28672 layer not written yet "
+                    "(tests/golden/make_lbadmm_final.py)")
+    s = res.stats
+    print(f"  gpu {s['rel_err_wtilde']:.6f} oracle {g['rel_err_wtilde']:.6f}", flush=True)
+    assert abs(s["rel_err_wtilde"] - g["rel_err_wtilde"]) < 1e-3
