@@ -11,9 +11,9 @@
 //              inverse partial sums S_ij += L_ik M_kj (i > k >= j); its first
 //              workgroup instead updates the next diagonal tile and factors
 //              it, so no launch is spent on the diagonal alone.
-// Diagonal tiles: one wave factors the tile in registers (one row per lane,
-// column broadcasts through LDS, no barrier per column) while a second wave
-// forms L^-1 from the same broadcasts. Off-diagonal tiles: 64 x 64 x 64
+// Diagonal tiles: one wave, 2 x 2 blocks of 32: two in-register
+// factorisations with their inverses (readlane broadcasts) and four block
+// products on the MFMA. Off-diagonal tiles: 64 x 64 x 64
 // products on the 32x32x2 fp32 MFMA.
 // The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
 // M_ij = -M_ii sum_{l = j..i-1} L_il M_lj; the partial sums S_ij are kept in
@@ -104,152 +104,230 @@ __device__ void block_mm(const float* __restrict__ X, const float* __restrict__ 
   __syncthreads();  // Xs / Ys may be refilled by the caller's next product
 }
 
-// LDS of the diagonal-tile factorisation (aliases the product buffers of
-// the update kernel, which are idle by then).
-struct DiagSmem {
-  float col[NB][NB];  // col[j][i]: Schur column j at row i (i >= j), published by wave 0
-  float dpiv[NB];     // pivots d_j
-  float rs[NB];       // 1 / sqrt(d_j)
-  int ready;          // columns 0 .. ready - 1 of col are published
-};
-
-// Upper bound on the sleep iterations of the consumer wave (each s_sleep 1
-// is about 64 clocks, so about 0.1 s): the producer publishes all 64
-// columns within microseconds; the bound only guarantees the wait ends.
-constexpr int kSpinLimit = 1 << 22;
-
 __device__ __forceinline__ float bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
-// Wait until at least n columns are published; false if the bound ran out.
-__device__ __forceinline__ bool wait_ready(const DiagSmem& sm, int n) {
-  int spins = 0;
-  while (__hip_atomic_load(&sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < n) {
-    __builtin_amdgcn_s_sleep(1);
-    if (++spins > kSpinLimit) return false;
+// ---- 32 x 32 factorisation with its inverse on one wave ("half-wave" form)
+// Lanes 0-31 hold rows of the Schur complement t, lanes 32-63 columns of
+// E = Lt^-1 (Lt unit lower triangular, A = Lt D Lt^T). Step j broadcasts
+// p_c = t[j] of lane c (readlane) and every lane applies the same
+//   r[c] -= x p_c,  c > j,  x = r[j] / d_j,
+// which is the elimination t[c] -= (t[j] / d_j) p_c on rows and the same
+// row operation e[c] -= p_c (e[j] / d_j) on the identity. Lanes i <= j only
+// touch entries right of their diagonal, which are never read. After step j
+// r[j] is scaled by d_j^-1/2: lanes 0-31 then hold row i of L (c <= i),
+// lanes 32-63 column i of L^-1 = D^-1/2 Lt^-1 (exact zeros above the
+// diagonal).
+// Broadcasts go in groups of 8 pinned into SGPRs by an empty asm (no
+// instruction) before their FMAs, so they issue back to back instead of
+// alternating with their consumers through one SGPR.
+template <int J, int C>
+__device__ __forceinline__ void hw_cols(float (&r)[32], float src, float x) {
+  if constexpr (C < 32) {
+    constexpr int n = (32 - C) < 8 ? (32 - C) : 8;
+    float p[8];
+#pragma unroll
+    for (int q = 0; q < n; ++q) p[q] = bcast(src, C + q);
+    if constexpr (n == 8)
+      asm volatile("" : "+s"(p[0]), "+s"(p[1]), "+s"(p[2]), "+s"(p[3]), "+s"(p[4]), "+s"(p[5]),
+                   "+s"(p[6]), "+s"(p[7]));
+#pragma unroll
+    for (int q = 0; q < n; ++q) r[C + q] = fmaf(-x, p[q], r[C + q]);
+    hw_cols<J, C + n>(r, src, x);
   }
-  return true;
+}
+template <int J>
+__device__ __forceinline__ void hw_steps(float (&r)[32]) {
+  if constexpr (J < 32) {
+    const float src = r[J];
+    const float d = bcast(src, J);
+    const float x = src * __builtin_amdgcn_rcpf(d);
+    hw_cols<J, J + 1>(r, src, x);
+    r[J] = src * __builtin_amdgcn_rsqf(d);
+    hw_steps<J + 1>(r);
+  }
+}
+
+// LDS of the diagonal-tile factorisation: 32 x 32 blocks that change lane
+// layout between phases (aliases the product buffers of the update kernel).
+struct DiagSmem {
+  float Mc[32][33];  // Mc[c][i] = M11[i][c]
+  float Nc[32][33];  // Nc[c][i] = M22[i][c]
+  float Ls[32][33];  // L21
+  float Ts[32][33];  // A22 - L21 L21^T
+  float Ps[32][33];  // P = L21 M11
+};
+
+// Hand-off of LDS data between lanes of one wave: without a fence the
+// compiler, which proves independence per lane, may move one lane's read of a
+// value above another lane's write of it.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// 32 x 32 x 32 product on the 32x32x2 fp32 MFMA with k = 2 s + (lane / 32)
+// at step s; fa(s), fb(s) return this lane's A[lane % 32][k] and
+// B[k][lane % 32]. acc[v] is C[8 (v / 4) + 4 (lane / 32) + v % 4][lane % 32].
+template <class FA, class FB>
+__device__ __forceinline__ f32x16 mm32(FA fa, FB fb, f32x16 acc) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa(s), fb(s), acc, 0, 0, 0);
+  return acc;
 }
 
 // Diagonal tile k: A_kk = L L^T and M_kk = L^-1, written to A and M (zeros
-// above the diagonal). Right-looking elimination A = Lt D Lt^T (Lt unit lower
-// triangular, D the pivots), L = Lt D^1/2, L^-1 = D^-1/2 Lt^-1.
-//  - Wave 0 holds the Schur complement in registers, lane i holding row i.
-//    Step j broadcasts column j through LDS (uniform-address reads) and
-//    updates t[c] -= (t[j] / d_j) col_j[c] for c > j. Software pipelined:
-//    column j + 1 is final once its entry of step j is updated, so it is
-//    published, and its reads are in flight, while the rest of step j
-//    issues; the pivot comes by readlane.
-//  - Wave 1 applies the same row operations to the identity in column form
-//    (lane c holds column c of Lt^-1): e[i] -= col_j[i] (e[j] / d_j), i > j,
-//    reading the published columns, which it waits for in groups of 8
-//    through an LDS counter (bounded wait).
+// above the diagonal), on wave 0, in 2 x 2 blocks of 32:
+//   L11, M11 from A11 (half-wave factorisation);
+//   L21 = A21 M11^T;  T = A22 - L21 L21^T;
+//   L22, M22 from T (half-wave factorisation);
+//   M21 = -M22 (L21 M11).
+// The four products run on the MFMA; LDS only changes lane layouts between
+// them (one wave, so LDS order is program order and no barrier is needed).
 // Pivots <= 0 or non-finite set potrf_info (first such row, 1-based).
 __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, int r_real,
                                             DevStats* st, DiagSmem& sm) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
   const int64_t base = (int64_t)k * NB;
-  if (tid == 0) sm.ready = 0;
-  __syncthreads();
-  bool waited = true;
-  if (wave == 0) {
-    float t[NB];
+  float* A0 = A + base * rp + base;  // tile origin
+  float* M0 = M + base * rp + base;
+  float r[32];
+  float dg = 0.0f;  // this lane's diagonal of L (lanes 0-31), block 11 then 22
+  uint64_t badmask = 0;
+
+  // A21 in the A-operand layout of the first product and A22 in the
+  // accumulator layout of the second, loaded now so that their latency
+  // hides behind the first factorisation
+  float a21[16], a22[16];
 #pragma unroll
-    for (int c4 = 0; c4 < NB / 4; ++c4) {
-      const f32x4 v = *(const f32x4*)&A[(base + lane) * rp + base + 4 * c4];
-      t[4 * c4 + 0] = v[0];
-      t[4 * c4 + 1] = v[1];
-      t[4 * c4 + 2] = v[2];
-      t[4 * c4 + 3] = v[3];
+  for (int s = 0; s < 16; ++s) a21[s] = A0[(int64_t)(32 + i) * rp + 2 * s + h];
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    a22[v] = A0[(int64_t)(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * rp + 32 + i];
+
+  // ---- L11, M11
+  if (h == 0) {
+#pragma unroll
+    for (int c4 = 0; c4 < 8; ++c4) {
+      const f32x4 v = *(const f32x4*)&A0[(int64_t)i * rp + 4 * c4];
+      r[4 * c4] = v[0]; r[4 * c4 + 1] = v[1]; r[4 * c4 + 2] = v[2]; r[4 * c4 + 3] = v[3];
     }
-    float cv[2][NB];
-    sm.col[0][lane] = t[0];
-    __hip_atomic_store(&sm.ready, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
 #pragma unroll
-    for (int c = 1; c < NB; ++c) cv[0][c] = sm.col[0][c];
+    for (int c = 0; c < 32; ++c) r[c] = c == i ? 1.0f : 0.0f;
+  }
+  hw_steps<0>(r);
+  if (h == 0) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int b = j & 1;
-      const float d = bcast(t[j], j);
-      sm.dpiv[j] = d;
-      const float l = lane > j ? t[j] * __builtin_amdgcn_rcpf(d) : 0.0f;
-      if (j + 1 < NB) {
-        t[j + 1] = fmaf(-l, cv[b][j + 1], t[j + 1]);
-        sm.col[j + 1][lane] = t[j + 1];
-        __hip_atomic_store(&sm.ready, j + 2, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-#pragma unroll
-        for (int c = j + 2; c < NB; ++c) cv[b ^ 1][c] = sm.col[j + 1][c];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int c = j + 2; c < NB; ++c) t[c] = fmaf(-l, cv[b][c], t[c]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // t[c] (c < lane) = Lt_ic d_c, t[lane] = d_lane; L_ic = t[c] / sqrt(d_c)
-    const float di = sm.dpiv[lane];
-    sm.rs[lane] = 1.0f / sqrtf(di);
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int c4 = 0; c4 < NB / 4; ++c4) {
+    for (int c4 = 0; c4 < 8; ++c4) {
       f32x4 v;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int c = 4 * c4 + q;
-        v[q] = c < lane ? t[c] * sm.rs[c] : (c == lane ? sqrtf(di) : 0.0f);
+        v[q] = c <= i ? r[c] : 0.0f;
+        dg = c == i ? r[c] : dg;
       }
-      *(f32x4*)&A[(base + lane) * rp + base + 4 * c4] = v;
+      *(f32x4*)&A0[(int64_t)i * rp + 4 * c4] = v;
+      *(f32x4*)&A0[(int64_t)i * rp + 32 + 4 * c4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-  } else if (wave == 1) {
-    float e[NB];
+  } else {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) e[i] = i == lane ? 1.0f : 0.0f;
-    float cw[2][NB];
-    float* mrow = M + base * rp + base + lane;  // row j of the tile at step j
-    waited = wait_ready(sm, 9);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) cw[0][i] = sm.col[0][i];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int b = j & 1;
-      if (j + 1 < NB) {
-        if ((j + 1) % 8 == 0) waited = waited && wait_ready(sm, j + 9 < NB ? j + 9 : NB);
-        // The read address carries an opaque zero that depends on e[j], so
-        // the compiler cannot hoist a later step's reads into this one (all
-        // reads between two waits would otherwise be issued at once and
-        // overflow the register file). The shift keeps 256-byte alignment
-        // visible, so the reads still merge into 16-byte loads.
-        int z;
-        asm volatile("s_mov_b32 %0, 0" : "=s"(z) : "v"(e[j]));
-        const float* cj = &sm.col[j + 1][0] + (z << 6);
-#pragma unroll
-        for (int i = j + 1; i < NB; ++i) cw[b ^ 1][i] = cj[i];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // row j of Lt^-1 is final: M_jc = e[j] / sqrt(d_j), a contiguous row store
-      const float d = cw[b][j];
-      *mrow = e[j] * __builtin_amdgcn_rsqf(d);
-      mrow += rp;
-      const float f = e[j] * __builtin_amdgcn_rcpf(d);
-#pragma unroll
-      for (int i = j + 1; i < NB; ++i) e[i] = fmaf(-cw[b][i], f, e[i]);
-      // pin this step's updates here (no instruction): otherwise the
-      // instruction selector sinks each update towards its last use and keeps
-      // every broadcast value of the group of steps live
-#pragma unroll
-      for (int i = j + 1; i < NB; ++i) asm volatile("" : "+v"(e[i]));
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 32; ++q) {
+      M0[(int64_t)q * rp + i] = r[q];
+      M0[(int64_t)q * rp + 32 + i] = 0.0f;
+      sm.Mc[i][q] = r[q];
     }
   }
-  __syncthreads();
-  if (wave == 1) {
-    if (!waited && lane == 0) atomicMin(&st->potrf_info, (int)base + 1);
-  } else if (wave == 0) {
-    const float d = sm.dpiv[lane];
-    const bool bad = !(d > 0.0f && isfinite(d)) && (int)base + lane < r_real;
-    const uint64_t m = __ballot(bad);
-    if (m && lane == 0) atomicMin(&st->potrf_info, (int)base + __ffsll((unsigned long long)m));
+  {
+    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && (int)base + i < r_real;
+    badmask |= (uint64_t)(uint32_t)__ballot(bad);
   }
+
+  wave_lds_sync();  // Mc
+
+  // ---- L21 = A21 M11^T
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  acc = mm32([&](int s) { return a21[s]; },
+             [&](int s) { return sm.Mc[2 * s + h][i]; }, acc);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int iv = 8 * (v >> 2) + 4 * h + (v & 3);
+    A0[(int64_t)(32 + iv) * rp + i] = acc[v];
+    sm.Ls[iv][i] = acc[v];
+  }
+
+  wave_lds_sync();  // Ls
+
+  // ---- T = A22 - L21 L21^T
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = a22[v];
+  acc = mm32([&](int s) { return -sm.Ls[i][2 * s + h]; },
+             [&](int s) { return sm.Ls[i][2 * s + h]; }, acc);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sm.Ts[8 * (v >> 2) + 4 * h + (v & 3)][i] = acc[v];
+
+  // ---- P = L21 M11 (needs neither T nor the second factorisation)
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  acc = mm32([&](int s) { return sm.Ls[i][2 * s + h]; },
+             [&](int s) { return sm.Mc[i][2 * s + h]; }, acc);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sm.Ps[8 * (v >> 2) + 4 * h + (v & 3)][i] = acc[v];
+
+  wave_lds_sync();  // Ts, Ps
+
+  // ---- L22, M22
+  if (h == 0) {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) r[c] = sm.Ts[i][c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < 32; ++c) r[c] = c == i ? 1.0f : 0.0f;
+  }
+  hw_steps<0>(r);
+  dg = 0.0f;
+  if (h == 0) {
+#pragma unroll
+    for (int c4 = 0; c4 < 8; ++c4) {
+      f32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * c4 + q;
+        v[q] = c <= i ? r[c] : 0.0f;
+        dg = c == i ? r[c] : dg;
+      }
+      *(f32x4*)&A0[(int64_t)(32 + i) * rp + 32 + 4 * c4] = v;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      M0[(int64_t)(32 + q) * rp + 32 + i] = r[q];
+      sm.Nc[i][q] = r[q];
+    }
+  }
+  {
+    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && (int)base + 32 + i < r_real;
+    badmask |= (uint64_t)(uint32_t)__ballot(bad) << 32;
+  }
+
+  wave_lds_sync();  // Nc
+
+  // ---- M21 = -M22 P
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  acc = mm32([&](int s) { return -sm.Nc[2 * s + h][i]; },
+             [&](int s) { return sm.Ps[2 * s + h][i]; }, acc);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int iv = 8 * (v >> 2) + 4 * h + (v & 3);
+    M0[(int64_t)(32 + iv) * rp + i] = acc[v];
+  }
+  if (badmask && lane == 0)
+    atomicMin(&st->potrf_info, (int)base + __ffsll((unsigned long long)badmask));
 }
 
 __global__ __launch_bounds__(NT) void chol_diag0_kernel(float* A, float* M, int rp, int r_real,
