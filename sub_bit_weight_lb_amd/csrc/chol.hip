@@ -1,108 +1,42 @@
-// Blocked Cholesky factorisation with the inverse factor: G = L L^T and
-// M = L^-1, for the ridge-regularised system matrix G = V^T V + rho I of the
-// regularised solve (NanoQuant digest, section 核心方法, step (a): the linear
-// system is solved through a Cholesky factorisation; the implementation blog,
-// section 待办事项, names this factorisation as where LB-ADMM spends its time).
+// Blocked Cholesky factorisation with the inverse factor and G^-1: G = L L^T,
+// M = L^-1 and G^-1 = M^T M, for the ridge-regularised system matrix
+// G = V^T V + rho I of the regularised solve (NanoQuant digest, section
+// 核心方法, step (a): the linear system is solved through a Cholesky
+// factorisation; the implementation blog, section 待办事项, names this
+// factorisation as where LB-ADMM spends its time).
 //
-// Right-looking, block size 64, two launches per block column k:
-//   panel(k):  L_ik = A_ik M_kk^T for i > k (in place), and row k of the
-//              inverse factor, M_kj = -M_kk S_kj for j < k;
-//   update(k): trailing update A_ij -= L_ik L_jk^T (i >= j > k) and the
-//              inverse partial sums S_ij += L_ik M_kj (i > k >= j); its first
-//              workgroup instead updates the next diagonal tile and factors
-//              it, so no launch is spent on the diagonal alone.
+// Right-looking, block size 64 (R = rp / 64 block columns), one launch per
+// block column k plus one (k = 0 .. R). Launch k holds
+//   - the panel of step k: L_ik = (A_ik - L_{i,k-1} L_{k,k-1}^T) M_kk^T,
+//     i > k, each tile applying the last update of step k - 1 itself;
+//   - row k of the inverse: M_kj = -M_kk (S_kj + L_{k,k-1} M_{k-1,j}), j < k;
+//   - M_kk itself;
+//   - the rest of step k - 1: trailing update A_ij -= L_{i,k-1} L_{j,k-1}^T
+//     (i >= j > k), inverse partial sums S_ij += L_{i,k-1} M_{k-1,j}
+//     (i > k, j < k), and the G^-1 contribution of row k - 1 of M,
+//     G^-1_ij += M_{k-1,i}^T M_{k-1,j} (j <= i < k);
+//   - optionally L_{k-1,k-1} (only when L itself is wanted).
+// Every workgroup that needs M_kk (panel and inverse-row tiles) factors the
+// diagonal tile A_kk - L_{k,k-1} L_{k,k-1}^T itself: some 32 CUs each do
+// the same 64 x 64 factorisation, and no launch is spent on the diagonal
+// alone. The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
+// M_ij = -M_ii sum_{l = j..i-1} L_il M_lj; the partial sums S_ij are kept in
+// M's own tiles until row i of M is formed. No workgroup reads a tile that
+// another workgroup of the same launch writes; every dependency crosses a
+// launch boundary.
 // Diagonal tiles: one wave, 2 x 2 blocks of 32: two in-register
 // factorisations with their inverses (readlane broadcasts) and four block
-// products on the MFMA. Off-diagonal tiles: 64 x 64 x 64
-// products on the 32x32x2 fp32 MFMA.
-// The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
-// M_ij = -M_ii sum_{l = j..i-1} L_il M_lj; the partial sums S_ij are kept in
-// M's own tiles until row i of M is formed.
-// Workgroups of one launch never wait for each other: every dependency
-// crosses a launch boundary.
+// products on the MFMA. Off-diagonal tiles: 64 x 64 x 64 products on the
+// 32x32x2 fp32 MFMA.
 #include "common.h"
 #include <climits>
 
 namespace nq {
 namespace {
 
-constexpr int NB = kNB;   // 64
+constexpr int NB = kNB;     // 64
 constexpr int NT = 256;
-constexpr int LS = NB + 4;  // LDS row stride for MFMA tiles
-
-// Epilogues of the 64 x 64 block product P = op(X) op(Y).
-enum BlockEpi {
-  kBlkAxpby,  // out = alpha P + beta out
-  kBlkSymAcc  // symmetric accumulate into G^-1 (see block_mm)
-};
-
-// 64 x 64 x 64 block product on the 32x32x2 fp32 MFMA (ld = rp for all).
-// op(X) = X^T if TA else X; op(Y) = Y^T if TB else Y.
-// kBlkAxpby:  out = alpha P + beta out.
-// kBlkSymAcc: out is tile (i, j), i >= j, of a symmetric matrix and out2 its
-//   mirror tile (j, i) (out2 == out on the diagonal, where only P's lower
-//   triangle is used). v = P + (beta != 0 ? out : 0) is written to out and,
-//   transposed, to out2, so both halves hold the same sums and the result
-//   is exactly symmetric.
-template <bool TA, bool TB, BlockEpi EPI = kBlkAxpby>
-__device__ void block_mm(const float* __restrict__ X, const float* __restrict__ Y, float* out,
-                         int rp, float alpha, float beta, float* Xs, float* Ys,
-                         float* out2 = nullptr) {
-  const int tid = threadIdx.x;
-  // Both operands are staged [m or n][k] with k contiguous.
-  auto stage_rows = [&](const float* S, float* D) {  // operand(i, c) = S[i][c]
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + NT * q;
-      const int row = idx >> 4, c4 = idx & 15;
-      *(f32x4*)&D[row * LS + c4 * 4] = *(const f32x4*)&S[(int64_t)row * rp + c4 * 4];
-    }
-  };
-  auto stage_cols = [&](const float* S, float* D) {  // operand(i, c) = S[c][i]
-    const int col = tid & 63, cq = tid >> 6;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c0 = (cq + 4 * j) * 4;
-      f32x4 v = {S[(int64_t)(c0 + 0) * rp + col], S[(int64_t)(c0 + 1) * rp + col],
-                 S[(int64_t)(c0 + 2) * rp + col], S[(int64_t)(c0 + 3) * rp + col]};
-      *(f32x4*)&D[col * LS + c0] = v;
-    }
-  };
-  if (TA) stage_cols(X, Xs); else stage_rows(X, Xs);
-  if (TB) stage_rows(Y, Ys); else stage_cols(Y, Ys);
-  __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int half = lane >> 5, l32 = lane & 31;
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  const float* xs = Xs + (wm * 32 + l32) * LS + 4 * half;
-  const float* ys = Ys + (wn * 32 + l32) * LS + 4 * half;
-#pragma unroll
-  for (int kc = 0; kc < NB; kc += 8) {
-    const f32x4 a = *(const f32x4*)&xs[kc];
-    const f32x4 b = *(const f32x4*)&ys[kc];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
-  }
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = wm * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-    const int col = wn * 32 + l32;
-    float* o = out + (int64_t)row * rp + col;
-    if (EPI == kBlkAxpby) {
-      const float prev = beta != 0.0f ? *o : 0.0f;
-      *o = alpha * acc[v] + beta * prev;
-    } else {
-      if (out2 == out && col > row) continue;  // diagonal tile: lower triangle only
-      const float val = acc[v] + (beta != 0.0f ? *o : 0.0f);
-      *o = val;
-      out2[(int64_t)col * rp + row] = val;
-    }
-  }
-  __syncthreads();  // Xs / Ys may be refilled by the caller's next product
-}
+constexpr int TS = NB + 4;  // LDS row stride of a 64 x 64 tile
 
 __device__ __forceinline__ float bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -150,13 +84,19 @@ __device__ __forceinline__ void hw_steps(float (&r)[32]) {
 }
 
 // LDS of the diagonal-tile factorisation: 32 x 32 blocks that change lane
-// layout between phases (aliases the product buffers of the update kernel).
+// layout between phases.
 struct DiagSmem {
   float Mc[32][33];  // Mc[c][i] = M11[i][c]
   float Nc[32][33];  // Nc[c][i] = M22[i][c]
   float Ls[32][33];  // L21
   float Ts[32][33];  // A22 - L21 L21^T
   float Ps[32][33];  // P = L21 M11
+};
+
+// LDS of one workgroup of the step kernel.
+struct StepSmem {
+  DiagSmem dg;
+  float T[NB * TS];  // input tile of the diagonal factorisation, then M_kk
 };
 
 // Hand-off of LDS data between lanes of one wave: without a fence the
@@ -177,22 +117,104 @@ __device__ __forceinline__ f32x16 mm32(FA fa, FB fb, f32x16 acc) {
   return acc;
 }
 
-// Diagonal tile k: A_kk = L L^T and M_kk = L^-1, written to A and M (zeros
-// above the diagonal), on wave 0, in 2 x 2 blocks of 32:
-//   L11, M11 from A11 (half-wave factorisation);
-//   L21 = A21 M11^T;  T = A22 - L21 L21^T;
-//   L22, M22 from T (half-wave factorisation);
+// ---- 64 x 64 x 64 block products, one 32 x 32 quadrant (qm, qn) per wave
+// Operands are row-major tiles with leading dimension ld, in global memory
+// or LDS: A(m, k) = X[m][k] (or X[k][m] if TA), B(k, n) = Y[k][n] (or
+// Y[n][k] if TB). Each wave loads its MFMA fragments straight from the
+// operands, all of them before the first MFMA (one load latency, no LDS
+// staging, no barrier): in each group of 8 k the lane half h feeds
+// k = 4 h + s to MFMA step s, so a row-major operand fragment is one 16-byte
+// load. acc[v] is C[qm 32 + 8 (v / 4) + 4 h + v % 4][qn 32 + lane % 32].
+template <bool TA, bool TB>
+__device__ __forceinline__ f32x16 mm_quad(const float* X, int ldx, const float* Y, int ldy, int qm,
+                                          int qn) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  const int m = qm * 32 + l32, n = qn * 32 + l32;
+  f32x4 a[8], b[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int k0 = 8 * g + 4 * h;
+    if (TA) {
+      a[g] = f32x4{X[(int64_t)k0 * ldx + m], X[(int64_t)(k0 + 1) * ldx + m],
+                   X[(int64_t)(k0 + 2) * ldx + m], X[(int64_t)(k0 + 3) * ldx + m]};
+    } else {
+      a[g] = *(const f32x4*)&X[(int64_t)m * ldx + k0];
+    }
+    if (TB) {
+      b[g] = *(const f32x4*)&Y[(int64_t)n * ldy + k0];
+    } else {
+      b[g] = f32x4{Y[(int64_t)k0 * ldy + n], Y[(int64_t)(k0 + 1) * ldy + n],
+                   Y[(int64_t)(k0 + 2) * ldy + n], Y[(int64_t)(k0 + 3) * ldy + n]};
+    }
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[g][q], b[g][q], acc, 0, 0, 0);
+  return acc;
+}
+
+// Quadrant of wave w in a 4-wave product.
+__device__ __forceinline__ int wave_qm() { return (threadIdx.x >> 6) & 1; }
+__device__ __forceinline__ int wave_qn() { return threadIdx.x >> 7; }
+__device__ __forceinline__ int qrow(int qm, int v) {
+  return qm * 32 + 8 * (v >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (v & 3);
+}
+__device__ __forceinline__ int qcol(int qn) { return qn * 32 + (threadIdx.x & 31); }
+
+// out = alpha * acc + beta * out on quadrant (qm, qn) (global, ld rp).
+__device__ __forceinline__ void store_axpby(const f32x16& acc, float* out, int rp, float alpha,
+                                            float beta, int qm, int qn) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float* o = out + (int64_t)qrow(qm, v) * rp + qcol(qn);
+    const float prev = beta != 0.0f ? *o : 0.0f;
+    *o = alpha * acc[v] + beta * prev;
+  }
+}
+
+// Symmetric accumulate into G^-1: out is tile (i, j), i >= j, and out2 its
+// mirror (j, i) (out2 == out on the diagonal, where only the lower triangle
+// of the product is used). v = acc + (first ? 0 : out) goes to out and,
+// transposed, to out2, so both halves hold the same sums and G^-1 is
+// exactly symmetric.
+__device__ __forceinline__ void store_symacc(const f32x16& acc, float* out, float* out2, int rp,
+                                             bool first) {
+  const int qm = wave_qm(), qn = wave_qn();
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = qrow(qm, v), col = qcol(qn);
+    if (out2 == out && col > row) continue;
+    float* o = out + (int64_t)row * rp + col;
+    const float val = acc[v] + (first ? 0.0f : *o);
+    *o = val;
+    out2[(int64_t)col * rp + row] = val;
+  }
+}
+
+// Diagonal tile: Tin (LDS, stride TS) holds the 64 x 64 SPD tile; its factor
+// L and M = L^-1 are formed on wave 0 in 2 x 2 blocks of 32:
+//   L11, M11 from T11 (half-wave factorisation);
+//   L21 = T21 M11^T;  T22' = T22 - L21 L21^T;
+//   L22, M22 from T22' (half-wave factorisation);
 //   M21 = -M22 (L21 M11).
 // The four products run on the MFMA; LDS only changes lane layouts between
-// them (one wave, so LDS order is program order and no barrier is needed).
-// Pivots <= 0 or non-finite set potrf_info (first such row, 1-based).
-__device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, int r_real,
-                                            DevStats* st, DiagSmem& sm) {
+// them (one wave, so no barrier, but a wavefront fence at each hand-off).
+// M (zeros above the diagonal) goes to M0 with leading dimension rp, or
+// with M_LDS to Tin itself (stride TS; every part of the input is read
+// before the part of M that replaces it is written), or nowhere if M0 is
+// null. With WRITE_L, L (zeros above the diagonal) goes to L0 (ld rp).
+// With st, a pivot <= 0 or non-finite sets potrf_info (first such row
+// row0 + i, 1-based; rows at or past r_real are padding and not checked).
+template <bool M_LDS, bool WRITE_L>
+__device__ __forceinline__ void diag_factor(const float* Tin, float* M0, float* L0, int rp,
+                                            int row0, int r_real, DevStats* st, DiagSmem& sm) {
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
-  const int64_t base = (int64_t)k * NB;
-  float* A0 = A + base * rp + base;  // tile origin
-  float* M0 = M + base * rp + base;
+  const int ldm = M_LDS ? TS : rp;  // M0 is Tin itself when M_LDS
   float r[32];
   float dg = 0.0f;  // this lane's diagonal of L (lanes 0-31), block 11 then 22
   uint64_t badmask = 0;
@@ -202,22 +224,22 @@ __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, i
   // hides behind the first factorisation
   float a21[16], a22[16];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) a21[s] = A0[(int64_t)(32 + i) * rp + 2 * s + h];
+  for (int s = 0; s < 16; ++s) a21[s] = Tin[(32 + i) * TS + 2 * s + h];
 #pragma unroll
-  for (int v = 0; v < 16; ++v)
-    a22[v] = A0[(int64_t)(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * rp + 32 + i];
+  for (int v = 0; v < 16; ++v) a22[v] = Tin[(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * TS + 32 + i];
 
   // ---- L11, M11
   if (h == 0) {
 #pragma unroll
     for (int c4 = 0; c4 < 8; ++c4) {
-      const f32x4 v = *(const f32x4*)&A0[(int64_t)i * rp + 4 * c4];
+      const f32x4 v = *(const f32x4*)&Tin[i * TS + 4 * c4];
       r[4 * c4] = v[0]; r[4 * c4 + 1] = v[1]; r[4 * c4 + 2] = v[2]; r[4 * c4 + 3] = v[3];
     }
   } else {
 #pragma unroll
     for (int c = 0; c < 32; ++c) r[c] = c == i ? 1.0f : 0.0f;
   }
+  wave_lds_sync();  // every lane has read its part of the input tile
   hw_steps<0>(r);
   if (h == 0) {
 #pragma unroll
@@ -229,19 +251,23 @@ __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, i
         v[q] = c <= i ? r[c] : 0.0f;
         dg = c == i ? r[c] : dg;
       }
-      *(f32x4*)&A0[(int64_t)i * rp + 4 * c4] = v;
-      *(f32x4*)&A0[(int64_t)i * rp + 32 + 4 * c4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (WRITE_L) {
+        *(f32x4*)&L0[(int64_t)i * rp + 4 * c4] = v;
+        *(f32x4*)&L0[(int64_t)i * rp + 32 + 4 * c4] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
     }
   } else {
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-      M0[(int64_t)q * rp + i] = r[q];
-      M0[(int64_t)q * rp + 32 + i] = 0.0f;
+      if (M0) {
+        M0[q * ldm + i] = r[q];
+        M0[q * ldm + 32 + i] = 0.0f;
+      }
       sm.Mc[i][q] = r[q];
     }
   }
   {
-    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && (int)base + i < r_real;
+    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && row0 + i < r_real;
     badmask |= (uint64_t)(uint32_t)__ballot(bad);
   }
 
@@ -256,7 +282,7 @@ __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, i
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int iv = 8 * (v >> 2) + 4 * h + (v & 3);
-    A0[(int64_t)(32 + iv) * rp + i] = acc[v];
+    if (WRITE_L) L0[(int64_t)(32 + iv) * rp + i] = acc[v];
     sm.Ls[iv][i] = acc[v];
   }
 
@@ -300,17 +326,17 @@ __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, i
         v[q] = c <= i ? r[c] : 0.0f;
         dg = c == i ? r[c] : dg;
       }
-      *(f32x4*)&A0[(int64_t)(32 + i) * rp + 32 + 4 * c4] = v;
+      if (WRITE_L) *(f32x4*)&L0[(int64_t)(32 + i) * rp + 32 + 4 * c4] = v;
     }
   } else {
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-      M0[(int64_t)(32 + q) * rp + 32 + i] = r[q];
+      if (M0) M0[(32 + q) * ldm + 32 + i] = r[q];
       sm.Nc[i][q] = r[q];
     }
   }
   {
-    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && (int)base + 32 + i < r_real;
+    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && row0 + 32 + i < r_real;
     badmask |= (uint64_t)(uint32_t)__ballot(bad) << 32;
   }
 
@@ -321,39 +347,12 @@ __device__ __forceinline__ void diag_factor(float* A, float* M, int rp, int k, i
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
   acc = mm32([&](int s) { return -sm.Nc[2 * s + h][i]; },
              [&](int s) { return sm.Ps[2 * s + h][i]; }, acc);
+  if (M0) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int iv = 8 * (v >> 2) + 4 * h + (v & 3);
-    M0[(int64_t)(32 + iv) * rp + i] = acc[v];
+    for (int v = 0; v < 16; ++v) M0[(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * ldm + i] = acc[v];
   }
-  if (badmask && lane == 0)
-    atomicMin(&st->potrf_info, (int)base + __ffsll((unsigned long long)badmask));
-}
-
-__global__ __launch_bounds__(NT) void chol_diag0_kernel(float* A, float* M, int rp, int r_real,
-                                                        DevStats* st) {
-  __builtin_amdgcn_s_setprio(3);
-  __shared__ __attribute__((aligned(16))) DiagSmem dsm;
-  diag_factor(A, M, rp, 0, r_real, st, dsm);
-}
-
-__global__ __launch_bounds__(NT) void chol_panel_kernel(float* A, float* M, int rp, int k) {
-  __builtin_amdgcn_s_setprio(3);
-  __shared__ __attribute__((aligned(16))) float Xs[NB * LS];
-  __shared__ __attribute__((aligned(16))) float Ys[NB * LS];
-  const int R = rp / NB;
-  const int nL = R - k - 1;
-  const int b = blockIdx.x;
-  const int64_t kk = (int64_t)k * NB;
-  if (b < nL) {
-    const int64_t i0 = (int64_t)(k + 1 + b) * NB;
-    float* Aik = A + i0 * rp + kk;
-    block_mm<false, true>(Aik, M + kk * rp + kk, Aik, rp, 1.0f, 0.0f, Xs, Ys);
-  } else {
-    const int64_t j0 = (int64_t)(b - nL) * NB;
-    float* Mkj = M + kk * rp + j0;
-    block_mm<false, false>(M + kk * rp + kk, Mkj, Mkj, rp, -1.0f, 0.0f, Xs, Ys);
-  }
+  if (st && badmask && lane == 0)
+    atomicMin(&st->potrf_info, row0 + __ffsll((unsigned long long)badmask));
 }
 
 // Lower-triangle tile index t -> (i, j), i >= j.
@@ -365,64 +364,136 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
   j = t - ii * (ii + 1) / 2;
 }
 
-// Workgroups of update(k), in this order:
-//   1 (if k + 1 < R): A_{k+1,k+1} -= L_{k+1,k} L_{k+1,k}^T, then factor it;
-//   the other lower tiles of the trailing block: A_ij -= L_ik L_jk^T;
-//   inverse partial sums: S_ij += L_ik M_kj (i > k >= j), kept in M;
-//   if Ginv: Ginv_ij += M_ki^T M_kj for j <= i <= k (row k of M is final
-//     once panel(k) has run; tile (i, j) starts at k = i), plus mirror.
-// With k = R - 1 only the Ginv group is left (after the last panel).
-__global__ __launch_bounds__(NT) void chol_update_kernel(float* A, float* M, float* Ginv, int rp,
-                                                         int k, int r_real, DevStats* st) {
-  __builtin_amdgcn_s_setprio(3);
-  // product buffers and the diagonal-tile scratch share one LDS block
-  constexpr int kProdFloats = 2 * NB * LS;
-  constexpr int kDiagFloats = (int)(sizeof(DiagSmem) / sizeof(float));
-  __shared__ __attribute__((aligned(16))) float lds[kProdFloats > kDiagFloats ? kProdFloats
-                                                                             : kDiagFloats];
-  float* Xs = lds;
-  float* Ys = lds + NB * LS;
-  DiagSmem& dsm = *reinterpret_cast<DiagSmem*>(lds);
-  const int R = rp / NB;
-  const int n = R - k - 1;
+// sm.T = A_kk - L_{k,k-1} L_{k,k-1}^T (just A_00 for k = 0), the input of
+// the diagonal factorisation of step k. Ends with a barrier.
+__device__ __forceinline__ void diag_input(const float* A, int rp, int k, StepSmem& sm) {
   const int64_t kk = (int64_t)k * NB;
+  const float* Akk = A + kk * rp + kk;
+  if (k == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = threadIdx.x + NT * q;
+      const int r = idx >> 4, c4 = idx & 15;
+      *(f32x4*)&sm.T[r * TS + 4 * c4] = *(const f32x4*)&Akk[(int64_t)r * rp + 4 * c4];
+    }
+  } else {
+    const float* Lk = A + kk * rp + kk - NB;  // L_{k,k-1}
+    const int qm = wave_qm(), qn = wave_qn();
+    const f32x16 acc = mm_quad<false, true>(Lk, rp, Lk, rp, qm, qn);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      sm.T[qrow(qm, v) * TS + qcol(qn)] = Akk[(int64_t)qrow(qm, v) * rp + qcol(qn)] - acc[v];
+  }
+  __syncthreads();
+}
+
+// out -= X op(Y) on quadrants, computed by waves 1-3 while wave 0 factors the
+// diagonal tile: wave 1 takes quadrants (0, 0) and (1, 1), wave 2 (1, 0),
+// wave 3 (0, 1). Ends with a block-scope fence (the result is read back by
+// other waves after the next barrier).
+template <bool TB>
+__device__ __forceinline__ void side_update(const float* X, const float* Y, float* out, int rp,
+                                            float sign) {
+  const int wave = threadIdx.x >> 6;
+  if (wave == 0) return;
+  const int qm0 = wave == 3 ? 0 : (wave == 2 ? 1 : 0), qn0 = wave == 3 ? 1 : 0;
+  {
+    const f32x16 acc = mm_quad<false, TB>(X, rp, Y, rp, qm0, qn0);
+    store_axpby(acc, out, rp, sign, 1.0f, qm0, qn0);
+  }
+  if (wave == 1) {
+    const f32x16 acc = mm_quad<false, TB>(X, rp, Y, rp, 1, 1);
+    store_axpby(acc, out, rp, sign, 1.0f, 1, 1);
+  }
+  __threadfence_block();
+}
+
+// Launch k of the factorisation (see the file header). Workgroups, in order:
+//   [k < R]  1 diagonal (writes M_kk), R-1-k panel tiles, k inverse-row tiles;
+//   [k >= 1] 1 with want_L (writes L_{k-1,k-1}), n(n+1)/2 trailing tiles
+//            (n = R-1-k), n k partial sums, k(k+1)/2 G^-1 tiles if Ginv.
+__global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float* Ginv, int rp,
+                                                       int k, int r_real, int want_L,
+                                                       DevStats* st) {
+  __builtin_amdgcn_s_setprio(3);
+  __shared__ __attribute__((aligned(16))) StepSmem sm;
+  const int R = rp / NB;
+  const int n = R - 1 - k;
+  const int64_t kk = (int64_t)k * NB;
+  const int qm = wave_qm(), qn = wave_qn();
   int b = blockIdx.x;
-  if (n > 0) {
-    if (b == 0) {
-      const int64_t d0 = kk + NB;
-      block_mm<false, true>(A + d0 * rp + kk, A + d0 * rp + kk, A + d0 * rp + d0, rp, -1.0f, 1.0f,
-                            Xs, Ys);
-      __threadfence_block();
-      __syncthreads();
-      diag_factor(A, M, rp, k + 1, r_real, st, dsm);
+  if (k < R) {
+    if (b == 0) {  // M_kk
+      diag_input(A, rp, k, sm);
+      diag_factor<false, false>(sm.T, M + kk * rp + kk, nullptr, rp, (int)kk, r_real, st, sm.dg);
       return;
     }
     b -= 1;
-    const int nA = n * (n + 1) / 2 - 1;  // lower tiles of the trailing block but (k+1, k+1)
-    if (b < nA) {
-      int ii, jj;
-      tri_index(b + 1, ii, jj);
-      const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
-      block_mm<false, true>(A + i0 * rp + kk, A + j0 * rp + kk, A + i0 * rp + j0, rp, -1.0f, 1.0f,
-                            Xs, Ys);
+    if (b < n) {  // panel tile (i, k)
+      const int64_t i0 = (int64_t)(k + 1 + b) * NB;
+      float* Aik = A + i0 * rp + kk;
+      diag_input(A, rp, k, sm);
+      // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
+      if (k > 0) side_update<true>(Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f);
+      diag_factor<true, false>(sm.T, sm.T, nullptr, rp, (int)kk, r_real, nullptr, sm.dg);
+      __syncthreads();
+      const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
+      __syncthreads();  // every wave has read its operands before any overwrite
+      store_axpby(acc, Aik, rp, 1.0f, 0.0f, qm, qn);
       return;
     }
-    b -= nA;
-    const int nS = n * (k + 1);
-    if (b < nS) {
-      const int ii = b / (k + 1), jj = b % (k + 1);
-      const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)jj * NB;
-      block_mm<false, false>(A + i0 * rp + kk, M + kk * rp + j0, M + i0 * rp + j0, rp, 1.0f, 1.0f,
-                             Xs, Ys);
+    b -= n;
+    if (b < k) {  // inverse-row tile (k, j)
+      const int64_t j0 = (int64_t)b * NB;
+      float* Mkj = M + kk * rp + j0;
+      diag_input(A, rp, k, sm);
+      // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation
+      side_update<false>(A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f);
+      diag_factor<true, false>(sm.T, sm.T, nullptr, rp, (int)kk, r_real, nullptr, sm.dg);
+      __syncthreads();
+      const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
+      __syncthreads();
+      store_axpby(acc, Mkj, rp, -1.0f, 0.0f, qm, qn);
       return;
     }
-    b -= nS;
+    b -= k;
   }
+  if (k < 1) return;
+  const int p = k - 1;
+  const int64_t pp = (int64_t)p * NB;
+  if (want_L) {
+    if (b == 0) {  // L_pp
+      diag_input(A, rp, p, sm);
+      diag_factor<false, true>(sm.T, nullptr, A + pp * rp + pp, rp, (int)pp, r_real, nullptr,
+                               sm.dg);
+      return;
+    }
+    b -= 1;
+  }
+  const int nT = n > 0 ? n * (n + 1) / 2 : 0;
+  if (b < nT) {  // trailing tile (i, j), i >= j > k
+    int ii, jj;
+    tri_index(b, ii, jj);
+    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
+    const f32x16 acc = mm_quad<false, true>(A + i0 * rp + pp, rp, A + j0 * rp + pp, rp, qm, qn);
+    store_axpby(acc, A + i0 * rp + j0, rp, -1.0f, 1.0f, qm, qn);
+    return;
+  }
+  b -= nT;
+  const int nS = n > 0 ? n * k : 0;
+  if (b < nS) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
+    const int64_t i0 = (int64_t)(k + 1 + b / k) * NB, j0 = (int64_t)(b % k) * NB;
+    const f32x16 acc = mm_quad<false, false>(A + i0 * rp + pp, rp, M + pp * rp + j0, rp, qm, qn);
+    store_axpby(acc, M + i0 * rp + j0, rp, 1.0f, 1.0f, qm, qn);
+    return;
+  }
+  b -= nS;
+  // G^-1 tile (i, j), j <= i <= p: += M_pi^T M_pj
   int ii, jj;
   tri_index(b, ii, jj);
   const int64_t i0 = (int64_t)ii * NB, j0 = (int64_t)jj * NB;
-  block_mm<true, false, kBlkSymAcc>(M + kk * rp + i0, M + kk * rp + j0, Ginv + i0 * rp + j0, rp,
-                                    1.0f, ii == k ? 0.0f : 1.0f, Xs, Ys, Ginv + j0 * rp + i0);
+  const f32x16 acc = mm_quad<true, false>(M + pp * rp + i0, rp, M + pp * rp + j0, rp, qm, qn);
+  store_symacc(acc, Ginv + i0 * rp + j0, Ginv + j0 * rp + i0, rp, ii == p);
 }
 
 __global__ void zero_upper_kernel(float* A, int rp) {
@@ -435,23 +506,24 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 }  // namespace
 
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool zero_upper_L, hipStream_t s) {
+                                   DevStats* st, bool want_L, hipStream_t s) {
   if (rp % NB) return hipErrorInvalidValue;
   const int R = rp / NB;
   hipError_t e = launch_zero(M, (size_t)rp * rp, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chol_diag0_kernel, dim3(1), dim3(NT), 0, s, A, M, rp, r_real, st);
-  for (int k = 0; k < R; ++k) {
-    const int np = (R - k - 1) + k;
-    if (np > 0) hipLaunchKernelGGL(chol_panel_kernel, dim3(np), dim3(NT), 0, s, A, M, rp, k);
-    const int n = R - k - 1;
-    const int nb = (n > 0 ? 1 + (n * (n + 1) / 2 - 1) + n * (k + 1) : 0) +
-                   (Ginv ? (k + 1) * (k + 2) / 2 : 0);
+  for (int k = 0; k <= R; ++k) {
+    const int n = R - 1 - k;
+    int nb = k < R ? 1 + n + k : 0;
+    if (k >= 1) {
+      nb += want_L ? 1 : 0;
+      nb += n > 0 ? n * (n + 1) / 2 + n * k : 0;
+      nb += Ginv ? k * (k + 1) / 2 : 0;
+    }
     if (nb > 0)
-      hipLaunchKernelGGL(chol_update_kernel, dim3(nb), dim3(NT), 0, s, A, M, Ginv, rp, k, r_real,
-                         st);
+      hipLaunchKernelGGL(chol_step_kernel, dim3(nb), dim3(NT), 0, s, A, M, Ginv, rp, k, r_real,
+                         want_L ? 1 : 0, st);
   }
-  if (!zero_upper_L) return hipGetLastError();
+  if (!want_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;
   hipLaunchKernelGGL(zero_upper_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, A, rp);
   return hipGetLastError();
