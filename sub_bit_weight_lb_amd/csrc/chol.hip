@@ -147,6 +147,9 @@ __device__ __forceinline__ f32x16 mm_quad(const float* X, int ldx, const float* 
                    Y[(int64_t)(k0 + 2) * ldy + n], Y[(int64_t)(k0 + 3) * ldy + n]};
     }
   }
+  // all loads are in flight before the first MFMA (without the barrier the
+  // compiler keeps two to four in flight and waits before every MFMA group)
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -157,6 +160,17 @@ __device__ __forceinline__ f32x16 mm_quad(const float* X, int ldx, const float* 
   return acc;
 }
 
+// The quadrant (qm, qn) of a global tile in the accumulator layout.
+__device__ __forceinline__ f32x16 load_quad(const float* src, int rp, int qm, int qn) {
+  f32x16 v;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int row = qm * 32 + 8 * (q >> 2) + 4 * ((threadIdx.x & 63) >> 5) + (q & 3);
+    v[q] = src[(int64_t)row * rp + qn * 32 + (threadIdx.x & 31)];
+  }
+  return v;
+}
+
 // Quadrant of wave w in a 4-wave product.
 __device__ __forceinline__ int wave_qm() { return (threadIdx.x >> 6) & 1; }
 __device__ __forceinline__ int wave_qn() { return threadIdx.x >> 7; }
@@ -165,32 +179,35 @@ __device__ __forceinline__ int qrow(int qm, int v) {
 }
 __device__ __forceinline__ int qcol(int qn) { return qn * 32 + (threadIdx.x & 31); }
 
-// out = alpha * acc + beta * out on quadrant (qm, qn) (global, ld rp).
-__device__ __forceinline__ void store_axpby(const f32x16& acc, float* out, int rp, float alpha,
-                                            float beta, int qm, int qn) {
+// out = alpha * acc + prev on quadrant (qm, qn) (global, ld rp); prev is
+// the quadrant's old value (load_quad, issued before the product so that its
+// latency overlaps the MFMAs) or zero.
+__device__ __forceinline__ void store_quad(const f32x16& acc, const f32x16& prev, float* out,
+                                           int rp, float alpha, int qm, int qn) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float* o = out + (int64_t)qrow(qm, v) * rp + qcol(qn);
-    const float prev = beta != 0.0f ? *o : 0.0f;
-    *o = alpha * acc[v] + beta * prev;
-  }
+  for (int v = 0; v < 16; ++v) out[(int64_t)qrow(qm, v) * rp + qcol(qn)] = fmaf(alpha, acc[v], prev[v]);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) z[v] = 0.0f;
+  return z;
 }
 
 // Symmetric accumulate into G^-1: out is tile (i, j), i >= j, and out2 its
 // mirror (j, i) (out2 == out on the diagonal, where only the lower triangle
-// of the product is used). v = acc + (first ? 0 : out) goes to out and,
-// transposed, to out2, so both halves hold the same sums and G^-1 is
-// exactly symmetric.
-__device__ __forceinline__ void store_symacc(const f32x16& acc, float* out, float* out2, int rp,
-                                             bool first) {
+// of the product is used). v = acc + prev (the old lower tile, or zero for
+// its first contribution) goes to out and, transposed, to out2, so both
+// halves hold the same sums and G^-1 is exactly symmetric.
+__device__ __forceinline__ void store_symacc(const f32x16& acc, const f32x16& prev, float* out,
+                                             float* out2, int rp) {
   const int qm = wave_qm(), qn = wave_qn();
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int row = qrow(qm, v), col = qcol(qn);
     if (out2 == out && col > row) continue;
-    float* o = out + (int64_t)row * rp + col;
-    const float val = acc[v] + (first ? 0.0f : *o);
-    *o = val;
+    const float val = acc[v] + prev[v];
+    out[(int64_t)row * rp + col] = val;
     out2[(int64_t)col * rp + row] = val;
   }
 }
@@ -379,15 +396,15 @@ __device__ __forceinline__ void diag_input(const float* A, int rp, int k, StepSm
   } else {
     const float* Lk = A + kk * rp + kk - NB;  // L_{k,k-1}
     const int qm = wave_qm(), qn = wave_qn();
+    const f32x16 prev = load_quad(Akk, rp, qm, qn);
     const f32x16 acc = mm_quad<false, true>(Lk, rp, Lk, rp, qm, qn);
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      sm.T[qrow(qm, v) * TS + qcol(qn)] = Akk[(int64_t)qrow(qm, v) * rp + qcol(qn)] - acc[v];
+    for (int v = 0; v < 16; ++v) sm.T[qrow(qm, v) * TS + qcol(qn)] = prev[v] - acc[v];
   }
   __syncthreads();
 }
 
-// out -= X op(Y) on quadrants, computed by waves 1-3 while wave 0 factors the
+// out += sign X op(Y) on quadrants, computed by waves 1-3 while wave 0 factors the
 // diagonal tile: wave 1 takes quadrants (0, 0) and (1, 1), wave 2 (1, 0),
 // wave 3 (0, 1). Ends with a block-scope fence (the result is read back by
 // other waves after the next barrier).
@@ -398,12 +415,14 @@ __device__ __forceinline__ void side_update(const float* X, const float* Y, floa
   if (wave == 0) return;
   const int qm0 = wave == 3 ? 0 : (wave == 2 ? 1 : 0), qn0 = wave == 3 ? 1 : 0;
   {
+    const f32x16 prev = load_quad(out, rp, qm0, qn0);
     const f32x16 acc = mm_quad<false, TB>(X, rp, Y, rp, qm0, qn0);
-    store_axpby(acc, out, rp, sign, 1.0f, qm0, qn0);
+    store_quad(acc, prev, out, rp, sign, qm0, qn0);
   }
   if (wave == 1) {
+    const f32x16 prev = load_quad(out, rp, 1, 1);
     const f32x16 acc = mm_quad<false, TB>(X, rp, Y, rp, 1, 1);
-    store_axpby(acc, out, rp, sign, 1.0f, 1, 1);
+    store_quad(acc, prev, out, rp, sign, 1, 1);
   }
   __threadfence_block();
 }
@@ -439,7 +458,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
       __syncthreads();
       const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
       __syncthreads();  // every wave has read its operands before any overwrite
-      store_axpby(acc, Aik, rp, 1.0f, 0.0f, qm, qn);
+      store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
       return;
     }
     b -= n;
@@ -453,7 +472,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
       __syncthreads();
       const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
       __syncthreads();
-      store_axpby(acc, Mkj, rp, -1.0f, 0.0f, qm, qn);
+      store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
       return;
     }
     b -= k;
@@ -475,16 +494,18 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     int ii, jj;
     tri_index(b, ii, jj);
     const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
+    const f32x16 prev = load_quad(A + i0 * rp + j0, rp, qm, qn);
     const f32x16 acc = mm_quad<false, true>(A + i0 * rp + pp, rp, A + j0 * rp + pp, rp, qm, qn);
-    store_axpby(acc, A + i0 * rp + j0, rp, -1.0f, 1.0f, qm, qn);
+    store_quad(acc, prev, A + i0 * rp + j0, rp, -1.0f, qm, qn);
     return;
   }
   b -= nT;
   const int nS = n > 0 ? n * k : 0;
   if (b < nS) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
     const int64_t i0 = (int64_t)(k + 1 + b / k) * NB, j0 = (int64_t)(b % k) * NB;
+    const f32x16 prev = load_quad(M + i0 * rp + j0, rp, qm, qn);
     const f32x16 acc = mm_quad<false, false>(A + i0 * rp + pp, rp, M + pp * rp + j0, rp, qm, qn);
-    store_axpby(acc, M + i0 * rp + j0, rp, 1.0f, 1.0f, qm, qn);
+    store_quad(acc, prev, M + i0 * rp + j0, rp, 1.0f, qm, qn);
     return;
   }
   b -= nS;
@@ -492,8 +513,9 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   int ii, jj;
   tri_index(b, ii, jj);
   const int64_t i0 = (int64_t)ii * NB, j0 = (int64_t)jj * NB;
+  const f32x16 prev = ii == p ? zero16() : load_quad(Ginv + i0 * rp + j0, rp, qm, qn);
   const f32x16 acc = mm_quad<true, false>(M + pp * rp + i0, rp, M + pp * rp + j0, rp, qm, qn);
-  store_symacc(acc, Ginv + i0 * rp + j0, Ginv + j0 * rp + i0, rp, ii == p);
+  store_symacc(acc, prev, Ginv + i0 * rp + j0, Ginv + j0 * rp + i0, rp);
 }
 
 __global__ void zero_upper_kernel(float* A, int rp) {
