@@ -212,8 +212,9 @@ __device__ __forceinline__ void store_symacc(const f32x16& acc, const f32x16& pr
   }
 }
 
-// Diagonal tile: Tin (LDS, stride TS) holds the 64 x 64 SPD tile; its factor
-// L and M = L^-1 are formed on wave 0 in 2 x 2 blocks of 32:
+// Diagonal tile: Tin (LDS, stride TS) holds the lower blocks T11, T21, T22
+// of the 64 x 64 SPD tile; its factor L and M = L^-1 are formed on wave 0
+// in 2 x 2 blocks of 32 (parts 1 and 2 below):
 //   L11, M11 from T11 (half-wave factorisation);
 //   L21 = T21 M11^T;  T22' = T22 - L21 L21^T;
 //   L22, M22 from T22' (half-wave factorisation);
@@ -226,24 +227,16 @@ __device__ __forceinline__ void store_symacc(const f32x16& acc, const f32x16& pr
 // null. With WRITE_L, L (zeros above the diagonal) goes to L0 (ld rp).
 // With st, a pivot <= 0 or non-finite sets potrf_info (first such row
 // row0 + i, 1-based; rows at or past r_real are padding and not checked).
+// Part 1 (wave 0): L11, M11 from T11; needs only rows 0-31, columns 0-31 of
+// Tin. Sets bit i of badmask for a bad pivot in row i.
 template <bool M_LDS, bool WRITE_L>
-__device__ __forceinline__ void diag_factor(const float* Tin, float* M0, float* L0, int rp,
-                                            int row0, int r_real, DevStats* st, DiagSmem& sm) {
-  if (threadIdx.x >= 64) return;
+__device__ __forceinline__ void diag_part1(const float* Tin, float* M0, float* L0, int rp,
+                                           int row0, int r_real, DiagSmem& sm,
+                                           uint64_t& badmask) {
   const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
   const int ldm = M_LDS ? TS : rp;  // M0 is Tin itself when M_LDS
   float r[32];
-  float dg = 0.0f;  // this lane's diagonal of L (lanes 0-31), block 11 then 22
-  uint64_t badmask = 0;
-
-  // A21 in the A-operand layout of the first product and A22 in the
-  // accumulator layout of the second, loaded now so that their latency
-  // hides behind the first factorisation
-  float a21[16], a22[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) a21[s] = Tin[(32 + i) * TS + 2 * s + h];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) a22[v] = Tin[(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * TS + 32 + i];
+  float dg = 0.0f;  // this lane's diagonal of L11 (lanes 0-31)
 
   // ---- L11, M11
   if (h == 0) {
@@ -287,6 +280,25 @@ __device__ __forceinline__ void diag_factor(const float* Tin, float* M0, float* 
     const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && row0 + i < r_real;
     badmask |= (uint64_t)(uint32_t)__ballot(bad);
   }
+}
+
+// Part 2 (wave 0, after a barrier that makes T21 and T22 visible): L21,
+// T22 - L21 L21^T, L22, M22, M21; reports the first bad pivot.
+template <bool M_LDS, bool WRITE_L>
+__device__ __forceinline__ void diag_part2(const float* Tin, float* M0, float* L0, int rp,
+                                           int row0, int r_real, DevStats* st, DiagSmem& sm,
+                                           uint64_t badmask) {
+  const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
+  const int ldm = M_LDS ? TS : rp;
+  float r[32];
+  float dg = 0.0f;
+  // T21 in the A-operand layout of the first product, T22 in the accumulator
+  // layout of the second
+  float a21[16], a22[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) a21[s] = Tin[(32 + i) * TS + 2 * s + h];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) a22[v] = Tin[(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * TS + 32 + i];
 
   wave_lds_sync();  // Mc
 
@@ -381,26 +393,46 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
   j = t - ii * (ii + 1) / 2;
 }
 
-// sm.T = A_kk - L_{k,k-1} L_{k,k-1}^T (just A_00 for k = 0), the input of
-// the diagonal factorisation of step k. Ends with a barrier.
+// The lower blocks of T = A_kk - L_{k,k-1} L_{k,k-1}^T (just A_00 for k = 0),
+// the input of the diagonal factorisation of step k, into sm.T: wave 0
+// forms T11, wave 1 T21, wave 2 T22 (T12 is never read).
 __device__ __forceinline__ void diag_input(const float* A, int rp, int k, StepSmem& sm) {
+  const int wave = threadIdx.x >> 6;
+  if (wave == 3) return;
+  const int qm = wave == 0 ? 0 : 1, qn = wave == 2 ? 1 : 0;
   const int64_t kk = (int64_t)k * NB;
   const float* Akk = A + kk * rp + kk;
-  if (k == 0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = threadIdx.x + NT * q;
-      const int r = idx >> 4, c4 = idx & 15;
-      *(f32x4*)&sm.T[r * TS + 4 * c4] = *(const f32x4*)&Akk[(int64_t)r * rp + 4 * c4];
-    }
-  } else {
+  f32x16 t = load_quad(Akk, rp, qm, qn);
+  if (k > 0) {
     const float* Lk = A + kk * rp + kk - NB;  // L_{k,k-1}
-    const int qm = wave_qm(), qn = wave_qn();
-    const f32x16 prev = load_quad(Akk, rp, qm, qn);
     const f32x16 acc = mm_quad<false, true>(Lk, rp, Lk, rp, qm, qn);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sm.T[qrow(qm, v) * TS + qcol(qn)] = prev[v] - acc[v];
+    for (int v = 0; v < 16; ++v) t[v] -= acc[v];
   }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) sm.T[qrow(qm, v) * TS + qcol(qn)] = t[v];
+}
+
+// Diagonal tile k with work beside it. Wave 0 starts factoring T11 as soon
+// as it has formed it; waves 1 and 2 form T21 and T22 meanwhile. After a
+// barrier wave 0 finishes the factorisation while waves 1-3 run side().
+// Ends with a barrier (M in sm.T, when M_LDS, is then visible to all waves).
+template <bool M_LDS, bool WRITE_L, class Side>
+__device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* M0, float* L0,
+                                          int r_real, DevStats* st, StepSmem& sm, Side side) {
+  const int wave = threadIdx.x >> 6;
+  const int row0 = k * NB;
+  diag_input(A, rp, k, sm);
+  uint64_t bad = 0;
+  if (wave == 0) {
+    wave_lds_sync();  // T11 was written by other lanes of this wave
+    diag_part1<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, sm.dg, bad);
+  }
+  __syncthreads();
+  if (wave == 0)
+    diag_part2<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, st, sm.dg, bad);
+  else
+    side();
   __syncthreads();
 }
 
@@ -443,19 +475,17 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   int b = blockIdx.x;
   if (k < R) {
     if (b == 0) {  // M_kk
-      diag_input(A, rp, k, sm);
-      diag_factor<false, false>(sm.T, M + kk * rp + kk, nullptr, rp, (int)kk, r_real, st, sm.dg);
+      diag_step<false, false>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm, [] {});
       return;
     }
     b -= 1;
     if (b < n) {  // panel tile (i, k)
       const int64_t i0 = (int64_t)(k + 1 + b) * NB;
       float* Aik = A + i0 * rp + kk;
-      diag_input(A, rp, k, sm);
       // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
-      if (k > 0) side_update<true>(Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f);
-      diag_factor<true, false>(sm.T, sm.T, nullptr, rp, (int)kk, r_real, nullptr, sm.dg);
-      __syncthreads();
+      diag_step<true, false>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm, [&] {
+        if (k > 0) side_update<true>(Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f);
+      });
       const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
       __syncthreads();  // every wave has read its operands before any overwrite
       store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
@@ -465,11 +495,10 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     if (b < k) {  // inverse-row tile (k, j)
       const int64_t j0 = (int64_t)b * NB;
       float* Mkj = M + kk * rp + j0;
-      diag_input(A, rp, k, sm);
       // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation
-      side_update<false>(A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f);
-      diag_factor<true, false>(sm.T, sm.T, nullptr, rp, (int)kk, r_real, nullptr, sm.dg);
-      __syncthreads();
+      diag_step<true, false>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm, [&] {
+        side_update<false>(A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f);
+      });
       const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
       __syncthreads();
       store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
@@ -482,9 +511,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   const int64_t pp = (int64_t)p * NB;
   if (want_L) {
     if (b == 0) {  // L_pp
-      diag_input(A, rp, p, sm);
-      diag_factor<false, true>(sm.T, nullptr, A + pp * rp + pp, rp, (int)pp, r_real, nullptr,
-                               sm.dg);
+      diag_step<false, true>(A, rp, p, nullptr, A + pp * rp + pp, r_real, nullptr, sm, [] {});
       return;
     }
     b -= 1;
