@@ -213,14 +213,15 @@ __device__ __forceinline__ void store_symacc(const f32x16& acc, const f32x16& pr
 }
 
 // Diagonal tile: Tin (LDS, stride TS) holds the lower blocks T11, T21, T22
-// of the 64 x 64 SPD tile; its factor L and M = L^-1 are formed on wave 0
-// in 2 x 2 blocks of 32 (parts 1 and 2 below):
+// of the 64 x 64 SPD tile; its factor L and M = L^-1 are formed in 2 x 2
+// blocks of 32 (diag_step below: the two factorisations on wave 0, the
+// block products on all four waves):
 //   L11, M11 from T11 (half-wave factorisation);
 //   L21 = T21 M11^T;  T22' = T22 - L21 L21^T;
 //   L22, M22 from T22' (half-wave factorisation);
 //   M21 = -M22 (L21 M11).
-// The four products run on the MFMA; LDS only changes lane layouts between
-// them (one wave, so no barrier, but a wavefront fence at each hand-off).
+// LDS only changes lane layouts between the phases (a barrier, or a
+// wavefront fence where one wave hands data between its own lanes).
 // M (zeros above the diagonal) goes to M0 with leading dimension rp, or
 // with M_LDS to Tin itself (stride TS; every part of the input is read
 // before the part of M that replaces it is written), or nowhere if M0 is
@@ -282,60 +283,28 @@ __device__ __forceinline__ void diag_part1(const float* Tin, float* M0, float* L
   }
 }
 
-// Part 2 (wave 0, after a barrier that makes T21 and T22 visible): L21,
-// T22 - L21 L21^T, L22, M22, M21; reports the first bad pivot.
+// 32 x 32 x 32 product split over the four waves, one 16 x 16 block
+// (bi, bj) = (wave & 1, wave >> 1) each, on the 16x16x4 fp32 MFMA with
+// k = 4 s + lane / 16 at step s; fa(s), fb(s) return this lane's
+// A[16 bi + lane % 16][k] and B[k][16 bj + lane % 16]. c[v] is
+// C[16 bi + 4 (lane / 16) + v][16 bj + lane % 16].
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 mm16(FA fa, FB fb, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(fa(s), fb(s), c, 0, 0, 0);
+  return c;
+}
+
+// Second 32 x 32 factorisation (wave 0): L22, M22 from Ts (T22 - L21 L21^T);
+// L22 to L0 (WRITE_L), M22 to M0 (nullable), its columns to Nc. Sets bits
+// 32 + i of badmask for a bad pivot in row 32 + i.
 template <bool M_LDS, bool WRITE_L>
-__device__ __forceinline__ void diag_part2(const float* Tin, float* M0, float* L0, int rp,
-                                           int row0, int r_real, DevStats* st, DiagSmem& sm,
-                                           uint64_t badmask) {
+__device__ __forceinline__ void diag_factor2(float* M0, float* L0, int rp, int row0, int r_real,
+                                             DiagSmem& sm, uint64_t& badmask) {
   const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
   const int ldm = M_LDS ? TS : rp;
   float r[32];
   float dg = 0.0f;
-  // T21 in the A-operand layout of the first product, T22 in the accumulator
-  // layout of the second
-  float a21[16], a22[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) a21[s] = Tin[(32 + i) * TS + 2 * s + h];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) a22[v] = Tin[(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * TS + 32 + i];
-
-  wave_lds_sync();  // Mc
-
-  // ---- L21 = A21 M11^T
-  f32x16 acc;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  acc = mm32([&](int s) { return a21[s]; },
-             [&](int s) { return sm.Mc[2 * s + h][i]; }, acc);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int iv = 8 * (v >> 2) + 4 * h + (v & 3);
-    if (WRITE_L) L0[(int64_t)(32 + iv) * rp + i] = acc[v];
-    sm.Ls[iv][i] = acc[v];
-  }
-
-  wave_lds_sync();  // Ls
-
-  // ---- T = A22 - L21 L21^T
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = a22[v];
-  acc = mm32([&](int s) { return -sm.Ls[i][2 * s + h]; },
-             [&](int s) { return sm.Ls[i][2 * s + h]; }, acc);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) sm.Ts[8 * (v >> 2) + 4 * h + (v & 3)][i] = acc[v];
-
-  // ---- P = L21 M11 (needs neither T nor the second factorisation)
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  acc = mm32([&](int s) { return sm.Ls[i][2 * s + h]; },
-             [&](int s) { return sm.Mc[i][2 * s + h]; }, acc);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) sm.Ps[8 * (v >> 2) + 4 * h + (v & 3)][i] = acc[v];
-
-  wave_lds_sync();  // Ts, Ps
-
-  // ---- L22, M22
   if (h == 0) {
 #pragma unroll
     for (int c = 0; c < 32; ++c) r[c] = sm.Ts[i][c];
@@ -344,7 +313,6 @@ __device__ __forceinline__ void diag_part2(const float* Tin, float* M0, float* L
     for (int c = 0; c < 32; ++c) r[c] = c == i ? 1.0f : 0.0f;
   }
   hw_steps<0>(r);
-  dg = 0.0f;
   if (h == 0) {
 #pragma unroll
     for (int c4 = 0; c4 < 8; ++c4) {
@@ -364,24 +332,8 @@ __device__ __forceinline__ void diag_part2(const float* Tin, float* M0, float* L
       sm.Nc[i][q] = r[q];
     }
   }
-  {
-    const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && row0 + 32 + i < r_real;
-    badmask |= (uint64_t)(uint32_t)__ballot(bad) << 32;
-  }
-
-  wave_lds_sync();  // Nc
-
-  // ---- M21 = -M22 P
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  acc = mm32([&](int s) { return -sm.Nc[2 * s + h][i]; },
-             [&](int s) { return sm.Ps[2 * s + h][i]; }, acc);
-  if (M0) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) M0[(32 + 8 * (v >> 2) + 4 * h + (v & 3)) * ldm + i] = acc[v];
-  }
-  if (st && badmask && lane == 0)
-    atomicMin(&st->potrf_info, row0 + __ffsll((unsigned long long)badmask));
+  const bool bad = h == 0 && !(dg > 0.0f && isfinite(dg)) && row0 + 32 + i < r_real;
+  badmask |= (uint64_t)(uint32_t)__ballot(bad) << 32;
 }
 
 // Lower-triangle tile index t -> (i, j), i >= j.
@@ -413,50 +365,107 @@ __device__ __forceinline__ void diag_input(const float* A, int rp, int k, StepSm
   for (int v = 0; v < 16; ++v) sm.T[qrow(qm, v) * TS + qcol(qn)] = t[v];
 }
 
-// Diagonal tile k with work beside it. Wave 0 starts factoring T11 as soon
-// as it has formed it; waves 1 and 2 form T21 and T22 meanwhile. After a
-// barrier wave 0 finishes the factorisation while waves 1-3 run side().
-// Ends with a barrier (M in sm.T, when M_LDS, is then visible to all waves).
-template <bool M_LDS, bool WRITE_L, class Side>
-__device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* M0, float* L0,
-                                          int r_real, DevStats* st, StepSmem& sm, Side side) {
-  const int wave = threadIdx.x >> 6;
-  const int row0 = k * NB;
-  diag_input(A, rp, k, sm);
-  uint64_t bad = 0;
-  if (wave == 0) {
-    wave_lds_sync();  // T11 was written by other lanes of this wave
-    diag_part1<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, sm.dg, bad);
-  }
-  __syncthreads();
-  if (wave == 0)
-    diag_part2<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, st, sm.dg, bad);
-  else
-    side();
-  __syncthreads();
+// Work beside a diagonal factorisation: out += sign X op(Y) over the four
+// quadrants of a 64 x 64 tile (inactive for the workgroups that only factor).
+struct SideJob {
+  const float* X;
+  const float* Y;
+  float* out;
+  int rp;
+  float sign;
+  bool active;
+};
+template <bool TB>
+__device__ __forceinline__ void side_quad(const SideJob& j, int qm, int qn) {
+  const f32x16 prev = load_quad(j.out, j.rp, qm, qn);
+  const f32x16 acc = mm_quad<false, TB>(j.X, j.rp, j.Y, j.rp, qm, qn);
+  store_quad(acc, prev, j.out, j.rp, j.sign, qm, qn);
 }
 
-// out += sign X op(Y) on quadrants, computed by waves 1-3 while wave 0 factors the
-// diagonal tile: wave 1 takes quadrants (0, 0) and (1, 1), wave 2 (1, 0),
-// wave 3 (0, 1). Ends with a block-scope fence (the result is read back by
-// other waves after the next barrier).
-template <bool TB>
-__device__ __forceinline__ void side_update(const float* X, const float* Y, float* out, int rp,
-                                            float sign) {
-  const int wave = threadIdx.x >> 6;
-  if (wave == 0) return;
-  const int qm0 = wave == 3 ? 0 : (wave == 2 ? 1 : 0), qn0 = wave == 3 ? 1 : 0;
+// Diagonal tile k (input T = A_kk - L_{k,k-1} L_{k,k-1}^T) with work beside
+// it, in phases separated by barriers:
+//   1. wave 0 forms T11 and factors it (L11, M11); waves 1, 2 form T21, T22;
+//      wave 3 does side quadrant (0, 1);
+//   2. L21 = T21 M11^T (four waves);
+//   3. T22 - L21 L21^T and P = L21 M11 (four waves);
+//   4. wave 0 factors T22 - L21 L21^T (L22, M22); waves 1, 2, 3 do side
+//      quadrants (0, 0), (1, 0), (1, 1);
+//   5. M21 = -M22 P (four waves).
+// Ends with a barrier (M in sm.T, when M_LDS, and the side job's result are
+// then visible to all waves of the workgroup).
+template <bool M_LDS, bool WRITE_L, bool TB>
+__device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* M0, float* L0,
+                                          int r_real, DevStats* st, StepSmem& sm,
+                                          const SideJob& side) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int bi = wave & 1, bj = wave >> 1;
+  const int row0 = k * NB;
+  const int ldm = M_LDS ? TS : rp;
+  DiagSmem& d = sm.dg;
+  const float* Tin = sm.T;
+  uint64_t bad = 0;
+  // 1
+  diag_input(A, rp, k, sm);
+  if (wave == 0) {
+    wave_lds_sync();  // T11 was written by other lanes of this wave
+    diag_part1<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, d, bad);
+  } else if (wave == 3 && side.active) {
+    side_quad<TB>(side, 0, 1);
+    __threadfence_block();
+  }
+  __syncthreads();
+  // 2. L21 = T21 M11^T  (B(k, j) = M11[j][k] = Mc[k][j])
   {
-    const f32x16 prev = load_quad(out, rp, qm0, qn0);
-    const f32x16 acc = mm_quad<false, TB>(X, rp, Y, rp, qm0, qn0);
-    store_quad(acc, prev, out, rp, sign, qm0, qn0);
+    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    c = mm16([&](int s_) { return Tin[(32 + 16 * bi + i16) * TS + 4 * s_ + g]; },
+             [&](int s_) { return d.Mc[4 * s_ + g][16 * bj + i16]; }, c);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * bi + 4 * g + v, col = 16 * bj + i16;
+      d.Ls[row][col] = c[v];
+      if (WRITE_L) L0[(int64_t)(32 + row) * rp + col] = c[v];
+    }
   }
-  if (wave == 1) {
-    const f32x16 prev = load_quad(out, rp, 1, 1);
-    const f32x16 acc = mm_quad<false, TB>(X, rp, Y, rp, 1, 1);
-    store_quad(acc, prev, out, rp, sign, 1, 1);
+  __syncthreads();
+  // 3. Ts = T22 - L21 L21^T, Ps = L21 M11  (M11[k][j] = Mc[j][k])
+  {
+    f32x4 c;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) c[v] = Tin[(32 + 16 * bi + 4 * g + v) * TS + 32 + 16 * bj + i16];
+    c = mm16([&](int s_) { return -d.Ls[16 * bi + i16][4 * s_ + g]; },
+             [&](int s_) { return d.Ls[16 * bj + i16][4 * s_ + g]; }, c);
+    f32x4 q = {0.0f, 0.0f, 0.0f, 0.0f};
+    q = mm16([&](int s_) { return d.Ls[16 * bi + i16][4 * s_ + g]; },
+             [&](int s_) { return d.Mc[16 * bj + i16][4 * s_ + g]; }, q);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      d.Ts[16 * bi + 4 * g + v][16 * bj + i16] = c[v];
+      d.Ps[16 * bi + 4 * g + v][16 * bj + i16] = q[v];
+    }
   }
-  __threadfence_block();
+  __syncthreads();
+  // 4
+  if (wave == 0) {
+    diag_factor2<M_LDS, WRITE_L>(M0, L0, rp, row0, r_real, d, bad);
+  } else if (side.active) {
+    side_quad<TB>(side, wave == 1 ? 0 : 1, wave == 3 ? 1 : 0);
+    __threadfence_block();
+  }
+  __syncthreads();
+  // 5. M21 = -M22 P  (M22[i][k] = Nc[k][i])
+  {
+    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    c = mm16([&](int s_) { return -d.Nc[4 * s_ + g][16 * bi + i16]; },
+             [&](int s_) { return d.Ps[4 * s_ + g][16 * bj + i16]; }, c);
+    if (M0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) M0[(32 + 16 * bi + 4 * g + v) * ldm + 16 * bj + i16] = c[v];
+    }
+  }
+  if (st && wave == 0 && bad && lane == 0)
+    atomicMin(&st->potrf_info, row0 + __ffsll((unsigned long long)bad));
+  __syncthreads();
 }
 
 // Launch k of the factorisation (see the file header). Workgroups, in order:
@@ -475,7 +484,8 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   int b = blockIdx.x;
   if (k < R) {
     if (b == 0) {  // M_kk
-      diag_step<false, false>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm, [] {});
+      diag_step<false, false, true>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm,
+                                    SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false});
       return;
     }
     b -= 1;
@@ -483,9 +493,8 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
       const int64_t i0 = (int64_t)(k + 1 + b) * NB;
       float* Aik = A + i0 * rp + kk;
       // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
-      diag_step<true, false>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm, [&] {
-        if (k > 0) side_update<true>(Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f);
-      });
+      diag_step<true, false, true>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
+                                   SideJob{Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f, k > 0});
       const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
       __syncthreads();  // every wave has read its operands before any overwrite
       store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
@@ -496,9 +505,9 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
       const int64_t j0 = (int64_t)b * NB;
       float* Mkj = M + kk * rp + j0;
       // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation
-      diag_step<true, false>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm, [&] {
-        side_update<false>(A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f);
-      });
+      diag_step<true, false, false>(
+          A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
+          SideJob{A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f, true});
       const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
       __syncthreads();
       store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
@@ -511,7 +520,8 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   const int64_t pp = (int64_t)p * NB;
   if (want_L) {
     if (b == 0) {  // L_pp
-      diag_step<false, true>(A, rp, p, nullptr, A + pp * rp + pp, r_real, nullptr, sm, [] {});
+      diag_step<false, true, true>(A, rp, p, nullptr, A + pp * rp + pp, r_real, nullptr, sm,
+                                   SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false});
       return;
     }
     b -= 1;
