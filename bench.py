@@ -66,34 +66,44 @@ def read_traffic(m, n, r, launches_ms):
     return float(mt.group(1))
 
 
-def cpu_baseline(L, budget_s=12.0, max_iters=12):
+def cpu_baseline(L, budget_s=10.0, max_iters=12, budget_fp32_s=6.0):
+    """The CPU oracle on the same layer: a bounded number of ADMM iterations
+    in NumPy float64 (the parity oracle; reported as value) and, as a second
+    figure, in float32 (the oracle's dtype switch)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import lbadmm as O
     wl = L.workload
-    t0 = time.perf_counter()
-    Wt = O.precondition(L.W, L.d_out, L.d_in)
-    st = O.init_state(Wt, wl.r, wl.svid_steps, EU=L.EU, EV=L.EV)
-    t_prep = time.perf_counter() - t0
-    done = 0
-    t_iter = 0.0
-    while done < max_iters and (done == 0 or t_iter * (done + 1) / done < budget_s):
-        t1 = time.perf_counter()
-        st = O.iterate(Wt, st, wl.rho, wl.svid_steps, 1)
-        t_iter += time.perf_counter() - t1
-        done += 1
+
+    def timed(dtype, budget):
+        t0 = time.perf_counter()
+        Wt = O.precondition(L.W, L.d_out, L.d_in, dtype)
+        st = O.init_state(Wt, wl.r, wl.svid_steps, EU=L.EU, EV=L.EV, dtype=dtype)
+        t_prep = time.perf_counter() - t0
+        done, t_iter = 0, 0.0
+        while done < max_iters and (done == 0 or t_iter * (done + 1) / done < budget):
+            t1 = time.perf_counter()
+            st = O.iterate(Wt, st, wl.rho, wl.svid_steps, 1, dtype)
+            t_iter += time.perf_counter() - t1
+            done += 1
+        return done, t_iter, t_prep, bool(np.isfinite(st.U).all())
+
+    d64, t64, p64, fin64 = timed(np.float64, budget_s)
+    d32, t32, p32, fin32 = timed(np.float32, budget_fp32_s)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
-        "value": done / t_iter,
+        "value": d64 / t64,
         "unit": "iters/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{done} ADMM iterations (U-half + V-half) of the same {wl.m}x{wl.n} r={wl.r} "
-                   f"layer in NumPy float64 after preconditioning and init ({t_prep:.1f} s, not "
-                   f"counted); {t_iter:.1f} s of iterations"),
+        "sample": (f"{d64} ADMM iterations (U-half + V-half) of the same {wl.m}x{wl.n} r={wl.r} "
+                   f"layer in NumPy float64 after preconditioning and init ({p64:.1f} s, not "
+                   f"counted); {t64:.1f} s of iterations"),
+        "fp32_value": d32 / t32,
+        "fp32_sample": f"{d32} iterations in float32 mode, {t32:.1f} s",
         "host_cpus": len(os.sched_getaffinity(0)),
-        "s_per_iter": t_iter / done,
-        "finite": bool(np.isfinite(st.U).all()),
+        "s_per_iter": t64 / d64,
+        "finite": fin64 and fin32,
     }
 
 
