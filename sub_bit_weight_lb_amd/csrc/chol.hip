@@ -29,7 +29,9 @@
 // products on the MFMA. Off-diagonal tiles: 64 x 64 x 64 products on the
 // 32x32x2 fp32 MFMA.
 #include "common.h"
+#include <algorithm>
 #include <climits>
+#include <cstdlib>
 
 namespace nq {
 namespace {
@@ -37,6 +39,20 @@ namespace {
 constexpr int NB = kNB;     // 64
 constexpr int NT = 256;
 constexpr int TS = NB + 4;  // LDS row stride of a 64 x 64 tile
+
+// Workgroups per launch. Beside a running GEMM workgroup (110.6 KB of LDS)
+// a CU has room for one of these (38.5 KB), so a launch of at most one
+// workgroup per CU runs in a single round; the update tiles are then
+// shared out over the workgroups left after the diagonal ones. 0 = one
+// workgroup per tile. NQ_CHOL_BLOCKS overrides it.
+int chol_launch_cap() {
+  static const int cap = [] {
+    const char* e = std::getenv("NQ_CHOL_BLOCKS");
+    return e ? std::max(0, std::atoi(e)) : 256;
+  }();
+  return cap;
+}
+constexpr int kCholMinUpdBlocks = 32;
 
 __device__ __forceinline__ float bcast(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
@@ -474,7 +490,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 //            (n = R-1-k), n k partial sums, k(k+1)/2 G^-1 tiles if Ginv.
 __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float* Ginv, int rp,
                                                        int k, int r_real, int want_L,
-                                                       DevStats* st) {
+                                                       int upd_blocks, DevStats* st) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) StepSmem sm;
   const int R = rp / NB;
@@ -526,33 +542,44 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     }
     b -= 1;
   }
+  // The update tiles of step p are spread over upd_blocks workgroups, each
+  // taking every upd_blocks-th tile, so that a launch needs few enough
+  // workgroups to be resident at once beside a concurrently running GEMM.
   const int nT = n > 0 ? n * (n + 1) / 2 : 0;
-  if (b < nT) {  // trailing tile (i, j), i >= j > k
-    int ii, jj;
-    tri_index(b, ii, jj);
-    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
-    const f32x16 prev = load_quad(A + i0 * rp + j0, rp, qm, qn);
-    const f32x16 acc = mm_quad<false, true>(A + i0 * rp + pp, rp, A + j0 * rp + pp, rp, qm, qn);
-    store_quad(acc, prev, A + i0 * rp + j0, rp, -1.0f, qm, qn);
-    return;
-  }
-  b -= nT;
   const int nS = n > 0 ? n * k : 0;
-  if (b < nS) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
-    const int64_t i0 = (int64_t)(k + 1 + b / k) * NB, j0 = (int64_t)(b % k) * NB;
-    const f32x16 prev = load_quad(M + i0 * rp + j0, rp, qm, qn);
-    const f32x16 acc = mm_quad<false, false>(A + i0 * rp + pp, rp, M + pp * rp + j0, rp, qm, qn);
-    store_quad(acc, prev, M + i0 * rp + j0, rp, 1.0f, qm, qn);
-    return;
+  const int nG = Ginv ? k * (k + 1) / 2 : 0;
+  // Inside the loops the row stride is re-read through an empty asm, so the
+  // per-lane 64-bit fragment offsets are formed per tile rather than hoisted
+  // out of the loop, where they would hold ~100 extra registers.
+  int t = b;
+  for (; t < nT; t += upd_blocks) {  // trailing tile (i, j), i >= j > k
+    int ld = rp;
+    asm volatile("" : "+s"(ld));
+    int ii, jj;
+    tri_index(t, ii, jj);
+    const int64_t i0 = (int64_t)(k + 1 + ii) * NB, j0 = (int64_t)(k + 1 + jj) * NB;
+    const f32x16 prev = load_quad(A + i0 * ld + j0, ld, qm, qn);
+    const f32x16 acc = mm_quad<false, true>(A + i0 * ld + pp, ld, A + j0 * ld + pp, ld, qm, qn);
+    store_quad(acc, prev, A + i0 * ld + j0, ld, -1.0f, qm, qn);
   }
-  b -= nS;
-  // G^-1 tile (i, j), j <= i <= p: += M_pi^T M_pj
-  int ii, jj;
-  tri_index(b, ii, jj);
-  const int64_t i0 = (int64_t)ii * NB, j0 = (int64_t)jj * NB;
-  const f32x16 prev = ii == p ? zero16() : load_quad(Ginv + i0 * rp + j0, rp, qm, qn);
-  const f32x16 acc = mm_quad<true, false>(M + pp * rp + i0, rp, M + pp * rp + j0, rp, qm, qn);
-  store_symacc(acc, prev, Ginv + i0 * rp + j0, Ginv + j0 * rp + i0, rp);
+  for (t -= nT; t < nS; t += upd_blocks) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
+    int ld = rp;
+    asm volatile("" : "+s"(ld));
+    const int64_t i0 = (int64_t)(k + 1 + t / k) * NB, j0 = (int64_t)(t % k) * NB;
+    const f32x16 prev = load_quad(M + i0 * ld + j0, ld, qm, qn);
+    const f32x16 acc = mm_quad<false, false>(A + i0 * ld + pp, ld, M + pp * ld + j0, ld, qm, qn);
+    store_quad(acc, prev, M + i0 * ld + j0, ld, 1.0f, qm, qn);
+  }
+  for (t -= nS; t < nG; t += upd_blocks) {  // G^-1 tile (i, j), j <= i <= p: += M_pi^T M_pj
+    int ld = rp;
+    asm volatile("" : "+s"(ld));
+    int ii, jj;
+    tri_index(t, ii, jj);
+    const int64_t i0 = (int64_t)ii * NB, j0 = (int64_t)jj * NB;
+    const f32x16 prev = ii == p ? zero16() : load_quad(Ginv + i0 * ld + j0, ld, qm, qn);
+    const f32x16 acc = mm_quad<true, false>(M + pp * ld + i0, ld, M + pp * ld + j0, ld, qm, qn);
+    store_symacc(acc, prev, Ginv + i0 * ld + j0, Ginv + j0 * ld + i0, ld);
+  }
 }
 
 __global__ void zero_upper_kernel(float* A, int rp) {
@@ -572,15 +599,19 @@ hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int 
   if (e != hipSuccess) return e;
   for (int k = 0; k <= R; ++k) {
     const int n = R - 1 - k;
-    int nb = k < R ? 1 + n + k : 0;
+    int nb = k < R ? 1 + n + k : 0;  // diagonal, panel and inverse-row workgroups
+    int upd = 0;
     if (k >= 1) {
       nb += want_L ? 1 : 0;
-      nb += n > 0 ? n * (n + 1) / 2 + n * k : 0;
-      nb += Ginv ? k * (k + 1) / 2 : 0;
+      const int tiles = (n > 0 ? n * (n + 1) / 2 + n * k : 0) + (Ginv ? k * (k + 1) / 2 : 0);
+      upd = tiles;
+      const int cap = chol_launch_cap();
+      if (cap > 0 && nb + upd > cap) upd = std::max(cap - nb, std::min(tiles, kCholMinUpdBlocks));
+      upd = std::min(upd, tiles);
     }
-    if (nb > 0)
-      hipLaunchKernelGGL(chol_step_kernel, dim3(nb), dim3(NT), 0, s, A, M, Ginv, rp, k, r_real,
-                         want_L ? 1 : 0, st);
+    if (nb + upd > 0)
+      hipLaunchKernelGGL(chol_step_kernel, dim3(nb + upd), dim3(NT), 0, s, A, M, Ginv, rp, k,
+                         r_real, want_L ? 1 : 0, std::max(upd, 1), st);
   }
   if (!want_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;

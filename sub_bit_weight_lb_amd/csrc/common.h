@@ -33,28 +33,33 @@ struct DevStats {
 
 // ---------------------------------------------------------------- GEMM
 enum GemmEpilogue : int {
-  kEpiPlain = 0,   // C = A B
-  kEpiRhs = 1,     // C = A B + rho P                (P ld = ldc)
-  kEpiSolve = 2,   // C = A B;  X = C + X  (X holds Lambda on entry, ld = ldc)
+  kEpiPlain = 0,   // C = A B^T
+  kEpiRhs = 1,     // C = A B^T + rho P              (P ld = ldc)
+  kEpiSolve = 2,   // C = A B^T;  X = C + X  (X holds Lambda on entry, ld = ldc);
+                   // Ct = C^T when Ct is not null
 };
+// C = A B^T ("NT"): both operands are stored with k contiguous.
 struct GemmArgs {
   const float* A; int64_t lda;   // M x K
-  const float* B; int64_t ldb;   // K x N
+  const float* B; int64_t ldb;   // N x K (the right factor, transposed)
   float* C; int64_t ldc;         // M x N
   const float* P;                // kEpiRhs
   float* X;                      // kEpiSolve
+  float* Ct; int64_t ldct;       // kEpiSolve, optional: N x M
   float rho;
   int M, N, K;
 };
-// M % 256 == 0, N % 128 == 0, K % 32 == 0, ld multiples of 4, 16-byte aligned.
+// M % 256 == 0, N % 128 == 0, K % 32 == 0; every ld a multiple of 4 and every
+// pointer 16-byte aligned (else hipErrorInvalidValue, nothing launched).
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 
-// ---------------------------------------------------------------- SYRK / LAUUM
-// Partial Gram tiles: part[c] (rp x rp, ld rp), lower 128 x 128 tiles only,
-// chunk c covering k in [c*kchunk, (c+1)*kchunk) of A (K x rp, ld lda).
-// If tri_kstart, tile row I only uses k >= 128*I (A lower triangular).
-hipError_t launch_syrk_partial(const float* A, int64_t lda, int K, int rp, int kchunk,
-                               bool tri_kstart, float* part, hipStream_t s);
+// ---------------------------------------------------------------- Gram
+// Partial Gram tiles of A^T A for A (K x rp) given as At = A^T (rp x K, ld
+// ldat): part[c] (rp x rp, ld rp) holds, in its lower 128 x 128 tiles only,
+// the sum over k in [c*kchunk, (c+1)*kchunk). rp % 128 == 0, K and kchunk
+// multiples of 32.
+hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, int kchunk,
+                               float* part, hipStream_t s);
 // G = sum_c part[c] + rho I, written full-symmetric (ld ldg).
 hipError_t launch_gram_reduce(const float* part, int nchunks, int rp, float rho,
                               float* G, int64_t ldg, hipStream_t s);
@@ -109,6 +114,10 @@ hipError_t launch_init_philox(uint64_t seed, uint32_t stream_id, int64_t rows, i
                               float* dst, float* dst2, int rows_pad, int rp,
                               const DevStats* st, hipStream_t s);
 hipError_t launch_zero(float* p, size_t n, hipStream_t s);
+// dst (cols x rows, ld ldd) = src^T, src rows x cols (ld lds); rows and cols
+// multiples of 32.
+hipError_t launch_transpose(const float* src, int64_t rows, int64_t cols, int64_t lds, float* dst,
+                            int64_t ldd, hipStream_t s);
 // out (rows x r, ld r) = A + B for padded A, B (ld rp).
 hipError_t launch_add_compact(const float* A, const float* B, int64_t rows, int64_t r, int rp,
                               float* out, hipStream_t s);

@@ -1,165 +1,225 @@
-// fp32 MFMA GEMM C = A B (+ fused epilogue) for gfx950.
+// fp32 MFMA GEMMs of the regularised solve, NanoQuant digest section 核心方法
+// step (a), in "NT" form: C = A B^T with both operands stored k-contiguous.
 //
-// Used for the right-hand side of the regularised solve, R = Wt V + rho (Z - Lam)
-// (NanoQuant digest, section 核心方法, step (a)), and for applying the two
-// triangular solves, U = R L^-T L^-1 = R G^-1, as one product with the
-// symmetric inverse (epilogue also forms X = U + Lam for SVID, step (b)).
+//   right-hand side  R = Wt V + rho (Z - Lam): A = Wt (or Wt^T for the V-half),
+//                    B = V^T (or U^T), kept in HBM beside the factors;
+//   solve            U = R G^-1 = R L^-T L^-1, both triangular solves as one
+//                    product with the symmetric inverse (B = G^-1 = G^-T);
+//                    the epilogue also forms X = U + Lam for SVID, step (b),
+//                    and writes U^T for the next half's Gram and right-hand
+//                    side;
+//   Gram             G = V^T V + rho I: A = B = V^T, lower 128 x 128 tiles,
+//                    split over K into partial sums (gram_reduce adds them).
 //
-// Tiling: 256 x 128 block tile, BK = 32, 256 threads = 4 waves in a 2 x 2
-// arrangement, each wave owning 128 x 64 = 4 x 2 blocks of
-// v_mfma_f32_32x32x2_f32 (128 accumulators per lane). Double-buffered LDS,
-// one barrier per K step, global loads of the next step issued before the
-// current step's MFMAs, operand fragments of the next chunk of 8 k read from
-// LDS while the current chunk's 32 MFMAs run.
-//
-// K ordering inside a chunk of 8: lane half h (lanes 32..63 are h = 1) feeds
-// k = 4 h + s to MFMA step s = 0..3. Both tiles are stored k-contiguous in
-// LDS (A as [m][k], B transposed to [n][k] while staging), so each fragment
-// for 4 steps is a single ds_read_b128. Both operands use the same
-// permutation, so each MFMA step still sums over a distinct pair of k.
-// Row stride BK + 4 floats makes the 16-lane groups of a ds_read_b128 touch
-// 64 distinct banks.
-//
-// Tile order: the hardware hands workgroups to the 8 XCDs round-robin, so
-// workgroup b runs on XCD b % 8. Tiles are remapped so each XCD works on a
-// contiguous range of row panels and shares their A rows in its own L2.
+// Main loop (256 threads, 4 waves in a 2 x 2 arrangement):
+// - Tile TM x 128 with TM = 256 (one workgroup per CU) or 128 (two per CU),
+//   BK = 32, each wave (TM / 2) x 64 = (TM / 64) x 2 blocks of
+//   v_mfma_f32_32x32x2_f32.
+// - Operands go from global memory straight into LDS with
+//   global_load_lds_dwordx4 (no VGPR staging). Two stages: the DMA of step
+//   k + 1 is spread between the MFMAs of step k, a few instructions after
+//   every 8 MFMAs.
+// - LDS rows hold 32 floats as 8 slots of 16 B; row r keeps k-quad q in slot
+//   q ^ ((r >> 1) & 7). Each lane's DMA fetches the quad that belongs in its
+//   slot. Fragment reads are single ds_read_b128s, free of bank conflicts
+//   for 16 consecutive rows.
+// - K order inside a chunk of 8: lane half h (lanes 32..63 are h = 1) feeds
+//   k = 4 h + s to MFMA step s = 0..3, the same for both operands.
+// - Tile order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets
+//   a contiguous range of tiles, so row and column panels are shared in its
+//   L2.
 #include "common.h"
 
 namespace nq {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 32;
-constexpr int LDS_S = BK + 4;  // row stride (floats) of both LDS tiles
+constexpr int BK = 32;
+constexpr int TN = 128;
 constexpr int NT = 256;
-constexpr int A_F4 = BM * BK / 4 / NT;   // float4 loads of A per thread (8)
-constexpr int B_F1 = BK * BN / NT;       // scalar loads of B per thread (16)
 
-template <int EPI>
-__global__ __launch_bounds__(NT) void gemm_nn_kernel(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) float As[2][BM * LDS_S];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BN * LDS_S];
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* glb_ptr_t;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+// 16 B per lane from global memory to LDS at lds + 16 * lane (wave-uniform lds).
+__device__ __forceinline__ void dma16(const void* g, float* lds) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
+}
+
+template <int TM>
+struct Tile {
+  static constexpr int MI = TM / 64;            // 32-row blocks per wave
+  static constexpr int SA = TM * BK;            // floats of one A stage
+  static constexpr int SST = SA + TN * BK;      // floats of one stage (A then B)
+  static constexpr int NA = TM / 32, NB = TN / 32;  // DMA instructions per wave per stage
+  static constexpr int DPC = (NA + NB) / 4;     // DMA instructions per chunk of 8 k
+  static constexpr int LDS_FLOATS = 2 * SST;
+};
+
+// acc += A[0:TM, k0 : k0 + 32 nk] B[0:128, same]^T for the tile whose
+// operand rows start at Ag and Bg. Leaves every wave past a final barrier
+// with the LDS free.
+template <int TM>
+__device__ __forceinline__ void nt_mainloop(const float* __restrict__ Ag, int lda,
+                                            const float* __restrict__ Bg, int ldb, int k0,
+                                            int nk, float* lds,
+                                            f32x16 (&acc)[Tile<TM>::MI][2]) {
+  using T = Tile<TM>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int h = lane >> 5, l32 = lane & 31;
 
-  const int tilesN = p.N / BN;
-  const int nt = (p.M / BM) * tilesN;
-  const int b = blockIdx.x;
-  const int t = (nt % 8 == 0) ? (b % 8) * (nt / 8) + b / 8 : b;
-  const int tm = t / tilesN, tn = t % tilesN;
-
-  const float* __restrict__ Ag = p.A + (int64_t)tm * BM * p.lda;
-  const float* __restrict__ Bg = p.B + (int64_t)tn * BN;
-
-  // A: float4 idx = tid + NT i -> row idx / 8, k4 idx % 8.
-  // B: thread owns column n = tid % 128 and k rows kq*4 .. kq*4+3 for
-  //    kq = tid / 128 + 2 j (j = 0..3): four coalesced scalar row loads per
-  //    quad, stored as one float4 of the transposed tile.
-  f32x4 ra[A_F4];
-  float rb[B_F1];
-  const int bn = tid & (BN - 1), bq = tid >> 7;
-  auto gload = [&](int k0) {
+  // DMA instruction n of this wave covers 8 rows R .. R + 7 (A for n < NA,
+  // B after); lane -> row R + lane / 8, slot lane % 8. R / 2 is a multiple
+  // of 4, so the swizzle of the lane's row is (4 (n & 1) + lane / 16) & 7.
+  uint32_t a_lo[2], b_lo[2];
 #pragma unroll
-    for (int i = 0; i < A_F4; ++i) {
-      const int idx = tid + NT * i;
-      ra[i] = *(const f32x4*)(Ag + (int64_t)(idx >> 3) * p.lda + k0 + (idx & 7) * 4);
-    }
-#pragma unroll
-    for (int j = 0; j < B_F1 / 4; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        rb[j * 4 + c] = Bg[(int64_t)(k0 + (bq + 2 * j) * 4 + c) * p.ldb + bn];
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_F4; ++i) {
-      const int idx = tid + NT * i;
-      *(f32x4*)&As[buf][(idx >> 3) * LDS_S + (idx & 7) * 4] = ra[i];
-    }
-#pragma unroll
-    for (int j = 0; j < B_F1 / 4; ++j) {
-      f32x4 v = {rb[j * 4 + 0], rb[j * 4 + 1], rb[j * 4 + 2], rb[j * 4 + 3]};
-      *(f32x4*)&Bs[buf][bn * LDS_S + (bq + 2 * j) * 4] = v;
+  for (int par = 0; par < 2; ++par) {
+    const int q = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+    a_lo[par] = (uint32_t)(((lane >> 3) * lda + 4 * q) * 4);
+    b_lo[par] = (uint32_t)(((lane >> 3) * ldb + 4 * q) * 4);
+  }
+  auto dma = [&](int stage, int kk, int n) {
+    float* la = lds + stage * T::SST;
+    if (n < T::NA) {
+      const int R = (T::NA * wave + n) * 8;
+      dma16((const char*)(Ag + (int64_t)R * lda + kk) + a_lo[n & 1], la + R * BK);
+    } else {
+      const int i = n - T::NA;
+      const int R = (T::NB * wave + i) * 8;
+      dma16((const char*)(Bg + (int64_t)R * ldb + kk) + b_lo[i & 1], la + T::SA + R * BK);
     }
   };
-
-  f32x16 acc[4][2];
+  // fragment offsets: row (wm TM/2 + l32) of A, row (wn 64 + l32) of B,
+  // slot (2 c + h) ^ sw of chunk c
+  const int sw = (l32 >> 1) & 7;
+  int a_rd[4], b_rd[4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int c = 0; c < 4; ++c) {
+    a_rd[c] = (wm * (TM / 2) + l32) * BK + (((2 * c + h) ^ sw) * 4);
+    b_rd[c] = T::SA + (wn * 64 + l32) * BK + (((2 * c + h) ^ sw) * 4);
+  }
+  f32x4 af[2][T::MI], bf[2][2];
+  auto frag = [&](const float* st, int c, int slot) {
+#pragma unroll
+    for (int mi = 0; mi < T::MI; ++mi) af[slot][mi] = *(const f32x4*)&st[a_rd[c] + mi * 32 * BK];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) bf[slot][ni] = *(const f32x4*)&st[b_rd[c] + ni * 32 * BK];
+  };
+#pragma unroll
+  for (int mi = 0; mi < T::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.0f;
+  if (nk <= 0) return;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  const int a_off = (wm * 128 + l32) * LDS_S + 4 * half;
-  const int b_off = (wn * 64 + l32) * LDS_S + 4 * half;
-  const int nk = p.K / BK;
+#pragma unroll
+  for (int n = 0; n < T::NA + T::NB; ++n) dma(0, k0, n);
+  // Barriers are plain s_barrier: __syncthreads() adds a release fence,
+  // which would also wait for the DMA of the next stage in flight. Each
+  // wave waits for its own DMA (vmcnt) and LDS reads (lgkmcnt) itself.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+  frag(lds, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const float* as = As[buf] + a_off;
-    const float* bs = Bs[buf] + b_off;
-    f32x4 af[2][4], bf[2][2];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) af[0][mi] = *(const f32x4*)&as[mi * 32 * LDS_S];
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) bf[0][ni] = *(const f32x4*)&bs[ni * 32 * LDS_S];
+    const int cs = kt & 1;
+    const float* st = lds + cs * T::SST;
+    const bool more = kt + 1 < nk;
+    const int knext = k0 + (kt + 1) * BK;
 #pragma unroll
     for (int c = 0; c < BK / 8; ++c) {
       const int cur = c & 1, nxt = cur ^ 1;
-      if (c + 1 < BK / 8) {
+      if (c + 1 < BK / 8) frag(st, c + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          af[nxt][mi] = *(const f32x4*)&as[mi * 32 * LDS_S + (c + 1) * 8];
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          bf[nxt][ni] = *(const f32x4*)&bs[ni * 32 * LDS_S + (c + 1) * 8];
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < T::MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 2; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[cur][mi][s], bf[cur][ni][s],
                                                                acc[mi][ni], 0, 0, 0);
+        if (s < T::DPC && more) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma(cs ^ 1, knext, T::DPC * c + s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
+    // the other stage is complete once every wave's DMA has landed; this
+    // stage may be overwritten once every wave has read its fragments
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    asm volatile("s_barrier" ::: "memory");
+    if (more) frag(lds + (cs ^ 1) * T::SST, 0, 0);
   }
+}
 
-  // Epilogue through LDS, one 32 x 32 block per wave at a time: the block is
-  // written in the MFMA accumulator layout (lane l, register v holds row
-  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32), read back row-major as
-  // float4, and combined with P / Lam by coalesced float4 accesses. This also
-  // keeps the compiler from moving all 128 accumulators and their partner
-  // loads into VGPRs at once. The tiles' LDS is free after the last barrier.
+// XCD-aware tile order: workgroup b -> tile index.
+__device__ __forceinline__ int xcd_tile(int b, int nt) {
+  return (nt % 8 == 0) ? (b % 8) * (nt / 8) + b / 8 : b;
+}
+
+// Epilogue for one 32 x 32 accumulator block through a per-wave LDS block:
+// lane l, register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32;
+// it is written in that layout, read back row-major as float4, and stored
+// with coalesced float4 accesses (ld in floats). Returns via `store(row,
+// col4, value)`.
+template <class F>
+__device__ __forceinline__ void stage_block(const f32x16& a, float* stage, F&& store) {
   constexpr int ES = 36;  // row stride of the per-wave staging block
-  float* stage = &As[0][0] + wave * 32 * ES;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, l32 = lane & 31;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int v = 0; v < 16; ++v) stage[(8 * (v >> 2) + 4 * h + (v & 3)) * ES + l32] = a[v];
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): wave-local LDS round trip
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 8 * t + (lane >> 3), c4 = (lane & 7) * 4;
+    store(r, c4, *(const f32x4*)&stage[r * ES + c4]);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
+  constexpr int TM = 256;
+  using T = Tile<TM>;
+  __shared__ __attribute__((aligned(1024))) float lds[T::LDS_FLOATS];
+  const int tilesN = p.N / TN;
+  const int t = xcd_tile(blockIdx.x, (p.M / TM) * tilesN);
+  const int tm = t / tilesN, tn = t % tilesN;
+  f32x16 acc[T::MI][2];
+  nt_mainloop<TM>(p.A + (int64_t)tm * TM * p.lda, (int)p.lda, p.B + (int64_t)tn * TN * p.ldb,
+                  (int)p.ldb, 0, p.K / BK, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int h = lane >> 5, l32 = lane & 31;
+  float* stage = lds + wave * 32 * 36;
+#pragma unroll
+  for (int mi = 0; mi < T::MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
-      __builtin_amdgcn_sched_barrier(0);
+      const int row0 = tm * TM + wm * (TM / 2) + mi * 32;
+      const int col0 = tn * TN + wn * 64 + ni * 32;
+      if (EPI == kEpiSolve && p.Ct) {
+        // C^T straight from the accumulator layout: lane l holds column
+        // col0 + l % 32, rows row0 + 8 g + 4 (l / 32) + 0..3 in v = 4 g ..
+        float* ct = p.Ct + (int64_t)(col0 + l32) * p.ldct + row0 + 4 * h;
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        stage[(8 * (v >> 2) + 4 * half + (v & 3)) * ES + l32] = acc[mi][ni][v];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): wave-local LDS round trip
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 8 * t + (lane >> 3), c4 = (lane & 7) * 4;
-        const f32x4 val = *(const f32x4*)&stage[r * ES + c4];
-        const int row = tm * BM + wm * 128 + mi * 32 + r;
-        const int col = tn * BN + wn * 64 + ni * 32 + c4;
-        const int64_t idx = (int64_t)row * p.ldc + col;
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                           acc[mi][ni][4 * g + 3]};
+          *(f32x4*)&ct[8 * g] = v;
+        }
+      }
+      stage_block(acc[mi][ni], stage, [&](int r, int c4, const f32x4& val) {
+        const int64_t idx = (int64_t)(row0 + r) * p.ldc + col0 + c4;
         if (EPI == kEpiRhs) {
           const f32x4 pv = *(const f32x4*)&p.P[idx];
           *(f32x4*)&p.C[idx] = val + p.rho * pv;
@@ -170,23 +230,78 @@ __global__ __launch_bounds__(NT) void gemm_nn_kernel(GemmArgs p) {
         } else {
           *(f32x4*)&p.C[idx] = val;
         }
-      }
-      __builtin_amdgcn_wave_barrier();
+      });
     }
 }
+
+// Partial Gram tiles: work item w = chunk * tiles + lower tile (I, J),
+// I >= J, both operands the rows I and J panels of At (rp x K).
+__global__ __launch_bounds__(NT, 2) void gram_nt_kernel(const float* __restrict__ At,
+                                                        int64_t ldat, int K, int rp, int kchunk,
+                                                        int tiles, float* __restrict__ part) {
+  constexpr int TM = 128;
+  using T = Tile<TM>;
+  __shared__ __attribute__((aligned(1024))) float lds[T::LDS_FLOATS];
+  const int nch = (K + kchunk - 1) / kchunk;
+  const int w = xcd_tile(blockIdx.x, tiles * nch);
+  const int c = w / tiles, tt = w % tiles;
+  int I = (int)((sqrtf(8.0f * tt + 1.0f) - 1.0f) * 0.5f);
+  while ((I + 1) * (I + 2) / 2 <= tt) ++I;
+  while (I * (I + 1) / 2 > tt) --I;
+  const int J = tt - I * (I + 1) / 2;
+  const int kb = c * kchunk, ke = min(K, kb + kchunk);
+  f32x16 acc[T::MI][2];
+  nt_mainloop<TM>(At + (int64_t)I * TM * ldat, (int)ldat, At + (int64_t)J * TN * ldat, (int)ldat,
+                  kb, (ke - kb) / BK, lds, acc);
+
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  float* out = part + (int64_t)c * rp * rp;
+  float* stage = lds + wave * 32 * 36;
+#pragma unroll
+  for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int row0 = I * TM + wm * (TM / 2) + mi * 32;
+      const int col0 = J * TN + wn * 64 + ni * 32;
+      stage_block(acc[mi][ni], stage, [&](int r, int c4, const f32x4& val) {
+        *(f32x4*)&out[(int64_t)(row0 + r) * rp + col0 + c4] = val;
+      });
+    }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
-  if (a.M % BM || a.N % BN || a.K % BK || a.M <= 0 || a.N <= 0 || a.K <= 0)
+  if (a.M % 256 || a.N % TN || a.K % BK || a.M <= 0 || a.N <= 0 || a.K <= 0)
     return hipErrorInvalidValue;
-  const int nt = (a.M / BM) * (a.N / BN);
+  if (a.lda % 4 || a.ldb % 4 || a.ldc % 4 || a.lda < a.K || a.ldb < a.K || a.ldc < a.N ||
+      !aligned16(a.A) || !aligned16(a.B) || !aligned16(a.C))
+    return hipErrorInvalidValue;
+  if (epi == kEpiSolve && a.Ct && (a.ldct % 4 || a.ldct < a.M || !aligned16(a.Ct)))
+    return hipErrorInvalidValue;
+  const int nt = (a.M / 256) * (a.N / TN);
   dim3 grid(nt), block(NT);
   switch (epi) {
-    case kEpiRhs: hipLaunchKernelGGL(gemm_nn_kernel<kEpiRhs>, grid, block, 0, s, a); break;
-    case kEpiSolve: hipLaunchKernelGGL(gemm_nn_kernel<kEpiSolve>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(gemm_nn_kernel<kEpiPlain>, grid, block, 0, s, a); break;
+    case kEpiRhs: hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, grid, block, 0, s, a); break;
+    case kEpiSolve: hipLaunchKernelGGL(gemm_nt_kernel<kEpiSolve>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(gemm_nt_kernel<kEpiPlain>, grid, block, 0, s, a); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, int kchunk,
+                               float* part, hipStream_t s) {
+  if (rp % 128 || K % BK || kchunk % BK || kchunk <= 0 || K <= 0 || ldat % 4 || ldat < K ||
+      !aligned16(At))
+    return hipErrorInvalidValue;
+  const int R = rp / 128;
+  const int tiles = R * (R + 1) / 2;
+  const int nch = (K + kchunk - 1) / kchunk;
+  hipLaunchKernelGGL(gram_nt_kernel, dim3(tiles * nch), dim3(NT), 0, s, At, ldat, K, rp, kchunk,
+                     tiles, part);
   return hipGetLastError();
 }
 

@@ -2,17 +2,17 @@
 //
 // One handle = one layer shape. create() allocates every workspace buffer
 // once (one device allocation, zero-padded layouts); run() only enqueues
-// kernels and never allocates. Three streams per half-iteration:
-//   caller's stream: right-hand-side GEMM, then (after the chain) the solve
-//                    GEMM;
-//   chain stream:    Gram -> Cholesky + inverse factor -> L^-T L^-1, which
-//                    depends only on the other factor, like the RHS GEMM;
-//   SVID stream:     SVID + dual update of the factor just solved, which the
-//                    next half (the other factor) does not read, so it runs
-//                    under the next half's chain and RHS GEMM.
-// Events order the shared buffers: the chain of half h+1 starts after the
-// solve of half h (it overwrites G^-1), and the RHS GEMM of a factor waits
-// for that factor's previous SVID (it reads Z - Lam).
+// kernels and never allocates. Each factor is kept twice, as U (m x r) and
+// U^T (r x m), so that every product reads its operands k-contiguous: the
+// Gram and the right-hand side read the other factor's transpose, and the
+// solve writes both. Per half-iteration (run_half):
+//   caller's stream: the Gram, then (after both of the below) the solve;
+//   chain stream:    the Cholesky + inverse, a chain of latency-bound launches;
+//   GEMM stream:     the right-hand-side GEMM, then the SVID + dual update of
+//                    the factor solved by the previous half, which this half
+//                    does not read.
+// Events order the shared buffers: both side streams start after the Gram,
+// and the solve waits for both.
 #include "nq.h"
 #include "abi.h"
 #include "common.h"
@@ -70,14 +70,23 @@ nq_status check_device(int* dev) {
   return NQ_OK;
 }
 
-// Split-K choice for the Gram kernel: enough workgroups to cover the chip,
-// chunks of at least 256 rows, at most 4 chunks.
+// Split-K choice for the Gram kernel (128 x 128 lower tiles, two workgroups
+// per CU = 512 slots): the number of chunks (at most 4, at least 256 rows
+// each) that minimises rounds of workgroups per unit of K; ties go to fewer
+// chunks, which also keeps the reduction small.
 void gram_split(int K, int rp, int* nch, int* kchunk) {
   const int R = rp / 128;
-  const int tiles = R * (R + 1) / 2;
-  int c = (512 + tiles - 1) / tiles;
-  c = std::max(1, std::min(c, std::min(4, K / 256)));
-  int kc = (int)round_up((K + c - 1) / c, 32);
+  const int64_t tiles = (int64_t)R * (R + 1) / 2;
+  int best = 1;
+  double best_cost = 1e300;
+  for (int c = 1; c <= 4 && (c == 1 || K / c >= 256); ++c) {
+    const double cost = (double)((tiles * c + 511) / 512) / c;
+    if (cost < best_cost - 1e-12) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  const int kc = (int)round_up((K + best - 1) / best, 32);
   *kchunk = kc;
   *nch = (K + kc - 1) / kc;
 }
@@ -112,7 +121,7 @@ struct nq_lbadmm {
   int gU_nch = 1, gU_kc = 32, gV_nch = 1, gV_kc = 32;
   char* base = nullptr;
   size_t bytes = 0;
-  float *Wt, *WtT, *U, *V, *LamU, *PU, *LamV, *PV, *R, *G, *Minv, *Ginv, *gpart;
+  float *Wt, *WtT, *U, *V, *UT, *VT, *LamU, *PU, *LamV, *PV, *R, *G, *Minv, *Ginv, *gpart;
   SvidWork svU, svV;
   double *part_wt, *part_w, *err_parts;
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
@@ -144,6 +153,7 @@ size_t layout(nq_lbadmm* h) {
   Arena a;
   size_t o_Wt = a.take<float>(mp * np_), o_WtT = a.take<float>(np_ * mp);
   size_t o_U = a.take<float>(mp * rp), o_V = a.take<float>(np_ * rp);
+  size_t o_UT = a.take<float>(rp * mp), o_VT = a.take<float>(rp * np_);
   size_t o_LamU = a.take<float>(mp * rp), o_PU = a.take<float>(mp * rp);
   size_t o_LamV = a.take<float>(np_ * rp), o_PV = a.take<float>(np_ * rp);
   size_t o_R = a.take<float>(mx * rp);
@@ -170,6 +180,7 @@ size_t layout(nq_lbadmm* h) {
     char* b = h->base;
     h->Wt = (float*)(b + o_Wt); h->WtT = (float*)(b + o_WtT);
     h->U = (float*)(b + o_U); h->V = (float*)(b + o_V);
+    h->UT = (float*)(b + o_UT); h->VT = (float*)(b + o_VT);
     h->LamU = (float*)(b + o_LamU); h->PU = (float*)(b + o_PU);
     h->LamV = (float*)(b + o_LamV); h->PV = (float*)(b + o_PV);
     h->R = (float*)(b + o_R);
@@ -229,8 +240,9 @@ void prof_end(nq_lbadmm* h, long p, hipStream_t s) {
 struct Half {
   const float* Wside;  // M x K (padded, ld K)
   int M, K;            // rows of the factor being solved, rows of the other factor
-  const float* other;  // K x rp
+  const float* otherT; // the other factor transposed, rp x K (ld K)
   float* out;          // M x rp
+  float* outT;         // rp x M (ld M): out transposed
   float* Lam;          // M x rp
   float* P;            // M x rp
   const SvidWork* sv;
@@ -250,38 +262,41 @@ nq_status run_svid(nq_lbadmm* h, const Half& x, hipStream_t vs) {
 //   s (the caller's stream, whole chip): the Gram G = other^T other + rho I,
 //        which heads the critical path; later the solve out = R G^-1
 //        (X = out + Lam into Lam);
-//   chain_s (a reserved group of CUs): after the Gram, the blocked Cholesky
-//        with M = L^-1 and G^-1 = M^T M, a chain of latency-bound launches;
-//   gemm_s (the other CUs): after the Gram, R = Wside other + rho (Z - Lam),
-//        then the SVID of the previous half (`pending`), which has until the
-//        next half of its own factor (later on this stream) to finish.
-// The chain runs on CUs of its own because a wave sharing a SIMD with GEMM
-// waves issues several times slower, and the chain is the critical path.
+//   chain_s: after the Gram, the blocked Cholesky with M = L^-1 and
+//        G^-1 = M^T M, a chain of latency-bound launches;
+//   gemm_s: after the Gram, R = Wside other + rho (Z - Lam), then the SVID
+//        of the previous half (`pending`), which has until the next half of
+//        its own factor (later on this stream) to finish.
+// The two streams share the CUs (optionally split by CU masks, see
+// create_streams); the chain is the critical path.
 nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t s,
                    bool overlap) {
   const int rp = h->rp;
   hipStream_t cs = overlap ? h->chain_s : s;
   hipStream_t gs = overlap ? h->gemm_s : s;
   long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
-  HIPCHK(launch_syrk_partial(x.other, rp, x.K, rp, x.g_kc, false, h->gpart, s));
+  // G = other^T other + rho I from other^T (rp x K)
+  HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.g_kc, h->gpart, s));
   HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, s));
   if (overlap) {
     HIPCHK(hipEventRecord(h->ev_gram, s));
     HIPCHK(hipStreamWaitEvent(h->chain_s, h->ev_gram, 0));
     HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
   }
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, cs));
-  prof_end(h, pc, cs);
-  if (overlap) HIPCHK(hipEventRecord(h->ev_join, cs));
   // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last
-  // SVID, earlier on the same stream
+  // SVID, earlier on the same stream. Enqueued before the chain's launches:
+  // when the host only just keeps pace with the GPU, host order is start
+  // order, and the GEMM should not wait behind ~34 chain launches.
   GemmArgs g{};
-  g.A = x.Wside; g.lda = x.K; g.B = x.other; g.ldb = rp; g.C = h->R; g.ldc = rp;
+  g.A = x.Wside; g.lda = x.K; g.B = x.otherT; g.ldb = x.K; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
   long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, gs);
   HIPCHK(launch_gemm(g, kEpiRhs, gs));
   prof_end(h, pr, gs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, cs));
+  prof_end(h, pc, cs);
+  if (overlap) HIPCHK(hipEventRecord(h->ev_join, cs));
   if (pending) {
     nq_status st = run_svid(h, *pending, gs);
     if (st != NQ_OK) return st;
@@ -290,10 +305,11 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
     HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
     HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
   }
-  // out = R G^-1, X = out + Lam (into Lam)
+  // out = R G^-1 (G^-1 symmetric, so it is its own transposed operand),
+  // X = out + Lam (into Lam), outT = out^T
   GemmArgs q{};
   q.A = h->R; q.lda = rp; q.B = h->Ginv; q.ldb = rp; q.C = x.out; q.ldc = rp;
-  q.X = x.Lam; q.M = x.M; q.N = rp; q.K = rp;
+  q.X = x.Lam; q.Ct = x.outT; q.ldct = x.M; q.M = x.M; q.N = rp; q.K = rp;
   long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
   prof_end(h, ps, s);
@@ -480,12 +496,14 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
     HIPCHK(launch_init_philox(d.seed, 0u, d.m, d.r, h->U, h->LamU, mp, rp, h->st, s));
     HIPCHK(launch_init_philox(d.seed, 1u, d.n, d.r, h->V, h->LamV, np_, rp, h->st, s));
   }
+  HIPCHK(launch_transpose(h->U, mp, rp, rp, h->UT, mp, s));
+  HIPCHK(launch_transpose(h->V, np_, rp, rp, h->VT, np_, s));
   HIPCHK(launch_svid(h->LamU, h->PU, mp, rp, (int)d.r, d.svid_steps, 0, h->svU, s));
   HIPCHK(launch_svid(h->LamV, h->PV, np_, rp, (int)d.r, d.svid_steps, 0, h->svV, s));
   prof_end(h, pp, s);
 
-  Half hu{h->Wt, mp, np_, h->V, h->U, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc, 0};
-  Half hv{h->WtT, np_, mp, h->U, h->V, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc, 1};
+  Half hu{h->Wt, mp, np_, h->VT, h->U, h->UT, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc, 0};
+  Half hv{h->WtT, np_, mp, h->UT, h->V, h->VT, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc, 1};
   const Half* pending = nullptr;
   for (int it = 0; it < d.iters; ++it) {
     nq_status st = run_half(h, hu, pending, s, overlap);

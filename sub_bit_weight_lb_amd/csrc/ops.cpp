@@ -84,12 +84,14 @@ nq_status nq_op_gram(const float* A, int64_t rows, int64_t cols, int64_t lda, fl
   int nch = std::max<int64_t>(1, std::min<int64_t>({(512 + tiles - 1) / tiles, 4, K / 256}));
   const int kc = (int)round_up((K + nch - 1) / nch, 32);
   nch = (int)((K + kc - 1) / kc);
-  DevBuf a, part, g;
+  DevBuf a, at, part, g;
   NQ_HIPCHK(a.alloc(sizeof(float) * K * rp));
+  NQ_HIPCHK(at.alloc(sizeof(float) * rp * K));
   NQ_HIPCHK(part.alloc(sizeof(float) * nch * rp * rp));
   NQ_HIPCHK(g.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(stage_in(A, rows, cols, lda, a.f(), K, rp, s));
-  NQ_HIPCHK(launch_syrk_partial(a.f(), rp, (int)K, (int)rp, kc, false, part.f(), s));
+  NQ_HIPCHK(launch_transpose(a.f(), K, rp, rp, at.f(), K, s));
+  NQ_HIPCHK(launch_gram_partial(at.f(), K, (int)K, (int)rp, kc, part.f(), s));
   NQ_HIPCHK(launch_gram_reduce(part.f(), nch, (int)rp, rho, g.f(), rp, s));
   NQ_HIPCHK(stage_out(g.f(), rp, G, ldg, cols, cols, s));
   NQ_HIPCHK(hipStreamSynchronize(s));
@@ -104,17 +106,19 @@ nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ld
     return set_error(NQ_ERR_INVALID_ARG, "bad gemm arguments");
   hipStream_t s = (hipStream_t)stream;
   const int64_t Mp = round_up(rows, 256), Np = round_up(cols, 128), Kp = round_up(k, 32);
-  DevBuf a, b, p, c;
+  DevBuf a, b, bt, p, c;
   NQ_HIPCHK(a.alloc(sizeof(float) * Mp * Kp));
   NQ_HIPCHK(b.alloc(sizeof(float) * Kp * Np));
+  NQ_HIPCHK(bt.alloc(sizeof(float) * Np * Kp));
   NQ_HIPCHK(p.alloc(sizeof(float) * Mp * Np));
   NQ_HIPCHK(c.alloc(sizeof(float) * Mp * Np));
   NQ_HIPCHK(stage_in(A, rows, k, lda, a.f(), Mp, Kp, s));
   NQ_HIPCHK(stage_in(B, k, cols, ldb, b.f(), Kp, Np, s));
+  NQ_HIPCHK(launch_transpose(b.f(), Kp, Np, Np, bt.f(), Kp, s));  // the kernel reads B^T
   if (P) NQ_HIPCHK(stage_in(P, rows, cols, ldp, p.f(), Mp, Np, s));
   else NQ_HIPCHK(launch_zero(p.f(), (size_t)(Mp * Np), s));
   GemmArgs g{};
-  g.A = a.f(); g.lda = Kp; g.B = b.f(); g.ldb = Np; g.C = c.f(); g.ldc = Np;
+  g.A = a.f(); g.lda = Kp; g.B = bt.f(); g.ldb = Kp; g.C = c.f(); g.ldc = Np;
   g.P = p.f(); g.rho = rho; g.M = (int)Mp; g.N = (int)Np; g.K = (int)Kp;
   NQ_HIPCHK(launch_gemm(g, kEpiRhs, s));
   NQ_HIPCHK(stage_out(c.f(), Np, C, ldc, rows, cols, s));

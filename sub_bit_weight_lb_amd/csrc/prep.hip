@@ -171,6 +171,21 @@ __global__ void init_philox_kernel(uint64_t seed, uint32_t stream_id, int64_t ro
   }
 }
 
+// dst (cols x rows, ld ldd) = src^T for src (rows x cols, ld lds); 32 x 32
+// tiles through LDS, rows and cols multiples of 32.
+__global__ __launch_bounds__(256) void transpose_kernel(const float* __restrict__ src,
+                                                        int64_t lds, float* __restrict__ dst,
+                                                        int64_t ldd) {
+  __shared__ float tile[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int64_t r0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) tile[ty + 8 * q][tx] = src[(r0 + ty + 8 * q) * lds + c0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dst[(c0 + ty + 8 * q) * ldd + r0 + tx] = tile[tx][ty + 8 * q];
+}
+
 __global__ void zero_kernel(float* p, size_t n) {
   for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < n;
        q += (size_t)gridDim.x * blockDim.x)
@@ -262,6 +277,16 @@ hipError_t launch_set_diag(float* A, int64_t lda, int from, int to, float val, h
   if (to <= from) return hipSuccess;
   hipLaunchKernelGGL(set_diag_kernel, dim3((to - from + 255) / 256), dim3(256), 0, s, A, lda, from,
                      to, val);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const float* src, int64_t rows, int64_t cols, int64_t lds, float* dst,
+                            int64_t ldd, hipStream_t s) {
+  if (rows % 32 || cols % 32 || rows <= 0 || cols <= 0 || lds < cols || ldd < rows ||
+      rows / 32 > 65535)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)(cols / 32), (unsigned)(rows / 32)),
+                     dim3(256), 0, s, src, lds, dst, ldd);
   return hipGetLastError();
 }
 
