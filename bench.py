@@ -201,7 +201,7 @@ def main():
         "factorised_weights_per_s": round(args.steps * m * n / elapsed, 1),
         "flops_per_iter": F,
         "roofline": {
-            "kernel": "gemm_nn_kernel<kEpiRhs> (R = Wt V + rho (Z - Lam))",
+            "kernel": "gemm_nt_kernel<kEpiRhs> (R = Wt V + rho (Z - Lam), V read as V^T)",
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": FP32_MFMA_PEAK_TFLOPS,
