@@ -592,11 +592,13 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 }  // namespace
 
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool want_L, hipStream_t s) {
+                                   DevStats* st, bool want_L, bool m_zeroed, hipStream_t s) {
   if (rp % NB) return hipErrorInvalidValue;
   const int R = rp / NB;
-  hipError_t e = launch_zero(M, (size_t)rp * rp, s);
-  if (e != hipSuccess) return e;
+  if (!m_zeroed) {
+    hipError_t e = launch_zero(M, (size_t)rp * rp, s);
+    if (e != hipSuccess) return e;
+  }
   for (int k = 0; k <= R; ++k) {
     const int n = R - 1 - k;
     int nb = k < R ? 1 + n + k : 0;  // diagonal, panel and inverse-row workgroups

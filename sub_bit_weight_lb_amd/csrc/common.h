@@ -68,11 +68,12 @@ hipError_t launch_gram_reduce(const float* part, int nchunks, int rp, float rho,
 constexpr int kNB = 64;  // block size of the blocked Cholesky
 // A (rp x rp, ld rp, full symmetric on entry) is used as workspace; with
 // want_L its lower triangle becomes L and its upper triangle zero. M (rp x rp)
-// becomes L^-1 (lower, zero upper); Ginv (rp x rp, nullable) becomes
+// becomes L^-1 (lower, zero upper); it is zeroed first unless m_zeroed (the
+// caller guarantees M is all zeros). Ginv (rp x rp, nullable) becomes
 // G^-1 = M^T M, full and exactly symmetric. st->potrf_info gets
 // min(1 + failing column).
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool want_L, hipStream_t s);
+                                   DevStats* st, bool want_L, bool m_zeroed, hipStream_t s);
 
 // ---------------------------------------------------------------- SVID
 struct SvidWork {

@@ -135,6 +135,10 @@ struct nq_lbadmm {
             ev_t0 = nullptr, ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
+  // Minv (the Cholesky's L^-1 scratch) is zero between chains: each chain
+  // zeroes it again after its last launch, beside the solve. m_dirty is set
+  // while a chain's zeroing is not yet enqueued (a run that stops early).
+  bool m_dirty = false;
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
   std::vector<hipEvent_t> prof_ev;
   std::vector<int> prof_phase;  // phase of each pending pair
@@ -294,9 +298,15 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   HIPCHK(launch_gemm(g, kEpiRhs, gs));
   prof_end(h, pr, gs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, cs));
+  h->m_dirty = true;
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, true,
+                                 cs));
   prof_end(h, pc, cs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_join, cs));
+  // Minv back to zero for the next chain, off the critical path (the solve
+  // below reads only G^-1)
+  HIPCHK(launch_zero(h->Minv, (size_t)rp * rp, cs));
+  h->m_dirty = false;
   if (pending) {
     nq_status st = run_svid(h, *pending, gs);
     if (st != NQ_OK) return st;
@@ -480,6 +490,10 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
     if (ps != NQ_OK) return ps;
   }
   HIPCHK(hipEventRecord(h->ev_t0, s));
+  if (h->m_dirty) {
+    HIPCHK(launch_zero(h->Minv, (size_t)rp * rp, s));
+    h->m_dirty = false;
+  }
   long pp = prof_begin(h, NQ_PHASE_PREP, s);
   HIPCHK(launch_stats_init(h->st, s));
   HIPCHK(launch_check_precond(d_out, d.m, d_in, d.n, h->st, s));

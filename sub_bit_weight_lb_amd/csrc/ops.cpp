@@ -143,7 +143,7 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
   NQ_HIPCHK(stage_in(G, r, r, ldg, a.f(), rp, rp, s));
   NQ_HIPCHK(launch_set_diag(a.f(), rp, (int)r, (int)rp, 1.0f, s));
   NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), Ginv ? gi.f() : nullptr, (int)rp, (int)r, dst,
-                                    true, s));
+                                    true, false, s));
   if (Ginv) NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));
   if (L) NQ_HIPCHK(stage_out(a.f(), rp, L, ldl, r, r, s));
   DevStats hs;
