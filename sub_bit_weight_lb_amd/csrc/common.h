@@ -54,14 +54,21 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 
 // ---------------------------------------------------------------- Gram
+// Work split of G = A^T A (lower 128 x 128 tiles, tiles x K / 32 steps of 32)
+// into equal ranges of `steps` steps, one per workgroup (`wgs` of them); a
+// tile's segments go to at most `slots` partial buffers of rp x rp.
+struct GramPlan {
+  int steps, wgs, slots;
+};
+GramPlan gram_plan(int K, int rp);
 // Partial Gram tiles of A^T A for A (K x rp) given as At = A^T (rp x K, ld
-// ldat): part[c] (rp x rp, ld rp) holds, in its lower 128 x 128 tiles only,
-// the sum over k in [c*kchunk, (c+1)*kchunk). rp % 128 == 0, K and kchunk
-// multiples of 32.
-hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, int kchunk,
+// ldat) into part (p.slots buffers of rp x rp, ld rp; lower tiles only).
+// rp % 128 == 0, K a multiple of 32.
+hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, const GramPlan& p,
                                float* part, hipStream_t s);
-// G = sum_c part[c] + rho I, written full-symmetric (ld ldg).
-hipError_t launch_gram_reduce(const float* part, int nchunks, int rp, float rho,
+// G = the sum of each lower tile's segments, in slot order, + rho I, written
+// full-symmetric (ld ldg).
+hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
                               float* G, int64_t ldg, hipStream_t s);
 
 // ---------------------------------------------------------------- Cholesky / inverse

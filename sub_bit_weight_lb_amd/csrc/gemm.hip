@@ -30,6 +30,8 @@
 //   L2.
 #include "common.h"
 
+#include <algorithm>
+
 namespace nq {
 namespace {
 
@@ -234,40 +236,54 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
     }
 }
 
-// Partial Gram tiles: work item w = chunk * tiles + lower tile (I, J),
-// I >= J, both operands the rows I and J panels of At (rp x K).
+// Partial Gram tiles, stream-K: the tiles x T K steps of 32 (lower tile t =
+// I (I + 1) / 2 + J, I >= J, both operands the rows I and J panels of At)
+// are cut into ranges of L steps, one per workgroup, so every workgroup has
+// the same work. A range covers the end of one tile and the start of the
+// next; each segment goes to slot w - w0(t) of its tile, w0(t) = t T / L
+// being the first workgroup that touches tile t.
 __global__ __launch_bounds__(NT, 2) void gram_nt_kernel(const float* __restrict__ At,
-                                                        int64_t ldat, int K, int rp, int kchunk,
-                                                        int tiles, float* __restrict__ part) {
+                                                        int64_t ldat, int rp, int T, int L,
+                                                        int64_t S, int W,
+                                                        float* __restrict__ part) {
   constexpr int TM = 128;
-  using T = Tile<TM>;
-  __shared__ __attribute__((aligned(1024))) float lds[T::LDS_FLOATS];
-  const int nch = (K + kchunk - 1) / kchunk;
-  const int w = xcd_tile(blockIdx.x, tiles * nch);
-  const int c = w / tiles, tt = w % tiles;
-  int I = (int)((sqrtf(8.0f * tt + 1.0f) - 1.0f) * 0.5f);
-  while ((I + 1) * (I + 2) / 2 <= tt) ++I;
-  while (I * (I + 1) / 2 > tt) --I;
-  const int J = tt - I * (I + 1) / 2;
-  const int kb = c * kchunk, ke = min(K, kb + kchunk);
-  f32x16 acc[T::MI][2];
-  nt_mainloop<TM>(At + (int64_t)I * TM * ldat, (int)ldat, At + (int64_t)J * TN * ldat, (int)ldat,
-                  kb, (ke - kb) / BK, lds, acc);
-
+  using T_ = Tile<TM>;
+  __shared__ __attribute__((aligned(1024))) float lds[T_::LDS_FLOATS];
+  const int w = xcd_tile(blockIdx.x, W);
+  int64_t s0 = (int64_t)w * L;
+  const int64_t s1 = min(S, s0 + L);
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  float* out = part + (int64_t)c * rp * rp;
   float* stage = lds + wave * 32 * 36;
+  while (s0 < s1) {
+    const int t = (int)(s0 / T), ks = (int)(s0 % T);
+    const int ke = (int)min<int64_t>(T, ks + (s1 - s0));
+    int I = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while ((I + 1) * (I + 2) / 2 <= t) ++I;
+    while (I * (I + 1) / 2 > t) --I;
+    const int J = t - I * (I + 1) / 2;
+    const int slot = w - (int)((int64_t)t * T / L);
+    f32x16 acc[T_::MI][2];
+    nt_mainloop<TM>(At + (int64_t)I * TM * ldat, (int)ldat, At + (int64_t)J * TN * ldat,
+                    (int)ldat, ks * BK, ke - ks, lds, acc);
+    float* out = part + (int64_t)slot * rp * rp;
 #pragma unroll
-  for (int mi = 0; mi < T::MI; ++mi)
+    for (int mi = 0; mi < T_::MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int row0 = I * TM + wm * (TM / 2) + mi * 32;
-      const int col0 = J * TN + wn * 64 + ni * 32;
-      stage_block(acc[mi][ni], stage, [&](int r, int c4, const f32x4& val) {
-        *(f32x4*)&out[(int64_t)(row0 + r) * rp + col0 + c4] = val;
-      });
+      for (int ni = 0; ni < 2; ++ni) {
+        const int row0 = I * TM + wm * (TM / 2) + mi * 32;
+        const int col0 = J * TN + wn * 64 + ni * 32;
+        stage_block(acc[mi][ni], stage, [&](int r, int c4, const f32x4& val) {
+          *(f32x4*)&out[(int64_t)(row0 + r) * rp + col0 + c4] = val;
+        });
+      }
+    s0 += ke - ks;
+    if (s0 < s1) {
+      // the next segment's DMA overwrites the LDS this epilogue staged in
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("s_barrier" ::: "memory");
     }
+  }
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -292,16 +308,29 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, int kchunk,
+GramPlan gram_plan(int K, int rp) {
+  GramPlan p{};
+  const int R = rp / 128;
+  const int64_t tiles = (int64_t)R * (R + 1) / 2;
+  const int T = K / BK;
+  const int64_t S = tiles * T;
+  // two workgroups per CU; a tile gets at most 8 segments
+  int64_t L = std::max<int64_t>((S + 511) / 512, (T + 6) / 7);
+  L = std::max<int64_t>(L, 1);
+  p.steps = (int)L;
+  p.wgs = (int)((S + L - 1) / L);
+  p.slots = (int)((T + L - 1) / L) + 1;
+  return p;
+}
+
+hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, const GramPlan& p,
                                float* part, hipStream_t s) {
-  if (rp % 128 || K % BK || kchunk % BK || kchunk <= 0 || K <= 0 || ldat % 4 || ldat < K ||
-      !aligned16(At))
+  if (rp % 128 || K % BK || K <= 0 || ldat % 4 || ldat < K || !aligned16(At) || p.steps <= 0)
     return hipErrorInvalidValue;
   const int R = rp / 128;
-  const int tiles = R * (R + 1) / 2;
-  const int nch = (K + kchunk - 1) / kchunk;
-  hipLaunchKernelGGL(gram_nt_kernel, dim3(tiles * nch), dim3(NT), 0, s, At, ldat, K, rp, kchunk,
-                     tiles, part);
+  const int64_t S = (int64_t)R * (R + 1) / 2 * (K / BK);
+  hipLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, At, ldat, rp, K / BK, p.steps,
+                     S, p.wgs, part);
   return hipGetLastError();
 }
 

@@ -70,27 +70,6 @@ nq_status check_device(int* dev) {
   return NQ_OK;
 }
 
-// Split-K choice for the Gram kernel (128 x 128 lower tiles, two workgroups
-// per CU = 512 slots): the number of chunks (at most 4, at least 256 rows
-// each) that minimises rounds of workgroups per unit of K; ties go to fewer
-// chunks, which also keeps the reduction small.
-void gram_split(int K, int rp, int* nch, int* kchunk) {
-  const int R = rp / 128;
-  const int64_t tiles = (int64_t)R * (R + 1) / 2;
-  int best = 1;
-  double best_cost = 1e300;
-  for (int c = 1; c <= 4 && (c == 1 || K / c >= 256); ++c) {
-    const double cost = (double)((tiles * c + 511) / 512) / c;
-    if (cost < best_cost - 1e-12) {
-      best_cost = cost;
-      best = c;
-    }
-  }
-  const int kc = (int)round_up((K + best - 1) / best, 32);
-  *kchunk = kc;
-  *nch = (K + kc - 1) / kc;
-}
-
 struct Arena {
   size_t off = 0;
   template <class T>
@@ -118,7 +97,7 @@ struct nq_lbadmm {
   nq_lbadmm_desc d{};
   int device = 0;
   int mp = 0, np_ = 0, rp = 0;
-  int gU_nch = 1, gU_kc = 32, gV_nch = 1, gV_kc = 32;
+  GramPlan gU{}, gV{};  // Gram work splits of the U-half (K = n) and V-half (K = m)
   char* base = nullptr;
   size_t bytes = 0;
   float *Wt, *WtT, *U, *V, *UT, *VT, *LamU, *PU, *LamV, *PV, *R, *G, *Minv, *Ginv, *gpart;
@@ -153,7 +132,7 @@ namespace {
 size_t layout(nq_lbadmm* h) {
   const int64_t mp = h->mp, np_ = h->np_, rp = h->rp;
   const int64_t mx = std::max(mp, np_);
-  const int gch = std::max(h->gU_nch, h->gV_nch);
+  const int gch = std::max(h->gU.slots, h->gV.slots);
   Arena a;
   size_t o_Wt = a.take<float>(mp * np_), o_WtT = a.take<float>(np_ * mp);
   size_t o_U = a.take<float>(mp * rp), o_V = a.take<float>(np_ * rp);
@@ -209,8 +188,8 @@ void plan(nq_lbadmm* h) {
   h->mp = (int)round_up(h->d.m, kPadMN);
   h->np_ = (int)round_up(h->d.n, kPadMN);
   h->rp = (int)round_up(h->d.r, kPadR);
-  gram_split(h->np_, h->rp, &h->gU_nch, &h->gU_kc);  // U-half: Gram of V, K = n
-  gram_split(h->mp, h->rp, &h->gV_nch, &h->gV_kc);   // V-half: Gram of U, K = m
+  h->gU = gram_plan(h->np_, h->rp);  // U-half: Gram of V, K = n
+  h->gV = gram_plan(h->mp, h->rp);   // V-half: Gram of U, K = m
 }
 
 size_t pairs_per_run(const nq_lbadmm* h) { return 4 + (size_t)h->d.iters * 8; }
@@ -250,7 +229,7 @@ struct Half {
   float* Lam;          // M x rp
   float* P;            // M x rp
   const SvidWork* sv;
-  int g_nch, g_kc;
+  GramPlan gp;
   int factor;  // 0 = U, 1 = V
 };
 
@@ -280,8 +259,8 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   hipStream_t gs = overlap ? h->gemm_s : s;
   long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
   // G = other^T other + rho I from other^T (rp x K)
-  HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.g_kc, h->gpart, s));
-  HIPCHK(launch_gram_reduce(h->gpart, x.g_nch, rp, h->d.rho, h->G, rp, s));
+  HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s));
+  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, h->G, rp, s));
   if (overlap) {
     HIPCHK(hipEventRecord(h->ev_gram, s));
     HIPCHK(hipStreamWaitEvent(h->chain_s, h->ev_gram, 0));
@@ -516,8 +495,8 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   HIPCHK(launch_svid(h->LamV, h->PV, np_, rp, (int)d.r, d.svid_steps, 0, h->svV, s));
   prof_end(h, pp, s);
 
-  Half hu{h->Wt, mp, np_, h->VT, h->U, h->UT, h->LamU, h->PU, &h->svU, h->gU_nch, h->gU_kc, 0};
-  Half hv{h->WtT, np_, mp, h->UT, h->V, h->VT, h->LamV, h->PV, &h->svV, h->gV_nch, h->gV_kc, 1};
+  Half hu{h->Wt, mp, np_, h->VT, h->U, h->UT, h->LamU, h->PU, &h->svU, h->gU, 0};
+  Half hv{h->WtT, np_, mp, h->UT, h->V, h->VT, h->LamV, h->PV, &h->svV, h->gV, 1};
   const Half* pending = nullptr;
   for (int it = 0; it < d.iters; ++it) {
     nq_status st = run_half(h, hu, pending, s, overlap);

@@ -79,20 +79,16 @@ nq_status nq_op_gram(const float* A, int64_t rows, int64_t cols, int64_t lda, fl
     return set_error(NQ_ERR_INVALID_ARG, "bad gram arguments");
   hipStream_t s = (hipStream_t)stream;
   const int64_t K = round_up(rows, 32), rp = round_up(cols, 128);
-  const int R = (int)(rp / 128);
-  const int tiles = R * (R + 1) / 2;
-  int nch = std::max<int64_t>(1, std::min<int64_t>({(512 + tiles - 1) / tiles, 4, K / 256}));
-  const int kc = (int)round_up((K + nch - 1) / nch, 32);
-  nch = (int)((K + kc - 1) / kc);
+  const GramPlan plan = gram_plan((int)K, (int)rp);
   DevBuf a, at, part, g;
   NQ_HIPCHK(a.alloc(sizeof(float) * K * rp));
   NQ_HIPCHK(at.alloc(sizeof(float) * rp * K));
-  NQ_HIPCHK(part.alloc(sizeof(float) * nch * rp * rp));
+  NQ_HIPCHK(part.alloc(sizeof(float) * plan.slots * rp * rp));
   NQ_HIPCHK(g.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(stage_in(A, rows, cols, lda, a.f(), K, rp, s));
   NQ_HIPCHK(launch_transpose(a.f(), K, rp, rp, at.f(), K, s));
-  NQ_HIPCHK(launch_gram_partial(at.f(), K, (int)K, (int)rp, kc, part.f(), s));
-  NQ_HIPCHK(launch_gram_reduce(part.f(), nch, (int)rp, rho, g.f(), rp, s));
+  NQ_HIPCHK(launch_gram_partial(at.f(), K, (int)K, (int)rp, plan, part.f(), s));
+  NQ_HIPCHK(launch_gram_reduce(part.f(), (int)K, (int)rp, plan, rho, g.f(), rp, s));
   NQ_HIPCHK(stage_out(g.f(), rp, G, ldg, cols, cols, s));
   NQ_HIPCHK(hipStreamSynchronize(s));
   return NQ_OK;

@@ -1,4 +1,4 @@
-// Gram reduction: G = sum over K chunks of the partial Gram tiles + rho I,
+// Gram reduction: G = sum of each tile's K segments (stream-K partials) + rho I,
 // the system matrix V^T V + rho I of the regularised solve (NanoQuant
 // digest, section 核心方法 step (a)). The partial tiles (lower triangle only)
 // come from gram_nt_kernel in gemm.hip; they are summed in a fixed order,
@@ -11,8 +11,8 @@ namespace {
 // Full symmetric G from the lower triangles of the partial tiles.
 // 32 x 32 output tiles, 32 x 8 threads; upper tiles read the mirrored lower
 // tile and transpose it through LDS; diagonal tiles pick per element.
-__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part,
-                                                          int nchunks, int rp, float rho,
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int T,
+                                                          int L, int rp, float rho,
                                                           float* __restrict__ G, int64_t ldg) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ float tile[32][33];
@@ -21,12 +21,16 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
   const int64_t stride = (int64_t)rp * rp;
   const int si = ti >= tj ? ti : tj;  // source tile (lower triangle)
   const int sj = ti >= tj ? tj : ti;
+  // segments of the 128 x 128 Gram tile holding it: workgroups w0 .. w1
+  const int I = si / 4, J = sj / 4;
+  const int64_t t = (int64_t)I * (I + 1) / 2 + J;
+  const int nseg = (int)(((t + 1) * T - 1) / L - t * T / L) + 1;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = ty + 8 * q;
     const int64_t src = (int64_t)(si * 32 + r) * rp + sj * 32 + tx;
     float acc = 0.0f;
-    for (int c = 0; c < nchunks; ++c) acc += part[c * stride + src];
+    for (int c = 0; c < nseg; ++c) acc += part[c * stride + src];
     tile[r][tx] = acc;
   }
   __syncthreads();
@@ -45,11 +49,12 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_gram_reduce(const float* part, int nchunks, int rp, float rho, float* G,
-                              int64_t ldg, hipStream_t s) {
-  if (rp % 32) return hipErrorInvalidValue;
+hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
+                              float* G, int64_t ldg, hipStream_t s) {
+  if (rp % 128 || K % 32 || p.steps <= 0) return hipErrorInvalidValue;
   dim3 grid(rp / 32, rp / 32), block(256);
-  hipLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, part, nchunks, rp, rho, G, ldg);
+  hipLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, part, K / 32, p.steps, rp, rho, G,
+                     ldg);
   return hipGetLastError();
 }
 
