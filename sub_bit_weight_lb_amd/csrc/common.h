@@ -66,10 +66,11 @@ GramPlan gram_plan(int K, int rp);
 // rp % 128 == 0, K a multiple of 32.
 hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, const GramPlan& p,
                                float* part, hipStream_t s);
-// G = the sum of each lower tile's segments, in slot order, + rho I, written
-// full-symmetric (ld ldg).
+// G = the sum of each lower tile's segments, in slot order, + rho I (ld ldg):
+// full-symmetric if `full`, else the lower triangle and the whole of each
+// 64 x 64 diagonal block (what the blocked Cholesky reads).
 hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
-                              float* G, int64_t ldg, hipStream_t s);
+                              bool full, float* G, int64_t ldg, hipStream_t s);
 
 // ---------------------------------------------------------------- Cholesky / inverse
 constexpr int kNB = 64;  // block size of the blocked Cholesky

@@ -260,7 +260,7 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
   // G = other^T other + rho I from other^T (rp x K)
   HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s));
-  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, h->G, rp, s));
+  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, false, h->G, rp, s));
   if (overlap) {
     HIPCHK(hipEventRecord(h->ev_gram, s));
     HIPCHK(hipStreamWaitEvent(h->chain_s, h->ev_gram, 0));

@@ -88,7 +88,7 @@ nq_status nq_op_gram(const float* A, int64_t rows, int64_t cols, int64_t lda, fl
   NQ_HIPCHK(stage_in(A, rows, cols, lda, a.f(), K, rp, s));
   NQ_HIPCHK(launch_transpose(a.f(), K, rp, rp, at.f(), K, s));
   NQ_HIPCHK(launch_gram_partial(at.f(), K, (int)K, (int)rp, plan, part.f(), s));
-  NQ_HIPCHK(launch_gram_reduce(part.f(), (int)K, (int)rp, plan, rho, g.f(), rp, s));
+  NQ_HIPCHK(launch_gram_reduce(part.f(), (int)K, (int)rp, plan, rho, true, g.f(), rp, s));
   NQ_HIPCHK(stage_out(g.f(), rp, G, ldg, cols, cols, s));
   NQ_HIPCHK(hipStreamSynchronize(s));
   return NQ_OK;

@@ -12,11 +12,14 @@ namespace {
 // 32 x 32 output tiles, 32 x 8 threads; upper tiles read the mirrored lower
 // tile and transpose it through LDS; diagonal tiles pick per element.
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int T,
-                                                          int L, int rp, float rho,
+                                                          int L, int rp, float rho, int full,
                                                           float* __restrict__ G, int64_t ldg) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ float tile[32][33];
   const int ti = blockIdx.y, tj = blockIdx.x;
+  // without `full`, only what the blocked Cholesky reads: the lower triangle
+  // and the whole of each 64 x 64 diagonal block
+  if (!full && ti < tj && (ti >> 1) != (tj >> 1)) return;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int64_t stride = (int64_t)rp * rp;
   const int si = ti >= tj ? ti : tj;  // source tile (lower triangle)
@@ -50,11 +53,11 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 }  // namespace
 
 hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
-                              float* G, int64_t ldg, hipStream_t s) {
+                              bool full, float* G, int64_t ldg, hipStream_t s) {
   if (rp % 128 || K % 32 || p.steps <= 0) return hipErrorInvalidValue;
   dim3 grid(rp / 32, rp / 32), block(256);
-  hipLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, part, K / 32, p.steps, rp, rho, G,
-                     ldg);
+  hipLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, part, K / 32, p.steps, rp, rho,
+                     full ? 1 : 0, G, ldg);
   return hipGetLastError();
 }
 
