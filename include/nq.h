@@ -68,6 +68,9 @@ typedef enum nq_status {
                                        on `stream` after the right-hand-side GEMM        */
 #define NQ_FLAG_PROFILE       0x10u /* record HIP events around each phase of every run
                                        (see nq_lbadmm_profile)                           */
+#define NQ_FLAG_PROFILE_RHS_ONLY 0x20u /* with NQ_FLAG_PROFILE: time only
+                                       NQ_PHASE_GEMM_RHS (each event pair costs a little
+                                       device time; the other phases get none)           */
 
 /* Phases timed under NQ_FLAG_PROFILE. */
 typedef enum nq_phase {

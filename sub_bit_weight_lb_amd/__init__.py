@@ -20,7 +20,8 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE,  # noqa: F401
-                   NQ_FLAG_PROFILE, NQ_FLAG_SINGLE_STREAM, NQ_OK, PHASES, Desc, Stats)
+                   NQ_FLAG_PROFILE, NQ_FLAG_PROFILE_RHS_ONLY, NQ_FLAG_SINGLE_STREAM, NQ_OK,
+                   PHASES, Desc, Stats)
 
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
@@ -253,8 +254,10 @@ class LBADMM:
 
     def __init__(self, m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0, compute_error=True,
                  init_exact=False, balance=True, single_stream=False, profile=False):
+        """profile: False, True (every phase) or "rhs" (only the RHS GEMM)."""
         flags = 0
         flags |= NQ_FLAG_PROFILE if profile else 0
+        flags |= NQ_FLAG_PROFILE_RHS_ONLY if profile == "rhs" else 0
         flags |= NQ_FLAG_COMPUTE_ERROR if compute_error else 0
         flags |= NQ_FLAG_INIT_EXACT if init_exact else 0
         flags |= 0 if balance else NQ_FLAG_NO_BALANCE

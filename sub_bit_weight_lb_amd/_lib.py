@@ -21,6 +21,7 @@ NQ_FLAG_INIT_EXACT = 0x2
 NQ_FLAG_NO_BALANCE = 0x4
 NQ_FLAG_SINGLE_STREAM = 0x8
 NQ_FLAG_PROFILE = 0x10
+NQ_FLAG_PROFILE_RHS_ONLY = 0x20
 
 PHASES = ["gemm_rhs", "gemm_solve", "chain", "svid", "prep", "finish"]
 

@@ -36,7 +36,8 @@ nq_status hip_fail(hipError_t e, const char* what) { return hip_error(e, what); 
 #define HIPCHK(expr) NQ_HIPCHK(expr)
 
 constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
-                                  NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE;
+                                  NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE |
+                                  NQ_FLAG_PROFILE_RHS_ONLY;
 constexpr int kProfileRuns = 8;
 // CUs reserved for the Cholesky chain while the RHS GEMM runs on the rest.
 constexpr int kChainCUs = 0;
@@ -211,6 +212,7 @@ nq_status prof_harvest(nq_lbadmm* h) {
 // Start / end of a timed interval: returns the pair index (or -1 when off).
 long prof_begin(nq_lbadmm* h, int phase, hipStream_t s) {
   if (!(h->d.flags & NQ_FLAG_PROFILE)) return -1;
+  if ((h->d.flags & NQ_FLAG_PROFILE_RHS_ONLY) && phase != NQ_PHASE_GEMM_RHS) return -1;
   const size_t p = h->prof_next++;
   h->prof_phase[p] = phase;
   if (hipEventRecord(h->prof_ev[2 * p], s) != hipSuccess) return -1;
@@ -286,10 +288,6 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   // below reads only G^-1)
   HIPCHK(launch_zero(h->Minv, (size_t)rp * rp, cs));
   h->m_dirty = false;
-  if (pending) {
-    nq_status st = run_svid(h, *pending, gs);
-    if (st != NQ_OK) return st;
-  }
   if (overlap) {
     HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
     HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
@@ -302,6 +300,14 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
   prof_end(h, ps, s);
+  // The SVID of the previous half, on the GEMM stream after this half's RHS
+  // GEMM (stream order), where it runs beside the chain. Enqueued last: when
+  // the host only just keeps pace, the solve must not wait for its ~17
+  // launches to be submitted.
+  if (pending) {
+    nq_status st = run_svid(h, *pending, overlap ? gs : s);
+    if (st != NQ_OK) return st;
+  }
   return NQ_OK;
 }
 

@@ -138,3 +138,23 @@ def test_bad_inputs_reported(gpu):
     d[7] = 0.0
     with pytest.raises(nq.NQError, match="BAD_PRECONDITIONER"):
         run_gpu(type("L", (), dict(W=L.W, d_out=L.d_out, d_in=d, EU=L.EU, EV=L.EV)), 8, 1, gpu)
+
+
+@pytest.mark.parametrize("profile", [True, "rhs"])
+def test_profile_phases(gpu, profile):
+    """Every phase is timed with profile=True; with profile="rhs" only the
+    RHS GEMM (one interval per half-iteration). Results do not depend on it."""
+    import sub_bit_weight_lb_amd as nq
+    L = make_tiny(300, 260, 70, seed=4, iters=3)
+    h = nq.LBADMM(300, 260, 70, iters=3, profile=profile)
+    res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+    prof = h.profile(reset=True)
+    h.close()
+    assert prof["gemm_rhs"][1] == 2 * 3 and prof["gemm_rhs"][0] > 0.0
+    others = ("gemm_solve", "chain", "svid", "prep", "finish")
+    if profile == "rhs":
+        assert all(prof[p][1] == 0 for p in others)
+    else:
+        assert all(prof[p][1] > 0 for p in others)
+    plain, _ = run_gpu(L, 70, 3, gpu)
+    np.testing.assert_array_equal(H(res.U), H(plain.U))
