@@ -21,7 +21,8 @@
 // the same 64 x 64 factorisation, and no launch is spent on the diagonal
 // alone. The identity  sum_{l = j..i} L_il M_lj = delta_ij  gives
 // M_ij = -M_ii sum_{l = j..i-1} L_il M_lj; the partial sums S_ij are kept in
-// M's own tiles until row i of M is formed. No workgroup reads a tile that
+// M's own tiles until row i of M is formed, the first term (l = j) stored
+// rather than added, so M needs no zeroing beforehand. No workgroup reads a tile that
 // another workgroup of the same launch writes; every dependency crosses a
 // launch boundary.
 // Diagonal tiles: one wave, 2 x 2 blocks of 32: two in-register
@@ -390,10 +391,11 @@ struct SideJob {
   int rp;
   float sign;
   bool active;
+  bool first;  // out holds no earlier contribution: it is overwritten
 };
 template <bool TB>
 __device__ __forceinline__ void side_quad(const SideJob& j, int qm, int qn) {
-  const f32x16 prev = load_quad(j.out, j.rp, qm, qn);
+  const f32x16 prev = j.first ? zero16() : load_quad(j.out, j.rp, qm, qn);
   const f32x16 acc = mm_quad<false, TB>(j.X, j.rp, j.Y, j.rp, qm, qn);
   store_quad(acc, prev, j.out, j.rp, j.sign, qm, qn);
 }
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   if (k < R) {
     if (b == 0) {  // M_kk
       diag_step<false, false, true>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm,
-                                    SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false});
+                                    SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
       return;
     }
     b -= 1;
@@ -510,7 +512,8 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
       float* Aik = A + i0 * rp + kk;
       // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
       diag_step<true, false, true>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
-                                   SideJob{Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f, k > 0});
+                                   SideJob{Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f, k > 0,
+                                           false});
       const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
       __syncthreads();  // every wave has read its operands before any overwrite
       store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
@@ -520,10 +523,12 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     if (b < k) {  // inverse-row tile (k, j)
       const int64_t j0 = (int64_t)b * NB;
       float* Mkj = M + kk * rp + j0;
-      // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation
+      // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation; for j = k-1
+      // this is the only term, so the tile is overwritten
       diag_step<true, false, false>(
           A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
-          SideJob{A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f, true});
+          SideJob{A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f, true,
+                  b == k - 1});
       const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
       __syncthreads();
       store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
@@ -537,7 +542,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   if (want_L) {
     if (b == 0) {  // L_pp
       diag_step<false, true, true>(A, rp, p, nullptr, A + pp * rp + pp, r_real, nullptr, sm,
-                                   SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false});
+                                   SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
       return;
     }
     b -= 1;
@@ -565,8 +570,10 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   for (t -= nT; t < nS; t += upd_blocks) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
     int ld = rp;
     asm volatile("" : "+s"(ld));
-    const int64_t i0 = (int64_t)(k + 1 + t / k) * NB, j0 = (int64_t)(t % k) * NB;
-    const f32x16 prev = load_quad(M + i0 * ld + j0, ld, qm, qn);
+    const int jt = t % k;
+    const int64_t i0 = (int64_t)(k + 1 + t / k) * NB, j0 = (int64_t)jt * NB;
+    // S_ij's first term is the one of step p = j
+    const f32x16 prev = jt == p ? zero16() : load_quad(M + i0 * ld + j0, ld, qm, qn);
     const f32x16 acc = mm_quad<false, false>(A + i0 * ld + pp, ld, M + pp * ld + j0, ld, qm, qn);
     store_quad(acc, prev, M + i0 * ld + j0, ld, 1.0f, qm, qn);
   }
@@ -592,10 +599,10 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 }  // namespace
 
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool want_L, bool m_zeroed, hipStream_t s) {
+                                   DevStats* st, bool want_L, bool zero_m, hipStream_t s) {
   if (rp % NB) return hipErrorInvalidValue;
   const int R = rp / NB;
-  if (!m_zeroed) {
+  if (zero_m) {
     hipError_t e = launch_zero(M, (size_t)rp * rp, s);
     if (e != hipSuccess) return e;
   }

@@ -68,20 +68,23 @@ hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, con
                                float* part, hipStream_t s);
 // G = the sum of each lower tile's segments, in slot order, + rho I (ld ldg):
 // full-symmetric if `full`, else the lower triangle and the whole of each
-// 64 x 64 diagonal block (what the blocked Cholesky reads).
+// 64 x 64 diagonal block (what the blocked Cholesky reads). `done`
+// (nullable) is recorded when the kernel completes.
 hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
-                              bool full, float* G, int64_t ldg, hipStream_t s);
+                              bool full, float* G, int64_t ldg, hipStream_t s,
+                              hipEvent_t done = nullptr);
 
 // ---------------------------------------------------------------- Cholesky / inverse
 constexpr int kNB = 64;  // block size of the blocked Cholesky
 // A (rp x rp, ld rp, full symmetric on entry) is used as workspace; with
-// want_L its lower triangle becomes L and its upper triangle zero. M (rp x rp)
-// becomes L^-1 (lower, zero upper); it is zeroed first unless m_zeroed (the
-// caller guarantees M is all zeros). Ginv (rp x rp, nullable) becomes
-// G^-1 = M^T M, full and exactly symmetric. st->potrf_info gets
-// min(1 + failing column).
+// want_L its lower triangle becomes L and its upper triangle zero. The lower
+// 64 x 64 tiles of M (rp x rp) become those of L^-1 (the diagonal tiles with
+// zeros above their diagonal); M's other tiles are not written, and with
+// zero_m M is zeroed first so that they read as zero. Ginv (rp x rp,
+// nullable) becomes G^-1 = M^T M, full and exactly symmetric.
+// st->potrf_info gets min(1 + failing column).
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool want_L, bool m_zeroed, hipStream_t s);
+                                   DevStats* st, bool want_L, bool zero_m, hipStream_t s);
 
 // ---------------------------------------------------------------- SVID
 struct SvidWork {

@@ -6,13 +6,14 @@
 // U^T (r x m), so that every product reads its operands k-contiguous: the
 // Gram and the right-hand side read the other factor's transpose, and the
 // solve writes both. Per half-iteration (run_half):
-//   caller's stream: the Gram, then (after both of the below) the solve;
-//   chain stream:    the Cholesky + inverse, a chain of latency-bound launches;
+//   caller's stream: the Gram, the Cholesky + inverse (a chain of
+//                    latency-bound launches), then the solve;
 //   GEMM stream:     the right-hand-side GEMM, then the SVID + dual update of
 //                    the factor solved by the previous half, which this half
 //                    does not read.
-// Events order the shared buffers: both side streams start after the Gram,
-// and the solve waits for both.
+// Events order the shared buffers: the GEMM stream starts after the Gram,
+// and the solve waits for the right-hand side. The critical path (Gram,
+// chain, solve) stays on one stream, with no event between its kernels.
 #include "nq.h"
 #include "abi.h"
 #include "common.h"
@@ -39,8 +40,6 @@ constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
                                   NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE |
                                   NQ_FLAG_PROFILE_RHS_ONLY;
 constexpr int kProfileRuns = 8;
-// CUs reserved for the Cholesky chain while the RHS GEMM runs on the rest.
-constexpr int kChainCUs = 0;
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
@@ -107,18 +106,13 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
-  // chain_s: the Cholesky, on a reserved group of CUs; gemm_s: the RHS GEMM
-  // and the SVIDs, on the other CUs (see run_half)
-  hipStream_t chain_s = nullptr, gemm_s = nullptr;
-  int chain_cus = 0;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr, ev_gram = nullptr, ev_rhs = nullptr,
-            ev_t0 = nullptr, ev_t1 = nullptr;
+  // gemm_s: the RHS GEMM and the SVIDs, beside the caller's stream (see
+  // run_half)
+  hipStream_t gemm_s = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_gram = nullptr, ev_rhs = nullptr, ev_t0 = nullptr,
+            ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
-  // Minv (the Cholesky's L^-1 scratch) is zero between chains: each chain
-  // zeroes it again after its last launch, beside the solve. m_dirty is set
-  // while a chain's zeroing is not yet enqueued (a run that stops early).
-  bool m_dirty = false;
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
   std::vector<hipEvent_t> prof_ev;
   std::vector<int> prof_phase;  // phase of each pending pair
@@ -244,30 +238,28 @@ nq_status run_svid(nq_lbadmm* h, const Half& x, hipStream_t vs) {
 }
 
 // One ADMM half for the factor of x. With overlap:
-//   s (the caller's stream, whole chip): the Gram G = other^T other + rho I,
-//        which heads the critical path; later the solve out = R G^-1
-//        (X = out + Lam into Lam);
-//   chain_s: after the Gram, the blocked Cholesky with M = L^-1 and
-//        G^-1 = M^T M, a chain of latency-bound launches;
-//   gemm_s: after the Gram, R = Wside other + rho (Z - Lam), then the SVID
-//        of the previous half (`pending`), which has until the next half of
-//        its own factor (later on this stream) to finish.
-// The two streams share the CUs (optionally split by CU masks, see
-// create_streams); the chain is the critical path.
+//   s (the caller's stream): the critical path, in stream order: the Gram
+//        G = other^T other + rho I (alone on the chip), the blocked Cholesky
+//        with M = L^-1 and G^-1 = M^T M (a chain of latency-bound launches),
+//        then, once R is there, the solve out = R G^-1 (X = out + Lam into
+//        Lam);
+//   gemm_s: after the Gram, R = Wside other + rho (Z - Lam), beside the
+//        chain, then the SVID of the previous half (`pending`), which has
+//        until the next half of its own factor (later on this stream) to
+//        finish.
+// Without overlap every kernel goes to s in the same order.
 nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t s,
                    bool overlap) {
   const int rp = h->rp;
-  hipStream_t cs = overlap ? h->chain_s : s;
   hipStream_t gs = overlap ? h->gemm_s : s;
   long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
   // G = other^T other + rho I from other^T (rp x K)
   HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s));
-  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, false, h->G, rp, s));
-  if (overlap) {
-    HIPCHK(hipEventRecord(h->ev_gram, s));
-    HIPCHK(hipStreamWaitEvent(h->chain_s, h->ev_gram, 0));
-    HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
-  }
+  // ev_gram is recorded by the reduction's own completion: an event record
+  // of its own would put a marker (~8 us) between the Gram and the chain
+  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, false, h->G, rp, s,
+                            overlap ? h->ev_gram : nullptr));
+  if (overlap) HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
   // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last
   // SVID, earlier on the same stream. Enqueued before the chain's launches:
   // when the host only just keeps pace with the GPU, host order is start
@@ -279,19 +271,11 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   HIPCHK(launch_gemm(g, kEpiRhs, gs));
   prof_end(h, pr, gs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
-  h->m_dirty = true;
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, true,
-                                 cs));
-  prof_end(h, pc, cs);
-  if (overlap) HIPCHK(hipEventRecord(h->ev_join, cs));
-  // Minv back to zero for the next chain, off the critical path (the solve
-  // below reads only G^-1)
-  HIPCHK(launch_zero(h->Minv, (size_t)rp * rp, cs));
-  h->m_dirty = false;
-  if (overlap) {
-    HIPCHK(hipStreamWaitEvent(s, h->ev_join, 0));
-    HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
-  }
+  // Minv is the chain's L^-1 scratch; only G^-1 is read afterwards
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, false,
+                                 s));
+  prof_end(h, pc, s);
+  if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
   // out = R G^-1 (G^-1 symmetric, so it is its own transposed operand),
   // X = out + Lam (into Lam), outT = out^T
   GemmArgs q{};
@@ -353,35 +337,6 @@ nq_status nq_lbadmm_workspace_bytes(const nq_lbadmm_desc* desc, size_t* bytes) {
   return NQ_OK;
 }
 
-namespace {
-// The chain stream gets the last `chain_cus` CUs of the device, the GEMM
-// stream all the others. NQ_CHAIN_CUS overrides the count (0 = no masks,
-// both streams on the whole chip).
-hipError_t create_streams(nq_lbadmm* h) {
-  hipDeviceProp_t prop;
-  hipError_t e = hipGetDeviceProperties(&prop, h->device);
-  if (e != hipSuccess) return e;
-  const int ncu = prop.multiProcessorCount;
-  int res = kChainCUs;
-  if (const char* env = std::getenv("NQ_CHAIN_CUS")) res = std::atoi(env);
-  res = std::max(0, std::min(res, ncu / 2));
-  h->chain_cus = res;
-  if (res == 0) {
-    e = hipStreamCreateWithFlags(&h->chain_s, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->gemm_s, hipStreamNonBlocking);
-    return e;
-  }
-  const int words = (ncu + 31) / 32;
-  std::vector<uint32_t> chain(words, 0u), gemm(words, 0u);
-  for (int c = 0; c < ncu; ++c) {
-    std::vector<uint32_t>& m = c >= ncu - res ? chain : gemm;
-    m[c / 32] |= 1u << (c % 32);
-  }
-  e = hipExtStreamCreateWithCUMask(&h->chain_s, (uint32_t)words, chain.data());
-  if (e == hipSuccess) e = hipExtStreamCreateWithCUMask(&h->gemm_s, (uint32_t)words, gemm.data());
-  return e;
-}
-}  // namespace
 
 nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   if (!out) return fail(NQ_ERR_INVALID_ARG, "out is NULL");
@@ -402,9 +357,8 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
     return hip_fail(e, "hipMalloc(workspace)");
   }
   layout(h);
-  e = create_streams(h);
+  e = hipStreamCreateWithFlags(&h->gemm_s, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_gram, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_rhs, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t0);
@@ -433,17 +387,14 @@ void nq_lbadmm_destroy(nq_lbadmm_t h) {
   int cur = 0;
   if (hipGetDevice(&cur) == hipSuccess && cur != h->device) (void)hipSetDevice(h->device);
   if (h->last_stream || h->has_run) (void)hipStreamSynchronize(h->last_stream);
-  if (h->chain_s) (void)hipStreamSynchronize(h->chain_s);
   if (h->gemm_s) (void)hipStreamSynchronize(h->gemm_s);
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
-  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   if (h->ev_gram) (void)hipEventDestroy(h->ev_gram);
   if (h->ev_rhs) (void)hipEventDestroy(h->ev_rhs);
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
   for (hipEvent_t ev : h->prof_ev)
     if (ev) (void)hipEventDestroy(ev);
-  if (h->chain_s) (void)hipStreamDestroy(h->chain_s);
   if (h->gemm_s) (void)hipStreamDestroy(h->gemm_s);
   if (h->base) (void)hipFree(h->base);
   if (cur != h->device) (void)hipSetDevice(cur);
@@ -475,10 +426,6 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
     if (ps != NQ_OK) return ps;
   }
   HIPCHK(hipEventRecord(h->ev_t0, s));
-  if (h->m_dirty) {
-    HIPCHK(launch_zero(h->Minv, (size_t)rp * rp, s));
-    h->m_dirty = false;
-  }
   long pp = prof_begin(h, NQ_PHASE_PREP, s);
   HIPCHK(launch_stats_init(h->st, s));
   HIPCHK(launch_check_precond(d_out, d.m, d_in, d.n, h->st, s));

@@ -138,6 +138,7 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
   // [G 0; 0 I]: the identity keeps the padded system positive definite
   NQ_HIPCHK(stage_in(G, r, r, ldg, a.f(), rp, rp, s));
   NQ_HIPCHK(launch_set_diag(a.f(), rp, (int)r, (int)rp, 1.0f, s));
+  // m: L^-1 scratch, not returned (no zeroing needed)
   NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), Ginv ? gi.f() : nullptr, (int)rp, (int)r, dst,
                                     true, false, s));
   if (Ginv) NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));

@@ -5,6 +5,8 @@
 // so the result is deterministic, and written full-symmetric.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 namespace nq {
 namespace {
 
@@ -53,11 +55,13 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 }  // namespace
 
 hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
-                              bool full, float* G, int64_t ldg, hipStream_t s) {
+                              bool full, float* G, int64_t ldg, hipStream_t s, hipEvent_t done) {
   if (rp % 128 || K % 32 || p.steps <= 0) return hipErrorInvalidValue;
   dim3 grid(rp / 32, rp / 32), block(256);
-  hipLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, part, K / 32, p.steps, rp, rho,
-                     full ? 1 : 0, G, ldg);
+  // `done` is recorded by the kernel's own completion (no marker of its own
+  // between this kernel and the next one on s)
+  hipExtLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, nullptr, done, 0u, part, K / 32,
+                        p.steps, rp, rho, full ? 1 : 0, G, ldg);
   return hipGetLastError();
 }
 
