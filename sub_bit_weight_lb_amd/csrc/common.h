@@ -48,6 +48,8 @@ struct GemmArgs {
   float* Ct; int64_t ldct;       // kEpiSolve, optional: N x M
   float rho;
   int M, N, K;
+  int yield;                     // s_sleep units per K step (0: none), to leave
+                                 // issue cycles to a kernel running beside it
 };
 // M % 256 == 0, N % 128 == 0, K % 32 == 0; every ld a multiple of 4 and every
 // pointer 16-byte aligned (else hipErrorInvalidValue, nothing launched).

@@ -16,9 +16,12 @@
 //   BK = 32, each wave (TM / 2) x 64 = (TM / 64) x 2 blocks of
 //   v_mfma_f32_32x32x2_f32.
 // - Operands go from global memory straight into LDS with
-//   global_load_lds_dwordx4 (no VGPR staging). Two stages: the DMA of step
-//   k + 1 is spread between the MFMAs of step k, a few instructions after
-//   every 8 MFMAs.
+//   buffer_load_dwordx4 ... lds (no VGPR staging; the uniform part of each
+//   address in an SGPR, so a copy costs no vector instruction). Two stages:
+//   the copies of step k + 1 are spread over the first half of step k's
+//   MFMAs (one or two after each group of 8), early enough to land before
+//   the step ends. The last step is peeled, so the loop carries no branch
+//   per copy.
 // - LDS rows hold 32 floats as 8 slots of 16 B; row r keeps k-quad q in slot
 //   q ^ ((r >> 1) & 7). Each lane's DMA fetches the quad that belongs in its
 //   slot. Fragment reads are single ds_read_b128s, free of bank conflicts
@@ -31,20 +34,33 @@
 #include "common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace nq {
 namespace {
 
 constexpr int BK = 32;
+// MFMA groups of a step after which operand copies are issued
+#ifndef NQ_DMA_SLOTS
+#define NQ_DMA_SLOTS 8
+#endif
 constexpr int TN = 128;
 constexpr int NT = 256;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* glb_ptr_t;
 
-// 16 B per lane from global memory to LDS at lds + 16 * lane (wave-uniform lds).
-__device__ __forceinline__ void dma16(const void* g, float* lds) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)lds, 16, 0, 0);
+// Buffer resource over `base` (raw, byte offsets, reads past 2^31 bytes
+// return zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+// 16 B per lane from rsrc + voff (per lane) + soff (uniform) to LDS at
+// lds + 16 * lane (wave-uniform lds). The uniform part of the address stays
+// in an SGPR: no vector address arithmetic per copy.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff,
+                                      float* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
 template <int TM>
@@ -64,7 +80,7 @@ template <int TM>
 __device__ __forceinline__ void nt_mainloop(const float* __restrict__ Ag, int lda,
                                             const float* __restrict__ Bg, int ldb, int k0,
                                             int nk, float* lds,
-                                            f32x16 (&acc)[Tile<TM>::MI][2]) {
+                                            f32x16 (&acc)[Tile<TM>::MI][2], int yield = 0) {
   using T = Tile<TM>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,15 +97,16 @@ __device__ __forceinline__ void nt_mainloop(const float* __restrict__ Ag, int ld
     a_lo[par] = (uint32_t)(((lane >> 3) * lda + 4 * q) * 4);
     b_lo[par] = (uint32_t)(((lane >> 3) * ldb + 4 * q) * 4);
   }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ag), rb = make_rsrc(Bg);
   auto dma = [&](int stage, int kk, int n) {
     float* la = lds + stage * T::SST;
     if (n < T::NA) {
       const int R = (T::NA * wave + n) * 8;
-      dma16((const char*)(Ag + (int64_t)R * lda + kk) + a_lo[n & 1], la + R * BK);
+      dma16(ra, a_lo[n & 1], (R * lda + kk) * 4, la + R * BK);
     } else {
       const int i = n - T::NA;
       const int R = (T::NB * wave + i) * 8;
-      dma16((const char*)(Bg + (int64_t)R * ldb + kk) + b_lo[i & 1], la + T::SA + R * BK);
+      dma16(rb, b_lo[i & 1], (R * ldb + kk) * 4, la + T::SA + R * BK);
     }
   };
   // fragment offsets: row (wm TM/2 + l32) of A, row (wn 64 + l32) of B,
@@ -124,10 +141,12 @@ __device__ __forceinline__ void nt_mainloop(const float* __restrict__ Ag, int ld
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   asm volatile("s_barrier" ::: "memory");
   frag(lds, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  // One K step; the last one (MORE false) issues no DMA. The steps before
+  // it are a loop without a branch per DMA.
+  auto step = [&](int kt, auto more_tag) {
+    constexpr bool MORE = decltype(more_tag)::value;
     const int cs = kt & 1;
     const float* st = lds + cs * T::SST;
-    const bool more = kt + 1 < nk;
     const int knext = k0 + (kt + 1) * BK;
 #pragma unroll
     for (int c = 0; c < BK / 8; ++c) {
@@ -142,10 +161,16 @@ __device__ __forceinline__ void nt_mainloop(const float* __restrict__ Ag, int ld
           for (int ni = 0; ni < 2; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[cur][mi][s], bf[cur][ni][s],
                                                                acc[mi][ni], 0, 0, 0);
-        if (s < T::DPC && more) {
-          __builtin_amdgcn_sched_barrier(0);
-          dma(cs ^ 1, knext, T::DPC * c + s);
-          __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MORE) {
+          // copies n in [j N / S, (j + 1) N / S) after MFMA group j = 4 c + s
+          constexpr int N = T::NA + T::NB, S = NQ_DMA_SLOTS;
+          const int j = 4 * c + s;
+          if (j < S) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int n = j * N / S; n < (j + 1) * N / S; ++n) dma(cs ^ 1, knext, n);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -154,8 +179,12 @@ __device__ __forceinline__ void nt_mainloop(const float* __restrict__ Ag, int ld
     // stage may be overwritten once every wave has read its fragments
     __builtin_amdgcn_s_waitcnt(0x0070);
     asm volatile("s_barrier" ::: "memory");
-    if (more) frag(lds + (cs ^ 1) * T::SST, 0, 0);
-  }
+    if constexpr (MORE) frag(lds + (cs ^ 1) * T::SST, 0, 0);
+    // leave issue cycles to a co-resident kernel: ~64 cycles per unit
+    for (int y = 0; y < yield; ++y) __builtin_amdgcn_s_sleep(1);
+  };
+  for (int kt = 0; kt + 1 < nk; ++kt) step(kt, std::true_type{});
+  step(nk - 1, std::false_type{});
 }
 
 // XCD-aware tile order: workgroup b -> tile index.
@@ -196,7 +225,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
   const int tm = t / tilesN, tn = t % tilesN;
   f32x16 acc[T::MI][2];
   nt_mainloop<TM>(p.A + (int64_t)tm * TM * p.lda, (int)p.lda, p.B + (int64_t)tn * TN * p.ldb,
-                  (int)p.ldb, 0, p.K / BK, lds, acc);
+                  (int)p.ldb, 0, p.K / BK, lds, acc, p.yield);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -298,6 +327,9 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     return hipErrorInvalidValue;
   if (epi == kEpiSolve && a.Ct && (a.ldct % 4 || a.ldct < a.M || !aligned16(a.Ct)))
     return hipErrorInvalidValue;
+  // operand copies address a tile's rows as 32-bit byte offsets
+  if ((int64_t)256 * a.lda * 4 >= (int64_t)1 << 31 || (int64_t)TN * a.ldb * 4 >= (int64_t)1 << 31)
+    return hipErrorInvalidValue;
   const int nt = (a.M / 256) * (a.N / TN);
   dim3 grid(nt), block(NT);
   switch (epi) {
@@ -327,6 +359,7 @@ hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, con
                                float* part, hipStream_t s) {
   if (rp % 128 || K % BK || K <= 0 || ldat % 4 || ldat < K || !aligned16(At) || p.steps <= 0)
     return hipErrorInvalidValue;
+  if ((int64_t)128 * ldat * 4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
   const int R = rp / 128;
   const int64_t S = (int64_t)R * (R + 1) / 2 * (K / BK);
   hipLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, At, ldat, rp, K / BK, p.steps,

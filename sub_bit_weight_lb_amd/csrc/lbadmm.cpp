@@ -18,6 +18,7 @@
 #include "abi.h"
 #include "common.h"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdlib>
@@ -40,6 +41,7 @@ constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
                                   NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE |
                                   NQ_FLAG_PROFILE_RHS_ONLY;
 constexpr int kProfileRuns = 8;
+constexpr int kRhsYield = 24;
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
@@ -113,6 +115,11 @@ struct nq_lbadmm {
             ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
+  // s_sleep units (~64 cycles each) per K step of the RHS GEMM while it runs
+  // beside the chain: the chain is the critical path and a wave sharing a
+  // SIMD with an MFMA-bound wave gets little issue time; the RHS has slack.
+  // NQ_RHS_YIELD overrides it.
+  int rhs_yield = kRhsYield;
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
   std::vector<hipEvent_t> prof_ev;
   std::vector<int> prof_phase;  // phase of each pending pair
@@ -267,6 +274,7 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   GemmArgs g{};
   g.A = x.Wside; g.lda = x.K; g.B = x.otherT; g.ldb = x.K; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
+  g.yield = overlap ? h->rhs_yield : 0;
   long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, gs);
   HIPCHK(launch_gemm(g, kEpiRhs, gs));
   prof_end(h, pr, gs);
@@ -357,6 +365,7 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
     return hip_fail(e, "hipMalloc(workspace)");
   }
   layout(h);
+  if (const char* y = std::getenv("NQ_RHS_YIELD")) h->rhs_yield = std::max(0, std::atoi(y));
   e = hipStreamCreateWithFlags(&h->gemm_s, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_gram, hipEventDisableTiming);
