@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--iters", type=int, default=None, help="override ADMM iterations per run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--kernels", action="store_true",
+                    help="only run the GEMM kernels alone on the layer's shapes, 20 launches "
+                         "each (for a kernel-trace profile of their standalone durations)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -142,6 +145,26 @@ def main():
     from synth import make_layer
 
     dev = torch.device("cuda:0")
+    if args.kernels:
+        # RHS shape (m x n times n x r), solve shape (m x r times r x r), Gram
+        # (n x r); op_gemm_rhs also runs a transpose kernel per call, which a
+        # kernel trace lists on its own line
+        g = torch.Generator(device="cpu").manual_seed(0)
+        from synth.layers import WORKLOADS
+        wl = WORKLOADS[WORKLOAD]
+        for (mm, kk, nn) in ((wl.m, wl.n, wl.r), (wl.m, wl.r, wl.r)):
+            a = torch.randn(mm, kk, generator=g).to(dev)
+            b = torch.randn(kk, nn, generator=g).to(dev)
+            for _ in range(20):
+                nq.op_gemm_rhs(a, b)
+            torch.cuda.synchronize()
+            print(f"gemm {mm}x{nn}x{kk}: 20 launches", flush=True)
+        v = (0.05 * torch.randn(wl.n, wl.r, generator=g)).to(dev)
+        for _ in range(20):
+            nq.op_gram(v, rho=wl.rho)
+        torch.cuda.synchronize()
+        print(f"gram {wl.n}x{wl.r}: 20 launches", flush=True)
+        return
     L = make_layer(WORKLOAD)
     wl = L.workload
     m, n, r = wl.m, wl.n, wl.r
@@ -210,6 +233,9 @@ def main():
         "flops_per_iter": F,
         "roofline": {
             "kernel": "gemm_nt_kernel<kEpiRhs> (R = Wt V + rho (Z - Lam), V read as V^T)",
+            "note": ("timed as it runs in the pipeline: beside the Cholesky chain, yielding "
+                     "issue cycles to it (s_sleep after each K step); the same kernel alone: "
+                     "see the standalone kernel profile"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": FP32_MFMA_PEAK_TFLOPS,
