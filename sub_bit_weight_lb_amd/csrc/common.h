@@ -35,8 +35,7 @@ struct DevStats {
 enum GemmEpilogue : int {
   kEpiPlain = 0,   // C = A B^T
   kEpiRhs = 1,     // C = A B^T + rho P              (P ld = ldc)
-  kEpiSolve = 2,   // C = A B^T;  X = C + X  (X holds Lambda on entry, ld = ldc);
-                   // Ct = C^T when Ct is not null
+  kEpiSolve = 2,   // C = A B^T; Ct = C^T when Ct is not null
 };
 // C = A B^T ("NT"): both operands are stored with k contiguous.
 struct GemmArgs {
@@ -44,7 +43,6 @@ struct GemmArgs {
   const float* B; int64_t ldb;   // N x K (the right factor, transposed)
   float* C; int64_t ldc;         // M x N
   const float* P;                // kEpiRhs
-  float* X;                      // kEpiSolve
   float* Ct; int64_t ldct;       // kEpiSolve, optional: N x M
   float rho;
   int M, N, K;
@@ -101,10 +99,12 @@ constexpr int kSvidReduceRows = 16;
 int svid_nchunks(int rows_pad);            // 64-row chunks of the column pass
 int svid_partials(int rows_pad, int rp);   // partial rows the SVID work arrays hold
 // mode 0: init (P = Z, X left as is), mode 1: update (X <- X - Z, P = 2Z - X_old),
-// mode 2: plain (Z written to P; X untouched).
-// rows_pad % 8 == 0, rp % 128 == 0.
+// mode 2: plain (Z written to P; X untouched). With Uadd (nullable, same
+// layout as X), X is first replaced by X + Uadd (formed by the first step).
+// rows_pad % 8 == 0, rp % 128 == 0, T >= 1.
 hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int T,
-                       int mode, const SvidWork& w, hipStream_t s);
+                       int mode, const SvidWork& w, hipStream_t s,
+                       const float* Uadd = nullptr);
 
 // ---------------------------------------------------------------- elementwise
 hipError_t launch_stats_init(DevStats* st, hipStream_t s);

@@ -5,9 +5,8 @@
 //                    B = V^T (or U^T), kept in HBM beside the factors;
 //   solve            U = R G^-1 = R L^-T L^-1, both triangular solves as one
 //                    product with the symmetric inverse (B = G^-1 = G^-T);
-//                    the epilogue also forms X = U + Lam for SVID, step (b),
-//                    and writes U^T for the next half's Gram and right-hand
-//                    side;
+//                    the epilogue also writes U^T for the next half's Gram
+//                    and right-hand side;
 //   Gram             G = V^T V + rho I: A = B = V^T, lower 128 x 128 tiles,
 //                    split over K into partial sums (gram_reduce adds them).
 //
@@ -254,10 +253,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
         if (EPI == kEpiRhs) {
           const f32x4 pv = *(const f32x4*)&p.P[idx];
           *(f32x4*)&p.C[idx] = val + p.rho * pv;
-        } else if (EPI == kEpiSolve) {
-          const f32x4 xv = *(const f32x4*)&p.X[idx];
-          *(f32x4*)&p.C[idx] = val;
-          *(f32x4*)&p.X[idx] = val + xv;
         } else {
           *(f32x4*)&p.C[idx] = val;
         }

@@ -239,7 +239,8 @@ struct Half {
 // Z = SVID(X); Lam = X - Z; P = Z - Lam for the factor of half x.
 nq_status run_svid(nq_lbadmm* h, const Half& x, hipStream_t vs) {
   long pv = prof_begin(h, NQ_PHASE_SVID, vs);
-  HIPCHK(launch_svid(x.Lam, x.P, x.M, h->rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, vs));
+  // X = out + Lam is formed by the SVID's first step (into the Lam buffer)
+  HIPCHK(launch_svid(x.Lam, x.P, x.M, h->rp, (int)h->d.r, h->d.svid_steps, 1, *x.sv, vs, x.out));
   prof_end(h, pv, vs);
   return NQ_OK;
 }
@@ -248,8 +249,7 @@ nq_status run_svid(nq_lbadmm* h, const Half& x, hipStream_t vs) {
 //   s (the caller's stream): the critical path, in stream order: the Gram
 //        G = other^T other + rho I (alone on the chip), the blocked Cholesky
 //        with M = L^-1 and G^-1 = M^T M (a chain of latency-bound launches),
-//        then, once R is there, the solve out = R G^-1 (X = out + Lam into
-//        Lam);
+//        then, once R is there, the solve out = R G^-1 (and out^T);
 //   gemm_s: after the Gram, R = Wside other + rho (Z - Lam), beside the
 //        chain, then the SVID of the previous half (`pending`), which has
 //        until the next half of its own factor (later on this stream) to
@@ -285,10 +285,10 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   prof_end(h, pc, s);
   if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
   // out = R G^-1 (G^-1 symmetric, so it is its own transposed operand),
-  // X = out + Lam (into Lam), outT = out^T
+  // outT = out^T
   GemmArgs q{};
   q.A = h->R; q.lda = rp; q.B = h->Ginv; q.ldb = rp; q.C = x.out; q.ldc = rp;
-  q.X = x.Lam; q.Ct = x.outT; q.ldct = x.M; q.M = x.M; q.N = rp; q.K = rp;
+  q.Ct = x.outT; q.ldct = x.M; q.M = x.M; q.N = rp; q.K = rp;
   long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
   prof_end(h, ps, s);

@@ -10,7 +10,9 @@
 //
 // HBM-bound. Per power step one fused pass: each block holds a slab of full
 // rows in registers, forms a for its rows and then its rows' share of
-// |X|^T a, so X is read once per step; a small reduce then forms b. For
+// |X|^T a, so X is read once per step; a small reduce then forms b. In the
+// ADMM update the first pass also forms X = U + Lam from the new factor and
+// the dual (written over Lam), so the solve that produces U does not. For
 // r beyond 16384 a row pass and a column pass replace the fused one. All
 // reductions run in a fixed order, so results are bit-reproducible.
 #include "common.h"
@@ -102,9 +104,11 @@ __global__ __launch_bounds__(256) void colsum_kernel(const float* __restrict__ X
 //   a_i = sum_j |X_ij| b_j / bb          (rows of the slab, block reduction)
 //   part[slab][j] = sum_{i in slab} |X_ij| a_i,  aapart[slab] = sum a_i^2
 // so X is read once per step. Thread t owns float4 columns t + 256 u.
+// With Uadd (first step of an update), X is first formed as X + Uadd and
+// written back.
 template <int RS, int NU>
-__global__ __launch_bounds__(256) void svid_step_kernel(const float* __restrict__ X, int rp,
-                                                        const float* __restrict__ b,
+__global__ __launch_bounds__(256) void svid_step_kernel(float* X, const float* __restrict__ Uadd,
+                                                        int rp, const float* __restrict__ b,
                                                         const float* __restrict__ bbpart, int nbb,
                                                         float* __restrict__ a,
                                                         float* __restrict__ part,
@@ -131,6 +135,18 @@ __global__ __launch_bounds__(256) void svid_step_kernel(const float* __restrict_
       const int q = tid + 256 * u;
       x[r][u] = q < rp4 ? ((const f32x4*)(X + (i0 + r) * rp))[q] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  if (Uadd) {
+#pragma unroll
+    for (int r = 0; r < RS; ++r)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int q = tid + 256 * u;
+        if (q < rp4) {
+          x[r][u] += ((const f32x4*)(Uadd + (i0 + r) * rp))[q];
+          ((f32x4*)(X + (i0 + r) * rp))[q] = x[r][u];
+        }
+      }
+  }
   float s[RS];
 #pragma unroll
   for (int r = 0; r < RS; ++r) {
@@ -276,19 +292,28 @@ int svid_nchunks(int rows_pad) { return (rows_pad + CR - 1) / CR; }
 namespace {
 // Slab rows RS and float4s per thread NU for the fused step at this rp.
 template <int RS, int NU>
-void launch_step(float* X, int rows_pad, int rp, int nbb, const SvidWork& w, hipStream_t s) {
-  hipLaunchKernelGGL((svid_step_kernel<RS, NU>), dim3(rows_pad / RS), dim3(256), 0, s, X, rp, w.b,
-                     w.bbpart, nbb, w.a, w.colpart, w.aapart);
+void launch_step(float* X, const float* Uadd, int rows_pad, int rp, int nbb, const SvidWork& w,
+                 hipStream_t s) {
+  hipLaunchKernelGGL((svid_step_kernel<RS, NU>), dim3(rows_pad / RS), dim3(256), 0, s, X, Uadd,
+                     rp, w.b, w.bbpart, nbb, w.a, w.colpart, w.aapart);
 }
-bool fused_step(float* X, int rows_pad, int rp, int nbb, const SvidWork& w, hipStream_t s) {
+bool fused_step(float* X, const float* Uadd, int rows_pad, int rp, int nbb, const SvidWork& w,
+                hipStream_t s) {
   const int nu = (rp / 4 + 255) / 256;
-  if (nu <= 1) launch_step<8, 1>(X, rows_pad, rp, nbb, w, s);
-  else if (nu <= 2) launch_step<8, 2>(X, rows_pad, rp, nbb, w, s);
-  else if (nu <= 4) launch_step<4, 4>(X, rows_pad, rp, nbb, w, s);
-  else if (nu <= 8) launch_step<2, 8>(X, rows_pad, rp, nbb, w, s);
-  else if (nu <= 16) launch_step<1, 16>(X, rows_pad, rp, nbb, w, s);
+  if (nu <= 1) launch_step<8, 1>(X, Uadd, rows_pad, rp, nbb, w, s);
+  else if (nu <= 2) launch_step<8, 2>(X, Uadd, rows_pad, rp, nbb, w, s);
+  else if (nu <= 4) launch_step<4, 4>(X, Uadd, rows_pad, rp, nbb, w, s);
+  else if (nu <= 8) launch_step<2, 8>(X, Uadd, rows_pad, rp, nbb, w, s);
+  else if (nu <= 16) launch_step<1, 16>(X, Uadd, rows_pad, rp, nbb, w, s);
   else return false;
   return true;
+}
+// X += U (float4s), for the unfused path
+__global__ __launch_bounds__(256) void add_into_kernel(float* __restrict__ X,
+                                                       const float* __restrict__ U, int64_t n4) {
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4;
+       q += (int64_t)gridDim.x * blockDim.x)
+    ((f32x4*)X)[q] += ((const f32x4*)U)[q];
 }
 int fused_rows(int rp) {
   const int nu = (rp / 4 + 255) / 256;
@@ -302,14 +327,20 @@ int svid_partials(int rows_pad, int rp) {
 }
 
 hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int T, int mode,
-                       const SvidWork& w, hipStream_t s) {
-  if (rp % CB || rows_pad % 8) return hipErrorInvalidValue;
+                       const SvidWork& w, hipStream_t s, const float* Uadd) {
+  if (rp % CB || rows_pad % 8 || T < 1) return hipErrorInvalidValue;
   const int nbb = rp / CB;
   const int nch = svid_nchunks(rows_pad);
   const int rs = fused_rows(rp);
+  const int64_t n4 = (int64_t)rows_pad * rp / 4;
+  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
   hipLaunchKernelGGL(svid_init_b_kernel, dim3(nbb), dim3(CB), 0, s, w.b, w.bbpart, rp, r_real);
+  if (Uadd && !rs) {
+    hipLaunchKernelGGL(add_into_kernel, dim3(blocks), dim3(256), 0, s, X, Uadd, n4);
+    Uadd = nullptr;
+  }
   for (int t = 0; t < T; ++t) {
-    if (rs && fused_step(X, rows_pad, rp, nbb, w, s)) {
+    if (rs && fused_step(X, t == 0 ? Uadd : nullptr, rows_pad, rp, nbb, w, s)) {
       hipLaunchKernelGGL(svid_reduce1_kernel, dim3(rp / 128, NY), dim3(256), 0, s, w.colpart,
                          rows_pad / rs, rp, w.part2);
       hipLaunchKernelGGL(svid_reduce2_kernel, dim3(rp / 128), dim3(256), 0, s, w.part2, w.aapart,
@@ -325,8 +356,6 @@ hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int
     hipLaunchKernelGGL(svid_reduce2_kernel, dim3(rp / 128), dim3(256), 0, s, w.part2, w.aapart,
                        nch, rp, w.b, w.bbpart);
   }
-  const int64_t n4 = (int64_t)rows_pad * rp / 4;
-  const int blocks = (int)std::min<int64_t>((n4 + 255) / 256, 8192);
   hipLaunchKernelGGL(svid_final_kernel, dim3(blocks), dim3(256), 0, s, X, P, w.a, w.b, rp, n4,
                      mode);
   return hipGetLastError();
