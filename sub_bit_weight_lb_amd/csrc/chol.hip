@@ -490,9 +490,17 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 //   [k < R]  1 diagonal (writes M_kk), R-1-k panel tiles, k inverse-row tiles;
 //   [k >= 1] 1 with want_L (writes L_{k-1,k-1}), n(n+1)/2 trailing tiles
 //            (n = R-1-k), n k partial sums, k(k+1)/2 G^-1 tiles if Ginv.
+// With pin (a 256-workgroup grid: 32 workgroups on each of the 8 XCDs), the
+// ndiag workgroups that factor a diagonal tile are those on XCD 7, one per
+// CU, and the update workgroups those on XCDs 0-6; the others exit. A GEMM
+// that leaves XCD 7 free (GemmArgs::free_xcd7) then never shares a CU with
+// the diagonal work. The XCD comes from the hardware register: consecutive
+// workgroups go to consecutive XCDs, but the first one's XCD depends on the
+// queue's history.
 __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float* Ginv, int rp,
                                                        int k, int r_real, int want_L,
-                                                       int upd_blocks, DevStats* st) {
+                                                       int upd_blocks, DevStats* st, int pin,
+                                                       int ndiag, int dtiles) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) StepSmem sm;
   const int R = rp / NB;
@@ -500,64 +508,92 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   const int64_t kk = (int64_t)k * NB;
   const int qm = wave_qm(), qn = wave_qn();
   int b = blockIdx.x;
-  if (k < R) {
-    if (b == 0) {  // M_kk
-      diag_step<false, false, true>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm,
-                                    SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
-      return;
+  // update tiles [t_lo, t_hi) with stride t_step for this workgroup (pinned:
+  // the XCD 7 workgroups take the first dtiles after their diagonal work,
+  // which runs alone on that XCD, and the others the rest)
+  int t_lo = -1, t_hi = INT_MAX, t_step = upd_blocks;
+  if (pin) {
+    const int x = xcd_id(), i = b >> 3;
+    if (x == 7) {
+      t_lo = i;
+      t_hi = dtiles;
+      t_step = kPinDiagSlots;
+      b = i < ndiag ? i : INT_MAX;
+    } else {
+      const int u = i * 7 + x;
+      if (u >= upd_blocks) return;
+      t_lo = dtiles + u;
+      b = INT_MAX;
     }
-    b -= 1;
-    if (b < n) {  // panel tile (i, k)
-      const int64_t i0 = (int64_t)(k + 1 + b) * NB;
-      float* Aik = A + i0 * rp + kk;
-      // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
-      diag_step<true, false, true>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
-                                   SideJob{Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f, k > 0,
-                                           false});
-      const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
-      __syncthreads();  // every wave has read its operands before any overwrite
-      store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
-      return;
-    }
-    b -= n;
-    if (b < k) {  // inverse-row tile (k, j)
-      const int64_t j0 = (int64_t)b * NB;
-      float* Mkj = M + kk * rp + j0;
-      // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation; for j = k-1
-      // this is the only term, so the tile is overwritten
-      diag_step<true, false, false>(
-          A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
-          SideJob{A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f, true,
-                  b == k - 1});
-      const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
-      __syncthreads();
-      store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
-      return;
-    }
-    b -= k;
   }
+  // The diagonal, panel, inverse-row and L_pp workgroups; returns whether
+  // this workgroup was one of them.
+  auto role = [&]() -> bool {
+    if (k < R) {
+      if (b == 0) {  // M_kk
+        diag_step<false, false, true>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm,
+                                      SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
+        return true;
+      }
+      b -= 1;
+      if (b < n) {  // panel tile (i, k)
+        const int64_t i0 = (int64_t)(k + 1 + b) * NB;
+        float* Aik = A + i0 * rp + kk;
+        // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
+        diag_step<true, false, true>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
+                                     SideJob{Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f,
+                                             k > 0, false});
+        const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
+        __syncthreads();  // every wave has read its operands before any overwrite
+        store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
+        return true;
+      }
+      b -= n;
+      if (b < k) {  // inverse-row tile (k, j)
+        const int64_t j0 = (int64_t)b * NB;
+        float* Mkj = M + kk * rp + j0;
+        // S_kj += L_{k,k-1} M_{k-1,j} beside the factorisation; for j = k-1
+        // this is the only term, so the tile is overwritten
+        diag_step<true, false, false>(
+            A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
+            SideJob{A + kk * rp + kk - NB, M + (kk - NB) * rp + j0, Mkj, rp, 1.0f, true,
+                    b == k - 1});
+        const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
+        __syncthreads();
+        store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
+        return true;
+      }
+      b -= k;
+    }
+    if (k >= 1 && want_L) {
+      if (b == 0) {  // L_pp
+        const int64_t pq = (int64_t)(k - 1) * NB;
+        diag_step<false, true, true>(A, rp, k - 1, nullptr, A + pq * rp + pq, r_real, nullptr,
+                                     sm, SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
+        return true;
+      }
+      b -= 1;
+    }
+    return false;
+  };
+  if (role() && !pin) return;
   if (k < 1) return;
   const int p = k - 1;
   const int64_t pp = (int64_t)p * NB;
-  if (want_L) {
-    if (b == 0) {  // L_pp
-      diag_step<false, true, true>(A, rp, p, nullptr, A + pp * rp + pp, r_real, nullptr, sm,
-                                   SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
-      return;
-    }
-    b -= 1;
-  }
   // The update tiles of step p are spread over upd_blocks workgroups, each
   // taking every upd_blocks-th tile, so that a launch needs few enough
   // workgroups to be resident at once beside a concurrently running GEMM.
   const int nT = n > 0 ? n * (n + 1) / 2 : 0;
   const int nS = n > 0 ? n * k : 0;
   const int nG = Ginv ? k * (k + 1) / 2 : 0;
-  // Inside the loops the row stride is re-read through an empty asm, so the
-  // per-lane 64-bit fragment offsets are formed per tile rather than hoisted
-  // out of the loop, where they would hold ~100 extra registers.
-  int t = b;
-  for (; t < nT; t += upd_blocks) {  // trailing tile (i, j), i >= j > k
+  // Global tile index t over the three ranges; a workgroup takes t = first,
+  // first + step, ... below t_hi. Inside the loops the row stride is re-read
+  // through an empty asm, so the per-lane 64-bit fragment offsets are formed
+  // per tile rather than hoisted out of the loop, where they would hold ~100
+  // extra registers.
+  int t = pin ? t_lo : b;
+  const int eT = min(nT, t_hi);
+  for (; t < eT; t += t_step) {  // trailing tile (i, j), i >= j > k
     int ld = rp;
     asm volatile("" : "+s"(ld));
     int ii, jj;
@@ -567,7 +603,9 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     const f32x16 acc = mm_quad<false, true>(A + i0 * ld + pp, ld, A + j0 * ld + pp, ld, qm, qn);
     store_quad(acc, prev, A + i0 * ld + j0, ld, -1.0f, qm, qn);
   }
-  for (t -= nT; t < nS; t += upd_blocks) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
+  if (t < nT) return;  // stopped by t_hi
+  const int eS = min(nS, t_hi - nT);
+  for (t -= nT; t < eS; t += t_step) {  // partial sum S_ij += L_ip M_pj, i > k, j < k
     int ld = rp;
     asm volatile("" : "+s"(ld));
     const int jt = t % k;
@@ -577,7 +615,9 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     const f32x16 acc = mm_quad<false, false>(A + i0 * ld + pp, ld, M + pp * ld + j0, ld, qm, qn);
     store_quad(acc, prev, M + i0 * ld + j0, ld, 1.0f, qm, qn);
   }
-  for (t -= nS; t < nG; t += upd_blocks) {  // G^-1 tile (i, j), j <= i <= p: += M_pi^T M_pj
+  if (t < nS) return;
+  const int eG = min(nG, t_hi - nT - nS);
+  for (t -= nS; t < eG; t += t_step) {  // G^-1 tile (i, j), j <= i <= p: += M_pi^T M_pj
     int ld = rp;
     asm volatile("" : "+s"(ld));
     int ii, jj;
@@ -598,9 +638,25 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 
 }  // namespace
 
+// Update tiles per launch that the XCD 7 workgroups take after their
+// diagonal work (pinned mode); NQ_PIN_DIAG_TILES overrides it.
+int pin_diag_tiles() {
+  static const int d = [] {
+    const char* e = std::getenv("NQ_PIN_DIAG_TILES");
+    return e ? std::max(0, std::atoi(e)) : 64;
+  }();
+  return d;
+}
+
+bool cholesky_pinnable(int rp, bool want_L) {
+  return rp % NB == 0 && rp / NB + (want_L ? 1 : 0) <= kPinDiagSlots;
+}
+
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool want_L, bool zero_m, hipStream_t s) {
+                                   DevStats* st, bool want_L, bool zero_m, hipStream_t s,
+                                   bool pin) {
   if (rp % NB) return hipErrorInvalidValue;
+  if (pin && !cholesky_pinnable(rp, want_L)) return hipErrorInvalidValue;
   const int R = rp / NB;
   if (zero_m) {
     hipError_t e = launch_zero(M, (size_t)rp * rp, s);
@@ -609,18 +665,24 @@ hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int 
   for (int k = 0; k <= R; ++k) {
     const int n = R - 1 - k;
     int nb = k < R ? 1 + n + k : 0;  // diagonal, panel and inverse-row workgroups
-    int upd = 0;
+    int upd = 0, upd_tiles = 0;
     if (k >= 1) {
       nb += want_L ? 1 : 0;
       const int tiles = (n > 0 ? n * (n + 1) / 2 + n * k : 0) + (Ginv ? k * (k + 1) / 2 : 0);
-      upd = tiles;
-      const int cap = chol_launch_cap();
-      if (cap > 0 && nb + upd > cap) upd = std::max(cap - nb, std::min(tiles, kCholMinUpdBlocks));
-      upd = std::min(upd, tiles);
+      upd = upd_tiles = tiles;
+      if (pin) {
+        upd = std::min(tiles, kPinUpdSlots);
+      } else {
+        const int cap = chol_launch_cap();
+        if (cap > 0 && nb + upd > cap)
+          upd = std::max(cap - nb, std::min(tiles, kCholMinUpdBlocks));
+        upd = std::min(upd, tiles);
+      }
     }
     if (nb + upd > 0)
-      hipLaunchKernelGGL(chol_step_kernel, dim3(nb + upd), dim3(NT), 0, s, A, M, Ginv, rp, k,
-                         r_real, want_L ? 1 : 0, std::max(upd, 1), st);
+      hipLaunchKernelGGL(chol_step_kernel, dim3(pin ? kPinGrid : nb + upd), dim3(NT), 0, s, A, M,
+                         Ginv, rp, k, r_real, want_L ? 1 : 0, std::max(upd, 1), st,
+                         pin ? 1 : 0, nb, pin ? std::min(upd_tiles, pin_diag_tiles()) : 0);
   }
   if (!want_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;

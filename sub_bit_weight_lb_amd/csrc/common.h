@@ -18,6 +18,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 
+// XCD (accelerator complex die) the calling wave runs on, 0..7 on MI355X.
+__device__ __forceinline__ int xcd_id() {
+  return (int)(__builtin_amdgcn_s_getreg((31 << 11) | 20) & 7u);  // HW_REG_XCC_ID
+}
+
+hipError_t xcd_round_robin_ok(bool* ok);
+
 // Device-side status shared by all kernels of one run.
 struct DevStats {
   double sumsq_wt;      // ||Wt||_F^2
@@ -30,6 +37,11 @@ struct DevStats {
   int potrf_info;       // 0 or 1 + first failing pivot column (min over runs)
   int pad;
 };
+
+// Launch layout of the pinned overlap (MI355X: 8 XCDs x 32 CUs).
+constexpr int kPinGrid = 256;      // workgroups of a pinned launch, 32 per XCD
+constexpr int kPinDiagSlots = 32;  // XCD 7
+constexpr int kPinUpdSlots = 224;  // XCDs 0-6
 
 // ---------------------------------------------------------------- GEMM
 enum GemmEpilogue : int {
@@ -48,10 +60,19 @@ struct GemmArgs {
   int M, N, K;
   int yield;                     // s_sleep units per K step (0: none), to leave
                                  // issue cycles to a kernel running beside it
+  int free_xcd7;                 // kEpiRhs: run on XCDs 0-6 only (XCD 7 left to a
+                                 // pinned Cholesky chain); part is then required
+  float* part;                   // kPinUpdSlots x 256 x 128 floats of partial tiles
 };
 // M % 256 == 0, N % 128 == 0, K % 32 == 0; every ld a multiple of 4 and every
 // pointer 16-byte aligned (else hipErrorInvalidValue, nothing launched).
+// With free_xcd7, the 256 x 128 tiles go to the 224 workgroups of XCDs 0-6:
+// each takes whole tiles, and the tiles left over are split along K into
+// partial tiles (in part) that a second kernel adds up, with rho P, in a
+// fixed order.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
+// Floats of `part` a free_xcd7 launch of this shape needs (0 if none).
+size_t rhs_part_floats(int M, int N, int K);
 
 // ---------------------------------------------------------------- Gram
 // Work split of G = A^T A (lower 128 x 128 tiles, tiles x K / 32 steps of 32)
@@ -83,8 +104,13 @@ constexpr int kNB = 64;  // block size of the blocked Cholesky
 // zero_m M is zeroed first so that they read as zero. Ginv (rp x rp,
 // nullable) becomes G^-1 = M^T M, full and exactly symmetric.
 // st->potrf_info gets min(1 + failing column).
+// pin: place the diagonal work on XCD 7 (one workgroup per CU) and the
+// update tiles on XCDs 0-6, for a run beside a GEMM that leaves XCD 7 free;
+// needs cholesky_pinnable (at most kPinDiagSlots diagonal workgroups).
+bool cholesky_pinnable(int rp, bool want_L);
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
-                                   DevStats* st, bool want_L, bool zero_m, hipStream_t s);
+                                   DevStats* st, bool want_L, bool zero_m, hipStream_t s,
+                                   bool pin = false);
 
 // ---------------------------------------------------------------- SVID
 struct SvidWork {

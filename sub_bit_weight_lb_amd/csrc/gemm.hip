@@ -214,23 +214,46 @@ __device__ __forceinline__ void stage_block(const f32x16& a, float* stage, F&& s
   __builtin_amdgcn_wave_barrier();
 }
 
+// Work split of the 256 x 128 tiles over nwg workgroups: F whole tiles each,
+// then the E tiles left over cut along K into C chunks (E C <= nwg).
+__host__ __device__ inline void tile_split(int tiles, int nwg, int ksteps, int& F, int& E,
+                                           int& C) {
+  F = tiles / nwg;
+  E = tiles - F * nwg;
+  C = E > 0 ? nwg / E : 0;
+  if (C > ksteps) C = ksteps;
+}
+
+// One 256 x 128 tile: K steps [ks, ke) into acc, then either the full
+// epilogue (whole K) or a plain store of the partial tile to `part` (ld 128).
 template <int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, int t, int ks, int ke, float* part,
+                                          float* lds) {
   constexpr int TM = 256;
   using T = Tile<TM>;
-  __shared__ __attribute__((aligned(1024))) float lds[T::LDS_FLOATS];
   const int tilesN = p.N / TN;
-  const int t = xcd_tile(blockIdx.x, (p.M / TM) * tilesN);
   const int tm = t / tilesN, tn = t % tilesN;
   f32x16 acc[T::MI][2];
   nt_mainloop<TM>(p.A + (int64_t)tm * TM * p.lda, (int)p.lda, p.B + (int64_t)tn * TN * p.ldb,
-                  (int)p.ldb, 0, p.K / BK, lds, acc, p.yield);
+                  (int)p.ldb, ks * BK, ke - ks, lds, acc, p.yield);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int h = lane >> 5, l32 = lane & 31;
   float* stage = lds + wave * 32 * 36;
+  if (part) {
+#pragma unroll
+    for (int mi = 0; mi < T::MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int r0 = wm * (TM / 2) + mi * 32, c0 = wn * 64 + ni * 32;
+        stage_block(acc[mi][ni], stage, [&](int r, int c4, const f32x4& val) {
+          *(f32x4*)&part[(r0 + r) * TN + c0 + c4] = val;
+        });
+      }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < T::MI; ++mi)
 #pragma unroll
@@ -258,6 +281,56 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
         }
       });
     }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) float lds[Tile<256>::LDS_FLOATS];
+  const int tiles = (p.M / 256) * (p.N / TN);
+  const int ksteps = p.K / BK;
+  if (!p.free_xcd7) {
+    gemm_tile<EPI>(p, xcd_tile(blockIdx.x, tiles), 0, ksteps, nullptr, lds);
+    return;
+  }
+  // consecutive workgroups go to consecutive XCDs (the first one's XCD
+  // depends on the queue's history): with 32 per XCD, blockIdx / 8 numbers
+  // the workgroups of one XCD. XCD 7 is left to the chain.
+  const int x = xcd_id(), i = blockIdx.x >> 3;
+  if (x == 7) return;
+  const int per = gridDim.x / 8, nwg = 7 * per, w = i * 7 + x;
+  int F, E, C;
+  tile_split(tiles, nwg, ksteps, F, E, C);
+  for (int f = 0; f < F; ++f) {
+    if (f > 0) {  // the next tile's copies overwrite the LDS the epilogue staged in
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("s_barrier" ::: "memory");
+    }
+    gemm_tile<EPI>(p, f * nwg + x * per + i, 0, ksteps, nullptr, lds);
+  }
+  if (w < E * C) {
+    if (F > 0) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("s_barrier" ::: "memory");
+    }
+    const int e = w / C, c = w % C;
+    gemm_tile<EPI>(p, F * nwg + e, c * ksteps / C, (c + 1) * ksteps / C,
+                   p.part + (int64_t)(e * C + c) * 256 * TN, lds);
+  }
+}
+
+// The leftover tiles of a free_xcd7 launch: C = sum of the C partial tiles
+// in chunk order, + rho P. Block (e, y) covers rows 8 y .. 8 y + 7 of tile e.
+__global__ __launch_bounds__(256) void rhs_fixup_kernel(GemmArgs p, int F, int nwg, int C) {
+  const int e = blockIdx.x;
+  const int r = blockIdx.y * 8 + (threadIdx.x >> 5), c4 = (threadIdx.x & 31) * 4;
+  const int tilesN = p.N / TN;
+  const int t = F * nwg + e;
+  const int tm = t / tilesN, tn = t % tilesN;
+  const float* src = p.part + (int64_t)e * C * 256 * TN + r * TN + c4;
+  f32x4 sum = *(const f32x4*)src;
+  for (int cc = 1; cc < C; ++cc) sum += *(const f32x4*)(src + (int64_t)cc * 256 * TN);
+  const int64_t idx = (int64_t)(tm * 256 + r) * p.ldc + tn * TN + c4;
+  *(f32x4*)&p.C[idx] = sum + p.rho * *(const f32x4*)&p.P[idx];
 }
 
 // Partial Gram tiles, stream-K: the tiles x T K steps of 32 (lower tile t =
@@ -326,6 +399,16 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   if ((int64_t)256 * a.lda * 4 >= (int64_t)1 << 31 || (int64_t)TN * a.ldb * 4 >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   const int nt = (a.M / 256) * (a.N / TN);
+  if (a.free_xcd7) {
+    if (epi != kEpiRhs || !a.part || !aligned16(a.part)) return hipErrorInvalidValue;
+    constexpr int kGrid = kPinGrid, kWgs = kPinUpdSlots;  // 8 XCDs x 32; XCDs 0-6
+    hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, dim3(kGrid), dim3(NT), 0, s, a);
+    int F, E, C;
+    tile_split(nt, kWgs, a.K / BK, F, E, C);
+    if (E > 0)
+      hipLaunchKernelGGL(rhs_fixup_kernel, dim3(E, 256 / 8), dim3(256), 0, s, a, F, kWgs, C);
+    return hipGetLastError();
+  }
   dim3 grid(nt), block(NT);
   switch (epi) {
     case kEpiRhs: hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, grid, block, 0, s, a); break;
@@ -333,6 +416,13 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     default: hipLaunchKernelGGL(gemm_nt_kernel<kEpiPlain>, grid, block, 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+size_t rhs_part_floats(int M, int N, int K) {
+  if (M % 256 || N % TN || K % BK || M <= 0 || N <= 0 || K <= 0) return 0;
+  int F, E, C;
+  tile_split((M / 256) * (N / TN), kPinUpdSlots, K / BK, F, E, C);
+  return (size_t)E * C * 256 * TN;
 }
 
 GramPlan gram_plan(int K, int rp) {

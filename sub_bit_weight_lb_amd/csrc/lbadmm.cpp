@@ -108,6 +108,7 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
+  float* rhs_part;  // partial tiles of the RHS GEMM when it leaves XCD 7 free
   // gemm_s: the RHS GEMM and the SVIDs, beside the caller's stream (see
   // run_half)
   hipStream_t gemm_s = nullptr;
@@ -120,6 +121,10 @@ struct nq_lbadmm {
   // SIMD with an MFMA-bound wave gets little issue time; the RHS has slack.
   // NQ_RHS_YIELD overrides it.
   int rhs_yield = kRhsYield;
+  // Pinned overlap: the chain's diagonal work on XCD 7 (one workgroup per CU),
+  // the RHS GEMM on XCDs 0-6. Needs 8 x 32 CUs and at most 32 diagonal
+  // workgroups per launch (r_p <= 2048); NQ_PIN=0 turns it off.
+  bool pin = false;
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
   std::vector<hipEvent_t> prof_ev;
   std::vector<int> prof_phase;  // phase of each pending pair
@@ -161,6 +166,8 @@ size_t layout(nq_lbadmm* h) {
   size_t o_s1c = a.take<float>(mp), o_s2c = a.take<float>(np_);
   size_t o_SU = a.take<int8_t>(mp * rp), o_SV = a.take<int8_t>(np_ * rp);
   size_t o_st = a.take<DevStats>(1);
+  size_t o_rp = a.take<float>(std::max(rhs_part_floats((int)mp, (int)rp, (int)np_),
+                                        rhs_part_floats((int)np_, (int)rp, (int)mp)));
   if (h->base) {
     char* b = h->base;
     h->Wt = (float*)(b + o_Wt); h->WtT = (float*)(b + o_WtT);
@@ -182,6 +189,7 @@ size_t layout(nq_lbadmm* h) {
     h->s1c = (float*)(b + o_s1c); h->s2c = (float*)(b + o_s2c);
     h->SU = (int8_t*)(b + o_SU); h->SV = (int8_t*)(b + o_SV);
     h->st = (DevStats*)(b + o_st);
+    h->rhs_part = (float*)(b + o_rp);
   }
   return a.off;
 }
@@ -275,13 +283,15 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   g.A = x.Wside; g.lda = x.K; g.B = x.otherT; g.ldb = x.K; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
   g.yield = overlap ? h->rhs_yield : 0;
+  g.free_xcd7 = overlap && h->pin ? 1 : 0;
+  g.part = h->rhs_part;
   long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, gs);
   HIPCHK(launch_gemm(g, kEpiRhs, gs));
   prof_end(h, pr, gs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
   // Minv is the chain's L^-1 scratch; only G^-1 is read afterwards
   HIPCHK(launch_cholesky_inverse(h->G, h->Minv, h->Ginv, rp, (int)h->d.r, h->st, false, false,
-                                 s));
+                                 s, overlap && h->pin));
   prof_end(h, pc, s);
   if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
   // out = R G^-1 (G^-1 symmetric, so it is its own transposed operand),
@@ -366,6 +376,15 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   }
   layout(h);
   if (const char* y = std::getenv("NQ_RHS_YIELD")) h->rhs_yield = std::max(0, std::atoi(y));
+  {
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      h->pin = ncu == kPinGrid && cholesky_pinnable(h->rp, false);
+    if (const char* y = std::getenv("NQ_PIN")) h->pin = h->pin && std::atoi(y) != 0;
+    bool rr = false;
+    if (h->pin && xcd_round_robin_ok(&rr) == hipSuccess) h->pin = rr;
+    else h->pin = false;
+  }
   e = hipStreamCreateWithFlags(&h->gemm_s, hipStreamNonBlocking);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_gram, hipEventDisableTiming);

@@ -295,4 +295,30 @@ hipError_t launch_zero(float* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Whether consecutive workgroups of a 256-workgroup launch go to consecutive
+// XCDs (the layout the pinned chain and the XCD-7-free GEMM rely on): one
+// probe launch, checked on the host. Synchronous; called once per handle.
+namespace {
+__global__ void xcd_probe_kernel(int* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = xcd_id();
+}
+}  // namespace
+
+hipError_t xcd_round_robin_ok(bool* ok) {
+  *ok = false;
+  int* d = nullptr;
+  hipError_t e = hipMalloc((void**)&d, 256 * sizeof(int));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(256), dim3(64), 0, 0, d);
+  int h[256];
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
+  (void)hipFree(d);
+  if (e != hipSuccess) return e;
+  bool good = true;
+  for (int b = 0; b < 256; ++b) good = good && h[b] == (h[0] + b) % 8;
+  *ok = good;
+  return hipSuccess;
+}
+
 }  // namespace nq
