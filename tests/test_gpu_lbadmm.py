@@ -158,3 +158,32 @@ def test_profile_phases(gpu, profile):
         assert all(prof[p][1] > 0 for p in others)
     plain, _ = run_gpu(L, 70, 3, gpu)
     np.testing.assert_array_equal(H(res.U), H(plain.U))
+
+
+@pytest.mark.parametrize("shape", [(512, 384, 1100), (768, 640, 300)])
+def test_launch_layouts_agree(gpu, shape, monkeypatch):
+    """The pinned overlap (the chain's diagonal work on one XCD, the RHS GEMM
+    on the others with leftover tiles split along K), the unpinned overlap
+    and the single-stream order compute the same iteration."""
+    import sub_bit_weight_lb_amd as nq
+    m, n, r = shape
+    L = make_tiny(m, n, r, seed=21 + r, iters=2)
+    outs = {}
+    for name, env, single in (("default", None, False), ("unpinned", "0", False),
+                              ("single", None, True)):
+        if env is None:
+            monkeypatch.delenv("NQ_PIN", raising=False)
+        else:
+            monkeypatch.setenv("NQ_PIN", env)
+        h = nq.LBADMM(m, n, r, iters=2, single_stream=single)
+        res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+        outs[name] = {k: H(v) for k, v in h.state().items()}
+        h.close()
+        print(f"case {shape} layout {name}: err {res.stats['rel_err_wtilde']:.6f}", flush=True)
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    ref = O.iterate(Wt, O.init_state(Wt, r, 5, EU=L.EU, EV=L.EV), 1.0, 5, 2)
+    for name, st in outs.items():
+        assert relerr(st["U"], ref.U) < 1e-4, (name, relerr(st["U"], ref.U))
+        assert relerr(st["V"], ref.V) < 1e-4, (name, relerr(st["V"], ref.V))
+        for k in ("U", "V", "Lam_U", "Lam_V"):
+            assert relerr(st[k], outs["single"][k]) < 2e-5, (name, k, relerr(st[k], outs["single"][k]))
