@@ -204,6 +204,18 @@ __device__ __forceinline__ void store_quad(const f32x16& acc, const f32x16& prev
 #pragma unroll
   for (int v = 0; v < 16; ++v) out[(int64_t)qrow(qm, v) * rp + qcol(qn)] = fmaf(alpha, acc[v], prev[v]);
 }
+// The transpose of quadrant (qm, qn) of a tile, v = alpha acc, into outT
+// (ld rp): lane l holds column qn 32 + l % 32, rows qm 32 + 8 g + 4 (l / 32)
+// + 0..3 in registers 4 g .. 4 g + 3, one float4 each.
+__device__ __forceinline__ void store_quad_t(const f32x16& acc, float* outT, int rp, float alpha,
+                                             int qm, int qn) {
+  const int lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
+  float* row = outT + (int64_t)(qn * 32 + l32) * rp + qm * 32 + 4 * h;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *(f32x4*)&row[8 * g] = f32x4{alpha * acc[4 * g], alpha * acc[4 * g + 1],
+                                 alpha * acc[4 * g + 2], alpha * acc[4 * g + 3]};
+}
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
@@ -250,7 +262,7 @@ __device__ __forceinline__ void store_symacc(const f32x16& acc, const f32x16& pr
 template <bool M_LDS, bool WRITE_L>
 __device__ __forceinline__ void diag_part1(const float* Tin, float* M0, float* L0, int rp,
                                            int row0, int r_real, DiagSmem& sm,
-                                           uint64_t& badmask) {
+                                           uint64_t& badmask, float* Mt0) {
   const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
   const int ldm = M_LDS ? TS : rp;  // M0 is Tin itself when M_LDS
   float r[32];
@@ -291,6 +303,10 @@ __device__ __forceinline__ void diag_part1(const float* Tin, float* M0, float* L
         M0[q * ldm + i] = r[q];
         M0[q * ldm + 32 + i] = 0.0f;
       }
+      if (Mt0) {  // M^T, ld rp: row i of M11^T, and zeros below it in M^T
+        Mt0[(int64_t)i * rp + q] = r[q];
+        Mt0[(int64_t)(32 + i) * rp + q] = 0.0f;
+      }
       sm.Mc[i][q] = r[q];
     }
   }
@@ -317,7 +333,7 @@ __device__ __forceinline__ f32x4 mm16(FA fa, FB fb, f32x4 c) {
 // 32 + i of badmask for a bad pivot in row 32 + i.
 template <bool M_LDS, bool WRITE_L>
 __device__ __forceinline__ void diag_factor2(float* M0, float* L0, int rp, int row0, int r_real,
-                                             DiagSmem& sm, uint64_t& badmask) {
+                                             DiagSmem& sm, uint64_t& badmask, float* Mt0) {
   const int lane = threadIdx.x, i = lane & 31, h = lane >> 5;
   const int ldm = M_LDS ? TS : rp;
   float r[32];
@@ -346,6 +362,7 @@ __device__ __forceinline__ void diag_factor2(float* M0, float* L0, int rp, int r
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
       if (M0) M0[(32 + q) * ldm + 32 + i] = r[q];
+      if (Mt0) Mt0[(int64_t)(32 + i) * rp + 32 + q] = r[q];
       sm.Nc[i][q] = r[q];
     }
   }
@@ -414,7 +431,7 @@ __device__ __forceinline__ void side_quad(const SideJob& j, int qm, int qn) {
 template <bool M_LDS, bool WRITE_L, bool TB>
 __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* M0, float* L0,
                                           int r_real, DevStats* st, StepSmem& sm,
-                                          const SideJob& side) {
+                                          const SideJob& side, float* Mt0 = nullptr) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i16 = lane & 15, g = lane >> 4;
   const int bi = wave & 1, bj = wave >> 1;
@@ -427,7 +444,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
   diag_input(A, rp, k, sm);
   if (wave == 0) {
     wave_lds_sync();  // T11 was written by other lanes of this wave
-    diag_part1<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, d, bad);
+    diag_part1<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, d, bad, Mt0);
   } else if (wave == 3 && side.active) {
     side_quad<TB>(side, 0, 1);
     __threadfence_block();
@@ -465,7 +482,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
   __syncthreads();
   // 4
   if (wave == 0) {
-    diag_factor2<M_LDS, WRITE_L>(M0, L0, rp, row0, r_real, d, bad);
+    diag_factor2<M_LDS, WRITE_L>(M0, L0, rp, row0, r_real, d, bad, Mt0);
   } else if (side.active) {
     side_quad<TB>(side, wave == 1 ? 0 : 1, wave == 3 ? 1 : 0);
     __threadfence_block();
@@ -479,6 +496,9 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
     if (M0) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) M0[(32 + 16 * bi + 4 * g + v) * ldm + 16 * bj + i16] = c[v];
+    }
+    if (Mt0) {  // M21^T: rows 16 bj + i16, columns 32 + 16 bi + 4 g .. + 3
+      *(f32x4*)&Mt0[(int64_t)(16 * bj + i16) * rp + 32 + 16 * bi + 4 * g] = c;
     }
   }
   if (st && wave == 0 && bad && lane == 0)
@@ -500,7 +520,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float* Ginv, int rp,
                                                        int k, int r_real, int want_L,
                                                        int upd_blocks, DevStats* st, int pin,
-                                                       int ndiag, int dtiles) {
+                                                       int ndiag, int dtiles, float* Mt) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) StepSmem sm;
   const int R = rp / NB;
@@ -532,7 +552,8 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     if (k < R) {
       if (b == 0) {  // M_kk
         diag_step<false, false, true>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm,
-                                      SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false});
+                                      SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false},
+                                      Mt ? Mt + kk * rp + kk : nullptr);
         return true;
       }
       b -= 1;
@@ -561,6 +582,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
         const f32x16 acc = mm_quad<false, false>(sm.T, TS, Mkj, rp, qm, qn);  // M_kk S_kj
         __syncthreads();
         store_quad(acc, zero16(), Mkj, rp, -1.0f, qm, qn);
+        if (Mt) store_quad_t(acc, Mt + j0 * rp + kk, rp, -1.0f, qm, qn);
         return true;
       }
       b -= k;
@@ -654,7 +676,7 @@ bool cholesky_pinnable(int rp, bool want_L) {
 
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
-                                   bool pin) {
+                                   bool pin, float* Mt) {
   if (rp % NB) return hipErrorInvalidValue;
   if (pin && !cholesky_pinnable(rp, want_L)) return hipErrorInvalidValue;
   const int R = rp / NB;
@@ -682,7 +704,7 @@ hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int 
     if (nb + upd > 0)
       hipLaunchKernelGGL(chol_step_kernel, dim3(pin ? kPinGrid : nb + upd), dim3(NT), 0, s, A, M,
                          Ginv, rp, k, r_real, want_L ? 1 : 0, std::max(upd, 1), st,
-                         pin ? 1 : 0, nb, pin ? std::min(upd_tiles, pin_diag_tiles()) : 0);
+                         pin ? 1 : 0, nb, pin ? std::min(upd_tiles, pin_diag_tiles()) : 0, Mt);
   }
   if (!want_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;

@@ -75,16 +75,35 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 size_t rhs_part_floats(int M, int N, int K);
 
 // ---------------------------------------------------------------- Gram
-// Work split of G = A^T A (lower 128 x 128 tiles, tiles x K / 32 steps of 32)
-// into equal ranges of `steps` steps, one per workgroup (`wgs` of them); a
-// tile's segments go to at most `slots` partial buffers of rp x rp.
-struct GramPlan {
-  int steps, wgs, slots;
+// K steps (of 32) of the lower 128 x 128 tiles of a Gram product, tile
+// t = I (I + 1) / 2 + J (I >= J) in that order: T steps each, or with tri
+// (A upper triangular, K = rp: rows of A below row 128 I of tile row I's
+// panel are zero) T - 4 I steps from step 4 I.
+struct GramSteps {
+  int T, tri;
+  __host__ __device__ int len(int I) const { return tri ? T - 4 * I : T; }
+  __host__ __device__ int first(int I) const { return tri ? 4 * I : 0; }
+  // steps of the tile rows before row I
+  __host__ __device__ int64_t row_start(int I) const {
+    const int64_t i = I;
+    return (int64_t)T * i * (i + 1) / 2 - (tri ? 4 * (i - 1) * i * (i + 1) / 3 : 0);
+  }
+  // steps before tile (I, J)
+  __host__ __device__ int64_t tile_start(int I, int J) const {
+    return row_start(I) + (int64_t)J * len(I);
+  }
 };
-GramPlan gram_plan(int K, int rp);
+// Work split of a Gram product (GramSteps over R = rp / 128 tile rows) into
+// equal ranges of `steps` steps, one per workgroup (`wgs` of them); a tile's
+// segments go to at most `slots` partial buffers of rp x rp.
+struct GramPlan {
+  int steps, wgs, slots, tri;
+};
+GramPlan gram_plan(int K, int rp, bool tri = false);
 // Partial Gram tiles of A^T A for A (K x rp) given as At = A^T (rp x K, ld
 // ldat) into part (p.slots buffers of rp x rp, ld rp; lower tiles only).
-// rp % 128 == 0, K a multiple of 32.
+// rp % 128 == 0, K a multiple of 32; with p.tri, K == rp and A upper
+// triangular (At lower triangular), whose zero K ranges are skipped.
 hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, const GramPlan& p,
                                float* part, hipStream_t s);
 // G = the sum of each lower tile's segments, in slot order, + rho I (ld ldg):
@@ -108,9 +127,12 @@ constexpr int kNB = 64;  // block size of the blocked Cholesky
 // update tiles on XCDs 0-6, for a run beside a GEMM that leaves XCD 7 free;
 // needs cholesky_pinnable (at most kPinDiagSlots diagonal workgroups).
 bool cholesky_pinnable(int rp, bool want_L);
+// Mt (nullable): the upper block triangle of M^T (the lower blocks are never
+// written and must read as zero), for a G^-1 = M^T M formed outside the
+// chain (Ginv null).
 hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
-                                   bool pin = false);
+                                   bool pin = false, float* Mt = nullptr);
 
 // ---------------------------------------------------------------- SVID
 struct SvidWork {

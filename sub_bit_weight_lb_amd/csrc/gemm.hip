@@ -333,15 +333,16 @@ __global__ __launch_bounds__(256) void rhs_fixup_kernel(GemmArgs p, int F, int n
   *(f32x4*)&p.C[idx] = sum + p.rho * *(const f32x4*)&p.P[idx];
 }
 
-// Partial Gram tiles, stream-K: the tiles x T K steps of 32 (lower tile t =
-// I (I + 1) / 2 + J, I >= J, both operands the rows I and J panels of At)
-// are cut into ranges of L steps, one per workgroup, so every workgroup has
-// the same work. A range covers the end of one tile and the start of the
-// next; each segment goes to slot w - w0(t) of its tile, w0(t) = t T / L
-// being the first workgroup that touches tile t.
+// Partial Gram tiles, stream-K: the K steps of 32 of the lower tiles (tile
+// t = I (I + 1) / 2 + J, I >= J, both operands the rows I and J panels of
+// At; GramSteps gives each tile's steps) are cut into ranges of L steps, one
+// per workgroup, so every workgroup has the same work. A range covers the
+// end of one tile and the start of the next; each segment goes to slot
+// w - w0(t) of its tile, w0(t) = (steps before tile t) / L being the first
+// workgroup that touches tile t.
 __global__ __launch_bounds__(NT, 2) void gram_nt_kernel(const float* __restrict__ At,
-                                                        int64_t ldat, int rp, int T, int L,
-                                                        int64_t S, int W,
+                                                        int64_t ldat, int rp, GramSteps gs,
+                                                        int L, int64_t S, int W,
                                                         float* __restrict__ part) {
   constexpr int TM = 128;
   using T_ = Tile<TM>;
@@ -352,17 +353,19 @@ __global__ __launch_bounds__(NT, 2) void gram_nt_kernel(const float* __restrict_
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   float* stage = lds + wave * 32 * 36;
+  const int R = rp / TM;
+  int I = 0;
   while (s0 < s1) {
-    const int t = (int)(s0 / T), ks = (int)(s0 % T);
-    const int ke = (int)min<int64_t>(T, ks + (s1 - s0));
-    int I = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while ((I + 1) * (I + 2) / 2 <= t) ++I;
-    while (I * (I + 1) / 2 > t) --I;
-    const int J = t - I * (I + 1) / 2;
-    const int slot = w - (int)((int64_t)t * T / L);
+    // tile row I holding step s0 (rows only move forward)
+    while (I + 1 < R && gs.row_start(I + 1) <= s0) ++I;
+    const int len = gs.len(I);
+    const int64_t off = s0 - gs.row_start(I);
+    const int J = (int)(off / len), ks = (int)(off % len);
+    const int ke = (int)min<int64_t>(len, ks + (s1 - s0));
+    const int slot = w - (int)(gs.tile_start(I, J) / L);
     f32x16 acc[T_::MI][2];
     nt_mainloop<TM>(At + (int64_t)I * TM * ldat, (int)ldat, At + (int64_t)J * TN * ldat,
-                    (int)ldat, ks * BK, ke - ks, lds, acc);
+                    (int)ldat, (gs.first(I) + ks) * BK, ke - ks, lds, acc);
     float* out = part + (int64_t)slot * rp * rp;
 #pragma unroll
     for (int mi = 0; mi < T_::MI; ++mi)
@@ -425,18 +428,19 @@ size_t rhs_part_floats(int M, int N, int K) {
   return (size_t)E * C * 256 * TN;
 }
 
-GramPlan gram_plan(int K, int rp) {
+GramPlan gram_plan(int K, int rp, bool tri) {
   GramPlan p{};
   const int R = rp / 128;
-  const int64_t tiles = (int64_t)R * (R + 1) / 2;
   const int T = K / BK;
-  const int64_t S = tiles * T;
+  const GramSteps gs{T, tri ? 1 : 0};
+  const int64_t S = gs.row_start(R);
   // two workgroups per CU; a tile gets at most 8 segments
   int64_t L = std::max<int64_t>((S + 511) / 512, (T + 6) / 7);
   L = std::max<int64_t>(L, 1);
   p.steps = (int)L;
   p.wgs = (int)((S + L - 1) / L);
   p.slots = (int)((T + L - 1) / L) + 1;
+  p.tri = tri ? 1 : 0;
   return p;
 }
 
@@ -445,10 +449,12 @@ hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, con
   if (rp % 128 || K % BK || K <= 0 || ldat % 4 || ldat < K || !aligned16(At) || p.steps <= 0)
     return hipErrorInvalidValue;
   if ((int64_t)128 * ldat * 4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
+  if (p.tri && K != rp) return hipErrorInvalidValue;
   const int R = rp / 128;
-  const int64_t S = (int64_t)R * (R + 1) / 2 * (K / BK);
-  hipLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, At, ldat, rp, K / BK, p.steps,
-                     S, p.wgs, part);
+  const GramSteps gs{K / BK, p.tri};
+  const int64_t S = gs.row_start(R);
+  hipLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, At, ldat, rp, gs, p.steps, S,
+                     p.wgs, part);
   return hipGetLastError();
 }
 

@@ -13,9 +13,10 @@ namespace {
 // Full symmetric G from the lower triangles of the partial tiles.
 // 32 x 32 output tiles, 32 x 8 threads; upper tiles read the mirrored lower
 // tile and transpose it through LDS; diagonal tiles pick per element.
-__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int T,
-                                                          int L, int rp, float rho, int full,
-                                                          float* __restrict__ G, int64_t ldg) {
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part,
+                                                          GramSteps gs, int L, int rp, float rho,
+                                                          int full, float* __restrict__ G,
+                                                          int64_t ldg) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ float tile[32][33];
   const int ti = blockIdx.y, tj = blockIdx.x;
@@ -28,8 +29,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
   const int sj = ti >= tj ? tj : ti;
   // segments of the 128 x 128 Gram tile holding it: workgroups w0 .. w1
   const int I = si / 4, J = sj / 4;
-  const int64_t t = (int64_t)I * (I + 1) / 2 + J;
-  const int nseg = (int)(((t + 1) * T - 1) / L - t * T / L) + 1;
+  const int64_t t0 = gs.tile_start(I, J);
+  const int nseg = (int)((t0 + gs.len(I) - 1) / L - t0 / L) + 1;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = ty + 8 * q;
@@ -60,8 +61,8 @@ hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& 
   dim3 grid(rp / 32, rp / 32), block(256);
   // `done` is recorded by the kernel's own completion (no marker of its own
   // between this kernel and the next one on s)
-  hipExtLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, nullptr, done, 0u, part, K / 32,
-                        p.steps, rp, rho, full ? 1 : 0, G, ldg);
+  hipExtLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, nullptr, done, 0u, part,
+                        GramSteps{K / 32, p.tri}, p.steps, rp, rho, full ? 1 : 0, G, ldg);
   return hipGetLastError();
 }
 
