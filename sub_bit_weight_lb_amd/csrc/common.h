@@ -105,7 +105,7 @@ GramPlan gram_plan(int K, int rp, bool tri = false);
 // rp % 128 == 0, K a multiple of 32; with p.tri, K == rp and A upper
 // triangular (At lower triangular), whose zero K ranges are skipped.
 hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, const GramPlan& p,
-                               float* part, hipStream_t s);
+                               float* part, hipStream_t s, hipEvent_t done = nullptr);
 // G = the sum of each lower tile's segments, in slot order, + rho I (ld ldg):
 // full-symmetric if `full`, else the lower triangle and the whole of each
 // 64 x 64 diagonal block (what the blocked Cholesky reads). `done`

@@ -32,6 +32,8 @@
 //   L2.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -445,7 +447,7 @@ GramPlan gram_plan(int K, int rp, bool tri) {
 }
 
 hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, const GramPlan& p,
-                               float* part, hipStream_t s) {
+                               float* part, hipStream_t s, hipEvent_t done) {
   if (rp % 128 || K % BK || K <= 0 || ldat % 4 || ldat < K || !aligned16(At) || p.steps <= 0)
     return hipErrorInvalidValue;
   if ((int64_t)128 * ldat * 4 >= (int64_t)1 << 31) return hipErrorInvalidValue;
@@ -453,8 +455,10 @@ hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, con
   const int R = rp / 128;
   const GramSteps gs{K / BK, p.tri};
   const int64_t S = gs.row_start(R);
-  hipLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, At, ldat, rp, gs, p.steps, S,
-                     p.wgs, part);
+  // `done` is recorded by the kernel's own completion (no marker of its own
+  // between this kernel and the next one on s)
+  hipExtLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, nullptr, done, 0u, At, ldat,
+                        rp, gs, p.steps, S, p.wgs, part);
   return hipGetLastError();
 }
 

@@ -276,11 +276,12 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   hipStream_t gs = overlap ? h->gemm_s : s;
   long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
   // G = other^T other + rho I from other^T (rp x K)
-  HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s));
-  // ev_gram is recorded by the reduction's own completion: an event record
-  // of its own would put a marker (~8 us) between the Gram and the chain
-  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, false, h->G, rp, s,
-                            overlap ? h->ev_gram : nullptr));
+  // ev_gram is recorded by the Gram kernel's own completion (an event record
+  // of its own would put a marker, ~8 us, on s): the RHS GEMM, which does not
+  // read G, starts beside the short reduction
+  HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s,
+                             overlap ? h->ev_gram : nullptr));
+  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, false, h->G, rp, s));
   if (overlap) HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
   // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last
   // SVID, earlier on the same stream. Enqueued before the chain's launches:

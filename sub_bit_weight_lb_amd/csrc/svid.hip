@@ -14,7 +14,11 @@
 // ADMM update the first pass also forms X = U + Lam from the new factor and
 // the dual (written over Lam), so the solve that produces U does not. For
 // r beyond 16384 a row pass and a column pass replace the fused one. All
-// reductions run in a fixed order, so results are bit-reproducible.
+// reductions run in a fixed order, so results are bit-reproducible. Every
+// kernel raises its waves' issue priority: in the ADMM loop the SVID runs
+// beside the solve and the next Gram, MFMA-bound kernels whose waves would
+// otherwise take most issue cycles of a shared SIMD, and the next RHS GEMM
+// waits for it.
 #include "common.h"
 
 namespace nq {
@@ -30,6 +34,7 @@ __device__ inline float wave_sum(float v) {
 }
 
 __global__ void svid_init_b_kernel(float* b, float* bbpart, int rp, int r_real) {
+  __builtin_amdgcn_s_setprio(3);
   const int j = blockIdx.x * CB + threadIdx.x;
   b[j] = j < r_real ? 1.0f : 0.0f;
   if (threadIdx.x == 0) {
@@ -113,6 +118,7 @@ __global__ __launch_bounds__(256) void svid_step_kernel(float* X, const float* _
                                                         float* __restrict__ a,
                                                         float* __restrict__ part,
                                                         float* __restrict__ aapart) {
+  __builtin_amdgcn_s_setprio(3);
   __shared__ float red[RS][4];
   __shared__ float arow[RS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(256) void svid_step_kernel(float* X, const float* _
 constexpr int NY = kSvidReduceRows;  // row groups of the reduce
 __global__ __launch_bounds__(256) void svid_reduce1_kernel(const float* __restrict__ part, int nch,
                                                            int rp, float* __restrict__ part2) {
+  __builtin_amdgcn_s_setprio(3);
   __shared__ f32x4 red[8][32];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int q = blockIdx.x * 32 + tx;  // float4 column index
@@ -222,6 +229,7 @@ __global__ __launch_bounds__(256) void svid_reduce2_kernel(const float* __restri
                                                            const float* __restrict__ aapart,
                                                            int nch, int rp, float* __restrict__ b,
                                                            float* __restrict__ bbpart) {
+  __builtin_amdgcn_s_setprio(3);
   __shared__ float fred[256];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int q = blockIdx.x * 32 + tx;
@@ -260,6 +268,7 @@ __global__ __launch_bounds__(256) void svid_final_kernel(float* __restrict__ X,
                                                          const float* __restrict__ a,
                                                          const float* __restrict__ b, int rp,
                                                          int64_t n4, int mode) {
+  __builtin_amdgcn_s_setprio(3);
   const int rp4 = rp / 4;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4;
        q += (int64_t)gridDim.x * blockDim.x) {

@@ -10,46 +10,68 @@
 namespace nq {
 namespace {
 
-// Full symmetric G from the lower triangles of the partial tiles.
-// 32 x 32 output tiles, 32 x 8 threads; upper tiles read the mirrored lower
-// tile and transpose it through LDS; diagonal tiles pick per element.
+// G from the partial tiles. Workgroup (q, t): rows 32 q .. 32 q + 31 of
+// lower Gram tile t = I (I + 1) / 2 + J. Each thread loads its 4 float4s
+// from every segment at once, sums them in slot order, and stores the strip
+// into G (+ rho on the diagonal; in a diagonal tile only its lower half);
+// the mirror above the diagonal (all of it if `full`, else inside the
+// 64 x 64 diagonal blocks) goes through LDS as 128 rows of 32.
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part,
                                                           GramSteps gs, int L, int rp, float rho,
                                                           int full, float* __restrict__ G,
                                                           int64_t ldg) {
   __builtin_amdgcn_s_setprio(3);
-  __shared__ float tile[32][33];
-  const int ti = blockIdx.y, tj = blockIdx.x;
-  // without `full`, only what the blocked Cholesky reads: the lower triangle
-  // and the whole of each 64 x 64 diagonal block
-  if (!full && ti < tj && (ti >> 1) != (tj >> 1)) return;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const int64_t stride = (int64_t)rp * rp;
-  const int si = ti >= tj ? ti : tj;  // source tile (lower triangle)
-  const int sj = ti >= tj ? tj : ti;
-  // segments of the 128 x 128 Gram tile holding it: workgroups w0 .. w1
-  const int I = si / 4, J = sj / 4;
+  __shared__ float tile[32][129];
+  const int t = blockIdx.y;
+  int I = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+  while (I * (I + 1) / 2 > t) --I;
+  while ((I + 1) * (I + 2) / 2 <= t) ++I;
+  const int J = t - I * (I + 1) / 2;
   const int64_t t0 = gs.tile_start(I, J);
   const int nseg = (int)((t0 + gs.len(I) - 1) / L - t0 / L) + 1;
+  const int64_t stride = (int64_t)rp * rp;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int r0 = I * 128 + blockIdx.x * 32, c0 = J * 128;
+  const int gj = c0 + tx * 4;
+  f32x4 v[4];
+  {
+    const float* src = part + (int64_t)(r0 + ty) * rp + gj;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = ty + 8 * q;
-    const int64_t src = (int64_t)(si * 32 + r) * rp + sj * 32 + tx;
-    float acc = 0.0f;
-    for (int c = 0; c < nseg; ++c) acc += part[c * stride + src];
-    tile[r][tx] = acc;
+    for (int k = 0; k < 4; ++k) v[k] = *(const f32x4*)(src + (int64_t)8 * k * rp);
+    for (int c = 1; c < nseg; ++c) {
+      f32x4 w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) w[k] = *(const f32x4*)(src + c * stride + (int64_t)8 * k * rp);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] += w[k];
+    }
   }
-  __syncthreads();
+  const bool diag = I == J;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = ty + 8 * q;
-    float v;
-    if (ti > tj) v = tile[r][tx];
-    else if (ti < tj) v = tile[tx][r];
-    else v = (r >= tx) ? tile[r][tx] : tile[tx][r];
-    const int gi = ti * 32 + r, gj = tj * 32 + tx;
-    if (gi == gj) v += rho;
-    G[(int64_t)gi * ldg + gj] = v;
+  for (int k = 0; k < 4; ++k) {
+    const int gi = r0 + ty + 8 * k;
+    float* dst = G + (int64_t)gi * ldg + gj;
+    if (!diag) {
+      *(f32x4*)dst = v[k];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gi == gj + e) dst[e] = v[k][e] + rho;
+        else if (gi > gj + e) dst[e] = v[k][e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[ty + 8 * k][tx * 4 + e] = v[k][e];
+  }
+  // mirror: rows c0 .. c0 + 127 of G, columns r0 .. r0 + 31
+  // (an off-diagonal tile has no element inside a 64 x 64 diagonal block)
+  if (!full && !diag) return;
+  __syncthreads();
+  const int gi = r0 + tx;
+#pragma unroll 4
+  for (int k = 0; k < 16; ++k) {
+    const int cc = ty + 8 * k, gq = c0 + cc;
+    if (gi > gq && (full || (gi >> 6) == (gq >> 6))) G[(int64_t)gq * ldg + gi] = tile[tx][cc];
   }
 }
 
@@ -58,7 +80,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 hipError_t launch_gram_reduce(const float* part, int K, int rp, const GramPlan& p, float rho,
                               bool full, float* G, int64_t ldg, hipStream_t s, hipEvent_t done) {
   if (rp % 128 || K % 32 || p.steps <= 0) return hipErrorInvalidValue;
-  dim3 grid(rp / 32, rp / 32), block(256);
+  const int R = rp / 128;
+  dim3 grid(4, R * (R + 1) / 2), block(256);
   // `done` is recorded by the kernel's own completion (no marker of its own
   // between this kernel and the next one on s)
   hipExtLaunchKernelGGL(gram_reduce_kernel, grid, block, 0, s, nullptr, done, 0u, part,
