@@ -1,21 +1,26 @@
-// Blocked Cholesky factorisation with the inverse factor and G^-1: G = L L^T,
-// M = L^-1 and G^-1 = M^T M, for the ridge-regularised system matrix
+// Blocked Cholesky factorisation with the inverse factor: G = L L^T and
+// M = L^-1 (and M^T), for the ridge-regularised system matrix
 // G = V^T V + rho I of the regularised solve (NanoQuant digest, section
 // 核心方法, step (a): the linear system is solved through a Cholesky
 // factorisation; the implementation blog, section 待办事项, names this
 // factorisation as where LB-ADMM spends its time).
 //
 // Right-looking, block size 64 (R = rp / 64 block columns), one launch per
-// block column k plus one (k = 0 .. R). Launch k holds
+// block column k (k = 0 .. R - 1; one more, k = R, only when L itself is
+// wanted). Launch k holds
 //   - the panel of step k: L_ik = (A_ik - L_{i,k-1} L_{k,k-1}^T) M_kk^T,
 //     i > k, each tile applying the last update of step k - 1 itself;
 //   - row k of the inverse: M_kj = -M_kk (S_kj + L_{k,k-1} M_{k-1,j}), j < k;
 //   - M_kk itself;
 //   - the rest of step k - 1: trailing update A_ij -= L_{i,k-1} L_{j,k-1}^T
-//     (i >= j > k), inverse partial sums S_ij += L_{i,k-1} M_{k-1,j}
-//     (i > k, j < k), and the G^-1 contribution of row k - 1 of M,
-//     G^-1_ij += M_{k-1,i}^T M_{k-1,j} (j <= i < k);
+//     (i >= j > k) and inverse partial sums S_ij += L_{i,k-1} M_{k-1,j}
+//     (i > k, j < k);
 //   - optionally L_{k-1,k-1} (only when L itself is wanted).
+// Optionally M^T as well (M_kk and each inverse-row tile stored transposed),
+// the operand of G^-1 = M^T M, which a triangular Gram product forms
+// afterwards (G^-1 used to be accumulated here, row by row of M, as a third
+// kind of update tile; the update tiles run beside the RHS GEMM, so that
+// work now waits for the chain's end).
 // Every workgroup that needs M_kk (panel and inverse-row tiles) factors the
 // diagonal tile A_kk - L_{k,k-1} L_{k,k-1}^T itself: some 32 CUs each do
 // the same 64 x 64 factorisation, and no launch is spent on the diagonal
@@ -221,24 +226,6 @@ __device__ __forceinline__ f32x16 zero16() {
 #pragma unroll
   for (int v = 0; v < 16; ++v) z[v] = 0.0f;
   return z;
-}
-
-// Symmetric accumulate into G^-1: out is tile (i, j), i >= j, and out2 its
-// mirror (j, i) (out2 == out on the diagonal, where only the lower triangle
-// of the product is used). v = acc + prev (the old lower tile, or zero for
-// its first contribution) goes to out and, transposed, to out2, so both
-// halves hold the same sums and G^-1 is exactly symmetric.
-__device__ __forceinline__ void store_symacc(const f32x16& acc, const f32x16& prev, float* out,
-                                             float* out2, int rp) {
-  const int qm = wave_qm(), qn = wave_qn();
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int row = qrow(qm, v), col = qcol(qn);
-    if (out2 == out && col > row) continue;
-    const float val = acc[v] + prev[v];
-    out[(int64_t)row * rp + col] = val;
-    out2[(int64_t)col * rp + row] = val;
-  }
 }
 
 // Diagonal tile: Tin (LDS, stride TS) holds the lower blocks T11, T21, T22
@@ -509,7 +496,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 // Launch k of the factorisation (see the file header). Workgroups, in order:
 //   [k < R]  1 diagonal (writes M_kk), R-1-k panel tiles, k inverse-row tiles;
 //   [k >= 1] 1 with want_L (writes L_{k-1,k-1}), n(n+1)/2 trailing tiles
-//            (n = R-1-k), n k partial sums, k(k+1)/2 G^-1 tiles if Ginv.
+//            (n = R-1-k), n k partial sums.
 // With pin (a 256-workgroup grid: 32 workgroups on each of the 8 XCDs), the
 // ndiag workgroups that factor a diagonal tile are those on XCD 7, one per
 // CU, and the update workgroups those on XCDs 0-6; the others exit. A GEMM
@@ -517,7 +504,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 // the diagonal work. The XCD comes from the hardware register: consecutive
 // workgroups go to consecutive XCDs, but the first one's XCD depends on the
 // queue's history.
-__global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float* Ginv, int rp,
+__global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, int rp,
                                                        int k, int r_real, int want_L,
                                                        int upd_blocks, DevStats* st, int pin,
                                                        int ndiag, int dtiles, float* Mt) {
@@ -607,8 +594,7 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
   // workgroups to be resident at once beside a concurrently running GEMM.
   const int nT = n > 0 ? n * (n + 1) / 2 : 0;
   const int nS = n > 0 ? n * k : 0;
-  const int nG = Ginv ? k * (k + 1) / 2 : 0;
-  // Global tile index t over the three ranges; a workgroup takes t = first,
+  // Global tile index t over the two ranges; a workgroup takes t = first,
   // first + step, ... below t_hi. Inside the loops the row stride is re-read
   // through an empty asm, so the per-lane 64-bit fragment offsets are formed
   // per tile rather than hoisted out of the loop, where they would hold ~100
@@ -637,18 +623,6 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, float
     const f32x16 acc = mm_quad<false, false>(A + i0 * ld + pp, ld, M + pp * ld + j0, ld, qm, qn);
     store_quad(acc, prev, M + i0 * ld + j0, ld, 1.0f, qm, qn);
   }
-  if (t < nS) return;
-  const int eG = min(nG, t_hi - nT - nS);
-  for (t -= nS; t < eG; t += t_step) {  // G^-1 tile (i, j), j <= i <= p: += M_pi^T M_pj
-    int ld = rp;
-    asm volatile("" : "+s"(ld));
-    int ii, jj;
-    tri_index(t, ii, jj);
-    const int64_t i0 = (int64_t)ii * NB, j0 = (int64_t)jj * NB;
-    const f32x16 prev = ii == p ? zero16() : load_quad(Ginv + i0 * ld + j0, ld, qm, qn);
-    const f32x16 acc = mm_quad<true, false>(M + pp * ld + i0, ld, M + pp * ld + j0, ld, qm, qn);
-    store_symacc(acc, prev, Ginv + i0 * ld + j0, Ginv + j0 * ld + i0, ld);
-  }
 }
 
 __global__ void zero_upper_kernel(float* A, int rp) {
@@ -674,7 +648,7 @@ bool cholesky_pinnable(int rp, bool want_L) {
   return rp % NB == 0 && rp / NB + (want_L ? 1 : 0) <= kPinDiagSlots;
 }
 
-hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
+hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
                                    bool pin, float* Mt) {
   if (rp % NB) return hipErrorInvalidValue;
@@ -690,7 +664,7 @@ hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int 
     int upd = 0, upd_tiles = 0;
     if (k >= 1) {
       nb += want_L ? 1 : 0;
-      const int tiles = (n > 0 ? n * (n + 1) / 2 + n * k : 0) + (Ginv ? k * (k + 1) / 2 : 0);
+      const int tiles = n > 0 ? n * (n + 1) / 2 + n * k : 0;
       upd = upd_tiles = tiles;
       if (pin) {
         upd = std::min(tiles, kPinUpdSlots);
@@ -703,7 +677,7 @@ hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int 
     }
     if (nb + upd > 0)
       hipLaunchKernelGGL(chol_step_kernel, dim3(pin ? kPinGrid : nb + upd), dim3(NT), 0, s, A, M,
-                         Ginv, rp, k, r_real, want_L ? 1 : 0, std::max(upd, 1), st,
+                         rp, k, r_real, want_L ? 1 : 0, std::max(upd, 1), st,
                          pin ? 1 : 0, nb, pin ? std::min(upd_tiles, pin_diag_tiles()) : 0, Mt);
   }
   if (!want_L) return hipGetLastError();

@@ -120,17 +120,16 @@ constexpr int kNB = 64;  // block size of the blocked Cholesky
 // want_L its lower triangle becomes L and its upper triangle zero. The lower
 // 64 x 64 tiles of M (rp x rp) become those of L^-1 (the diagonal tiles with
 // zeros above their diagonal); M's other tiles are not written, and with
-// zero_m M is zeroed first so that they read as zero. Ginv (rp x rp,
-// nullable) becomes G^-1 = M^T M, full and exactly symmetric.
+// zero_m M is zeroed first so that they read as zero.
 // st->potrf_info gets min(1 + failing column).
 // pin: place the diagonal work on XCD 7 (one workgroup per CU) and the
 // update tiles on XCDs 0-6, for a run beside a GEMM that leaves XCD 7 free;
 // needs cholesky_pinnable (at most kPinDiagSlots diagonal workgroups).
 bool cholesky_pinnable(int rp, bool want_L);
 // Mt (nullable): the upper block triangle of M^T (the lower blocks are never
-// written and must read as zero), for a G^-1 = M^T M formed outside the
-// chain (Ginv null).
-hipError_t launch_cholesky_inverse(float* A, float* M, float* Ginv, int rp, int r_real,
+// written and must read as zero), the operand of G^-1 = M^T M
+// (launch_gram_partial with a triangular plan).
+hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
                                    bool pin = false, float* Mt = nullptr);
 

@@ -300,7 +300,7 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   // M = L^-1 (and M^T); G^-1 = M^T M as a triangular Gram product of M^T
   // after the chain, in ~30 us, rather than inside it, where its 38 % of the
   // chain's update tiles would run beside the RHS GEMM
-  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, nullptr, rp, (int)h->d.r, h->st, false, false,
+  HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, false,
                                  s, overlap && h->pin, h->Mt));
   HIPCHK(launch_gram_partial(h->Mt, rp, rp, rp, h->gI, h->gpart, s));
   HIPCHK(launch_gram_reduce(h->gpart, rp, rp, h->gI, 0.0f, true, h->Ginv, rp, s));

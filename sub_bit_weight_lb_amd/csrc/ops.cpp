@@ -128,10 +128,17 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
     return set_error(NQ_ERR_INVALID_ARG, "bad cholesky arguments");
   hipStream_t s = (hipStream_t)stream;
   const int64_t rp = round_up(r, 128);
-  DevBuf a, m, gi, st;
+  DevBuf a, m, mt, part, gi, st;
   NQ_HIPCHK(a.alloc(sizeof(float) * rp * rp));
   NQ_HIPCHK(m.alloc(sizeof(float) * rp * rp));
-  if (Ginv) NQ_HIPCHK(gi.alloc(sizeof(float) * rp * rp));
+  const GramPlan plan = gram_plan((int)rp, (int)rp, true);
+  if (Ginv) {
+    NQ_HIPCHK(mt.alloc(sizeof(float) * rp * rp));
+    NQ_HIPCHK(part.alloc(sizeof(float) * plan.slots * rp * rp));
+    NQ_HIPCHK(gi.alloc(sizeof(float) * rp * rp));
+    // the chain writes only the upper block triangle of M^T
+    NQ_HIPCHK(launch_zero(mt.f(), (size_t)rp * rp, s));
+  }
   NQ_HIPCHK(st.alloc(sizeof(DevStats)));
   DevStats* dst = (DevStats*)st.p;
   NQ_HIPCHK(launch_stats_init(dst, s));
@@ -139,9 +146,15 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* 
   NQ_HIPCHK(stage_in(G, r, r, ldg, a.f(), rp, rp, s));
   NQ_HIPCHK(launch_set_diag(a.f(), rp, (int)r, (int)rp, 1.0f, s));
   // m: L^-1 scratch, not returned (no zeroing needed)
-  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), Ginv ? gi.f() : nullptr, (int)rp, (int)r, dst,
-                                    true, false, s));
-  if (Ginv) NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));
+  NQ_HIPCHK(launch_cholesky_inverse(a.f(), m.f(), (int)rp, (int)r, dst, true, false, s, false,
+                                    Ginv ? mt.f() : nullptr));
+  if (Ginv) {
+    // G^-1 = M^T M, as in the ADMM loop: triangular Gram of M^T, then the
+    // full-symmetric reduction with no shift
+    NQ_HIPCHK(launch_gram_partial(mt.f(), rp, (int)rp, (int)rp, plan, part.f(), s));
+    NQ_HIPCHK(launch_gram_reduce(part.f(), (int)rp, (int)rp, plan, 0.0f, true, gi.f(), rp, s));
+    NQ_HIPCHK(stage_out(gi.f(), rp, Ginv, ldgi, r, r, s));
+  }
   if (L) NQ_HIPCHK(stage_out(a.f(), rp, L, ldl, r, r, s));
   DevStats hs;
   NQ_HIPCHK(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s));
