@@ -6,6 +6,11 @@ events and the error computation on).
   float64 oracle element by element; the whole run against the oracle's
   end-of-run figures stored under tests/golden/ (written by
   tests/golden/make_lbadmm_final.py, which calls only oracle/).
+- The seven layers of one Llama-2-7B-shaped block (q, k, v, o at 4096 x 4096,
+  r = 2048; gate and up at 11008 x 4096 and down at 4096 x 11008, r = 2970,
+  which pads to 3072 and so runs the unpinned overlap): one iteration of q,
+  gate and down against the oracle, and the 40-iteration run of every layer
+  against its stored end-of-run figures.
 - 8192 x 28672, r = 6144: the oracle cannot run an iteration in seconds here,
   so the initial SVID projections are compared in full, the first U-half
   solve through sampled entries of its normal equations U G = R (G and R
@@ -25,6 +30,7 @@ pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 ATTN = "llama2-7b-attn-4096x4096-r2048"
+BLOCK_ONE = ["llama2-7b-block.q_proj", "llama2-7b-block.gate_proj", "llama2-7b-block.down_proj"]
 MLP = "llama2-7b-mlp-11008x4096-r1536"
 DOWN70 = "llama2-70b-down-8192x28672-r6144"
 
@@ -91,7 +97,7 @@ def load_golden(name):
         return json.load(f)
 
 
-@pytest.mark.parametrize("name", [ATTN, MLP])
+@pytest.mark.parametrize("name", [ATTN, MLP] + BLOCK_ONE)
 def test_one_iteration_full_size(gpu, name):
     L = make_layer(name)
     wl = L.workload
