@@ -187,8 +187,9 @@ nq_status nq_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
 
 /* ---- building blocks (the same kernels the run uses; for tests and tools) ----
  * These take caller buffers of any shape, copy into zero-padded temporaries
- * allocated with hipMallocAsync on `stream` (freed on the same stream), run
- * the kernels, and copy results out. They are not meant for the hot path. */
+ * (hipMalloc, freed before the call returns), run the kernels on `stream`,
+ * copy results out and wait for `stream`. They are not meant for the hot
+ * path. */
 
 /* Wt = d_out_i * (W_ij * d_in_j) in float32, the two products rounded in that
  * order ("方法步骤详情": Wt = D_out W D_in). Wt (device) m x n, ld ldwt. */
@@ -209,9 +210,11 @@ nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ld
                          int64_t rows, int64_t cols, int64_t k, void* stream);
 
 /* Cholesky factorisation G = L L^T of an SPD r x r matrix (lower triangle of
- * G read) and the inverse Ginv = L^-T L^-1 (full symmetric). L (device,
- * nullable) receives the factor with zeros above the diagonal. *info (host)
- * is 0 or 1 + the first failing column; the call waits for `stream`. */
+ * G read) and the inverse Ginv = L^-T L^-1 (full symmetric; formed, as in the
+ * run, as the Gram product M^T M of M = L^-1). Ginv (device, nullable)
+ * ld ldgi; L (device, nullable) ld ldl receives the factor with zeros above
+ * the diagonal. *info (host) is 0 or 1 + the first failing column; the call
+ * waits for `stream`. */
 nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg,
                                  float* L, int64_t ldl, float* Ginv, int64_t ldgi,
                                  int64_t* info, void* stream);
