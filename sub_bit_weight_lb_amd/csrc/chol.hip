@@ -228,6 +228,42 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
+// Quadrant (qm, qn) of the 64 x 64 tile at rows r0, columns c0 (r0 >= c0)
+// of a Gram product not yet reduced, in the accumulator layout: the sum of
+// its stream-K segments in slot order, + rho on the diagonal. In a diagonal
+// tile the elements above the diagonal are read from their mirror below it,
+// as the reduction writes them.
+__device__ __forceinline__ f32x16 load_quad_gram(const GramSrc& g, int rp, int r0, int c0, int qm,
+                                                 int qn) {
+  const int I = r0 / 128, J = c0 / 128;
+  const int64_t t0 = g.gs.tile_start(I, J);
+  const int nseg = (int)((t0 + g.gs.len(I) - 1) / g.L - t0 / g.L) + 1;
+  const int64_t plane = (int64_t)rp * rp;
+  int64_t off[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = r0 + qrow(qm, v), col = c0 + qcol(qn);
+    off[v] = row >= col ? (int64_t)row * rp + col : (int64_t)col * rp + row;
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = g.part[off[v]];
+  for (int c = 1; c < nseg; ++c) {
+    const float* p = g.part + c * plane;
+    f32x16 w;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) w[v] = p[off[v]];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] += w[v];
+  }
+  if (r0 == c0 && qm == qn) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (qrow(qm, v) == qcol(qn)) acc[v] += g.rho;
+  }
+  return acc;
+}
+
 // Diagonal tile: Tin (LDS, stride TS) holds the lower blocks T11, T21, T22
 // of the 64 x 64 SPD tile; its factor L and M = L^-1 are formed in 2 x 2
 // blocks of 32 (diag_step below: the two factorisations on wave 0, the
@@ -366,16 +402,18 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
   j = t - ii * (ii + 1) / 2;
 }
 
-// The lower blocks of T = A_kk - L_{k,k-1} L_{k,k-1}^T (just A_00 for k = 0),
-// the input of the diagonal factorisation of step k, into sm.T: wave 0
-// forms T11, wave 1 T21, wave 2 T22 (T12 is never read).
-__device__ __forceinline__ void diag_input(const float* A, int rp, int k, StepSmem& sm) {
+// The lower blocks of T = A_kk - L_{k,k-1} L_{k,k-1}^T (just A_00 for k = 0,
+// summed from the Gram's segments with g), the input of the diagonal
+// factorisation of step k, into sm.T: wave 0 forms T11, wave 1 T21, wave 2
+// T22 (T12 is never read).
+__device__ __forceinline__ void diag_input(const float* A, int rp, int k, StepSmem& sm,
+                                           const GramSrc& g) {
   const int wave = threadIdx.x >> 6;
   if (wave == 3) return;
   const int qm = wave == 0 ? 0 : 1, qn = wave == 2 ? 1 : 0;
   const int64_t kk = (int64_t)k * NB;
   const float* Akk = A + kk * rp + kk;
-  f32x16 t = load_quad(Akk, rp, qm, qn);
+  f32x16 t = g.part ? load_quad_gram(g, rp, 0, 0, qm, qn) : load_quad(Akk, rp, qm, qn);
   if (k > 0) {
     const float* Lk = A + kk * rp + kk - NB;  // L_{k,k-1}
     const f32x16 acc = mm_quad<false, true>(Lk, rp, Lk, rp, qm, qn);
@@ -418,7 +456,8 @@ __device__ __forceinline__ void side_quad(const SideJob& j, int qm, int qn) {
 template <bool M_LDS, bool WRITE_L, bool TB>
 __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* M0, float* L0,
                                           int r_real, DevStats* st, StepSmem& sm,
-                                          const SideJob& side, float* Mt0 = nullptr) {
+                                          const SideJob& side, float* Mt0 = nullptr,
+                                          const GramSrc& gsrc = GramSrc{}) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i16 = lane & 15, g = lane >> 4;
   const int bi = wave & 1, bj = wave >> 1;
@@ -428,7 +467,7 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
   const float* Tin = sm.T;
   uint64_t bad = 0;
   // 1
-  diag_input(A, rp, k, sm);
+  diag_input(A, rp, k, sm, gsrc);
   if (wave == 0) {
     wave_lds_sync();  // T11 was written by other lanes of this wave
     diag_part1<M_LDS, WRITE_L>(sm.T, M0, L0, rp, row0, r_real, d, bad, Mt0);
@@ -507,13 +546,17 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, int rp,
                                                        int k, int r_real, int want_L,
                                                        int upd_blocks, DevStats* st, int pin,
-                                                       int ndiag, int dtiles, float* Mt) {
+                                                       int ndiag, int dtiles, float* Mt,
+                                                       GramSrc gsrc) {
   __builtin_amdgcn_s_setprio(3);
   __shared__ __attribute__((aligned(16))) StepSmem sm;
   const int R = rp / NB;
   const int n = R - 1 - k;
   const int64_t kk = (int64_t)k * NB;
   const int qm = wave_qm(), qn = wave_qn();
+  // the first launch reduces the Gram product into A (see the launcher)
+  GramSrc g = gsrc;
+  if (k != 0) g.part = nullptr;
   int b = blockIdx.x;
   // update tiles [t_lo, t_hi) with stride t_step for this workgroup (pinned:
   // the XCD 7 workgroups take the first dtiles after their diagonal work,
@@ -540,17 +583,22 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, int r
       if (b == 0) {  // M_kk
         diag_step<false, false, true>(A, rp, k, M + kk * rp + kk, nullptr, r_real, st, sm,
                                       SideJob{nullptr, nullptr, nullptr, rp, 0.0f, false, false},
-                                      Mt ? Mt + kk * rp + kk : nullptr);
+                                      Mt ? Mt + kk * rp + kk : nullptr, g);
         return true;
       }
       b -= 1;
       if (b < n) {  // panel tile (i, k)
         const int64_t i0 = (int64_t)(k + 1 + b) * NB;
         float* Aik = A + i0 * rp + kk;
+        if (g.part) {  // A_i0 from the Gram's segments (read back below, after barriers)
+          const f32x16 t = load_quad_gram(g, rp, (int)i0, 0, qm, qn);
+          store_quad(t, zero16(), Aik, rp, 1.0f, qm, qn);
+        }
         // A_ik -= L_{i,k-1} L_{k,k-1}^T beside the factorisation
         diag_step<true, false, true>(A, rp, k, sm.T, nullptr, r_real, nullptr, sm,
                                      SideJob{Aik - NB, A + kk * rp + kk - NB, Aik, rp, -1.0f,
-                                             k > 0, false});
+                                             k > 0, false},
+                                     nullptr, g);
         const f32x16 acc = mm_quad<false, true>(Aik, rp, sm.T, TS, qm, qn);  // (.) M_kk^T
         __syncthreads();  // every wave has read its operands before any overwrite
         store_quad(acc, zero16(), Aik, rp, 1.0f, qm, qn);
@@ -586,6 +634,25 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, int r
     return false;
   };
   if (role() && !pin) return;
+  if (g.part) {
+    // The rest of the Gram reduction: every lower 64 x 64 tile (i, j) but
+    // the panel tiles (i, 0), i > 0, with the diagonal tiles in full.
+    int t = pin ? t_lo : b;
+    const int nred = R * (R + 1) / 2 - (R - 1);
+    for (; t < nred && t < t_hi; t += t_step) {
+      // t = 0: tile (0, 0); t = 1 + u: the u-th lower tile of rows and
+      // columns 1 .. R-1
+      int ii = 0, jj = 0;
+      if (t > 0) {
+        tri_index(t - 1, ii, jj);
+        ++ii;
+        ++jj;
+      }
+      const f32x16 v = load_quad_gram(g, rp, ii * NB, jj * NB, qm, qn);
+      store_quad(v, zero16(), A + (int64_t)ii * NB * rp + jj * NB, rp, 1.0f, qm, qn);
+    }
+    return;
+  }
   if (k < 1) return;
   const int p = k - 1;
   const int64_t pp = (int64_t)p * NB;
@@ -650,8 +717,9 @@ bool cholesky_pinnable(int rp, bool want_L) {
 
 hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
-                                   bool pin, float* Mt) {
+                                   bool pin, float* Mt, GramSrc src) {
   if (rp % NB) return hipErrorInvalidValue;
+  if (src.part && (want_L || rp % 128 || src.L <= 0)) return hipErrorInvalidValue;
   if (pin && !cholesky_pinnable(rp, want_L)) return hipErrorInvalidValue;
   const int R = rp / NB;
   if (zero_m) {
@@ -662,9 +730,12 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
     const int n = R - 1 - k;
     int nb = k < R ? 1 + n + k : 0;  // diagonal, panel and inverse-row workgroups
     int upd = 0, upd_tiles = 0;
-    if (k >= 1) {
-      nb += want_L ? 1 : 0;
-      const int tiles = n > 0 ? n * (n + 1) / 2 + n * k : 0;
+    // launch 0 with src: the update workgroups reduce the Gram tiles the
+    // diagonal and panel ones do not (XCD 7, busy with those, takes none)
+    const bool red = k == 0 && src.part;
+    if (k >= 1 || red) {
+      nb += k >= 1 && want_L ? 1 : 0;
+      const int tiles = red ? 1 + (R - 1) * R / 2 : n > 0 ? n * (n + 1) / 2 + n * k : 0;
       upd = upd_tiles = tiles;
       if (pin) {
         upd = std::min(tiles, kPinUpdSlots);
@@ -678,7 +749,8 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
     if (nb + upd > 0)
       hipLaunchKernelGGL(chol_step_kernel, dim3(pin ? kPinGrid : nb + upd), dim3(NT), 0, s, A, M,
                          rp, k, r_real, want_L ? 1 : 0, std::max(upd, 1), st,
-                         pin ? 1 : 0, nb, pin ? std::min(upd_tiles, pin_diag_tiles()) : 0, Mt);
+                         pin ? 1 : 0, nb, pin && !red ? std::min(upd_tiles, pin_diag_tiles()) : 0,
+                         Mt, src);
   }
   if (!want_L) return hipGetLastError();
   const int64_t tot = (int64_t)rp * rp;

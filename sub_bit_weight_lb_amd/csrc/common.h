@@ -93,6 +93,15 @@ struct GramSteps {
     return row_start(I) + (int64_t)J * len(I);
   }
 };
+// A Gram product not yet reduced: the partial tiles `part` of a stream-K
+// launch with steps gs and ranges of L steps, to be summed per tile in slot
+// order, + rho on the diagonal (what launch_gram_reduce writes).
+struct GramSrc {
+  const float* part;
+  GramSteps gs;
+  int L;
+  float rho;
+};
 // Work split of a Gram product (GramSteps over R = rp / 128 tile rows) into
 // equal ranges of `steps` steps, one per workgroup (`wgs` of them); a tile's
 // segments go to at most `slots` partial buffers of rp x rp.
@@ -129,9 +138,15 @@ bool cholesky_pinnable(int rp, bool want_L);
 // Mt (nullable): the upper block triangle of M^T (the lower blocks are never
 // written and must read as zero), the operand of G^-1 = M^T M
 // (launch_gram_partial with a triangular plan).
+// src.part (nullable): A holds nothing yet; its tiles are the unreduced
+// Gram product src, which the first launch reduces into A itself (the
+// diagonal and panel workgroups sum their own tiles, the otherwise idle
+// update workgroups the rest), in place of launch_gram_reduce (lower
+// triangle and diagonal 64 x 64 blocks). Not with want_L.
 hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
-                                   bool pin = false, float* Mt = nullptr);
+                                   bool pin = false, float* Mt = nullptr,
+                                   GramSrc src = GramSrc{nullptr, GramSteps{0, 0}, 1, 0.0f});
 
 // ---------------------------------------------------------------- SVID
 struct SvidWork {

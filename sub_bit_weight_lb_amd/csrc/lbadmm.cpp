@@ -281,7 +281,6 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   // read G, starts beside the short reduction
   HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s,
                              overlap ? h->ev_gram : nullptr));
-  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, false, h->G, rp, s));
   if (overlap) HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
   // R = Wside other + rho (Z - Lam); Z - Lam comes from this factor's last
   // SVID, earlier on the same stream. Enqueued before the chain's launches:
@@ -298,10 +297,13 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   prof_end(h, pr, gs);
   if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
   // M = L^-1 (and M^T); G^-1 = M^T M as a triangular Gram product of M^T
-  // after the chain, in ~30 us, rather than inside it, where its 38 % of the
-  // chain's update tiles would run beside the RHS GEMM
+  // after the chain rather than inside it, where its 38 % of the chain's
+  // update tiles would run beside the RHS GEMM. The chain's first launch
+  // reduces the Gram segments into G itself (its update workgroups are
+  // otherwise idle): G has no reduction launch of its own.
   HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, false,
-                                 s, overlap && h->pin, h->Mt));
+                                 s, overlap && h->pin, h->Mt,
+                                 GramSrc{h->gpart, GramSteps{x.K / 32, 0}, x.gp.steps, h->d.rho}));
   HIPCHK(launch_gram_partial(h->Mt, rp, rp, rp, h->gI, h->gpart, s));
   HIPCHK(launch_gram_reduce(h->gpart, rp, rp, h->gI, 0.0f, true, h->Ginv, rp, s));
   prof_end(h, pc, s);
