@@ -185,6 +185,35 @@ void nq_lbadmm_destroy(nq_lbadmm_t h);
 nq_status nq_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                         uint32_t* bits, int64_t ld_words, void* stream);
 
+/* ---- applying a factorised layer ----
+ * The layer is kept as W ~ diag(s1) S_U S_V^T diag(s2) (m x n; "研究动机"),
+ * and applied without forming W, as the pages' binary GEMV/GEMM kernels do
+ * ("技术新颖性"). */
+
+/* Transposed sign bits: in holds rows x cols signs (rows x ld_in uint32
+ * words, the layout of nq_pack_signs), out (cols x ld_out words, ld_out >=
+ * ceil(rows/32)) receives the cols x rows signs of the transpose, bits past
+ * `rows` in each last word zero, words past ceil(rows/32) untouched. Both on
+ * the device; no allocation. Used once per layer to turn the V_bits of a run
+ * (n x r) into the S_V^T bits (r x n) that nq_binary_matmul reads. */
+nq_status nq_transpose_signs(const uint32_t* in, int64_t rows, int64_t cols, int64_t ld_in,
+                             uint32_t* out, int64_t ld_out, void* stream);
+
+/* Y = X W^T for W = diag(s1) S_U S_V^T diag(s2): row b of Y is
+ * s1 * (S_U (S_V^T (s2 * x_b))). All pointers on the device.
+ *   U_bits  m x ldu words (ldu >= ceil(r/32)): S_U, as nq_lbadmm_run returns it;
+ *   Vt_bits r x ldvt words (ldvt >= ceil(n/32)): S_V^T (nq_transpose_signs of V_bits);
+ *   s1 (m), s2 (n) float32; X: B x n float32, row stride ldx >= n;
+ *   Y: B x m float32, row stride ldy >= m (written, not read);
+ *   work: B * r float32 of caller scratch (the r projections per input).
+ * Two launches on `stream`, no allocation, no host synchronisation. Sums run
+ * in a fixed order, so results are bit-reproducible. m == 0 or B == 0 is a
+ * no-op; otherwise n, r >= 1. NQ_ERR_INVALID_ARG for bad sizes or strides. */
+nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits,
+                           int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
+                           const float* s2, const float* X, int64_t B, int64_t ldx, float* Y,
+                           int64_t ldy, float* work, void* stream);
+
 /* ---- building blocks (the same kernels the run uses; for tests and tools) ----
  * These take caller buffers of any shape, copy into zero-padded temporaries
  * (hipMalloc, freed before the call returns), run the kernels on `stream`,

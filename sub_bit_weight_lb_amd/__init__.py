@@ -9,6 +9,7 @@ loudly when libnq.so or the GPU is missing. There is no CPU fallback.
 Functions mirror the C names without the ``nq_`` prefix:
     lbadmm_create / lbadmm_run / lbadmm_query / lbadmm_get_state /
     lbadmm_destroy / lbadmm_workspace_bytes / pack_signs /
+    transpose_signs / binary_matmul /
     op_precondition / op_gram / op_gemm_rhs / op_cholesky_inverse / op_svid
 plus the conveniences ``LBADMM`` (a handle object) and ``lbadmm`` (one call).
 """
@@ -25,7 +26,8 @@ from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE
 
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
-    "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "op_precondition", "op_gram",
+    "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "transpose_signs",
+    "binary_matmul", "op_precondition", "op_gram",
     "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
 ]
@@ -172,6 +174,50 @@ def pack_signs(X, bits=None, stream=None):
         _ptr(bits, "bits", torch.int32, 2, need_contig=False), bits.stride(0), _stream(stream)),
         "nq_pack_signs")
     return bits
+
+
+def transpose_signs(bits, rows, cols, out=None, stream=None):
+    """Sign bits of the transpose: bits holds rows x cols signs (int32 words,
+    rows x ceil(cols/32) or wider, unit column stride); returns (or fills) the
+    cols x ceil(rows/32) words of the cols x rows transpose."""
+    torch = _torch()
+    if bits.dim() != 2 or bits.stride(1) != 1 or bits.shape[0] != rows:
+        raise ValueError("bits must be 2-D, rows x words, unit column stride")
+    if out is None:
+        out = torch.empty((cols, (rows + 31) // 32), dtype=torch.int32, device=bits.device)
+    _check(_lib.load().nq_transpose_signs(
+        _ptr(bits, "bits", torch.int32, 2, need_contig=False), rows, cols, bits.stride(0),
+        _ptr(out, "out", torch.int32, 2, need_contig=False), out.stride(0), _stream(stream)),
+        "nq_transpose_signs")
+    return out
+
+
+def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None):
+    """Y = X W^T for the factorised layer W = diag(s1) S_U S_V^T diag(s2):
+    U_bits (m x ceil(r/32) int32), Vt_bits (r x ceil(n/32) int32, from
+    transpose_signs of the run's V_bits), s1 (m), s2 (n), X (B x n float32,
+    or a vector of length n). Returns Y (B x m, or length m)."""
+    torch = _torch()
+    vec = X.dim() == 1
+    X2 = X.unsqueeze(0) if vec else X
+    if X2.dim() != 2 or X2.stride(1) != 1:
+        raise ValueError("X must be 1-D or 2-D with unit column stride")
+    B, n = X2.shape
+    m = U_bits.shape[0]
+    if Vt_bits.shape[0] != r or s1.numel() != m or s2.numel() != n:
+        raise ValueError("shapes of U_bits, Vt_bits, s1, s2 and X do not agree")
+    if Y is None:
+        Y = torch.empty((B, m), dtype=torch.float32, device=X.device)
+    if work is None:
+        work = torch.empty((max(B * r, 1),), dtype=torch.float32, device=X.device)
+    _check(_lib.load().nq_binary_matmul(
+        _ptr(U_bits, "U_bits", torch.int32, 2, need_contig=False), U_bits.stride(0),
+        _ptr(Vt_bits, "Vt_bits", torch.int32, 2, need_contig=False), Vt_bits.stride(0),
+        m, n, r, _ptr(s1, "s1", torch.float32), _ptr(s2, "s2", torch.float32),
+        _ptr(X2, "X", torch.float32, 2, need_contig=False), B, X2.stride(0),
+        _ptr(Y, "Y", torch.float32, 2, need_contig=False), Y.stride(0),
+        _ptr(work, "work", torch.float32), _stream(stream)), "nq_binary_matmul")
+    return Y[0] if vec else Y
 
 
 def op_precondition(W, d_out, d_in, stream=None):

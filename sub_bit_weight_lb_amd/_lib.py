@@ -55,6 +55,8 @@ SIGNATURES = {
     "nq_lbadmm_destroy": (None, [P]),
     "nq_lbadmm_profile": (ST, [P, C.POINTER(C.c_double), C.POINTER(I64), C.c_int32]),
     "nq_pack_signs": (ST, [P, I64, I64, I64, P, I64, P]),
+    "nq_transpose_signs": (ST, [P, I64, I64, I64, P, I64, P]),
+    "nq_binary_matmul": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P, P]),
     "nq_op_precondition": (ST, [P, I64, I64, I64, P, P, P, I64, P]),
     "nq_op_gram": (ST, [P, I64, I64, I64, F32, P, I64, P]),
     "nq_op_gemm_rhs": (ST, [P, I64, P, I64, P, I64, F32, P, I64, I64, I64, I64, P]),

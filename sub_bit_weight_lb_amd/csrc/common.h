@@ -226,5 +226,17 @@ hipError_t launch_error(const int8_t* SU, const int8_t* SV, int mp, int np_, int
 // ---------------------------------------------------------------- packing
 hipError_t launch_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                              uint32_t* bits, int64_t ld_words, hipStream_t s);
+// ---------------------------------------------------------------- binary layer (binmm.hip)
+// out (cols x ld_out words) = the sign bits of in (rows x cols, ld_in words)
+// transposed; tails of the last words zero.
+hipError_t launch_transpose_bits(const uint32_t* in, int64_t rows, int64_t cols, int64_t ld_in,
+                                 uint32_t* out, int64_t ld_out, hipStream_t s);
+// Y (B x m, ld ldy) = s1 * ((X * s2) S_V S_U^T) from S_U bits (m x r, ld ldu
+// words) and S_V^T bits (r x n, ld ldvt words); X B x n (ld ldx); T: B r
+// floats of scratch.
+hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t* svt,
+                                int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
+                                const float* s2, const float* X, int64_t B, int64_t ldx,
+                                float* Y, int64_t ldy, float* T, hipStream_t s);
 
 }  // namespace nq

@@ -53,6 +53,35 @@ nq_status nq_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
   return NQ_OK;
 }
 
+nq_status nq_transpose_signs(const uint32_t* in, int64_t rows, int64_t cols, int64_t ld_in,
+                             uint32_t* out, int64_t ld_out, void* stream) {
+  if (rows < 0 || cols < 0) return set_error(NQ_ERR_INVALID_ARG, "rows and cols must be >= 0");
+  if (rows == 0 || cols == 0) return NQ_OK;
+  if (!in || !out) return set_error(NQ_ERR_INVALID_ARG, "in and out are required");
+  if (ld_in < (cols + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ld_in < ceil(cols/32)");
+  if (ld_out < (rows + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ld_out < ceil(rows/32)");
+  NQ_HIPCHK(launch_transpose_bits(in, rows, cols, ld_in, out, ld_out, (hipStream_t)stream));
+  return NQ_OK;
+}
+
+nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits,
+                           int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
+                           const float* s2, const float* X, int64_t B, int64_t ldx, float* Y,
+                           int64_t ldy, float* work, void* stream) {
+  if (m < 0 || n < 0 || r < 0 || B < 0)
+    return set_error(NQ_ERR_INVALID_ARG, "m, n, r and B must be >= 0");
+  if (m == 0 || B == 0) return NQ_OK;
+  if (n == 0 || r == 0) return set_error(NQ_ERR_INVALID_ARG, "n and r must be >= 1 when m, B >= 1");
+  if (!U_bits || !Vt_bits || !s1 || !s2 || !X || !Y || !work)
+    return set_error(NQ_ERR_INVALID_ARG, "U_bits, Vt_bits, s1, s2, X, Y and work are required");
+  if (ldu < (r + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ldu < ceil(r/32)");
+  if (ldvt < (n + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ldvt < ceil(n/32)");
+  if (ldx < n || ldy < m) return set_error(NQ_ERR_INVALID_ARG, "ldx < n or ldy < m");
+  NQ_HIPCHK(launch_binary_matmul(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy,
+                                 work, (hipStream_t)stream));
+  return NQ_OK;
+}
+
 nq_status nq_op_precondition(const float* W, int64_t ldw, int64_t m, int64_t n,
                              const float* d_out, const float* d_in, float* Wt, int64_t ldwt,
                              void* stream) {

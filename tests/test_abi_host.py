@@ -125,6 +125,30 @@ def test_pack_signs_argument_checks(lib):
     assert lib.nq_pack_signs(fake, -1, 40, 40, fake, 2, None) == L.NQ_ERR_INVALID_ARG
 
 
+def test_binary_layer_argument_checks(lib):
+    f = C.c_void_p(0x1000)
+    # transpose: empty is a no-op; strides below the packed widths are rejected
+    assert lib.nq_transpose_signs(None, 0, 5, 1, None, 1, None) == 0
+    assert lib.nq_transpose_signs(f, 40, 70, 2, f, 2, None) == L.NQ_ERR_INVALID_ARG   # ld_in < 3
+    assert lib.nq_transpose_signs(f, 40, 70, 3, f, 1, None) == L.NQ_ERR_INVALID_ARG   # ld_out < 2
+    assert lib.nq_transpose_signs(None, 4, 4, 1, f, 1, None) == L.NQ_ERR_INVALID_ARG
+    # matmul: m == 0 or B == 0 is a no-op
+    args = dict(ldu=2, ldvt=3, m=10, n=70, r=40, B=2, ldx=70, ldy=10)
+
+    def call(work=f, **kw):
+        a = dict(args, **kw)
+        return lib.nq_binary_matmul(f, a["ldu"], f, a["ldvt"], a["m"], a["n"], a["r"], f, f, f,
+                                    a["B"], a["ldx"], f, a["ldy"], work, None)
+    assert call(m=0) == 0 and call(B=0) == 0
+    assert call(work=None) == L.NQ_ERR_INVALID_ARG
+    assert call(ldu=1) == L.NQ_ERR_INVALID_ARG          # < ceil(40/32)
+    assert call(ldvt=2) == L.NQ_ERR_INVALID_ARG         # < ceil(70/32)
+    assert call(ldx=69) == L.NQ_ERR_INVALID_ARG
+    assert call(ldy=9) == L.NQ_ERR_INVALID_ARG
+    assert call(r=0) == L.NQ_ERR_INVALID_ARG
+    assert call(n=-1) == L.NQ_ERR_INVALID_ARG
+
+
 def test_ops_argument_checks(lib):
     f = C.c_void_p(0x1000)
     info = C.c_int64(0)
