@@ -107,6 +107,68 @@ def cpu_baseline(L, budget_s=10.0, max_iters=12, budget_fp32_s=6.0):
     }
 
 
+def binary_bench(nq, torch, dev, reps=20, replays=5):
+    """nq_binary_matmul (Y = X W^T for W = diag(s1) S_U S_V^T diag(s2)) on the
+    factorised-layer shapes. Random sign words on the device. Calls are
+    captured in a HIP graph (no host overhead in the timing) and replayed;
+    "warm" reuses one set of bits, "cold" rotates through copies of the bits
+    totalling > 256 MB (more than the last-level cache), so each call reads
+    its bits from HBM. Algorithmic bytes per call: the bits, X, Y, s1, s2 and
+    the B r projections written and read back."""
+    out = []
+    g = torch.Generator(device="cpu").manual_seed(0)
+    for (m, n, r) in ((4096, 4096, 2048), (11008, 4096, 1536), (8192, 28672, 6144)):
+        wu, wv = (r + 31) // 32, (n + 31) // 32
+        bits_bytes = 4 * (m * wu + r * wv)
+        ncopy = max(1, -(-320 * 2**20 // bits_bytes))
+        U = [torch.randint(-2**31, 2**31 - 1, (m, wu), dtype=torch.int32, generator=g).to(dev)
+             for _ in range(ncopy)]
+        Vt = [torch.randint(-2**31, 2**31 - 1, (r, wv), dtype=torch.int32, generator=g).to(dev)
+              for _ in range(ncopy)]
+        s1 = torch.rand(m, generator=g).to(dev)
+        s2 = torch.rand(n, generator=g).to(dev)
+        for B in (1, 8):
+            X = torch.randn(B, n, generator=g).to(dev)
+            Y = torch.empty(B, m, device=dev)
+            work = torch.empty(8 * B * r, device=dev)
+            nq.binary_matmul(U[0], Vt[0], s1, s2, X, r, Y=Y, work=work)
+            ref = Y.clone()
+            res = {"m": m, "n": n, "r": r, "B": B}
+            alg = bits_bytes + 4 * (B * n + B * m + m + n + 2 * B * r)
+            for mode, sets in (("warm", [0] * reps), ("cold", [i % ncopy for i in range(reps)])):
+                st = torch.cuda.Stream()
+                st.wait_stream(torch.cuda.current_stream())
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(st):
+                    nq.binary_matmul(U[0], Vt[0], s1, s2, X, r, Y=Y, work=work)  # warm-up on st
+                    torch.cuda.synchronize()
+                    with torch.cuda.graph(graph, stream=st):
+                        for i in sets:
+                            nq.binary_matmul(U[i], Vt[i], s1, s2, X, r, Y=Y, work=work)
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                if mode == "warm" and not torch.equal(Y, ref):
+                    raise RuntimeError("graph replay differs from the eager call")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(replays):
+                    graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (replays * reps)
+                res[f"{mode}_us"] = round(us, 2)
+                res[f"{mode}_GBps"] = round(alg / us / 1e3, 1)
+                del graph
+            res["alg_bytes"] = alg
+            res["cold_frac_of_8TBps"] = round(res["cold_GBps"] / 8000.0, 4)
+            print(json.dumps(res), flush=True)
+            out.append(res)
+        del U, Vt
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +182,9 @@ def main():
     ap.add_argument("--kernels", action="store_true",
                     help="only run the GEMM kernels alone on the layer's shapes, 20 launches "
                          "each (for a kernel-trace profile of their standalone durations)")
+    ap.add_argument("--binary", action="store_true",
+                    help="only time the binary-layer product (nq_binary_matmul) on the layer "
+                         "shapes, warm and with its sign bits rotated through > 256 MB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -164,6 +229,9 @@ def main():
             nq.op_gram(v, rho=wl.rho)
         torch.cuda.synchronize()
         print(f"gram {wl.n}x{wl.r}: 20 launches", flush=True)
+        return
+    if args.binary:
+        print(json.dumps({"binary_matmul": binary_bench(nq, torch, dev)}), flush=True)
         return
     L = make_layer(WORKLOAD)
     wl = L.workload

@@ -205,7 +205,8 @@ nq_status nq_transpose_signs(const uint32_t* in, int64_t rows, int64_t cols, int
  *   Vt_bits r x ldvt words (ldvt >= ceil(n/32)): S_V^T (nq_transpose_signs of V_bits);
  *   s1 (m), s2 (n) float32; X: B x n float32, row stride ldx >= n;
  *   Y: B x m float32, row stride ldy >= m (written, not read);
- *   work: B * r float32 of caller scratch (the r projections per input).
+ *   work: 8 * B * r float32 of caller scratch (partial sums of the r
+ *         projections per input).
  * Two launches on `stream`, no allocation, no host synchronisation. Sums run
  * in a fixed order, so results are bit-reproducible. m == 0 or B == 0 is a
  * no-op; otherwise n, r >= 1. NQ_ERR_INVALID_ARG for bad sizes or strides. */

@@ -196,7 +196,8 @@ def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None)
     """Y = X W^T for the factorised layer W = diag(s1) S_U S_V^T diag(s2):
     U_bits (m x ceil(r/32) int32), Vt_bits (r x ceil(n/32) int32, from
     transpose_signs of the run's V_bits), s1 (m), s2 (n), X (B x n float32,
-    or a vector of length n). Returns Y (B x m, or length m)."""
+    or a vector of length n); work, if given, holds 8 B r float32. Returns Y
+    (B x m, or length m)."""
     torch = _torch()
     vec = X.dim() == 1
     X2 = X.unsqueeze(0) if vec else X
@@ -209,7 +210,7 @@ def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None)
     if Y is None:
         Y = torch.empty((B, m), dtype=torch.float32, device=X.device)
     if work is None:
-        work = torch.empty((max(B * r, 1),), dtype=torch.float32, device=X.device)
+        work = torch.empty((max(8 * B * r, 1),), dtype=torch.float32, device=X.device)
     _check(_lib.load().nq_binary_matmul(
         _ptr(U_bits, "U_bits", torch.int32, 2, need_contig=False), U_bits.stride(0),
         _ptr(Vt_bits, "Vt_bits", torch.int32, 2, need_contig=False), Vt_bits.stride(0),

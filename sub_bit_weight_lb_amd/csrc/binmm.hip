@@ -12,20 +12,23 @@
 // S_V^T and the second y = s1 * (S_U T) over the m rows of S_U, so one
 // kernel serves both.
 //
-// bin_rowdot_kernel: four waves, four rows per wave. A chunk of 64 words
-// (2048 columns) of v goes to LDS bit-major (the value of column 32 w + i at
-// [i][w]), so lane l, which holds word l of the chunk for each of its rows,
-// reads its 32 values without bank conflicts and uses each one for four
-// rows. The words are fetched before the chunk of v is staged. Each lane sums
-// +-v over its bits in column order, then the wave sums its lanes in a fixed
-// tree: the result does not depend on timing. Bits past `cols` in a row's
-// last word meet v = 0 there, so they add nothing.
+// bin_rowdot_kernel: four waves, RPW rows per wave; lane l holds word l of
+// a 64-word (2048-column) chunk of each of its rows. For the chunk the
+// workgroup builds, per group of 4 columns, the 16 signed sums
+// +-x0 +-x1 +-x2 +-x3 in LDS, laid out [nibble index][value][word] so that
+// the 64 lanes' lookups hit distinct banks. A row then costs one lookup and
+// one add per 4 bits instead of a select and an add per bit. The words are
+// fetched before the tables are built. Each lane adds its 8 lookups per word
+// in order, then the wave sums its lanes in a fixed tree: the result does
+// not depend on timing. Bits past `cols` in a row's last word meet x = 0
+// there, so they add nothing.
 #include "common.h"
+
+#include <algorithm>
 
 namespace nq {
 namespace {
 
-constexpr int RPW = 4;   // rows per wave
 constexpr int CW = 64;   // words per column chunk, one per lane
 
 __device__ inline float wave_sum64(float v) {
@@ -34,47 +37,100 @@ __device__ inline float wave_sum64(float v) {
   return v;
 }
 
-template <int BT>
+template <int BT, int RPW, int NS>
 __global__ __launch_bounds__(256) void bin_rowdot_kernel(
     const uint32_t* __restrict__ bits, int64_t ldw, int64_t rows, int64_t cols,
-    const float* __restrict__ v, int64_t ldv, const float* __restrict__ pre,
-    const float* __restrict__ post, float* __restrict__ out, int64_t ldo, int64_t B) {
-  __shared__ float vs[BT][32][CW + 1];
+    const float* __restrict__ v, int64_t ldv, int nsum, int64_t vstride,
+    const float* __restrict__ pre, const float* __restrict__ post, float* __restrict__ out,
+    int64_t ldo, int64_t ostride, int64_t wsplit, int64_t B) {
+  // tab[b][j][q][w]: sum over the 4 columns 32 w + 4 j + t (t = 0..3) of
+  // (bit t of q ? +x : -x), for word w of the chunk and nibble j of it
+  __shared__ float tab[BT][8][16][CW];
+  // the chunk's inputs, word-major with a pad so that the table builders
+  // (one word per lane) read distinct banks
+  __shared__ float xs[BT][CW][33];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t b0 = (int64_t)blockIdx.y * BT;
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
-  const int64_t nwords = (cols + 31) / 32;
+  // this workgroup's words of each row: [w_lo, w_hi)
+  const int64_t w_lo = (int64_t)blockIdx.z * wsplit;
+  const int64_t nwords = min((cols + 31) / 32, w_lo + wsplit);
+  out += (int64_t)blockIdx.z * ostride;
   float acc[RPW][BT];
 #pragma unroll
   for (int r = 0; r < RPW; ++r)
 #pragma unroll
     for (int b = 0; b < BT; ++b) acc[r][b] = 0.0f;
-  for (int64_t cw0 = 0; cw0 < nwords; cw0 += CW) {
+  // table builder: word tw of the chunk, nibbles tj and tj + 1
+  const int tw = threadIdx.x & 63, tj = 2 * (threadIdx.x >> 6);
+  for (int64_t cw0 = w_lo; cw0 < nwords; cw0 += CW) {
     const int64_t w = cw0 + lane;
     uint32_t word[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       word[r] = (row0 + r < rows && w < nwords) ? bits[(row0 + r) * ldw + w] : 0u;
-    __syncthreads();  // every wave is done with the previous chunk of v
-    for (int e = threadIdx.x; e < BT * 32 * CW; e += 256) {
-      const int b = e / (32 * CW), rem = e % (32 * CW);
-      const int ww = rem / 32, i = rem % 32;
-      const int64_t c = (cw0 + ww) * 32 + i;
-      float x = 0.0f;
-      if (b0 + b < B && c < cols) {
-        x = v[(b0 + b) * ldv + c];
-        if (pre) x *= pre[c];
+    __syncthreads();  // every wave is done with the previous chunk's tables
+    // inputs of the chunk, coalesced: element e is column 32 cw0 + e, the
+    // sum of nsum (<= NS) partial vectors in order; every load of a pass is
+    // issued before the sums
+#pragma unroll
+    for (int e0 = 0; e0 < BT * 32 * CW; e0 += 256 * 4) {
+      float part[4][NS];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 256 * u + threadIdx.x;
+        const int b = e / (32 * CW), k = e % (32 * CW);
+        const int64_t c = cw0 * 32 + k;
+        const bool ok = b0 + b < B && c < cols;
+        const float* vp = v + (b0 + b) * ldv + c;
+#pragma unroll
+        for (int z = 0; z < NS; ++z) part[u][z] = ok && z < nsum ? vp[z * vstride] : 0.0f;
       }
-      vs[b][i][ww] = x;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + 256 * u + threadIdx.x;
+        const int b = e / (32 * CW), k = e % (32 * CW);
+        const int64_t c = cw0 * 32 + k;
+        float y = part[u][0];
+#pragma unroll
+        for (int z = 1; z < NS; ++z)
+          if (z < nsum) y += part[u][z];
+        if (pre && b0 + b < B && c < cols) y *= pre[c];
+        xs[b][k >> 5][k & 31] = y;
+      }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
 #pragma unroll
-      for (int b = 0; b < BT; ++b) {
-        const float x = vs[b][i][lane];
+    for (int b = 0; b < BT; ++b) {
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) acc[r][b] += ((word[r] >> i) & 1u) ? x : -x;
+      for (int h = 0; h < 2; ++h) {
+        const int j = tj + h;
+        float x[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = xs[b][tw][4 * j + t];
+        // q = 0 is -x0 - x1 - x2 - x3; setting bit t adds 2 x_t
+        const float base = -x[0] - x[1] - x[2] - x[3];
+        const float d0 = 2.0f * x[0], d1 = 2.0f * x[1], d2 = 2.0f * x[2], d3 = 2.0f * x[3];
+        float* tq = &tab[b][j][0][tw];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          float e = base;
+          if (q & 1) e += d0;
+          if (q & 2) e += d1;
+          if (q & 4) e += d2;
+          if (q & 8) e += d3;
+          tq[q * CW] = e;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int q = (word[r] >> (4 * j)) & 15u;
+#pragma unroll
+        for (int b = 0; b < BT; ++b) acc[r][b] += tab[b][j][q][lane];
       }
     }
   }
@@ -121,21 +177,45 @@ __global__ __launch_bounds__(256) void transpose_bits_kernel(const uint32_t* __r
   }
 }
 
-template <int BT>
+// One row-dot launch: `split` workgroups share each block of rows, each
+// taking wsplit words (a multiple of CW) of every row and writing its own
+// partial result at out + z ostride; the input is the sum of nsum partial
+// vectors v + z vstride.
+template <int BT, int RPW, int NS>
 void rowdot(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
-            int64_t ldv, const float* pre, const float* post, float* out, int64_t ldo, int64_t B,
-            hipStream_t s) {
-  const dim3 grid((unsigned)((rows + 4 * RPW - 1) / (4 * RPW)), (unsigned)((B + BT - 1) / BT));
-  hipLaunchKernelGGL(bin_rowdot_kernel<BT>, grid, dim3(256), 0, s, bits, ldw, rows, cols, v, ldv,
-                     pre, post, out, ldo, B);
+            int64_t ldv, int nsum, int64_t vstride, const float* pre, const float* post,
+            float* out, int64_t ldo, int64_t ostride, int split, int64_t B, hipStream_t s) {
+  const int64_t nw = (cols + 31) / 32;
+  const int64_t wsplit = ((nw + split - 1) / split + CW - 1) / CW * CW;
+  const dim3 grid((unsigned)((rows + 4 * RPW - 1) / (4 * RPW)), (unsigned)((B + BT - 1) / BT),
+                  (unsigned)split);
+  hipLaunchKernelGGL((bin_rowdot_kernel<BT, RPW, NS>), grid, dim3(256), 0, s, bits, ldw, rows, cols, v, ldv,
+                     nsum, vstride, pre, post, out, ldo, ostride, wsplit, B);
 }
 
+template <int RPW, int NS>
 void rowdot_any(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
-                int64_t ldv, const float* pre, const float* post, float* out, int64_t ldo,
-                int64_t B, hipStream_t s) {
-  if (B == 1) rowdot<1>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, B, s);
-  else if (B == 2) rowdot<2>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, B, s);
-  else rowdot<4>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, B, s);
+                int64_t ldv, int nsum, int64_t vstride, const float* pre, const float* post,
+                float* out, int64_t ldo, int64_t ostride, int split, int64_t B, hipStream_t s) {
+  // two inputs per workgroup at most: their tables (64 KB) and inputs fill
+  // most of the LDS
+  if (B == 1) rowdot<1, RPW, NS>(bits, ldw, rows, cols, v, ldv, nsum, vstride, pre, post, out, ldo, ostride, split, B, s);
+  else rowdot<2, RPW, NS>(bits, ldw, rows, cols, v, ldv, nsum, vstride, pre, post, out, ldo, ostride, split, B, s);
+}
+
+// rows per wave: the first product (r rows, long rows of n columns) shares
+// each chunk's tables among 64 rows per workgroup and splits its columns;
+// the second (m rows of r columns) keeps 16 rows per workgroup for a wide grid
+constexpr int kRpw1 = 16, kRpw2 = 4;
+
+// Workgroups sharing the rows of the first product: enough for about 1024
+// workgroups in all, at most kBinSplit, at most one per 64-word chunk.
+int first_split(int64_t r, int64_t n, int64_t B) {
+  const int64_t wgs = ((r + 4 * kRpw1 - 1) / (4 * kRpw1)) * ((B + 1) / 2);
+  int64_t sp = (1024 + wgs - 1) / wgs;
+  sp = std::min<int64_t>(sp, kBinSplit);
+  sp = std::min<int64_t>(sp, ((n + 31) / 32 + CW - 1) / CW);
+  return (int)std::max<int64_t>(sp, 1);
 }
 
 }  // namespace
@@ -156,13 +236,15 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
                                 const float* s2, const float* X, int64_t B, int64_t ldx,
                                 float* Y, int64_t ldy, float* T, hipStream_t s) {
   if (m <= 0 || n <= 0 || r <= 0 || B <= 0) return hipSuccess;
-  if ((r + 4 * RPW - 1) / (4 * RPW) > 0x7fffffff || (m + 4 * RPW - 1) / (4 * RPW) > 0x7fffffff ||
-      (B + 3) / 4 > 65535)
+  if ((r + 4 * kRpw1 - 1) / (4 * kRpw1) > 0x7fffffff || (m + 4 * kRpw2 - 1) / (4 * kRpw2) > 0x7fffffff ||
+      (B + 1) / 2 > 65535)
     return hipErrorInvalidValue;
-  // T = (X * s2) S_V: the r rows of S_V^T against x
-  rowdot_any(svt, ldvt, r, n, X, ldx, s2, nullptr, T, r, B, s);
-  // Y = s1 * (T S_U^T): the m rows of S_U against T
-  rowdot_any(su, ldu, m, r, T, r, nullptr, s1, Y, ldy, B, s);
+  // T = (X * s2) S_V: the r rows of S_V^T against x, their words split over
+  // sp workgroups, each writing a partial T (sp x B x r)
+  const int sp = first_split(r, n, B);
+  rowdot_any<kRpw1, 1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, sp, B, s);
+  // Y = s1 * (T S_U^T): the m rows of S_U against the sum of the partials
+  rowdot_any<kRpw2, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
   return hipGetLastError();
 }
 

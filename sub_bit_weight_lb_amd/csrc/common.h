@@ -232,8 +232,9 @@ hipError_t launch_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t
 hipError_t launch_transpose_bits(const uint32_t* in, int64_t rows, int64_t cols, int64_t ld_in,
                                  uint32_t* out, int64_t ld_out, hipStream_t s);
 // Y (B x m, ld ldy) = s1 * ((X * s2) S_V S_U^T) from S_U bits (m x r, ld ldu
-// words) and S_V^T bits (r x n, ld ldvt words); X B x n (ld ldx); T: B r
-// floats of scratch.
+// words) and S_V^T bits (r x n, ld ldvt words); X B x n (ld ldx); T:
+// kBinSplit B r floats of scratch (partial projections).
+constexpr int kBinSplit = 8;
 hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t* svt,
                                 int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
                                 const float* s2, const float* X, int64_t B, int64_t ldx,
