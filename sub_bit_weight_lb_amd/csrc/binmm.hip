@@ -210,8 +210,8 @@ constexpr int kRpw1 = 16, kRpw2 = 4;
 
 // Workgroups sharing the rows of the first product: enough for about 1024
 // workgroups in all, at most kBinSplit, at most one per 64-word chunk.
-int first_split(int64_t r, int64_t n, int64_t B) {
-  const int64_t wgs = ((r + 4 * kRpw1 - 1) / (4 * kRpw1)) * ((B + 1) / 2);
+int first_split(int64_t r, int64_t n, int64_t B, int rpw) {
+  const int64_t wgs = ((r + 4 * rpw - 1) / (4 * rpw)) * ((B + 1) / 2);
   int64_t sp = (1024 + wgs - 1) / wgs;
   sp = std::min<int64_t>(sp, kBinSplit);
   sp = std::min<int64_t>(sp, ((n + 31) / 32 + CW - 1) / CW);
@@ -241,8 +241,14 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
     return hipErrorInvalidValue;
   // T = (X * s2) S_V: the r rows of S_V^T against x, their words split over
   // sp workgroups, each writing a partial T (sp x B x r)
-  const int sp = first_split(r, n, B);
-  rowdot_any<kRpw1, 1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, sp, B, s);
+  // (below 4096 rows and for one or two inputs, 16 rows per workgroup: 64
+  // would leave most CUs idle)
+  const int rpw1 = r >= 4096 || B > 2 ? kRpw1 : kRpw2;
+  const int sp = first_split(r, n, B, rpw1);
+  if (rpw1 == kRpw1)
+    rowdot_any<kRpw1, 1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, sp, B, s);
+  else
+    rowdot_any<kRpw2, 1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, sp, B, s);
   // Y = s1 * (T S_U^T): the m rows of S_U against the sum of the partials
   rowdot_any<kRpw2, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
   return hipGetLastError();
