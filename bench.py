@@ -127,7 +127,7 @@ def binary_bench(nq, torch, dev, reps=20, replays=5):
               for _ in range(ncopy)]
         s1 = torch.rand(m, generator=g).to(dev)
         s2 = torch.rand(n, generator=g).to(dev)
-        for B in (1, 8):
+        for B in (1, 8, 16):
             X = torch.randn(B, n, generator=g).to(dev)
             Y = torch.empty(B, m, device=dev)
             work = torch.empty(8 * B * r, device=dev)

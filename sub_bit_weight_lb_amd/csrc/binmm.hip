@@ -12,6 +12,10 @@
 // S_V^T and the second y = s1 * (S_U T) over the m rows of S_U, so one
 // kernel serves both.
 //
+// Up to eight inputs go through bin_rowdot_kernel (two per pass), nine or
+// more through bin_mfma_kernel (below), 16 inputs per pass on the matrix
+// cores.
+//
 // bin_rowdot_kernel: four waves, RPW rows per wave; lane l holds word l of
 // a 64-word (2048-column) chunk of each of its rows. For the chunk the
 // workgroup builds, per group of 4 columns, the 16 signed sums
@@ -144,6 +148,73 @@ __global__ __launch_bounds__(256) void bin_rowdot_kernel(
     }
 }
 
+// The same row dots for up to 16 inputs at once, on the matrix cores:
+// out[b][n] = sum_k v[b][k] sign(n, k), i.e. a (B x K) x (K x N) product
+// whose right operand is +-1, exact in fp32. v_mfma_f32_16x16x4f32 takes
+// A[b][k] for b = lane % 16, k = lane / 16 (from the inputs staged in LDS)
+// and B[k][n] for n = lane % 16 (+-1 from bit k of row n's word, one word
+// load per 8 MFMA steps); lane l ends with out[4 (l / 16) + v][n]. Four waves,
+// 16 rows (n) each; inputs staged 256 columns at a time (the sum of nsum
+// partial vectors, times pre). Sums run in a fixed order.
+template <int NS>
+__global__ __launch_bounds__(256) void bin_mfma_kernel(
+    const uint32_t* __restrict__ bits, int64_t ldw, int64_t rows, int64_t cols,
+    const float* __restrict__ v, int64_t ldv, int nsum, int64_t vstride,
+    const float* __restrict__ pre, const float* __restrict__ post, float* __restrict__ out,
+    int64_t ldo, int64_t ostride, int64_t wsplit, int64_t B) {
+  constexpr int KC = 256;                 // input columns per stage
+  __shared__ float zs[16][KC + 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t b0 = (int64_t)blockIdx.y * 16;
+  const int64_t n = ((int64_t)blockIdx.x * 4 + wave) * 16 + (lane & 15);
+  const int64_t nw = (cols + 31) / 32;
+  const int64_t w_lo = (int64_t)blockIdx.z * wsplit;
+  const int64_t w_hi = min(nw, w_lo + wsplit);
+  out += (int64_t)blockIdx.z * ostride;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int kq = lane >> 4;               // this lane's k within a step of 4
+  for (int64_t wc = w_lo; wc < w_hi; wc += KC / 32) {
+    __syncthreads();  // the previous stage's inputs are consumed
+    // inputs b0 .. b0 + 15, columns 32 wc .. + KC, coalesced
+#pragma unroll
+    for (int u = 0; u < 16 * KC / 256; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int bb = e / KC, k = e % KC;
+      const int64_t c = wc * 32 + k;
+      const bool ok = b0 + bb < B && c < cols && wc * 32 + k < w_hi * 32;
+      const float* vp = v + (b0 + bb) * ldv + c;
+      float y = ok ? vp[0] : 0.0f;
+#pragma unroll
+      for (int z = 1; z < NS; ++z) {
+        const float t = ok && z < nsum ? vp[z * vstride] : 0.0f;
+        if (z < nsum) y += t;
+      }
+      if (ok && pre) y *= pre[c];
+      zs[bb][k] = y;
+    }
+    __syncthreads();
+    const int64_t wend = min(w_hi, wc + KC / 32);
+    for (int64_t w = wc; w < wend; ++w) {
+      const uint32_t word = n < rows ? bits[n * ldw + w] : 0u;
+      const int kb = (int)(w - wc) * 32;
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const int k = 4 * s8 + kq;
+        const float a = zs[lane & 15][kb + k];
+        const float bsg = (word >> k) & 1u ? 1.0f : -1.0f;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bsg, acc, 0, 0, 0);
+      }
+    }
+  }
+  if (n < rows) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = b0 + 4 * kq + q;
+      if (b < B) out[b * ldo + n] = post ? acc[q] * post[n] : acc[q];
+    }
+  }
+}
+
 // out (cols x ld_out words) bit (c, i) = in bit (i, c), in holding rows x cols
 // signs (rows x ld_in words). Wave (row block of 64, input word cw): lane l
 // reads the word of row 64 q + l; the ballot of bit j over the lanes is
@@ -193,6 +264,17 @@ void rowdot(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const
                      nsum, vstride, pre, post, out, ldo, ostride, wsplit, B);
 }
 
+template <int NS>
+void rowdot_mfma(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
+                 int64_t ldv, int nsum, int64_t vstride, const float* pre, const float* post,
+                 float* out, int64_t ldo, int64_t ostride, int split, int64_t B, hipStream_t s) {
+  const int64_t nw = (cols + 31) / 32;
+  const int64_t wsplit = ((nw + split - 1) / split + 7) / 8 * 8;
+  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((B + 15) / 16), (unsigned)split);
+  hipLaunchKernelGGL((bin_mfma_kernel<NS>), grid, dim3(256), 0, s, bits, ldw, rows, cols, v, ldv,
+                     nsum, vstride, pre, post, out, ldo, ostride, wsplit, B);
+}
+
 template <int RPW, int NS>
 void rowdot_any(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
                 int64_t ldv, int nsum, int64_t vstride, const float* pre, const float* post,
@@ -236,11 +318,22 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
                                 const float* s2, const float* X, int64_t B, int64_t ldx,
                                 float* Y, int64_t ldy, float* T, hipStream_t s) {
   if (m <= 0 || n <= 0 || r <= 0 || B <= 0) return hipSuccess;
-  if ((r + 4 * kRpw1 - 1) / (4 * kRpw1) > 0x7fffffff || (m + 4 * kRpw2 - 1) / (4 * kRpw2) > 0x7fffffff ||
-      (B + 1) / 2 > 65535)
+  if ((r + 4 * kRpw2 - 1) / (4 * kRpw2) > 0x7fffffff || (m + 4 * kRpw2 - 1) / (4 * kRpw2) > 0x7fffffff ||
+      (B + 15) / 16 > 65535)
     return hipErrorInvalidValue;
   // T = (X * s2) S_V: the r rows of S_V^T against x, their words split over
   // sp workgroups, each writing a partial T (sp x B x r)
+  if (B >= 9) {
+    // nine or more inputs: the matrix-core form, 16 inputs per pass (one
+    // pass costs about what four passes of two inputs through the tables
+    // cost); the first product split as below, over 64-row workgroups
+    const int64_t wgs = ((r + 63) / 64) * ((B + 15) / 16);
+    int64_t sp = std::min<int64_t>((1024 + wgs - 1) / wgs, kBinSplit);
+    sp = std::max<int64_t>(1, std::min<int64_t>(sp, ((n + 31) / 32 + 7) / 8));
+    rowdot_mfma<1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, (int)sp, B, s);
+    rowdot_mfma<kBinSplit>(su, ldu, m, r, T, r, (int)sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
+    return hipGetLastError();
+  }
   // (below 4096 rows and for one or two inputs, 16 rows per workgroup: 64
   // would leave most CUs idle)
   const int rpw1 = r >= 4096 || B > 2 ? kRpw1 : kRpw2;

@@ -1,5 +1,7 @@
 """GPU parity of the binary-layer product (nq_binary_matmul) and the sign
-transpose (nq_transpose_signs) against the CPU oracle.
+transpose (nq_transpose_signs) against the CPU oracle. Up to eight inputs
+run the lookup-table kernel, nine or more the matrix-core kernel; the
+shapes below cover both.
 
 The transpose is bit-exact against oracle.lbadmm.pack_signs of the
 transposed sign matrix. The product is compared with oracle.binary in
@@ -59,7 +61,8 @@ def test_transpose_signs_bit_exact(gpu, rows, cols):
 
 @pytest.mark.parametrize("m,n,r,B", [(1, 1, 1, 1), (64, 48, 8, 1), (300, 200, 70, 3), (257, 1000, 33, 2),
                                      (100, 4100, 2049, 5), (4096, 4096, 2048, 1), (4096, 4096, 2048, 8),
-                                     (11008, 4096, 1536, 4)])
+                                     (11008, 4096, 1536, 4), (300, 200, 70, 9), (257, 1000, 33, 33),
+                                     (65, 4100, 2049, 16), (4096, 4096, 2048, 24)])
 def test_binary_matmul_matches_oracle(gpu, m, n, r, B):
     import sub_bit_weight_lb_amd as nq
     rng = np.random.default_rng(m + 3 * n + 7 * r + B)
@@ -76,7 +79,9 @@ def test_binary_matmul_matches_oracle(gpu, m, n, r, B):
 
 
 def test_binary_matmul_strided_vector_and_repeatable(gpu):
-    """Row strides above the widths, a 1-D input, and bit-identical repeats."""
+    """Row strides above the widths, a 1-D input, and bit-identical repeats
+    (one input and three inputs take different kernel instances, so those
+    two agree to rounding, not bit for bit)."""
     import torch
     import sub_bit_weight_lb_amd as nq
     rng = np.random.default_rng(5)
@@ -96,7 +101,12 @@ def test_binary_matmul_strided_vector_and_repeatable(gpu):
     assert np.all(H(Yw[:, m:]) == 7.0)           # past the row width: untouched
     y1 = nq.binary_matmul(ub[:, :2], vt[:, :10], T(s1, gpu), T(s2, gpu), Xw[1, :n], r)
     assert y1.dim() == 1
-    np.testing.assert_array_equal(H(y1), H(Yw[1, :m]))   # same sums, same order
+    assert relerr(H(y1), ref[1]) < 1e-5
+    y1b = nq.binary_matmul(ub[:, :2], vt[:, :10], T(s1, gpu), T(s2, gpu), Xw[1, :n], r)
+    np.testing.assert_array_equal(H(y1), H(y1b))          # same call, same sums
+    Yw2 = torch.empty((B, m), dtype=torch.float32, device=gpu)
+    nq.binary_matmul(ub[:, :2], vt[:, :10], T(s1, gpu), T(s2, gpu), Xw[:, :n], r, Y=Yw2)
+    np.testing.assert_array_equal(H(Yw2), H(Yw[:, :m]))
 
 
 def test_binary_matmul_on_a_factorised_layer(gpu):
@@ -116,15 +126,17 @@ def test_binary_matmul_on_a_factorised_layer(gpu):
     assert relerr(Y, X.astype(np.float64) @ W_hat.T) < 1e-5
 
 
-def test_binary_matmul_full_size_70b_down(gpu):
-    """8192 x 28672 at r = 6144 (the largest layer), B = 2, against the whole
-    float64 oracle output."""
+@pytest.mark.parametrize("B", [2, 16])
+def test_binary_matmul_full_size_70b_down(gpu, B):
+    """8192 x 28672 at r = 6144 (the largest layer), against the whole
+    float64 oracle output: B = 2 (lookup-table kernel) and B = 16 (matrix
+    cores)."""
     import sub_bit_weight_lb_amd as nq
-    m, n, r, B = 8192, 28672, 6144, 2
+    m, n, r = 8192, 28672, 6144
     rng = np.random.default_rng(70)
     SU, SV, s1, s2 = layer(rng, m, n, r)
     X = rng.standard_normal((B, n)).astype(np.float32)
-    print("case matmul 8192x28672 r=6144 B=2", flush=True)
+    print(f"case matmul 8192x28672 r=6144 B={B}", flush=True)
     ub, vb = O.pack_signs(SU), O.pack_signs(SV)
     Vt = nq.transpose_signs(T(vb.view(np.int32), gpu), n, r)
     Y = H(nq.binary_matmul(T(ub.view(np.int32), gpu), Vt, T(s1, gpu), T(s2, gpu), T(X, gpu), r))
