@@ -31,6 +31,8 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 ATTN = "llama2-7b-attn-4096x4096-r2048"
 BLOCK_ONE = ["llama2-7b-block.q_proj", "llama2-7b-block.gate_proj", "llama2-7b-block.down_proj"]
+BLOCK_ALL = ["llama2-7b-block." + p for p in
+             ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")]
 MLP = "llama2-7b-mlp-11008x4096-r1536"
 DOWN70 = "llama2-70b-down-8192x28672-r6144"
 
@@ -118,7 +120,7 @@ def test_one_iteration_full_size(gpu, name):
     assert sign_agreement(st["V"], ref.V) >= 0.999
 
 
-@pytest.mark.parametrize("name", [ATTN, MLP])
+@pytest.mark.parametrize("name", [ATTN, MLP] + BLOCK_ALL)
 def test_full_run_vs_stored_oracle(gpu, name):
     g = load_golden(name)
     assert g is not None, f"missing tests/golden/lbadmm_final_{name}.json"
