@@ -287,7 +287,8 @@ void rowdot_any(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, c
 
 // rows per wave: the first product (r rows, long rows of n columns) shares
 // each chunk's tables among 64 rows per workgroup and splits its columns;
-// the second (m rows of r columns) keeps 16 rows per workgroup for a wide grid
+// the second (m rows of r columns) keeps 16 rows per workgroup for a wide
+// grid when there are one or two inputs
 constexpr int kRpw1 = 16, kRpw2 = 4;
 
 // Workgroups sharing the rows of the first product: enough for about 1024
@@ -343,7 +344,12 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
   else
     rowdot_any<kRpw2, 1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, sp, B, s);
   // Y = s1 * (T S_U^T): the m rows of S_U against the sum of the partials
-  rowdot_any<kRpw2, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
+  // (more than two inputs: 64 rows per workgroup, so each table serves more
+  // rows; one or two: 16, for a wider grid)
+  if (B > 2)
+    rowdot_any<kRpw1, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
+  else
+    rowdot_any<kRpw2, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
   return hipGetLastError();
 }
 
