@@ -14,7 +14,9 @@
 //
 // Up to eight inputs go through bin_rowdot_kernel (two per pass), nine or
 // more through bin_mfma_kernel (below), 16 inputs per pass on the matrix
-// cores.
+// cores. The first product's rows are long (n columns), so their words are
+// split over up to kBinSplit workgroups (grid z), each writing a partial T;
+// the second product sums the partials in order as it stages its input.
 //
 // bin_rowdot_kernel: four waves, RPW rows per wave; lane l holds word l of
 // a 64-word (2048-column) chunk of each of its rows. For the chunk the
