@@ -66,6 +66,54 @@ def read_traffic(m, n, r, launches_ms):
     return float(mt.group(1))
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bpw(m, n, r, scale_bits=16):
+    """Bits per weight of the factorised layer: the sign bits r (m + n), plus
+    the two scale vectors at `scale_bits` each (fp16 by default)."""
+    return (r * (m + n) + scale_bits * (m + n)) / (m * n)
+
+
+def hbm_bench(nq, torch, dev, L, reps=20):
+    """The HBM-bound kernels alone at the layer's shape, with HIP events: the
+    SVID + dual update (one launch per update, on the state a run leaves) for
+    each factor, and whole runs of one iteration split by phase (prep =
+    precondition + init, finish = balance + scales + packing + error)."""
+    wl = L.workload
+    m, n, r = wl.m, wl.n, wl.r
+
+    def t(x):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    W, d_out, d_in, EU, EV = t(L.W), t(L.d_out), t(L.d_in), t(L.EU), t(L.EV)
+    h = nq.LBADMM(m, n, r, rho=wl.rho, iters=1, svid_steps=wl.svid_steps, compute_error=True,
+                  profile=True)
+    out = h.alloc_outputs(dev)
+    h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
+    h.profile(reset=True)
+    for _ in range(reps):
+        h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
+    ph = h.profile(reset=True)
+    res = {"prep_ms": round(ph["prep"][0] / ph["prep"][1], 4),
+           "finish_ms": round(ph["finish"][0] / ph["finish"][1], 4)}
+    for f, rows in ((0, m), (1, n)):
+        ms = h.time_svid(f, reps=reps)
+        gbs = 16.0 * rows * r / (ms * 1e-3) / 1e9
+        res["svid_" + "UV"[f]] = {"avg_us": round(ms * 1e3, 2), "bytes": 16 * rows * r,
+                                  "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+    h.close()
+    return res
+
+
 def cpu_baseline(L, budget_s=10.0, max_iters=12, budget_fp32_s=6.0):
     """The CPU oracle on the same layer: a bounded number of ADMM iterations
     in NumPy float64 (the parity oracle; reported as value) and, as a second
@@ -90,7 +138,10 @@ def cpu_baseline(L, budget_s=10.0, max_iters=12, budget_fp32_s=6.0):
 
     d64, t64, p64, fin64 = timed(np.float64, budget_s)
     d32, t32, p32, fin32 = timed(np.float32, budget_fp32_s)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] + [1])
+    blas = sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                   for i in pools if i.get("user_api") == "blas"})
     return {
         "value": d64 / t64,
         "unit": "iters/s",
@@ -102,6 +153,8 @@ def cpu_baseline(L, budget_s=10.0, max_iters=12, budget_fp32_s=6.0):
         "fp32_value": d32 / t32,
         "fp32_sample": f"{d32} iterations in float32 mode, {t32:.1f} s",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "blas": ", ".join(blas) or "unknown",
+        "cpu_model": cpu_model(),
         "s_per_iter": t64 / d64,
         "finite": fin64 and fin32,
     }
@@ -182,6 +235,9 @@ def main():
     ap.add_argument("--kernels", action="store_true",
                     help="only run the GEMM kernels alone on the layer's shapes, 20 launches "
                          "each (for a kernel-trace profile of their standalone durations)")
+    ap.add_argument("--hbm", action="store_true",
+                    help="only time the HBM-bound kernels (SVID + dual update, prep, finish) "
+                         "on the layer's shape (for counter and kernel-trace profiles)")
     ap.add_argument("--binary", action="store_true",
                     help="only time the binary-layer product (nq_binary_matmul) on the layer "
                          "shapes, warm and with its sign bits rotated through > 256 MB")
@@ -235,6 +291,9 @@ def main():
         return
     L = make_layer(WORKLOAD)
     wl = L.workload
+    if args.hbm:
+        print(json.dumps({"hbm_kernels": hbm_bench(nq, torch, dev, L)}), flush=True)
+        return
     m, n, r = wl.m, wl.n, wl.r
     iters = wl.iters if args.iters is None else args.iters
 
@@ -269,6 +328,15 @@ def main():
     status, stats = nq.lbadmm_query(h.handle)
     if status != 0:
         raise SystemExit(f"run reported {nq.status_string(status)}")
+    # The SVID + dual update alone (one persistent launch per update), on the
+    # state the last run left: algorithmic bytes 16 per element of the factor
+    # (read the latent and Lam, write Lam and P).
+    svid = {}
+    for f, rows in ((0, m), (1, n)):
+        ms = h.time_svid(f, reps=20)
+        gbs = 16.0 * rows * r / (ms * 1e-3) / 1e9
+        svid["UV"[f]] = {"avg_us": round(ms * 1e3, 2), "bytes": 16 * rows * r,
+                         "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
     h.close()
 
     elapsed = t1 - t0
@@ -332,6 +400,9 @@ def main():
                                   / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
             "source": "the untimed run with every phase timed",
         },
+        "svid_update_standalone": svid,
+        "bpw": round(bpw(m, n, r, 0), 4),
+        "bpw_with_fp16_scales": round(bpw(m, n, r, 16), 4),
         "rel_err_wtilde": stats["rel_err_wtilde"],
         "rel_err_w": stats["rel_err_w"],
     }

@@ -52,7 +52,9 @@ typedef enum nq_status {
   NQ_ERR_INVALID_ARG = 1,           /* bad size, pointer, ld, rho, iters, flags    */
   NQ_ERR_UNSUPPORTED = 2,           /* no usable gfx950 device / shape not allowed */
   NQ_ERR_OUT_OF_MEMORY = 3,         /* device allocation failed                    */
-  NQ_ERR_HIP = 4,                   /* a HIP runtime call failed                   */
+  NQ_ERR_HIP = 4,                   /* a HIP runtime call failed, or an SVID
+                                       launch's workgroups were not all resident
+                                       within its wait bound (about 0.5 s)         */
   NQ_ERR_NOT_POSITIVE_DEFINITE = 5, /* a Cholesky pivot was <= 0 or not finite     */
   NQ_ERR_NONFINITE = 6,             /* NaN/Inf in the input or produced on device  */
   NQ_ERR_BAD_PRECONDITIONER = 7     /* an entry of d_out or d_in is not > 0        */
@@ -84,9 +86,9 @@ typedef enum nq_phase {
 } nq_phase;
 
 typedef struct nq_lbadmm_desc {
-  int64_t m;          /* rows of W (output features), >= 1                         */
-  int64_t n;          /* columns of W (input features), >= 1                       */
-  int64_t r;          /* rank of the binary factors, >= 1                          */
+  int64_t m;          /* rows of W (output features), 1 .. 2^21 - 256              */
+  int64_t n;          /* columns of W (input features), 1 .. 2^21 - 256            */
+  int64_t r;          /* rank of the binary factors, 1 .. 2^13                     */
   float rho;          /* ADMM penalty, > 0 and finite                              */
   int32_t iters;      /* ADMM iterations (each: U-half then V-half), >= 0          */
   int32_t svid_steps; /* alternating rank-1 steps inside SVID, >= 1                */
@@ -173,6 +175,18 @@ nq_status nq_lbadmm_get_state(nq_lbadmm_t h, float* U, float* V,
  * NQ_ERR_INVALID_ARG if the handle was created without NQ_FLAG_PROFILE. */
 nq_status nq_lbadmm_profile(nq_lbadmm_t h, double* ms, int64_t* count, int32_t reset);
 
+/* Measurement of the SVID + dual update on its own (digest, section 核心方法
+ * steps (b) and (c)): after a run, enqueue on `stream` `reps` (>= 1) updates
+ * of factor `factor` (0 = U, 1 = V) back to back, each exactly as a
+ * half-iteration makes it (X = latent + Lam, `svid_steps` rank-1 steps on
+ * |X|, Lam = X - Z, P = Z - Lam, one launch), wait, and return the average
+ * device time per update in ms from HIP events (*avg_ms, host). The handle's
+ * duals and proxies change; the next run starts afresh from its inputs.
+ * NQ_ERR_INVALID_ARG before the first run or for a bad factor / reps;
+ * NQ_ERR_HIP if a launch failed or its workgroups were not co-resident. */
+nq_status nq_lbadmm_time_svid(nq_lbadmm_t h, int32_t factor, int32_t reps, void* stream,
+                              double* avg_ms);
+
 /* Free the handle and its workspace (NULL is ignored). Waits for its work. */
 void nq_lbadmm_destroy(nq_lbadmm_t h);
 
@@ -255,6 +269,16 @@ nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg,
 nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                      int32_t T, float* Z, int64_t ldz, float* a, float* b,
                      void* stream);
+
+/* SVID fused with the dual update, as one half-iteration does it ("核心方法"
+ * (b) and (c)): X = U + Lam, Z = SVID_T(X), Lam_out = X - Z. U and Lam
+ * (device) rows x cols, ld ldi; Z and Lam_out (device) rows x cols, ld ldo;
+ * a (rows), b (cols) device, nullable. Staged through padded temporaries
+ * (rows to 256, cols to 128); the call waits for `stream`. NQ_ERR_HIP also
+ * when the launch's workgroups were not all resident within its wait bound. */
+nq_status nq_op_svid_dual(const float* U, const float* Lam, int64_t rows, int64_t cols,
+                          int64_t ldi, int32_t T, float* Z, float* Lam_out, int64_t ldo,
+                          float* a, float* b, void* stream);
 
 const char* nq_status_string(nq_status s);
 const char* nq_last_error_message(void);

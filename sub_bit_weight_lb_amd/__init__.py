@@ -154,6 +154,15 @@ def lbadmm_profile(h, reset=False) -> dict:
     return {p: (float(ms[i]), int(cnt[i])) for i, p in enumerate(PHASES)}
 
 
+def lbadmm_time_svid(h, factor, reps=10, stream=None) -> float:
+    """Average device ms of one SVID + dual update of factor 0 (U) or 1 (V),
+    `reps` back to back on the handle's state after a run."""
+    ms = C.c_double()
+    _check(_lib.load().nq_lbadmm_time_svid(C.c_void_p(h), int(factor), int(reps), _stream(stream),
+                                           C.byref(ms)), "nq_lbadmm_time_svid")
+    return float(ms.value)
+
+
 def lbadmm_destroy(h):
     if h:
         _lib.load().nq_lbadmm_destroy(C.c_void_p(h))
@@ -285,6 +294,24 @@ def op_svid(X, T, stream=None):
     return Z, a, b
 
 
+def op_svid_dual(U, Lam, T, stream=None):
+    """X = U + Lam, Z = SVID_T(X), Lam_out = X - Z: returns (Z, Lam_out, a, b)."""
+    torch = _torch()
+    rows, cols = U.shape
+    if tuple(Lam.shape) != (rows, cols):
+        raise ValueError("U and Lam must have the same shape")
+    f32 = torch.float32
+    Z = torch.empty((rows, cols), dtype=f32, device=U.device)
+    Lo = torch.empty((rows, cols), dtype=f32, device=U.device)
+    a = torch.empty((rows,), dtype=f32, device=U.device)
+    b = torch.empty((cols,), dtype=f32, device=U.device)
+    _check(_lib.load().nq_op_svid_dual(_ptr(U, "U", f32, 2), _ptr(Lam, "Lam", f32, 2), rows, cols,
+                                       cols, int(T), _ptr(Z, "Z", f32, 2), _ptr(Lo, "Lam_out", f32, 2),
+                                       cols, _ptr(a, "a", f32, 1), _ptr(b, "b", f32, 1),
+                                       _stream(stream)), "nq_op_svid_dual")
+    return Z, Lo, a, b
+
+
 @dataclass
 class Result:
     U: "object"
@@ -332,6 +359,9 @@ class LBADMM:
 
     def profile(self, reset=False):
         return lbadmm_profile(self.handle, reset)
+
+    def time_svid(self, factor, reps=10, stream=None):
+        return lbadmm_time_svid(self.handle, factor, reps, stream)
 
     def state(self, stream=None):
         torch = _torch()

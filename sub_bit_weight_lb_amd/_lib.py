@@ -54,6 +54,7 @@ SIGNATURES = {
     "nq_lbadmm_get_state": (ST, [P, P, P, P, P, P, P, P]),
     "nq_lbadmm_destroy": (None, [P]),
     "nq_lbadmm_profile": (ST, [P, C.POINTER(C.c_double), C.POINTER(I64), C.c_int32]),
+    "nq_lbadmm_time_svid": (ST, [P, C.c_int32, C.c_int32, P, C.POINTER(C.c_double)]),
     "nq_pack_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_transpose_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_binary_matmul": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P, P]),
@@ -62,6 +63,7 @@ SIGNATURES = {
     "nq_op_gemm_rhs": (ST, [P, I64, P, I64, P, I64, F32, P, I64, I64, I64, I64, P]),
     "nq_op_cholesky_inverse": (ST, [P, I64, I64, P, I64, P, I64, C.POINTER(I64), P]),
     "nq_op_svid": (ST, [P, I64, I64, I64, C.c_int32, P, I64, P, P, P]),
+    "nq_op_svid_dual": (ST, [P, P, I64, I64, I64, C.c_int32, P, P, I64, P, P, P]),
     "nq_status_string": (C.c_char_p, [ST]),
     "nq_last_error_message": (C.c_char_p, []),
     "nq_version": (C.c_int32, []),

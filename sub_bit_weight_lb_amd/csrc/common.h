@@ -35,7 +35,12 @@ struct DevStats {
   int nonfinite;        // NaN/Inf seen
   int bad_precond;      // some d <= 0
   int potrf_info;       // 0 or 1 + first failing pivot column (min over runs)
-  int pad;
+  int sync_timeout;     // an SVID launch's exchange wait ran out (workgroups not co-resident)
+  // the first wait that ran out: workgroup, step, phase (0 partials, 1 b),
+  // the tag expected and the tag read, the launch's epoch
+  uint32_t to_wg, to_step, to_phase, to_want, to_seen, to_epoch;
+  uint64_t to_start, to_now;  // the waiting workgroup's start and the expiry, 100 MHz ticks
+  uint32_t to_src, to_src_prog;  // the workgroup it waited for, and its progress word then
 };
 
 // Launch layout of the pinned overlap (MI355X: 8 XCDs x 32 CUs).
@@ -149,21 +154,40 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    GramSrc src = GramSrc{nullptr, GramSteps{0, 0}, 1, 0.0f});
 
 // ---------------------------------------------------------------- SVID
-struct SvidWork {
-  float* a;        // rows_pad
-  float* b;        // rp
-  float* colpart;  // svid_partials(rows_pad, rp) x rp
-  float* aapart;   // svid_partials(rows_pad, rp)
-  float* bbpart;   // rp / 128
-  float* part2;    // kSvidReduceRows x rp
+// Exchange words of the persistent SVID launch (64-bit: value, tag), in a
+// zero-initialised buffer of svid_sync_words(rp, G) words: part (rp / 4
+// column quads x G slabs x 4), aa (G), b (rp), then two 32-bit control words
+// (the epoch and the count of finished workgroups) and G progress words.
+struct SvidSync {
+  uint64_t* part;
+  uint64_t* aa;
+  uint64_t* b;
+  uint32_t* ctl;
+  uint32_t* prog;  // G words: per workgroup, (tag << 2) | stage of its progress
 };
-constexpr int kSvidReduceRows = 16;
-int svid_nchunks(int rows_pad);            // 64-row chunks of the column pass
-int svid_partials(int rows_pad, int rp);   // partial rows the SVID work arrays hold
-// mode 0: init (P = Z, X left as is), mode 1: update (X <- X - Z, P = 2Z - X_old),
-// mode 2: plain (Z written to P; X untouched). With Uadd (nullable, same
-// layout as X), X is first replaced by X + Uadd (formed by the first step).
-// rows_pad % 8 == 0, rp % 128 == 0, T >= 1.
+struct SvidWork {
+  float* a;     // rows_pad: a of the last step
+  float* b;     // rp: b of the last step
+  SvidSync sy;
+  DevStats* st; // sync_timeout is raised there
+  int G;        // workgroups (svid_grid())
+};
+// Launch layout of one SVID update: G workgroups of TX threads (TY = 1), RS
+// rows each; a thread holds NU float4 columns of RPT rows per chunk, NCH
+// chunks per step (1: the slab stays in registers); a workgroup reduces NQO
+// consecutive column quads (a power of two) over the slabs.
+struct SvidPlan {
+  int G, RS, TX, TY, NU, RPT, NCH, NQO, inst;
+};
+int svid_grid();  // workgroups of an SVID launch on the current device: 64, 128 or 256
+size_t svid_sync_words(int rp, int G);
+SvidSync svid_sync_at(uint64_t* base, int rp, int G);
+bool svid_plan(int rows_pad, int rp, int G, SvidPlan* out);
+int svid_nchunks(int rows_pad);  // 64-row chunks of the column-norm pass
+// mode 0: init (P = Z, X zeroed: Lam = 0), mode 1: update (X <- X - Z,
+// P = Z - X_new), mode 2: plain (Z written to P; X untouched). With Uadd
+// (nullable, same layout as X), X is first replaced by X + Uadd. rp % 128 ==
+// 0, T >= 1; one launch.
 hipError_t launch_svid(float* X, float* P, int rows_pad, int rp, int r_real, int T,
                        int mode, const SvidWork& w, hipStream_t s,
                        const float* Uadd = nullptr);

@@ -41,13 +41,19 @@ constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
                                   NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE |
                                   NQ_FLAG_PROFILE_RHS_ONLY;
 constexpr int kProfileRuns = 8;
+constexpr int64_t kMaxMN = (1 << 21) - 256;
+constexpr int64_t kMaxR = 1 << 13;
 constexpr int kRhsYield = 8;
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
   if (d->m < 1 || d->n < 1 || d->r < 1) return fail(NQ_ERR_INVALID_ARG, "m, n, r must be >= 1");
-  if (d->m > (1 << 22) || d->n > (1 << 22) || d->r > (1 << 16))
-    return fail(NQ_ERR_INVALID_ARG, "m, n must be <= 2^22 and r <= 2^16");
+  // the tiled products address 256 rows of an operand with 32-bit byte
+  // offsets (padded m and n below 2^21); an SVID workgroup reduces at most
+  // 32 columns over 256 slabs
+  if (d->m > kMaxMN || d->n > kMaxMN)
+    return fail(NQ_ERR_INVALID_ARG, "m and n must be <= 2^21 - 256");
+  if (d->r > kMaxR) return fail(NQ_ERR_INVALID_ARG, "r must be <= 2^13");
   if (!(d->rho > 0.0f) || !std::isfinite(d->rho))
     return fail(NQ_ERR_INVALID_ARG, "rho must be finite and > 0");
   if (d->iters < 0) return fail(NQ_ERR_INVALID_ARG, "iters must be >= 0");
@@ -120,6 +126,7 @@ struct nq_lbadmm {
             ev_t1 = nullptr;
   hipStream_t last_stream = nullptr;
   bool has_run = false;
+  bool stats_valid = false;  // the stats block describes the last run (not a time_svid call)
   // s_sleep units (~64 cycles each) per K step of the RHS GEMM while it runs
   // beside the chain: the chain is the critical path and a wave sharing a
   // SIMD with an MFMA-bound wave gets little issue time; the RHS has slack.
@@ -129,6 +136,7 @@ struct nq_lbadmm {
   // the RHS GEMM on XCDs 0-6. Needs 8 x 32 CUs and at most 32 diagonal
   // workgroups per launch (r_p <= 2048); NQ_PIN=0 turns it off.
   bool pin = false;
+  int svid_g = 256;  // workgroups of an SVID launch (svid_grid())
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
   std::vector<hipEvent_t> prof_ev;
   std::vector<int> prof_phase;  // phase of each pending pair
@@ -155,14 +163,10 @@ size_t layout(nq_lbadmm* h) {
   size_t o_Mt = a.take<float>(rp * rp);
   size_t o_gp = a.take<float>((size_t)gch * rp * rp);
   const int nchU = svid_nchunks((int)mp), nchV = svid_nchunks((int)np_);
-  const int spU = std::max(nchU, svid_partials((int)mp, (int)rp));
-  const int spV = std::max(nchV, svid_partials((int)np_, (int)rp));
-  size_t o_sUa = a.take<float>(mp), o_sUb = a.take<float>(rp),
-         o_sUc = a.take<float>((size_t)spU * rp), o_sUaa = a.take<float>(spU),
-         o_sUbb = a.take<float>(rp / 128), o_sUp2 = a.take<float>(kSvidReduceRows * rp);
-  size_t o_sVa = a.take<float>(np_), o_sVb = a.take<float>(rp),
-         o_sVc = a.take<float>((size_t)spV * rp), o_sVaa = a.take<float>(spV),
-         o_sVbb = a.take<float>(rp / 128), o_sVp2 = a.take<float>(kSvidReduceRows * rp);
+  // SVID exchange words, sized for the largest grid (256 workgroups)
+  const size_t syw = svid_sync_words((int)rp, 256);
+  size_t o_sUa = a.take<float>(mp), o_sUb = a.take<float>(rp), o_sUs = a.take<uint64_t>(syw);
+  size_t o_sVa = a.take<float>(np_), o_sVb = a.take<float>(rp), o_sVs = a.take<uint64_t>(syw);
   const int npre = precondition_nblocks((int)mp, (int)np_);
   size_t o_pwt = a.take<double>(npre), o_pw = a.take<double>(npre);
   size_t o_err = a.take<double>(2 * (size_t)error_nparts((int)mp, (int)np_));
@@ -184,17 +188,18 @@ size_t layout(nq_lbadmm* h) {
     h->G = (float*)(b + o_G); h->Minv = (float*)(b + o_M); h->Ginv = (float*)(b + o_Gi);
     h->Mt = (float*)(b + o_Mt);
     h->gpart = (float*)(b + o_gp);
-    h->svU = SvidWork{(float*)(b + o_sUa), (float*)(b + o_sUb), (float*)(b + o_sUc),
-                      (float*)(b + o_sUaa), (float*)(b + o_sUbb), (float*)(b + o_sUp2)};
-    h->svV = SvidWork{(float*)(b + o_sVa), (float*)(b + o_sVb), (float*)(b + o_sVc),
-                      (float*)(b + o_sVaa), (float*)(b + o_sVbb), (float*)(b + o_sVp2)};
+    h->st = (DevStats*)(b + o_st);
+    const int G = h->svid_g;
+    h->svU = SvidWork{(float*)(b + o_sUa), (float*)(b + o_sUb),
+                      svid_sync_at((uint64_t*)(b + o_sUs), (int)rp, G), h->st, G};
+    h->svV = SvidWork{(float*)(b + o_sVa), (float*)(b + o_sVb),
+                      svid_sync_at((uint64_t*)(b + o_sVs), (int)rp, G), h->st, G};
     h->part_wt = (double*)(b + o_pwt); h->part_w = (double*)(b + o_pw);
     h->err_parts = (double*)(b + o_err);
     h->colpartU = (float*)(b + o_cpU); h->colpartV = (float*)(b + o_cpV);
     h->cbal = (float*)(b + o_cb); h->s1w = (float*)(b + o_s1w); h->s2w = (float*)(b + o_s2w);
     h->s1c = (float*)(b + o_s1c); h->s2c = (float*)(b + o_s2c);
     h->SU = (int8_t*)(b + o_SU); h->SV = (int8_t*)(b + o_SV);
-    h->st = (DevStats*)(b + o_st);
     h->rhs_part = (float*)(b + o_rp);
   }
   return a.off;
@@ -327,9 +332,23 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   return NQ_OK;
 }
 
+std::string svid_timeout_text(const DevStats& hs) {
+  return "an SVID launch's workgroups were not all resident within about 0.5 s (results invalid; "
+         "first expired wait: workgroup " + std::to_string(hs.to_wg) + ", step " +
+         std::to_string(hs.to_step) + (hs.to_phase ? ", b" : ", partials") + ", tag wanted " +
+         std::to_string(hs.to_want) + ", read " + std::to_string(hs.to_seen) + ", epoch " +
+         std::to_string(hs.to_epoch) + ", waited " +
+         std::to_string((long long)(hs.to_now - hs.to_start)) + " ticks from start " +
+         std::to_string((unsigned long long)hs.to_start) + "; awaited workgroup " +
+         std::to_string(hs.to_src) + " at tag " + std::to_string(hs.to_src_prog >> 2) +
+         " stage " + std::to_string(hs.to_src_prog & 3) + ")";
+}
+
 nq_status status_from(const DevStats& hs) {
   if (hs.bad_precond) return fail(NQ_ERR_BAD_PRECONDITIONER, "an entry of d_out or d_in is not > 0");
   if (hs.nonfinite) return fail(NQ_ERR_NONFINITE, "NaN or Inf in the input or the result");
+  if (hs.sync_timeout)
+    return fail(NQ_ERR_HIP, svid_timeout_text(hs));
   if (hs.potrf_info != 0x7fffffff)
     return fail(NQ_ERR_NOT_POSITIVE_DEFINITE,
                 "Cholesky pivot <= 0 at column " + std::to_string(hs.potrf_info - 1));
@@ -381,7 +400,15 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   nq_lbadmm* h = new nq_lbadmm();
   h->d = *desc;
   h->device = dev;
+  h->svid_g = svid_grid();
   plan(h);
+  {
+    SvidPlan sp;
+    if (!svid_plan(h->mp, h->rp, h->svid_g, &sp) || !svid_plan(h->np_, h->rp, h->svid_g, &sp)) {
+      delete h;
+      return fail(NQ_ERR_UNSUPPORTED, "no SVID launch layout for this shape");
+    }
+  }
   h->bytes = layout(h);
   hipError_t e = hipMalloc((void**)&h->base, h->bytes);
   if (e != hipSuccess) {
@@ -403,6 +430,7 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_gram, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_rhs, hipEventDisableTiming);
+
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t0);
   if (e == hipSuccess) e = hipEventCreate(&h->ev_t1);
   if (e == hipSuccess && (h->d.flags & NQ_FLAG_PROFILE)) {
@@ -433,6 +461,7 @@ void nq_lbadmm_destroy(nq_lbadmm_t h) {
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   if (h->ev_gram) (void)hipEventDestroy(h->ev_gram);
   if (h->ev_rhs) (void)hipEventDestroy(h->ev_rhs);
+
   if (h->ev_t0) (void)hipEventDestroy(h->ev_t0);
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
   for (hipEvent_t ev : h->prof_ev)
@@ -530,6 +559,7 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   HIPCHK(hipEventRecord(h->ev_t1, s));
   h->last_stream = s;
   h->has_run = true;
+  h->stats_valid = true;
   if (stats) return nq_lbadmm_query(h, stats);
   return NQ_OK;
 }
@@ -554,6 +584,8 @@ nq_status nq_lbadmm_profile(nq_lbadmm_t h, double* ms, int64_t* count, int32_t r
 nq_status nq_lbadmm_query(nq_lbadmm_t h, nq_lbadmm_stats* stats) {
   if (!h || !stats) return fail(NQ_ERR_INVALID_ARG, "handle and stats are required");
   if (!h->has_run) return fail(NQ_ERR_INVALID_ARG, "handle has not run");
+  if (!h->stats_valid)
+    return fail(NQ_ERR_INVALID_ARG, "nq_lbadmm_time_svid ran since the last run; run again");
   HIPCHK(hipEventSynchronize(h->ev_t1));
   DevStats hs;
   HIPCHK(hipMemcpy(&hs, h->st, sizeof(DevStats), hipMemcpyDeviceToHost));
@@ -587,5 +619,35 @@ extern "C" nq_status nq_lbadmm_get_state(nq_lbadmm_t h, float* U, float* V, floa
   if (Lam_V) HIPCHK(hipMemcpy2DAsync(Lam_V, dp, h->LamV, sp, dp, n, hipMemcpyDeviceToDevice, s));
   if (Z_U) HIPCHK(launch_add_compact(h->PU, h->LamU, m, r, (int)rp, Z_U, s));
   if (Z_V) HIPCHK(launch_add_compact(h->PV, h->LamV, n, r, (int)rp, Z_V, s));
+  return NQ_OK;
+}
+
+extern "C" nq_status nq_lbadmm_time_svid(nq_lbadmm_t h, int32_t factor, int32_t reps,
+                                         void* stream, double* avg_ms) {
+  if (!h || !avg_ms) return fail(NQ_ERR_INVALID_ARG, "handle and avg_ms are required");
+  if (factor != 0 && factor != 1) return fail(NQ_ERR_INVALID_ARG, "factor must be 0 (U) or 1 (V)");
+  if (reps < 1) return fail(NQ_ERR_INVALID_ARG, "reps must be >= 1");
+  if (!h->has_run) return fail(NQ_ERR_INVALID_ARG, "handle has not run");
+  hipStream_t s = (hipStream_t)stream;
+  const bool u = factor == 0;
+  const int rows = u ? h->mp : h->np_;
+  float* lam = u ? h->LamU : h->LamV;
+  float* P = u ? h->PU : h->PV;
+  const float* lat = u ? h->U : h->V;
+  const SvidWork& w = u ? h->svU : h->svV;
+  HIPCHK(hipStreamWaitEvent(s, h->ev_t1, 0));  // after the last run
+  HIPCHK(launch_stats_init(h->st, s));
+  HIPCHK(hipEventRecord(h->ev_t0, s));
+  for (int i = 0; i < reps; ++i)
+    HIPCHK(launch_svid(lam, P, rows, h->rp, (int)h->d.r, h->d.svid_steps, 1, w, s, lat));
+  HIPCHK(hipEventRecord(h->ev_t1, s));
+  HIPCHK(hipEventSynchronize(h->ev_t1));
+  float ms = 0.0f;
+  HIPCHK(hipEventElapsedTime(&ms, h->ev_t0, h->ev_t1));
+  DevStats hs;
+  HIPCHK(hipMemcpy(&hs, h->st, sizeof(DevStats), hipMemcpyDeviceToHost));
+  *avg_ms = (double)ms / reps;
+  h->stats_valid = false;  // the stats block no longer describes a run
+  if (hs.sync_timeout) return fail(NQ_ERR_HIP, svid_timeout_text(hs));
   return NQ_OK;
 }

@@ -4,6 +4,7 @@
 // allocate, so they are for tests and tools, not for the hot path.
 #include <algorithm>
 #include <cstdint>
+#include <string>
 #include <vector>
 
 #include "abi.h"
@@ -197,25 +198,77 @@ nq_status nq_op_svid(const float* X, int64_t rows, int64_t cols, int64_t ldx, in
                      int64_t ldz, float* a, float* b, void* stream) {
   if (rows < 1 || cols < 1 || T < 1 || ldx < cols || !X || (Z && ldz < cols))
     return set_error(NQ_ERR_INVALID_ARG, "bad svid arguments");
+  if (rows > (1 << 21) || cols > (1 << 13)) return set_error(NQ_ERR_INVALID_ARG, "svid shape too large");
   hipStream_t s = (hipStream_t)stream;
-  const int64_t rows_pad = round_up(rows, 8), rp = round_up(cols, 128);
-  const int nch = std::max(svid_nchunks((int)rows_pad), svid_partials((int)rows_pad, (int)rp));
-  DevBuf x, p, wa, wb, wc, waa, wbb, wp2;
+  const int64_t rows_pad = round_up(rows, 256), rp = round_up(cols, 128);
+  DevBuf x, p, wa, wb, sync, st;
   NQ_HIPCHK(x.alloc(sizeof(float) * rows_pad * rp));
   NQ_HIPCHK(p.alloc(sizeof(float) * rows_pad * rp));
   NQ_HIPCHK(wa.alloc(sizeof(float) * rows_pad));
   NQ_HIPCHK(wb.alloc(sizeof(float) * rp));
-  NQ_HIPCHK(wc.alloc(sizeof(float) * nch * rp));
-  NQ_HIPCHK(waa.alloc(sizeof(float) * nch));
-  NQ_HIPCHK(wbb.alloc(sizeof(float) * (rp / 128)));
-  NQ_HIPCHK(wp2.alloc(sizeof(float) * kSvidReduceRows * rp));
-  SvidWork w{wa.f(), wb.f(), wc.f(), waa.f(), wbb.f(), wp2.f()};
+  const int G = svid_grid();
+  const size_t nw = svid_sync_words((int)rp, G);
+  NQ_HIPCHK(sync.alloc(sizeof(uint64_t) * nw));
+  NQ_HIPCHK(st.alloc(sizeof(DevStats)));
+  NQ_HIPCHK(hipMemsetAsync(sync.p, 0, sizeof(uint64_t) * nw, s));
+  NQ_HIPCHK(launch_stats_init((DevStats*)st.p, s));
+  SvidWork w{wa.f(), wb.f(), svid_sync_at((uint64_t*)sync.p, (int)rp, G), (DevStats*)st.p, G};
   NQ_HIPCHK(stage_in(X, rows, cols, ldx, x.f(), rows_pad, rp, s));
   NQ_HIPCHK(launch_svid(x.f(), p.f(), (int)rows_pad, (int)rp, (int)cols, T, 2, w, s));
   if (Z) NQ_HIPCHK(stage_out(p.f(), rp, Z, ldz, rows, cols, s));
   if (a) NQ_HIPCHK(hipMemcpyAsync(a, wa.f(), sizeof(float) * rows, hipMemcpyDeviceToDevice, s));
   if (b) NQ_HIPCHK(hipMemcpyAsync(b, wb.f(), sizeof(float) * cols, hipMemcpyDeviceToDevice, s));
+  DevStats hs;
+  NQ_HIPCHK(hipMemcpyAsync(&hs, st.p, sizeof(hs), hipMemcpyDeviceToHost, s));
   NQ_HIPCHK(hipStreamSynchronize(s));
+  if (hs.sync_timeout)
+    return set_error(NQ_ERR_HIP, "the SVID launch's workgroups were not all resident within about 0.5 s "
+                                 "(first expired wait: workgroup " + std::to_string(hs.to_wg) +
+                                 ", step " + std::to_string(hs.to_step) + ", tag wanted " +
+                                 std::to_string(hs.to_want) + ", read " +
+                                 std::to_string(hs.to_seen) + ")");
+  return NQ_OK;
+}
+
+nq_status nq_op_svid_dual(const float* U, const float* Lam, int64_t rows, int64_t cols,
+                          int64_t ldi, int32_t T, float* Z, float* Lam_out, int64_t ldo,
+                          float* a, float* b, void* stream) {
+  if (rows < 1 || cols < 1 || T < 1 || ldi < cols || ldo < cols || !U || !Lam || !Z || !Lam_out)
+    return set_error(NQ_ERR_INVALID_ARG, "bad svid_dual arguments");
+  if (rows > (1 << 21) || cols > (1 << 13)) return set_error(NQ_ERR_INVALID_ARG, "svid shape too large");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t rows_pad = round_up(rows, 256), rp = round_up(cols, 128);
+  DevBuf u, x, p, wa, wb, sync, st;
+  NQ_HIPCHK(u.alloc(sizeof(float) * rows_pad * rp));
+  NQ_HIPCHK(x.alloc(sizeof(float) * rows_pad * rp));
+  NQ_HIPCHK(p.alloc(sizeof(float) * rows_pad * rp));
+  NQ_HIPCHK(wa.alloc(sizeof(float) * rows_pad));
+  NQ_HIPCHK(wb.alloc(sizeof(float) * rp));
+  const int G = svid_grid();
+  const size_t nw = svid_sync_words((int)rp, G);
+  NQ_HIPCHK(sync.alloc(sizeof(uint64_t) * nw));
+  NQ_HIPCHK(st.alloc(sizeof(DevStats)));
+  NQ_HIPCHK(hipMemsetAsync(sync.p, 0, sizeof(uint64_t) * nw, s));
+  NQ_HIPCHK(launch_stats_init((DevStats*)st.p, s));
+  SvidWork w{wa.f(), wb.f(), svid_sync_at((uint64_t*)sync.p, (int)rp, G), (DevStats*)st.p, G};
+  NQ_HIPCHK(stage_in(U, rows, cols, ldi, u.f(), rows_pad, rp, s));
+  NQ_HIPCHK(stage_in(Lam, rows, cols, ldi, x.f(), rows_pad, rp, s));
+  NQ_HIPCHK(launch_svid(x.f(), p.f(), (int)rows_pad, (int)rp, (int)cols, T, 1, w, s, u.f()));
+  // Z = P + Lam_out (P = Z - Lam_out is what the update stores)
+  NQ_HIPCHK(launch_add_compact(p.f(), x.f(), rows, cols, (int)rp, u.f(), s));
+  NQ_HIPCHK(stage_out(u.f(), cols, Z, ldo, rows, cols, s));
+  NQ_HIPCHK(stage_out(x.f(), rp, Lam_out, ldo, rows, cols, s));
+  if (a) NQ_HIPCHK(hipMemcpyAsync(a, wa.f(), sizeof(float) * rows, hipMemcpyDeviceToDevice, s));
+  if (b) NQ_HIPCHK(hipMemcpyAsync(b, wb.f(), sizeof(float) * cols, hipMemcpyDeviceToDevice, s));
+  DevStats hs;
+  NQ_HIPCHK(hipMemcpyAsync(&hs, st.p, sizeof(hs), hipMemcpyDeviceToHost, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  if (hs.sync_timeout)
+    return set_error(NQ_ERR_HIP, "the SVID launch's workgroups were not all resident within about 0.5 s "
+                                 "(first expired wait: workgroup " + std::to_string(hs.to_wg) +
+                                 ", step " + std::to_string(hs.to_step) + ", tag wanted " +
+                                 std::to_string(hs.to_want) + ", read " +
+                                 std::to_string(hs.to_seen) + ")");
   return NQ_OK;
 }
 

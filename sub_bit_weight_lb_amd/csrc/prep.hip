@@ -16,7 +16,10 @@ __global__ void stats_init_kernel(DevStats* st) {
   st->nonfinite = 0;
   st->bad_precond = 0;
   st->potrf_info = 0x7fffffff;
-  st->pad = 0;
+  st->sync_timeout = 0;
+  st->to_wg = st->to_step = st->to_phase = st->to_want = st->to_seen = st->to_epoch = 0;
+  st->to_start = st->to_now = 0;
+  st->to_src = st->to_src_prog = 0;
 }
 
 __global__ void check_precond_kernel(const float* __restrict__ d_out, int64_t m,

@@ -66,7 +66,9 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("bad", [dict(m=0), dict(n=-1), dict(r=0), dict(rho=0.0),
                                  dict(rho=float("nan")), dict(rho=float("inf")), dict(iters=-1),
-                                 dict(svid_steps=0), dict(flags=0x100), dict(r=1 << 17)])
+                                 dict(svid_steps=0), dict(flags=0x100), dict(r=1 << 17),
+                                 dict(r=(1 << 13) + 1), dict(m=(1 << 21) - 255),
+                                 dict(n=(1 << 21) - 255)])
 def test_create_rejects_bad_desc_before_device_work(lib, bad):
     h = C.c_void_p(0)
     st = lib.nq_lbadmm_create(C.byref(_desc(**bad)), C.byref(h))
@@ -75,6 +77,20 @@ def test_create_rejects_bad_desc_before_device_work(lib, bad):
     assert lib.nq_last_error_message().decode()
     sz = C.c_size_t(0)
     assert lib.nq_lbadmm_workspace_bytes(C.byref(_desc(**bad)), C.byref(sz)) == L.NQ_ERR_INVALID_ARG
+
+
+def test_desc_limits_accept_the_largest_shapes(lib):
+    # padded m, n below 2^21 (32-bit row offsets of the tiled products) and
+    # r <= 2^13 (the SVID's per-workgroup column blocks) are sized, not refused
+    sz = C.c_size_t(0)
+    assert lib.nq_lbadmm_workspace_bytes(
+        C.byref(_desc(m=(1 << 21) - 256, n=256, r=128)), C.byref(sz)) == 0
+    assert lib.nq_lbadmm_workspace_bytes(C.byref(_desc(r=1 << 13)), C.byref(sz)) == 0
+
+
+def test_time_svid_rejects_bad_arguments(lib):
+    ms = C.c_double(0.0)
+    assert lib.nq_lbadmm_time_svid(None, 0, 1, None, C.byref(ms)) == L.NQ_ERR_INVALID_ARG
 
 
 def test_create_null_arguments(lib):

@@ -101,6 +101,31 @@ def test_svid(gpu, rows, cols, T_):
     assert np.all((H(Z) >= 0) == (X >= 0))
 
 
+# shapes cover each launch layout: the slab held in registers (4096 x 2048,
+# 4096 x 1536), streamed slabs (11264 x 1536, 4096 x 3072, 8192 x 6144),
+# guarded column blocks (300 x 70, 1000 x 260) and a grid of 128 (256 x 128)
+@pytest.mark.parametrize("rows,cols,T_", [(256, 128, 5), (300, 70, 5), (1000, 260, 3),
+                                          (4096, 2048, 5), (4096, 1536, 5), (11264, 1536, 5),
+                                          (4096, 3072, 5), (8192, 6144, 2)])
+def test_svid_dual(gpu, rows, cols, T_):
+    """X = U + Lam, Z = SVID_T(X), Lam' = X - Z against the oracle's SVID."""
+    import sub_bit_weight_lb_amd as nq
+    print(f"case svid_dual {rows}x{cols} T={T_}", flush=True)
+    rng = np.random.default_rng(rows * 3 + cols)
+    U = (0.05 * rng.standard_normal((rows, cols))).astype(np.float32)
+    Lam = (0.01 * rng.standard_normal((rows, cols))).astype(np.float32)
+    Z, Lo, a, b = nq.op_svid_dual(T(U, gpu), T(Lam, gpu), T_)
+    X = U.astype(np.float64) + Lam.astype(np.float64)
+    Zr, ar, br = O.svid(X, T_)
+    assert relerr(H(a), ar) < 1e-5
+    assert relerr(H(b), br) < 1e-5
+    assert relerr(H(Z), Zr) < 1e-5
+    assert relerr(H(Lo), X - Zr) < 1e-5
+    # the sign of Z follows X = U + Lam as the GPU forms it (fp32 add)
+    Xf = U + Lam
+    assert np.all((H(Z) >= 0) == (Xf >= 0))
+
+
 def test_svid_exact_sign_rank1(gpu):
     import sub_bit_weight_lb_amd as nq
     rng = np.random.default_rng(5)
