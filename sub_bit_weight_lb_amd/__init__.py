@@ -192,8 +192,14 @@ def transpose_signs(bits, rows, cols, out=None, stream=None):
     torch = _torch()
     if bits.dim() != 2 or bits.stride(1) != 1 or bits.shape[0] != rows:
         raise ValueError("bits must be 2-D, rows x words, unit column stride")
+    if bits.shape[1] < (cols + 31) // 32:
+        raise ValueError(f"bits has {bits.shape[1]} words per row, needs ceil(cols/32)")
     if out is None:
         out = torch.empty((cols, (rows + 31) // 32), dtype=torch.int32, device=bits.device)
+    elif (out.dim() != 2 or out.stride(1) != 1 or out.shape[0] < cols
+          or out.shape[1] < (rows + 31) // 32):
+        raise ValueError(f"out must be 2-D with unit column stride and at least {cols} x "
+                         f"{(rows + 31) // 32} words, got {tuple(out.shape)}")
     _check(_lib.load().nq_transpose_signs(
         _ptr(bits, "bits", torch.int32, 2, need_contig=False), rows, cols, bits.stride(0),
         _ptr(out, "out", torch.int32, 2, need_contig=False), out.stride(0), _stream(stream)),
@@ -213,21 +219,49 @@ def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None)
     if X2.dim() != 2 or X2.stride(1) != 1:
         raise ValueError("X must be 1-D or 2-D with unit column stride")
     B, n = X2.shape
-    m = U_bits.shape[0]
-    if Vt_bits.shape[0] != r or s1.numel() != m or s2.numel() != n:
-        raise ValueError("shapes of U_bits, Vt_bits, s1, s2 and X do not agree")
-    if Y is None:
-        Y = torch.empty((B, m), dtype=torch.float32, device=X.device)
+    m = _check_binmm_shapes(U_bits, Vt_bits, s1, s2, n, r)
+    Y2 = _binmm_out(Y, B, m, vec, X.device)
     if work is None:
         work = torch.empty((max(8 * B * r, 1),), dtype=torch.float32, device=X.device)
+    elif work.numel() < 8 * B * r:
+        raise ValueError(f"work holds {work.numel()} floats, needs 8 * B * r = {8 * B * r}")
     _check(_lib.load().nq_binary_matmul(
         _ptr(U_bits, "U_bits", torch.int32, 2, need_contig=False), U_bits.stride(0),
         _ptr(Vt_bits, "Vt_bits", torch.int32, 2, need_contig=False), Vt_bits.stride(0),
         m, n, r, _ptr(s1, "s1", torch.float32), _ptr(s2, "s2", torch.float32),
         _ptr(X2, "X", torch.float32, 2, need_contig=False), B, X2.stride(0),
-        _ptr(Y, "Y", torch.float32, 2, need_contig=False), Y.stride(0),
+        _ptr(Y2, "Y", torch.float32, 2, need_contig=False), Y2.stride(0),
         _ptr(work, "work", torch.float32), _stream(stream)), "nq_binary_matmul")
-    return Y[0] if vec else Y
+    return Y2[0] if vec else Y2
+
+
+def _check_binmm_shapes(U_bits, Vt_bits, s1, s2, n, r):
+    """Checks the factor operands of the binary-layer product against n and r
+    (the C ABI cannot see buffer sizes); returns m."""
+    for t, name in ((U_bits, "U_bits"), (Vt_bits, "Vt_bits")):
+        if t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{name} must be 2-D with unit column stride")
+    m = U_bits.shape[0]
+    if U_bits.shape[1] < (r + 31) // 32:
+        raise ValueError(f"U_bits has {U_bits.shape[1]} words per row, needs ceil(r/32)")
+    if Vt_bits.shape[0] != r or Vt_bits.shape[1] < (n + 31) // 32:
+        raise ValueError(f"Vt_bits must be r x (>= ceil(n/32)) words, got {tuple(Vt_bits.shape)}")
+    if s1.numel() != m or s2.numel() != n:
+        raise ValueError("s1 must hold m and s2 n values")
+    return m
+
+
+def _binmm_out(Y, B, m, vec, device):
+    """Y as a B x m view with unit column stride (a vector when X is one),
+    allocated when None."""
+    torch = _torch()
+    if Y is None:
+        return torch.empty((B, m), dtype=torch.float32, device=device)
+    Y2 = Y.unsqueeze(0) if (vec and Y.dim() == 1) else Y
+    if Y2.dim() != 2 or Y2.stride(1) != 1 or Y2.shape[0] < B or Y2.shape[1] < m:
+        raise ValueError(f"Y must be 2-D with unit column stride and at least {B} x {m}, "
+                         f"got {tuple(Y.shape)}")
+    return Y2
 
 
 def op_precondition(W, d_out, d_in, stream=None):
