@@ -229,6 +229,23 @@ nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* 
                            const float* s2, const float* X, int64_t B, int64_t ldx, float* Y,
                            int64_t ldy, float* work, void* stream);
 
+/* nq_binary_matmul for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. The same arguments and result (bit for bit) as
+ * nq_binary_matmul without `work`: the partial sums go to a fixed scratch
+ * array of 2^22 float32 (16 MiB) in the library, one per GPU, taken on the
+ * first call on a device (the current device) and held until the process
+ * ends. Limit: B * r <= 2^19 (8 B r floats must fit), else
+ * NQ_ERR_INVALID_ARG before any device work. Calls no allocating routine.
+ * Every call on one GPU uses that GPU's one array: calls whose device work
+ * overlaps (other streams, other threads) race and give wrong results; calls
+ * ordered on one stream are safe. Nothing in the array needs clearing
+ * between calls. */
+nq_status nq_binary_matmul_noalloc(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits,
+                                   int64_t ldvt, int64_t m, int64_t n, int64_t r,
+                                   const float* s1, const float* s2, const float* X, int64_t B,
+                                   int64_t ldx, float* Y, int64_t ldy, void* stream);
+
 /* ---- building blocks (the same kernels the run uses; for tests and tools) ----
  * These take caller buffers of any shape, copy into zero-padded temporaries
  * (hipMalloc, freed before the call returns), run the kernels on `stream`,

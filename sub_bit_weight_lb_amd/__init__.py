@@ -9,7 +9,7 @@ loudly when libnq.so or the GPU is missing. There is no CPU fallback.
 Functions mirror the C names without the ``nq_`` prefix:
     lbadmm_create / lbadmm_run / lbadmm_query / lbadmm_get_state /
     lbadmm_destroy / lbadmm_workspace_bytes / pack_signs /
-    transpose_signs / binary_matmul /
+    transpose_signs / binary_matmul / binary_matmul_noalloc /
     op_precondition / op_gram / op_gemm_rhs / op_cholesky_inverse / op_svid
 plus the conveniences ``LBADMM`` (a handle object) and ``lbadmm`` (one call).
 """
@@ -27,7 +27,7 @@ from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
     "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "transpose_signs",
-    "binary_matmul", "op_precondition", "op_gram",
+    "binary_matmul", "binary_matmul_noalloc", "op_precondition", "op_gram",
     "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
 ]
@@ -233,6 +233,38 @@ def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None)
         _ptr(Y2, "Y", torch.float32, 2, need_contig=False), Y2.stride(0),
         _ptr(work, "work", torch.float32), _stream(stream)), "nq_binary_matmul")
     return Y2[0] if vec else Y2
+
+
+# B * r limit of binary_matmul_noalloc: its fixed scratch holds 2^22 floats,
+# eight partial sums per input and rank
+NOALLOC_MAX_BR = 1 << 19
+
+
+def binary_matmul_noalloc(U_bits, Vt_bits, s1, s2, X, r, Y, stream=None):
+    """binary_matmul into a caller-given Y with no device allocation: the
+    library's fixed per-GPU scratch holds the partial sums, so B * r must not
+    exceed NOALLOC_MAX_BR. Calls that overlap on one GPU race; calls ordered
+    on one stream do not. Returns Y."""
+    torch = _torch()
+    vec = X.dim() == 1
+    X2 = X.unsqueeze(0) if vec else X
+    if X2.dim() != 2 or X2.stride(1) != 1:
+        raise ValueError("X must be 1-D or 2-D with unit column stride")
+    B, n = X2.shape
+    m = _check_binmm_shapes(U_bits, Vt_bits, s1, s2, n, r)
+    if Y is None:
+        raise ValueError("Y is required: this entry point allocates nothing")
+    Y2 = _binmm_out(Y, B, m, vec, X.device)
+    if B * r > NOALLOC_MAX_BR:
+        raise ValueError(f"B * r = {B * r} exceeds the fixed scratch ({NOALLOC_MAX_BR})")
+    _check(_lib.load().nq_binary_matmul_noalloc(
+        _ptr(U_bits, "U_bits", torch.int32, 2, need_contig=False), U_bits.stride(0),
+        _ptr(Vt_bits, "Vt_bits", torch.int32, 2, need_contig=False), Vt_bits.stride(0),
+        m, n, r, _ptr(s1, "s1", torch.float32), _ptr(s2, "s2", torch.float32),
+        _ptr(X2, "X", torch.float32, 2, need_contig=False), B, X2.stride(0),
+        _ptr(Y2, "Y", torch.float32, 2, need_contig=False), Y2.stride(0), _stream(stream)),
+        "nq_binary_matmul_noalloc")
+    return Y
 
 
 def _check_binmm_shapes(U_bits, Vt_bits, s1, s2, n, r):

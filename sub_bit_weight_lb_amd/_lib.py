@@ -58,6 +58,7 @@ SIGNATURES = {
     "nq_pack_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_transpose_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_binary_matmul": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P, P]),
+    "nq_binary_matmul_noalloc": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P]),
     "nq_op_precondition": (ST, [P, I64, I64, I64, P, P, P, I64, P]),
     "nq_op_gram": (ST, [P, I64, I64, I64, F32, P, I64, P]),
     "nq_op_gemm_rhs": (ST, [P, I64, P, I64, P, I64, F32, P, I64, I64, I64, I64, P]),

@@ -31,6 +31,8 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace nq {
 namespace {
@@ -353,6 +355,42 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
   else
     rowdot_any<kRpw2, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
   return hipGetLastError();
+}
+
+}  // namespace nq
+
+// ---------------------------------------------------------------- fixed scratch
+// The partial projections of launch_binary_matmul for callers that cannot
+// allocate: one array per GPU, held from the first use until the process
+// ends. Every slot the second product reads is written by the first product
+// of the same call, so nothing needs clearing between calls; two calls that
+// overlap on one GPU share the array and race.
+namespace nq {
+
+static __device__ __align__(256) float scratch[kBinScratchFloats];
+
+hipError_t binmm_fixed_scratch(float** out) {
+  static std::mutex mu;
+  static std::vector<float*> ptrs;
+  int dev = 0, count = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= count) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs.size() < (size_t)count) ptrs.resize((size_t)count, nullptr);
+  if (!ptrs[dev]) {
+    // the array's name is a host-side stand-in: the device copy's address
+    // comes from the runtime, once per device, with that device current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = (float*)p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 }  // namespace nq

@@ -263,5 +263,11 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
                                 int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
                                 const float* s2, const float* X, int64_t B, int64_t ldx,
                                 float* Y, int64_t ldy, float* T, hipStream_t s);
+// Floats in the fixed scratch array of binmm.hip (16 MiB per GPU): room for
+// kBinSplit B r partials while B r <= 2^19.
+constexpr int64_t kBinScratchFloats = int64_t(1) << 22;
+// *out = this GPU's copy of that array (the current device's), its address
+// looked up on first use on each device.
+hipError_t binmm_fixed_scratch(float** out);
 
 }  // namespace nq

@@ -39,6 +39,26 @@ hipError_t stage_out(const float* src, int64_t lds, float* dst, int64_t ldd, int
                           sizeof(float) * cols, rows, hipMemcpyDeviceToDevice, s);
 }
 
+// Argument checks shared by the two binary-layer entry points; *noop when
+// there is nothing to compute.
+nq_status check_binmm(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits, int64_t ldvt,
+                      int64_t m, int64_t n, int64_t r, const float* s1, const float* s2,
+                      const float* X, int64_t B, int64_t ldx, float* Y, int64_t ldy, bool* noop) {
+  if (m < 0 || n < 0 || r < 0 || B < 0)
+    return set_error(NQ_ERR_INVALID_ARG, "m, n, r and B must be >= 0");
+  if (m == 0 || B == 0) {
+    *noop = true;
+    return NQ_OK;
+  }
+  if (n == 0 || r == 0) return set_error(NQ_ERR_INVALID_ARG, "n and r must be >= 1 when m, B >= 1");
+  if (!U_bits || !Vt_bits || !s1 || !s2 || !X || !Y)
+    return set_error(NQ_ERR_INVALID_ARG, "U_bits, Vt_bits, s1, s2, X and Y are required");
+  if (ldu < (r + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ldu < ceil(r/32)");
+  if (ldvt < (n + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ldvt < ceil(n/32)");
+  if (ldx < n || ldy < m) return set_error(NQ_ERR_INVALID_ARG, "ldx < n or ldy < m");
+  return NQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,15 +89,27 @@ nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* 
                            int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
                            const float* s2, const float* X, int64_t B, int64_t ldx, float* Y,
                            int64_t ldy, float* work, void* stream) {
-  if (m < 0 || n < 0 || r < 0 || B < 0)
-    return set_error(NQ_ERR_INVALID_ARG, "m, n, r and B must be >= 0");
-  if (m == 0 || B == 0) return NQ_OK;
-  if (n == 0 || r == 0) return set_error(NQ_ERR_INVALID_ARG, "n and r must be >= 1 when m, B >= 1");
-  if (!U_bits || !Vt_bits || !s1 || !s2 || !X || !Y || !work)
-    return set_error(NQ_ERR_INVALID_ARG, "U_bits, Vt_bits, s1, s2, X, Y and work are required");
-  if (ldu < (r + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ldu < ceil(r/32)");
-  if (ldvt < (n + 31) / 32) return set_error(NQ_ERR_INVALID_ARG, "ldvt < ceil(n/32)");
-  if (ldx < n || ldy < m) return set_error(NQ_ERR_INVALID_ARG, "ldx < n or ldy < m");
+  bool noop = false;
+  nq_status st = check_binmm(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy, &noop);
+  if (st != NQ_OK || noop) return st;
+  if (!work) return set_error(NQ_ERR_INVALID_ARG, "work is required");
+  NQ_HIPCHK(launch_binary_matmul(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy,
+                                 work, (hipStream_t)stream));
+  return NQ_OK;
+}
+
+nq_status nq_binary_matmul_noalloc(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits,
+                                   int64_t ldvt, int64_t m, int64_t n, int64_t r,
+                                   const float* s1, const float* s2, const float* X, int64_t B,
+                                   int64_t ldx, float* Y, int64_t ldy, void* stream) {
+  bool noop = false;
+  nq_status st = check_binmm(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy, &noop);
+  if (st != NQ_OK || noop) return st;
+  if (B > kBinScratchFloats / kBinSplit / r)
+    return set_error(NQ_ERR_INVALID_ARG,
+                     "B * r exceeds the fixed scratch (B * r <= 2^19 for nq_binary_matmul_noalloc)");
+  float* work = nullptr;
+  NQ_HIPCHK(binmm_fixed_scratch(&work));
   NQ_HIPCHK(launch_binary_matmul(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy,
                                  work, (hipStream_t)stream));
   return NQ_OK;

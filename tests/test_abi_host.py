@@ -164,6 +164,17 @@ def test_binary_layer_argument_checks(lib):
     assert call(r=0) == L.NQ_ERR_INVALID_ARG
     assert call(n=-1) == L.NQ_ERR_INVALID_ARG
 
+    # the fixed-scratch variant: the same checks, and B * r <= 2^19
+    def call_na(**kw):
+        a = dict(args, **kw)
+        return lib.nq_binary_matmul_noalloc(f, a["ldu"], f, a["ldvt"], a["m"], a["n"], a["r"],
+                                            f, f, f, a["B"], a["ldx"], f, a["ldy"], None)
+    assert call_na(m=0) == 0 and call_na(B=0) == 0
+    assert call_na(ldu=1) == L.NQ_ERR_INVALID_ARG
+    assert call_na(ldy=9) == L.NQ_ERR_INVALID_ARG
+    assert call_na(r=4096, ldu=128, B=129) == L.NQ_ERR_INVALID_ARG
+    assert call_na(r=1 << 19, ldu=1 << 14, B=2) == L.NQ_ERR_INVALID_ARG
+
 
 def test_ops_argument_checks(lib):
     f = C.c_void_p(0x1000)
