@@ -91,6 +91,25 @@ def check_final_properties(res, r):
     assert s["potrf_info"] == 0 and s["nonfinite"] == 0
 
 
+def check_fingerprints(res, g):
+    """The stored end-of-run fingerprints of the balanced factors and scales.
+    The fp32 run follows the fp64 oracle's trajectory only approximately
+    (the errors agree to 1e-3 absolute), so norms and means are held to 0.5 %
+    and the fractions of non-negative entries to 0.005 absolute: wide enough
+    for that drift, far below what a lost balance, an unfolded
+    preconditioner or a flipped sign convention would change."""
+    U, V = H(res.U).astype(np.float64), H(res.V).astype(np.float64)
+    got = {"U_fro": np.linalg.norm(U), "V_fro": np.linalg.norm(V),
+           "s1_mean": float(np.mean(H(res.s1))), "s2_mean": float(np.mean(H(res.s2))),
+           "U_pos_frac": float(np.mean(U >= 0)), "V_pos_frac": float(np.mean(V >= 0))}
+    for k, v in got.items():
+        print(f"  {k}: gpu {v:.6g} oracle {g[k]:.6g}", flush=True)
+    for k in ("U_fro", "V_fro", "s1_mean", "s2_mean"):
+        assert abs(got[k] - g[k]) <= 5e-3 * abs(g[k]), k
+    for k in ("U_pos_frac", "V_pos_frac"):
+        assert abs(got[k] - g[k]) <= 5e-3, k
+
+
 def load_golden(name):
     path = os.path.join(GOLDEN, f"lbadmm_final_{name}.json")
     if not os.path.exists(path):
@@ -135,6 +154,7 @@ def test_full_run_vs_stored_oracle(gpu, name):
     assert abs(s["rel_err_w"] - g["rel_err_w"]) < 1e-3
     assert abs(s["sigma0"] - g["sigma0"]) / g["sigma0"] < 1e-6
     check_final_properties(res, wl.r)
+    check_fingerprints(res, g)
 
 
 @pytest.fixture(scope="module")
@@ -195,3 +215,6 @@ def test_70b_down_full_run(gpu, down70):
     s = res.stats
     print(f"  gpu {s['rel_err_wtilde']:.6f} oracle {g['rel_err_wtilde']:.6f}", flush=True)
     assert abs(s["rel_err_wtilde"] - g["rel_err_wtilde"]) < 1e-3
+    assert abs(s["rel_err_w"] - g["rel_err_w"]) < 1e-3
+    assert abs(s["sigma0"] - g["sigma0"]) / g["sigma0"] < 1e-6
+    check_fingerprints(res, g)

@@ -187,3 +187,57 @@ def test_launch_layouts_agree(gpu, shape, monkeypatch):
         assert relerr(st["V"], ref.V) < 1e-4, (name, relerr(st["V"], ref.V))
         for k in ("U", "V", "Lam_U", "Lam_V"):
             assert relerr(st[k], outs["single"][k]) < 2e-5, (name, k, relerr(st[k], outs["single"][k]))
+
+
+@pytest.mark.parametrize("shape, seed", [((64, 48, 8), 7), ((300, 200, 70), 0x1234567890ab),
+                                         ((1, 1, 1), 3)])
+def test_builtin_philox_start(gpu, shape, seed):
+    """U0 = V0 = NULL: the start is sigma0 times the library's Philox4x32-10
+    normals, compared with the tests' own generator (tests/philox_cpu.py,
+    pinned to the published known-answer vectors) to within one float32 ulp;
+    sigma0 against the oracle."""
+    import sub_bit_weight_lb_amd as nq
+    from philox_cpu import normals
+    m, n, r = shape
+    L = make_tiny(m, n, r, seed=21 + m)
+    print(f"case philox {shape} seed={seed:#x}", flush=True)
+    h = nq.LBADMM(m, n, r, iters=0, seed=seed, balance=False)
+    res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu))
+    st = {k: H(v) for k, v in h.state().items()}
+    h.close()
+    s0 = res.stats["sigma0"]
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    assert abs(s0 - O.init_scale(Wt, r)) / O.init_scale(Wt, r) < 1e-6
+    for k, rows, stream in (("U", m, 0), ("V", n, 1)):
+        z = normals(seed, stream, rows * r).reshape(rows, r)
+        want = np.float32(s0) * z.astype(np.float32)
+        got = st[k]
+        ulp = np.spacing(np.abs(want).astype(np.float32))
+        bad = np.abs(got - want) > ulp
+        assert not bad.any(), (k, int(bad.sum()), got[bad][:4], want[bad][:4])
+
+
+def test_finish_matches_oracle_on_gpu_state(gpu):
+    """The balanced factors, scales and bits the run returns against
+    oracle.finish applied to the GPU's own pre-balance state (get_state), so
+    that the finish is checked element by element apart from the iterations."""
+    import sub_bit_weight_lb_amd as nq
+    L = make_tiny(300, 260, 70, seed=9, iters=3)
+    m, n = L.W.shape
+    r = 70
+    h = nq.LBADMM(m, n, r, iters=3)
+    res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+    st = {k: H(v).astype(np.float64) for k, v in h.state().items()}
+    h.close()
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    Ub, Vb, s1, s2, _, _, ub, vb, e_wt, e_w = O.finish(
+        Wt, L.W.astype(np.float64), L.d_out, L.d_in, st["U"], st["V"])
+    for name, g, o in (("U", H(res.U), Ub), ("V", H(res.V), Vb)):
+        rms = np.sqrt(np.mean(o ** 2))
+        np.testing.assert_allclose(g, o, rtol=1e-5, atol=1e-6 * rms, err_msg=name)
+    np.testing.assert_allclose(H(res.s1), s1, rtol=1e-5, atol=0)
+    np.testing.assert_allclose(H(res.s2), s2, rtol=1e-5, atol=0)
+    np.testing.assert_array_equal(H(res.U_bits).view(np.uint32), ub)
+    np.testing.assert_array_equal(H(res.V_bits).view(np.uint32), vb)
+    assert abs(res.stats["rel_err_wtilde"] - e_wt) < 1e-5
+    assert abs(res.stats["rel_err_w"] - e_w) < 1e-5

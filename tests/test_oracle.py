@@ -140,6 +140,73 @@ def test_half_step_is_stationary_point():
     np.testing.assert_allclose(np.abs(Znew), np.outer(a, b), rtol=1e-14, atol=0)
 
 
+def test_iterate_sweep_order_is_gauss_seidel():
+    # [D] 核心方法: each iteration fixes V and solves for U, then does "the
+    # same" for V, which reads the U just computed. After one iteration from
+    # a known state, the V sub-problem's gradient must vanish with the
+    # returned U and the starting Z_V, Lam_V; with the starting U it must not
+    # (a Jacobi sweep would satisfy the latter instead).
+    rng = _rng(61)
+    m, n, r, rho = 30, 22, 5, 0.7
+    Wt = rng.standard_normal((m, n))
+    st0 = O.State(rng.standard_normal((m, r)), rng.standard_normal((n, r)),
+                  rng.standard_normal((m, r)), 0.1 * rng.standard_normal((m, r)),
+                  rng.standard_normal((n, r)), 0.1 * rng.standard_normal((n, r)))
+    st1 = O.iterate(Wt, st0, rho, 5, 1)
+
+    def grad_v(V, U, Z, Lam):
+        return -(Wt.T - V @ U.T) @ U + rho * (V - Z + Lam)
+
+    def grad_u(U, V, Z, Lam):
+        return -(Wt - U @ V.T) @ V + rho * (U - Z + Lam)
+
+    scale = np.linalg.norm(Wt.T @ st1.U)
+    assert np.linalg.norm(grad_v(st1.V, st1.U, st0.Z_V, st0.Lam_V)) / scale < 1e-12
+    assert np.linalg.norm(grad_v(st1.V, st0.U, st0.Z_V, st0.Lam_V)) / scale > 1e-2
+    # the U-half used the starting V (and the starting Z_U, Lam_U)
+    assert np.linalg.norm(grad_u(st1.U, st0.V, st0.Z_U, st0.Lam_U)) / scale < 1e-12
+    # dual updates with unit step on each half's own X = new latent + old dual
+    np.testing.assert_allclose(st1.Lam_V, st0.Lam_V + st1.V - st1.Z_V, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(st1.Lam_U, st0.Lam_U + st1.U - st1.Z_U, rtol=0, atol=1e-12)
+
+
+def test_objective_hand_values():
+    # 1x1 case worked by hand: Wt = 3, U = 1, V = 2, Z_U = 0.5, Lam_U = 0.25,
+    # Z_V = 1, Lam_V = -0.5, rho = 2:
+    #   1/2 (3 - 2)^2 = 0.5;  rho/2 (1 - 0.5 + 0.25)^2 = 0.5625;
+    #   rho/2 (2 - 1 - 0.5)^2 = 0.25;  total 1.3125
+    f = O.objective(np.array([[3.0]]), np.array([[1.0]]), np.array([[2.0]]),
+                    np.array([[0.5]]), np.array([[0.25]]), np.array([[1.0]]),
+                    np.array([[-0.5]]), 2.0)
+    assert f == pytest.approx(1.3125, abs=1e-15)
+    # 2x1 by 1x1 (rank 1): only the data term, entry by entry
+    f = O.objective(np.array([[1.0], [2.0]]), np.array([[1.0], [-1.0]]), np.array([[3.0]]),
+                    np.zeros((2, 1)), np.zeros((2, 1)), np.array([[3.0]]), np.zeros((1, 1)), 5.0)
+    assert f == pytest.approx(0.5 * ((1 - 3) ** 2 + (2 + 3) ** 2) + 0.5 * 5.0 * 2.0, abs=1e-14)
+
+
+def test_half_steps_minimise_the_objective():
+    # step (a) minimises the augmented Lagrangian over one factor: any
+    # perturbation of the returned U (V fixed) or V (U fixed) raises it
+    rng = _rng(62)
+    m, n, r, rho = 16, 12, 4, 1.1
+    Wt = rng.standard_normal((m, n))
+    st0 = O.State(rng.standard_normal((m, r)), rng.standard_normal((n, r)),
+                  rng.standard_normal((m, r)), 0.1 * rng.standard_normal((m, r)),
+                  rng.standard_normal((n, r)), 0.1 * rng.standard_normal((n, r)))
+    U, _, _, _, _ = O.admm_half(Wt, st0.V, st0.Z_U, st0.Lam_U, rho, 5)
+    f0 = O.objective(Wt, U, st0.V, st0.Z_U, st0.Lam_U, st0.Z_V, st0.Lam_V, rho)
+    for k in range(20):
+        d = 1e-3 * rng.standard_normal((m, r))
+        assert O.objective(Wt, U + d, st0.V, st0.Z_U, st0.Lam_U, st0.Z_V, st0.Lam_V, rho) > f0
+    V, _, _, _, _ = O.admm_half(Wt.T, U, st0.Z_V, st0.Lam_V, rho, 5)
+    g0 = O.objective(Wt, U, V, st0.Z_U, st0.Lam_U, st0.Z_V, st0.Lam_V, rho)
+    assert g0 <= f0
+    for k in range(20):
+        d = 1e-3 * rng.standard_normal((n, r))
+        assert O.objective(Wt, U, V + d, st0.Z_U, st0.Lam_U, st0.Z_V, st0.Lam_V, rho) > g0
+
+
 # --------------------------------------------------------------------- a7
 def test_svid_recovers_exact_sign_rank1():
     rng = _rng(7)
