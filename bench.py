@@ -11,6 +11,12 @@ One step = one whole per-layer run through the C ABI (precondition, init,
 inputs already resident in HBM. value = ADMM iterations per second over the
 timed steps (whole runs, so precondition and finish count against it).
 
+--workload NAME times another synthetic layer of synth/layers.py instead
+(the tiny 256 x 512 layer, the 11008 x 4096 r = 1536 MLP layer, the
+8192 x 28672 r = 6144 layer), or 'llama2-7b-block': the seven layers of one
+Llama-2-7B-shaped block run one after the other in each step, value = all
+their iterations per second.
+
 Also reported:
   roofline      the right-hand-side GEMM R = Wt V + rho (Z - Lam), the
                 largest kernel: algorithmic 2 m n r flops per launch over its
@@ -36,6 +42,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 WORKLOAD = "llama2-7b-attn-4096x4096-r2048"
+BLOCK = "llama2-7b-block"
+METRIC = "LB-ADMM iters/s on 4096x4096 r=2048 fp32 layer; % of fp32 MFMA peak"
 FP32_MFMA_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_rhs_4096x4096_r2048_counters.md")
@@ -114,49 +122,78 @@ def hbm_bench(nq, torch, dev, L, reps=20):
     return res
 
 
-def cpu_baseline(L, budget_s=10.0, max_iters=12, budget_fp32_s=6.0):
-    """The CPU oracle on the same layer: a bounded number of ADMM iterations
-    in NumPy float64 (the parity oracle; reported as value) and, as a second
-    figure, in float32 (the oracle's dtype switch)."""
+def cpu_baseline(layers, budget_s=10.0, budget_fp32_s=6.0, max_halves=24):
+    """The CPU oracle on the same workload: ADMM half-iterations (oracle
+    admm_half, U then V, as oracle iterate runs them) in NumPy float64 (the
+    parity oracle; reported as value) and, as a second figure, in float32
+    (the oracle's dtype switch). Each distinct layer shape of the workload is
+    sampled for its share of the budget (at least one half-iteration); the
+    workload's iterations/s is the total of its iterations over the time the
+    sampled rates give for all its layers."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import lbadmm as O
-    wl = L.workload
 
-    def timed(dtype, budget):
+    shapes = {}
+    for L in layers:
+        wl = L.workload
+        shapes.setdefault((wl.m, wl.n, wl.r), L)
+
+    def timed(L, dtype, budget):
+        wl = L.workload
         t0 = time.perf_counter()
         Wt = O.precondition(L.W, L.d_out, L.d_in, dtype)
         st = O.init_state(Wt, wl.r, wl.svid_steps, EU=L.EU, EV=L.EV, dtype=dtype)
         t_prep = time.perf_counter() - t0
-        done, t_iter = 0, 0.0
-        while done < max_iters and (done == 0 or t_iter * (done + 1) / done < budget):
+        halves, t_run = 0, 0.0
+        while halves < max_halves and (halves == 0 or t_run * (halves + 1) / halves < budget):
             t1 = time.perf_counter()
-            st = O.iterate(Wt, st, wl.rho, wl.svid_steps, 1, dtype)
-            t_iter += time.perf_counter() - t1
-            done += 1
-        return done, t_iter, t_prep, bool(np.isfinite(st.U).all())
+            if halves % 2 == 0:
+                st.U, st.Z_U, st.Lam_U, _, _ = O.admm_half(Wt, st.V, st.Z_U, st.Lam_U, wl.rho,
+                                                           wl.svid_steps)
+            else:
+                st.V, st.Z_V, st.Lam_V, _, _ = O.admm_half(Wt.T, st.U, st.Z_V, st.Lam_V, wl.rho,
+                                                           wl.svid_steps)
+            t_run += time.perf_counter() - t1
+            halves += 1
+        fin = bool(np.isfinite(st.U).all() and np.isfinite(st.V).all())
+        del Wt, st
+        return halves, t_run, t_prep, fin
 
-    d64, t64, p64, fin64 = timed(np.float64, budget_s)
-    d32, t32, p32, fin32 = timed(np.float32, budget_fp32_s)
+    res = {}
+    for dt, budget in ((np.float64, budget_s), (np.float32, budget_fp32_s)):
+        rates, notes, fin = {}, [], True
+        for key, L in shapes.items():
+            h, t, tp, f = timed(L, dt, budget / len(shapes))
+            print(f"cpu baseline: {np.dtype(dt).name} {key}: {h} half-iterations in {t:.1f} s",
+                  file=sys.stderr, flush=True)
+            rates[key] = 2.0 * t / h                         # seconds per iteration
+            fin = fin and f
+            notes.append(f"{h} half-iterations of {key[0]}x{key[1]} r={key[2]} "
+                         f"({t:.1f} s; preconditioning and init {tp:.1f} s, not counted)")
+        iters = sum(L.workload.iters for L in layers)
+        secs = sum(L.workload.iters * rates[(L.workload.m, L.workload.n, L.workload.r)]
+                   for L in layers)
+        res[dt] = (iters / secs, "; ".join(notes), fin, secs / iters)
     pools = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in pools] + [1])
     blas = sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
                    for i in pools if i.get("user_api") == "blas"})
+    v64, s64, f64, spi = res[np.float64]
+    v32, s32, f32, _ = res[np.float32]
     return {
-        "value": d64 / t64,
+        "value": v64,
         "unit": "iters/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{d64} ADMM iterations (U-half + V-half) of the same {wl.m}x{wl.n} r={wl.r} "
-                   f"layer in NumPy float64 after preconditioning and init ({p64:.1f} s, not "
-                   f"counted); {t64:.1f} s of iterations"),
-        "fp32_value": d32 / t32,
-        "fp32_sample": f"{d32} iterations in float32 mode, {t32:.1f} s",
+        "sample": f"NumPy float64: {s64}",
+        "fp32_value": v32,
+        "fp32_sample": f"float32 mode: {s32}",
         "host_cpus": len(os.sched_getaffinity(0)),
         "blas": ", ".join(blas) or "unknown",
         "cpu_model": cpu_model(),
-        "s_per_iter": t64 / d64,
-        "finite": fin64 and fin32,
+        "s_per_iter": spi,
+        "finite": f64 and f32,
     }
 
 
@@ -238,6 +275,10 @@ def main():
     ap.add_argument("--hbm", action="store_true",
                     help="only time the HBM-bound kernels (SVID + dual update, prep, finish) "
                          "on the layer's shape (for counter and kernel-trace profiles)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="a synthetic layer (synth.layers.WORKLOADS) or 'llama2-7b-block' "
+                         "(the seven layers of one Llama-2-7B-shaped block, run one after the "
+                         "other in each step)")
     ap.add_argument("--binary", action="store_true",
                     help="only time the binary-layer product (nq_binary_matmul) on the layer "
                          "shapes, warm and with its sign bits rotated through > 256 MB")
@@ -247,7 +288,6 @@ def main():
               "(the per-layer path runs on a single GPU)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.calibrate_copy:
@@ -272,7 +312,7 @@ def main():
         # kernel trace lists on its own line
         g = torch.Generator(device="cpu").manual_seed(0)
         from synth.layers import WORKLOADS
-        wl = WORKLOADS[WORKLOAD]
+        wl = WORKLOADS[workload_layers(args.workload)[0]]
         for (mm, kk, nn) in ((wl.m, wl.n, wl.r), (wl.m, wl.r, wl.r)):
             a = torch.randn(mm, kk, generator=g).to(dev)
             b = torch.randn(kk, nn, generator=g).to(dev)
@@ -289,90 +329,148 @@ def main():
     if args.binary:
         print(json.dumps({"binary_matmul": binary_bench(nq, torch, dev)}), flush=True)
         return
-    L = make_layer(WORKLOAD)
-    wl = L.workload
+    names = workload_layers(args.workload)
     if args.hbm:
-        print(json.dumps({"hbm_kernels": hbm_bench(nq, torch, dev, L)}), flush=True)
+        print(json.dumps({"hbm_kernels": hbm_bench(nq, torch, dev, make_layer(names[0]))}),
+              flush=True)
         return
-    m, n, r = wl.m, wl.n, wl.r
-    iters = wl.iters if args.iters is None else args.iters
+    layers = [make_layer(nm) for nm in names]
+    line = measure(nq, torch, dev, args, layers)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layers)
+    print(json.dumps(line), flush=True)
+
+
+def workload_layers(name):
+    """The layer names of a workload: one synthetic layer, or the seven
+    layers of the Llama-2-7B-shaped block."""
+    from synth.layers import BLOCK_LAYERS, WORKLOADS
+    if name == BLOCK:
+        return list(BLOCK_LAYERS)
+    if name not in WORKLOADS:
+        raise SystemExit(f"unknown workload {name!r}; one of {sorted(WORKLOADS) + [BLOCK]}")
+    return [name]
+
+
+def measure(nq, torch, dev, args, layers):
+    """One step = one whole per-layer run of every layer of the workload
+    through the C ABI, inputs resident in HBM."""
+    import numpy as np
 
     def t(x):
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
-    W, d_out, d_in, EU, EV = t(L.W), t(L.d_out), t(L.d_in), t(L.EU), t(L.EV)
-    print(f"bench: {WORKLOAD} iters={iters} warmup={args.warmup} steps={args.steps}",
+    runs = []
+    for L in layers:
+        wl = L.workload
+        iters = wl.iters if args.iters is None else args.iters
+        ins = [t(x) for x in (L.W, L.d_out, L.d_in, L.EU, L.EV)]
+        runs.append((wl, iters, ins))
+    name = args.workload
+    print(f"bench: {name} ({len(layers)} layer(s)) warmup={args.warmup} steps={args.steps}",
           file=sys.stderr, flush=True)
-    # Phase breakdown: one untimed run on a handle that times every phase
-    # (each event pair costs a little device time, ~1.5 % over a run).
-    hp = nq.LBADMM(m, n, r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
-                   compute_error=True, single_stream=args.single_stream, profile=True)
-    out = hp.alloc_outputs(dev)
-    hp.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
-    phases = hp.profile(reset=True)
-    hp.close()
-    # Timed runs: HIP events around the RHS GEMM only, on its own stream
-    # (the roofline's launch duration); no other events in the timed region.
-    h = nq.LBADMM(m, n, r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
-                  compute_error=True, single_stream=args.single_stream, profile="rhs")
+    # Phase breakdown: one untimed run per layer on a handle that times every
+    # phase (each event pair costs a little device time, ~1.5 % over a run).
+    phases_all = []
+    for wl, iters, ins in runs:
+        hp = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
+                       compute_error=True, single_stream=args.single_stream, profile=True)
+        out = hp.alloc_outputs(dev)
+        hp.run(*ins, out=out, want_stats=False)
+        phases_all.append(hp.profile(reset=True))
+        hp.close()
+        del out
+    # Timed runs: HIP events around the RHS GEMM only, on its own stream (the
+    # roofline's launch duration); no other events in the timed region.
+    handles = []
+    for wl, iters, ins in runs:
+        h = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
+                      compute_error=True, single_stream=args.single_stream, profile="rhs")
+        handles.append((h, h.alloc_outputs(dev)))
+
+    def step():
+        for (h, out), (_, _, ins) in zip(handles, runs):
+            h.run(*ins, out=out, want_stats=False)
+
     for _ in range(args.warmup):
-        h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
+        step()
     torch.cuda.synchronize()
-    h.profile(reset=True)
+    for h, _ in handles:
+        h.profile(reset=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = h.profile(reset=True)
-    status, stats = nq.lbadmm_query(h.handle)
-    if status != 0:
-        raise SystemExit(f"run reported {nq.status_string(status)}")
-    # The SVID + dual update alone (one persistent launch per update), on the
-    # state the last run left: algorithmic bytes 16 per element of the factor
-    # (read the latent and Lam, write Lam and P).
-    svid = {}
-    for f, rows in ((0, m), (1, n)):
-        ms = h.time_svid(f, reps=20)
-        gbs = 16.0 * rows * r / (ms * 1e-3) / 1e9
-        svid["UV"[f]] = {"avg_us": round(ms * 1e3, 2), "bytes": 16 * rows * r,
-                         "GBps": round(gbs, 1), "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
-    h.close()
+    rhs_ms, rhs_n, rhs_flops, stats_all, svid = 0.0, 0, 0.0, [], {}
+    for (h, _), (wl, iters, _) in zip(handles, runs):
+        prof = h.profile(reset=True)
+        status, stats = nq.lbadmm_query(h.handle)
+        if status != 0:
+            raise SystemExit(f"{wl.name}: run reported {nq.status_string(status)}")
+        stats_all.append(stats)
+        ms, cnt = prof["gemm_rhs"]
+        rhs_ms += ms
+        rhs_n += cnt
+        rhs_flops += cnt * 2.0 * wl.m * wl.n * wl.r
+        # The SVID + dual update alone (one persistent launch per update), on
+        # the state the last run left: algorithmic bytes 16 per element of
+        # the factor (read the latent and Lam, write Lam and P).
+        key = f"{wl.m}x{wl.n}-r{wl.r}"
+        if key not in svid:
+            svid[key] = {}
+            for f, rows in ((0, wl.m), (1, wl.n)):
+                ms = h.time_svid(f, reps=20)
+                gbs = 16.0 * rows * wl.r / (ms * 1e-3) / 1e9
+                svid[key]["UV"[f]] = {"avg_us": round(ms * 1e3, 2), "bytes": 16 * rows * wl.r,
+                                      "GBps": round(gbs, 1),
+                                      "frac_of_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+        h.close()
 
     elapsed = t1 - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    value = args.steps * iters / elapsed
-    F = flops_per_iter(m, n, r)
-    rhs_ms, rhs_n = prof["gemm_rhs"]
+    iters_step = sum(iters for _, iters, _ in runs)
+    value = args.steps * iters_step / elapsed
+    F = sum(iters * flops_per_iter(wl.m, wl.n, wl.r) for wl, iters, _ in runs)
     rhs_avg_s = rhs_ms / max(rhs_n, 1) / 1e3
-    rhs_flops = 2.0 * m * n * r
-    achieved = rhs_flops / rhs_avg_s / 1e12
-    traffic = read_traffic(m, n, r, rhs_avg_s)
+    achieved = rhs_flops / max(rhs_n, 1) / rhs_avg_s / 1e12
+    single = len(runs) == 1
+    wl0 = runs[0][0]
+    traffic = (read_traffic(wl0.m, wl0.n, wl0.r, rhs_avg_s)
+               if single and name == WORKLOAD else None)
+    weights = sum(wl.m * wl.n for wl, _, _ in runs)
+    bits = sum(wl.r * (wl.m + wl.n) for wl, _, _ in runs)
+    scale_bits = sum(16 * (wl.m + wl.n) for wl, _, _ in runs)
+    cfg = {"workload": name, "layers": len(runs), "parallelism": "single-gpu"}
+    if single:
+        cfg.update({"m": wl0.m, "n": wl0.n, "r": wl0.r, "rho": wl0.rho,
+                    "admm_iters_per_step": runs[0][1], "svid_steps": wl0.svid_steps})
+    else:
+        cfg["shapes"] = [f"{wl.m}x{wl.n}-r{wl.r}" for wl, _, _ in runs]
+        cfg["admm_iters_per_step"] = iters_step
     line = {
-        "metric": "LB-ADMM iters/s on 4096x4096 r=2048 fp32 layer; % of fp32 MFMA peak",
+        "metric": (METRIC if name == WORKLOAD
+                   else f"LB-ADMM iters/s on {name} fp32; % of fp32 MFMA peak"),
         "value": round(value, 3),
         "unit": "iters/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
+        "ms_per_step": round(1e3 * elapsed / args.steps, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "m": m, "n": n, "r": r, "rho": wl.rho,
-                   "admm_iters_per_step": iters, "svid_steps": wl.svid_steps,
-                   "parallelism": "single-gpu"},
-        "fp32_mfma_peak_frac": round(value * F / (FP32_MFMA_PEAK_TFLOPS * 1e12), 4),
-        "factorised_weights_per_s": round(args.steps * m * n / elapsed, 1),
-        "flops_per_iter": F,
+        "config": cfg,
+        "fp32_mfma_peak_frac": round(args.steps * F / elapsed / (FP32_MFMA_PEAK_TFLOPS * 1e12), 4),
+        "factorised_weights_per_s": round(args.steps * weights / elapsed, 1),
+        "flops_per_step": F,
         "roofline": {
             "kernel": "gemm_nt_kernel<kEpiRhs> (R = Wt V + rho (Z - Lam), V read as V^T)",
-            "note": ("timed as it runs in the pipeline: on 7 of the 8 XCDs (the eighth runs the "
-                     "Cholesky chain's diagonal work) and yielding issue cycles to the chain "
-                     "(s_sleep after each K step); the same kernel alone on the whole chip: "
-                     "see the standalone kernel profile"),
+            "note": ("timed as it runs in the pipeline, beside the Cholesky chain (for r_p <= "
+                     "2048 on 7 of the 8 XCDs, yielding issue cycles to the chain); averaged over "
+                     "every RHS launch of the timed steps; the same kernel alone on the whole "
+                     "chip: see the standalone kernel profile"),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": FP32_MFMA_PEAK_TFLOPS,
@@ -381,34 +479,39 @@ def main():
             "traffic": traffic,
             "avg_launch_ms": round(rhs_avg_s * 1e3, 4),
             "launches": rhs_n,
-            "flops_per_launch": rhs_flops,
+            "flops_per_launch": rhs_flops / max(rhs_n, 1),
         },
+        "svid_update_standalone": svid if not single else svid[next(iter(svid))],
+        "bpw": round(bits / weights, 4),
+        "bpw_with_fp16_scales": round((bits + scale_bits) / weights, 4),
+        "rel_err_wtilde": (stats_all[0]["rel_err_wtilde"] if single
+                           else [s["rel_err_wtilde"] for s in stats_all]),
+        "rel_err_w": (stats_all[0]["rel_err_w"] if single
+                      else [s["rel_err_w"] for s in stats_all]),
+    }
+    if single:
+        m, n, r, iters = wl0.m, wl0.n, wl0.r, runs[0][1]
+        phases = phases_all[0]
+        line["flops_per_iter"] = flops_per_iter(m, n, r)
         # from one untimed run with every phase timed (the chain phase is the
         # Gram plus the Cholesky chain; phases of different streams overlap)
-        "phase_ms_per_iter": {p: round(phases[p][0] / max(iters, 1), 4)
-                              for p in ("gemm_rhs", "gemm_solve", "chain", "svid")},
-        "phase_ms_per_step": {p: round(phases[p][0], 3) for p in ("prep", "finish")},
-        "phase_source": "one untimed run with every phase timed",
-        # the solve GEMM runs alone on the chip, on the critical path
-        "solve_gemm": {
-            "flops_per_launch": 2.0 * m * r * r,
-            "avg_launch_ms": round(phases["gemm_solve"][0] / max(phases["gemm_solve"][1], 1), 4),
-            "tflops": round(2.0 * m * r * r / (phases["gemm_solve"][0] / max(phases["gemm_solve"][1], 1)
-                                                / 1e3) / 1e12, 2),
-            "frac_of_peak": round(2.0 * m * r * r / (phases["gemm_solve"][0]
-                                                      / max(phases["gemm_solve"][1], 1) / 1e3)
-                                  / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
-            "source": "the untimed run with every phase timed",
-        },
-        "svid_update_standalone": svid,
-        "bpw": round(bpw(m, n, r, 0), 4),
-        "bpw_with_fp16_scales": round(bpw(m, n, r, 16), 4),
-        "rel_err_wtilde": stats["rel_err_wtilde"],
-        "rel_err_w": stats["rel_err_w"],
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(L)
-    print(json.dumps(line), flush=True)
+        line["phase_ms_per_iter"] = {p: round(phases[p][0] / max(iters, 1), 4)
+                                     for p in ("gemm_rhs", "gemm_solve", "chain", "svid")}
+        line["phase_ms_per_step"] = {p: round(phases[p][0], 3) for p in ("prep", "finish")}
+        line["phase_source"] = "one untimed run with every phase timed"
+        sol_s = phases["gemm_solve"][0] / max(phases["gemm_solve"][1], 1) / 1e3
+        # the solve GEMM runs alone on the chip, on the critical path; its
+        # launches alternate between the U-half (m rows) and the V-half (n
+        # rows), 2 rows r^2 flops each
+        sol_f = (m + n) * r * r
+        line["solve_gemm"] = {
+            "flops_per_launch": sol_f,
+            "avg_launch_ms": round(sol_s * 1e3, 4),
+            "tflops": round(sol_f / sol_s / 1e12, 2),
+            "frac_of_peak": round(sol_f / sol_s / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            "source": "the untimed run with every phase timed (mean over U- and V-half launches)",
+        }
+    return line
 
 
 if __name__ == "__main__":
