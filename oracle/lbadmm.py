@@ -177,18 +177,73 @@ class State:
                         self.a_U, self.b_U, self.a_V, self.b_V)))
 
 
-def admm_half(Wt_side, other, Z, Lam, rho, T):
+# ---------------------------------------------------------------------------
+# f4: an iterative solve in place of the Cholesky factor
+#     ([B] 待办事项: the author replaced the Cholesky solve of LB-ADMM by a
+#      gradient-descent solver, slower than Cholesky under CUDA and faster on
+#      another GPU; no details are given)
+# ---------------------------------------------------------------------------
+def iterative_solve(R, G, U0, steps, method="cg"):
+    """Approximate U with U G = R from the warm start U0, row by row.
+
+    READING: the sub-problem of step (a) is, for each row, the minimisation
+    of 1/2 u G u^T - u r^T (G = other^T other + rho I, symmetric positive
+    definite; r the row of R), whose gradient is g = u G - r. A
+    gradient-descent solver takes `steps` steps per row from the factor's
+    previous value:
+      "gd": steepest descent with the exact step along -g:
+            alpha = (g.g) / (g G g^T),  u <- u - alpha g;
+      "cg": conjugate gradients (Hestenes-Stiefel): d = -g at the start, then
+            alpha = (g.g) / (d G d^T),  u <- u + alpha d,  g <- g + alpha d G,
+            beta = (g_new.g_new) / (g.g),  d <- -g_new + beta d.
+    A row whose step denominator is not > 0 (a zero gradient) stays where it
+    is. steps = 0 returns U0.
+    """
+    R = np.asarray(R)
+    G = np.asarray(G)
+    U = np.array(U0, dtype=R.dtype, copy=True)
+    if method not in ("gd", "cg"):
+        raise ValueError("method is 'gd' or 'cg'")
+    for i in range(U.shape[0]):
+        u = U[i]
+        g = u @ G - R[i]
+        d = -g
+        gg = g @ g
+        for _ in range(steps):
+            if method == "gd":
+                d = -g
+                gg = g @ g
+            Gd = d @ G
+            den = d @ Gd
+            if not den > 0:
+                break
+            alpha = gg / den
+            u = u + alpha * d
+            g = g + alpha * Gd
+            if method == "cg":
+                gg_new = g @ g
+                d = -g + (gg_new / gg) * d
+                gg = gg_new
+        U[i] = u
+    return U
+
+
+def admm_half(Wt_side, other, Z, Lam, rho, T, solver=None, prev=None):
     """One half-iteration for the factor whose rows follow Wt_side's rows.
 
     U-half: Wt_side = Wt,   other = V.   V-half: Wt_side = Wt^T, other = U.
     Returns (new factor, Z, Lambda, a, b).
     READINGS: the solve uses the latent of the other factor (not its proxy);
     the dual is the scaled dual with unit step; SVID acts on X = new + Lambda.
+    solver = (method, steps) replaces the Cholesky solve by iterative_solve
+    warm-started from `prev`, the factor's value before this half.
     """
     G = gram(other, rho)
-    L = cholesky(G)
     R = rhs(Wt_side, other, Z, Lam, rho)
-    F = chol_solve(R, L)
+    if solver is None:
+        F = chol_solve(R, cholesky(G))
+    else:
+        F = iterative_solve(R, G, prev, solver[1], solver[0])
     X = F + Lam
     Znew, a, b = svid(X, T)
     Lnew = X - Znew
@@ -213,14 +268,17 @@ def init_state(Wt, r, T, EU=None, EV=None, U0=None, V0=None, dtype=np.float64):
     return State(U0, V0, Z_U, np.zeros_like(U0), Z_V, np.zeros_like(V0), aU, bU, aV, bV)
 
 
-def iterate(Wt, st: State, rho, T, iters, dtype=np.float64) -> State:
-    """Run ``iters`` full iterations (U-half, then V-half) from ``st``."""
+def iterate(Wt, st: State, rho, T, iters, dtype=np.float64, solver=None) -> State:
+    """Run ``iters`` full iterations (U-half, then V-half) from ``st``;
+    ``solver`` as in admm_half (None: Cholesky)."""
     Wt = np.asarray(Wt, dtype)
     WtT = Wt.T
     st = st.copy()
     for _ in range(iters):
-        st.U, st.Z_U, st.Lam_U, st.a_U, st.b_U = admm_half(Wt, st.V, st.Z_U, st.Lam_U, rho, T)
-        st.V, st.Z_V, st.Lam_V, st.a_V, st.b_V = admm_half(WtT, st.U, st.Z_V, st.Lam_V, rho, T)
+        st.U, st.Z_U, st.Lam_U, st.a_U, st.b_U = admm_half(Wt, st.V, st.Z_U, st.Lam_U, rho, T,
+                                                           solver, st.U)
+        st.V, st.Z_V, st.Lam_V, st.a_V, st.b_V = admm_half(WtT, st.U, st.Z_V, st.Lam_V, rho, T,
+                                                           solver, st.V)
     return st
 
 

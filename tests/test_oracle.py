@@ -207,6 +207,101 @@ def test_half_steps_minimise_the_objective():
         assert O.objective(Wt, U, V + d, st0.Z_U, st0.Lam_U, st0.Z_V, st0.Lam_V, rho) > g0
 
 
+# --------------------------------------------------------------------- f4
+def _spd_system(seed, m=9, n=14, r=6, rho=0.8):
+    rng = _rng(seed)
+    V = rng.standard_normal((n, r))
+    G = V.T @ V + rho * np.eye(r)
+    R = rng.standard_normal((m, r))
+    U0 = rng.standard_normal((m, r))
+    return G, R, U0
+
+
+def _energy_err(U, G, R):
+    """Per-row error in the G norm, ||u - u*||_G, against the exact solve
+    (numpy.linalg.solve on G u*^T = r^T)."""
+    X = np.linalg.solve(G, R.T).T
+    E = U - X
+    return np.sqrt(np.einsum("ij,jk,ik->i", E, G, E))
+
+
+def test_cg_terminates_in_r_steps():
+    # conjugate gradients on an r x r SPD system is exact after r steps
+    # (finite termination, up to rounding)
+    G, R, U0 = _spd_system(70)
+    U = O.iterative_solve(R, G, U0, G.shape[0], "cg")
+    np.testing.assert_allclose(U @ G, R, rtol=0, atol=1e-9)
+    # and stays there with more steps
+    U2 = O.iterative_solve(R, G, U0, 3 * G.shape[0], "cg")
+    np.testing.assert_allclose(U2 @ G, R, rtol=0, atol=1e-9)
+
+
+def test_gd_and_cg_decrease_the_energy_error_every_step():
+    G, R, U0 = _spd_system(71)
+    for method in ("gd", "cg"):
+        prev = _energy_err(U0, G, R)
+        for k in range(1, 6):
+            e = _energy_err(O.iterative_solve(R, G, U0, k, method), G, R)
+            assert np.all(e <= prev * (1 + 1e-12)), (method, k)
+            assert np.all(e < prev) or np.all(prev < 1e-12), (method, k)
+            prev = e
+    # the first step of both is the same exact line search along -g
+    np.testing.assert_allclose(O.iterative_solve(R, G, U0, 1, "gd"),
+                               O.iterative_solve(R, G, U0, 1, "cg"), rtol=1e-14, atol=1e-14)
+    # steepest descent's textbook rate: each step shrinks the G-norm error by
+    # at least (k - 1) / (k + 1), k the condition number of G
+    ev = np.linalg.eigvalsh(G)
+    q = (ev[-1] - ev[0]) / (ev[-1] + ev[0])
+    e0 = _energy_err(U0, G, R)
+    e3 = _energy_err(O.iterative_solve(R, G, U0, 3, "gd"), G, R)
+    assert np.all(e3 <= q ** 3 * e0 * (1 + 1e-9))
+
+
+def test_gd_converges_to_the_solve():
+    G, R, U0 = _spd_system(72, r=4, rho=3.0)
+    U = O.iterative_solve(R, G, U0, 400, "gd")
+    np.testing.assert_allclose(U, np.linalg.solve(G, R.T).T, rtol=0, atol=1e-10)
+
+
+def test_iterative_solve_edge_cases():
+    G, R, U0 = _spd_system(73)
+    np.testing.assert_array_equal(O.iterative_solve(R, G, U0, 0, "cg"), U0)
+    # a row already at the solution stays there; a zero right-hand side with a
+    # zero start stays zero
+    X = np.linalg.solve(G, R.T).T
+    U0b = U0.copy()
+    U0b[2] = X[2]
+    R0 = R.copy()
+    R0[4] = 0.0
+    U0b[4] = 0.0
+    for method in ("gd", "cg"):
+        U = O.iterative_solve(R0, G, U0b, 3, method)
+        np.testing.assert_allclose(U[2], X[2], rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(U[4], 0.0)
+    with pytest.raises(ValueError):
+        O.iterative_solve(R, G, U0, 1, "sor")
+
+
+def test_half_step_with_converged_iterative_solve_equals_cholesky():
+    rng = _rng(74)
+    m, n, r, rho = 12, 10, 5, 1.3
+    Wt = rng.standard_normal((m, n))
+    V = rng.standard_normal((n, r))
+    Z = rng.standard_normal((m, r))
+    Lam = 0.2 * rng.standard_normal((m, r))
+    U_prev = rng.standard_normal((m, r))
+    exact = O.admm_half(Wt, V, Z, Lam, rho, 5)
+    it = O.admm_half(Wt, V, Z, Lam, rho, 5, ("cg", 3 * r), U_prev)
+    for a, b in zip(exact, it):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-9)
+    # iterate threads the previous factor through as the warm start: with 0
+    # steps the latents never move from the start
+    st0 = O.State(U_prev, V, Z, Lam, rng.standard_normal((n, r)), 0.1 * rng.standard_normal((n, r)))
+    st = O.iterate(Wt, st0, rho, 5, 2, solver=("gd", 0))
+    np.testing.assert_array_equal(st.U, U_prev)
+    np.testing.assert_array_equal(st.V, V)
+
+
 # --------------------------------------------------------------------- a7
 def test_svid_recovers_exact_sign_rank1():
     rng = _rng(7)
