@@ -279,6 +279,10 @@ def main():
                     help="a synthetic layer (synth.layers.WORKLOADS) or 'llama2-7b-block' "
                          "(the seven layers of one Llama-2-7B-shaped block, run one after the "
                          "other in each step)")
+    ap.add_argument("--solver", default=None,
+                    help="METHOD:STEPS, an iterative solve of each half's system instead of the "
+                         "Cholesky factor: cg (conjugate gradients) or gd (steepest descent), "
+                         "STEPS steps per half, e.g. cg:8")
     ap.add_argument("--binary", action="store_true",
                     help="only time the binary-layer product (nq_binary_matmul) on the layer "
                          "shapes, warm and with its sign bits rotated through > 256 MB")
@@ -335,7 +339,11 @@ def main():
               flush=True)
         return
     layers = [make_layer(nm) for nm in names]
-    line = measure(nq, torch, dev, args, layers)
+    solver = None
+    if args.solver:
+        meth, _, k = args.solver.partition(":")
+        solver = (meth, int(k))
+    line = measure(nq, torch, dev, args, layers, solver)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers)
     print(json.dumps(line), flush=True)
@@ -352,7 +360,7 @@ def workload_layers(name):
     return [name]
 
 
-def measure(nq, torch, dev, args, layers):
+def measure(nq, torch, dev, args, layers, solver=None):
     """One step = one whole per-layer run of every layer of the workload
     through the C ABI, inputs resident in HBM."""
     import numpy as np
@@ -374,7 +382,8 @@ def measure(nq, torch, dev, args, layers):
     phases_all = []
     for wl, iters, ins in runs:
         hp = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
-                       compute_error=True, single_stream=args.single_stream, profile=True)
+                       compute_error=True, single_stream=args.single_stream, profile=True,
+                       solver=solver)
         out = hp.alloc_outputs(dev)
         hp.run(*ins, out=out, want_stats=False)
         phases_all.append(hp.profile(reset=True))
@@ -385,7 +394,8 @@ def measure(nq, torch, dev, args, layers):
     handles = []
     for wl, iters, ins in runs:
         h = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
-                      compute_error=True, single_stream=args.single_stream, profile="rhs")
+                      compute_error=True, single_stream=args.single_stream, profile="rhs",
+                      solver=solver)
         handles.append((h, h.alloc_outputs(dev)))
 
     def step():
@@ -440,7 +450,8 @@ def measure(nq, torch, dev, args, layers):
     weights = sum(wl.m * wl.n for wl, _, _ in runs)
     bits = sum(wl.r * (wl.m + wl.n) for wl, _, _ in runs)
     scale_bits = sum(16 * (wl.m + wl.n) for wl, _, _ in runs)
-    cfg = {"workload": name, "layers": len(runs), "parallelism": "single-gpu"}
+    cfg = {"workload": name, "layers": len(runs), "parallelism": "single-gpu",
+           "solve": "cholesky" if solver is None else f"{solver[0]} x{solver[1]}"}
     if single:
         cfg.update({"m": wl0.m, "n": wl0.n, "r": wl0.r, "rho": wl0.rho,
                     "admm_iters_per_step": runs[0][1], "svid_steps": wl0.svid_steps})

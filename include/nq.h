@@ -73,12 +73,21 @@ typedef enum nq_status {
 #define NQ_FLAG_PROFILE_RHS_ONLY 0x20u /* with NQ_FLAG_PROFILE: time only
                                        NQ_PHASE_GEMM_RHS (each event pair costs a little
                                        device time; the other phases get none)           */
+/* Iterative solve in place of the Cholesky factor (the gradient-descent
+ * solver of the implementation blog, section 待办事项): each half takes
+ * desc.solve_steps steps per row on u G = r, G = other^T other + rho I,
+ * from the factor's previous value. At most one of the two; neither = the
+ * exact Cholesky solve. */
+#define NQ_FLAG_SOLVE_CG      0x40u /* conjugate gradients                               */
+#define NQ_FLAG_SOLVE_GD      0x80u /* steepest descent, exact step along the gradient   */
 
 /* Phases timed under NQ_FLAG_PROFILE. */
 typedef enum nq_phase {
   NQ_PHASE_GEMM_RHS = 0,   /* R = Wt V + rho (Z - Lam) (one launch per half-iteration)   */
-  NQ_PHASE_GEMM_SOLVE = 1, /* U = R G^-1, X = U + Lam (one launch per half-iteration)    */
-  NQ_PHASE_CHAIN = 2,      /* Gram + Cholesky/inverse factor + L^-T L^-1 (per half)       */
+  NQ_PHASE_GEMM_SOLVE = 1, /* U = R G^-1 and U^T (one launch per half-iteration); with an
+                              iterative solve: all of its steps and U^T                   */
+  NQ_PHASE_CHAIN = 2,      /* Gram + Cholesky/inverse factor + L^-T L^-1 (per half); with
+                              an iterative solve: the Gram and its reduction to G          */
   NQ_PHASE_SVID = 3,       /* SVID power steps + dual update (per half)                   */
   NQ_PHASE_PREP = 4,       /* preconditioning, norms, init latents, initial SVIDs         */
   NQ_PHASE_FINISH = 5,     /* balancing, scales, packing, errors                          */
@@ -95,6 +104,8 @@ typedef struct nq_lbadmm_desc {
   uint64_t seed;      /* seed of the built-in initialiser (used when U0/V0 are
                          NULL): Philox4x32-10 counter-based normals               */
   uint32_t flags;     /* NQ_FLAG_*                                                 */
+  int32_t solve_steps; /* steps per half of NQ_FLAG_SOLVE_CG / _GD, 1 .. 10000;
+                          must be 0 without those flags                           */
 } nq_lbadmm_desc;
 
 typedef struct nq_lbadmm_stats {

@@ -21,8 +21,8 @@ from typing import Optional
 
 from . import _lib
 from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE,  # noqa: F401
-                   NQ_FLAG_PROFILE, NQ_FLAG_PROFILE_RHS_ONLY, NQ_FLAG_SINGLE_STREAM, NQ_OK,
-                   PHASES, Desc, Stats)
+                   NQ_FLAG_PROFILE, NQ_FLAG_PROFILE_RHS_ONLY, NQ_FLAG_SINGLE_STREAM,
+                   NQ_FLAG_SOLVE_CG, NQ_FLAG_SOLVE_GD, NQ_OK, PHASES, Desc, Stats)
 
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
@@ -83,23 +83,24 @@ def version() -> int:
     return int(_lib.load().nq_version())
 
 
-def _desc(m, n, r, rho, iters, svid_steps, seed, flags) -> Desc:
+def _desc(m, n, r, rho, iters, svid_steps, seed, flags, solve_steps=0) -> Desc:
     return Desc(int(m), int(n), int(r), float(rho), int(iters), int(svid_steps), int(seed),
-                int(flags))
+                int(flags), int(solve_steps))
 
 
-def lbadmm_workspace_bytes(m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0, flags=0) -> int:
+def lbadmm_workspace_bytes(m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0, flags=0,
+                           solve_steps=0) -> int:
     out = C.c_size_t(0)
-    d = _desc(m, n, r, rho, iters, svid_steps, seed, flags)
+    d = _desc(m, n, r, rho, iters, svid_steps, seed, flags, solve_steps)
     _check(_lib.load().nq_lbadmm_workspace_bytes(C.byref(d), C.byref(out)),
            "nq_lbadmm_workspace_bytes")
     return int(out.value)
 
 
 def lbadmm_create(m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0,
-                  flags=NQ_FLAG_COMPUTE_ERROR) -> int:
+                  flags=NQ_FLAG_COMPUTE_ERROR, solve_steps=0) -> int:
     h = C.c_void_p(0)
-    d = _desc(m, n, r, rho, iters, svid_steps, seed, flags)
+    d = _desc(m, n, r, rho, iters, svid_steps, seed, flags, solve_steps)
     _check(_lib.load().nq_lbadmm_create(C.byref(d), C.byref(h)), "nq_lbadmm_create")
     return h.value
 
@@ -393,9 +394,18 @@ class LBADMM:
     """One handle for one layer shape; reusable across runs of that shape."""
 
     def __init__(self, m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0, compute_error=True,
-                 init_exact=False, balance=True, single_stream=False, profile=False):
-        """profile: False, True (every phase) or "rhs" (only the RHS GEMM)."""
-        flags = 0
+                 init_exact=False, balance=True, single_stream=False, profile=False,
+                 solver=None):
+        """profile: False, True (every phase) or "rhs" (only the RHS GEMM).
+        solver: None (the Cholesky solve) or (method, steps) with method "cg"
+        (conjugate gradients) or "gd" (steepest descent): an iterative solve
+        of each half's system, warm-started from the factor's previous value."""
+        flags, steps = 0, 0
+        if solver is not None:
+            method, steps = solver
+            if method not in ("cg", "gd"):
+                raise ValueError("solver method is 'cg' or 'gd'")
+            flags |= NQ_FLAG_SOLVE_CG if method == "cg" else NQ_FLAG_SOLVE_GD
         flags |= NQ_FLAG_PROFILE if profile else 0
         flags |= NQ_FLAG_PROFILE_RHS_ONLY if profile == "rhs" else 0
         flags |= NQ_FLAG_COMPUTE_ERROR if compute_error else 0
@@ -403,7 +413,7 @@ class LBADMM:
         flags |= 0 if balance else NQ_FLAG_NO_BALANCE
         flags |= NQ_FLAG_SINGLE_STREAM if single_stream else 0
         self.m, self.n, self.r = int(m), int(n), int(r)
-        self.handle = lbadmm_create(m, n, r, rho, iters, svid_steps, seed, flags)
+        self.handle = lbadmm_create(m, n, r, rho, iters, svid_steps, seed, flags, steps)
 
     def alloc_outputs(self, device):
         torch = _torch()
@@ -458,9 +468,10 @@ class LBADMM:
 
 
 def lbadmm(W, d_out, d_in, r, rho=1.0, iters=50, svid_steps=5, U0=None, V0=None, seed=0,
-           compute_error=True, init_exact=False, balance=True, single_stream=False) -> Result:
+           compute_error=True, init_exact=False, balance=True, single_stream=False,
+           solver=None) -> Result:
     """Factorise one layer: W ~ diag(s1) sign(U) sign(V)^T diag(s2)."""
     m, n = W.shape
     with LBADMM(m, n, r, rho, iters, svid_steps, seed, compute_error, init_exact, balance,
-                single_stream) as h:
+                single_stream, solver=solver) as h:
         return h.run(W, d_out, d_in, U0, V0)

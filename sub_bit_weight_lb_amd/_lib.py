@@ -22,6 +22,8 @@ NQ_FLAG_NO_BALANCE = 0x4
 NQ_FLAG_SINGLE_STREAM = 0x8
 NQ_FLAG_PROFILE = 0x10
 NQ_FLAG_PROFILE_RHS_ONLY = 0x20
+NQ_FLAG_SOLVE_CG = 0x40
+NQ_FLAG_SOLVE_GD = 0x80
 
 PHASES = ["gemm_rhs", "gemm_solve", "chain", "svid", "prep", "finish"]
 
@@ -29,7 +31,7 @@ PHASES = ["gemm_rhs", "gemm_solve", "chain", "svid", "prep", "finish"]
 class Desc(C.Structure):
     _fields_ = [("m", C.c_int64), ("n", C.c_int64), ("r", C.c_int64), ("rho", C.c_float),
                 ("iters", C.c_int32), ("svid_steps", C.c_int32), ("seed", C.c_uint64),
-                ("flags", C.c_uint32)]
+                ("flags", C.c_uint32), ("solve_steps", C.c_int32)]
 
 
 class Stats(C.Structure):

@@ -247,6 +247,16 @@ hipError_t launch_error(const int8_t* SU, const int8_t* SV, int mp, int np_, int
                         const float* s1, const float* s2, double* parts,
                         DevStats* st, hipStream_t s);
 
+// ---------------------------------------------------------------- iterative solve (itsolve.hip)
+// Rows x rp arrays (ld rp), rp % 4 == 0 and rp <= 8192. init: d = -g,
+// delta = row sums of g^2. step (given Q = d G): alpha = delta / (d . Q)
+// (0 unless d . Q > 0), u += alpha d, g += alpha Q, delta = g . g, and unless
+// `last`, d = beta d - g with beta = delta_new / delta_old for conjugate
+// gradients (cg), 0 for steepest descent.
+hipError_t launch_itsolve_init(const float* g, float* d, float* delta, int rows, int rp,
+                               hipStream_t s);
+hipError_t launch_itsolve_step(const float* Q, float* d, float* u, float* g, float* delta,
+                               int rows, int rp, bool cg, bool last, hipStream_t s);
 // ---------------------------------------------------------------- packing
 hipError_t launch_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                              uint32_t* bits, int64_t ld_words, hipStream_t s);

@@ -39,7 +39,7 @@ nq_status hip_fail(hipError_t e, const char* what) { return hip_error(e, what); 
 
 constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
                                   NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE |
-                                  NQ_FLAG_PROFILE_RHS_ONLY;
+                                  NQ_FLAG_PROFILE_RHS_ONLY | NQ_FLAG_SOLVE_CG | NQ_FLAG_SOLVE_GD;
 constexpr int kProfileRuns = 8;
 constexpr int64_t kMaxMN = (1 << 21) - 256;
 constexpr int64_t kMaxR = 1 << 13;
@@ -60,6 +60,13 @@ nq_status check_desc(const nq_lbadmm_desc* d) {
   if (d->svid_steps < 1 || d->svid_steps > 10000)
     return fail(NQ_ERR_INVALID_ARG, "svid_steps must be in [1, 10000]");
   if (d->flags & ~kKnownFlags) return fail(NQ_ERR_INVALID_ARG, "unknown flag bits");
+  const uint32_t solver = d->flags & (NQ_FLAG_SOLVE_CG | NQ_FLAG_SOLVE_GD);
+  if (solver == (NQ_FLAG_SOLVE_CG | NQ_FLAG_SOLVE_GD))
+    return fail(NQ_ERR_INVALID_ARG, "NQ_FLAG_SOLVE_CG and NQ_FLAG_SOLVE_GD are exclusive");
+  if (solver && (d->solve_steps < 1 || d->solve_steps > 10000))
+    return fail(NQ_ERR_INVALID_ARG, "solve_steps must be in [1, 10000] with an iterative solve");
+  if (!solver && d->solve_steps != 0)
+    return fail(NQ_ERR_INVALID_ARG, "solve_steps must be 0 without an iterative solve");
   return NQ_OK;
 }
 
@@ -119,6 +126,9 @@ struct nq_lbadmm {
   int8_t *SU, *SV;
   DevStats* st;
   float* rhs_part;  // partial tiles of the RHS GEMM when it leaves XCD 7 free
+  // iterative solve (NQ_FLAG_SOLVE_CG / _GD): gradient, direction and its
+  // product with G (max(mp, np) x rp each) and the per-row g.g
+  float *itG = nullptr, *itD = nullptr, *itQ = nullptr, *itDelta = nullptr;
   // gemm_s: the RHS GEMM and the SVIDs, beside the caller's stream (see
   // run_half)
   hipStream_t gemm_s = nullptr;
@@ -146,6 +156,10 @@ struct nq_lbadmm {
 };
 
 namespace {
+
+bool iterative(const nq_lbadmm* h) {
+  return (h->d.flags & (NQ_FLAG_SOLVE_CG | NQ_FLAG_SOLVE_GD)) != 0;
+}
 
 // Lay out (or just size, when h->base is null) every workspace buffer.
 size_t layout(nq_lbadmm* h) {
@@ -177,6 +191,9 @@ size_t layout(nq_lbadmm* h) {
   size_t o_st = a.take<DevStats>(1);
   size_t o_rp = a.take<float>(std::max(rhs_part_floats((int)mp, (int)rp, (int)np_),
                                         rhs_part_floats((int)np_, (int)rp, (int)mp)));
+  const bool it = iterative(h);
+  size_t o_itG = it ? a.take<float>(mx * rp) : 0, o_itD = it ? a.take<float>(mx * rp) : 0;
+  size_t o_itQ = it ? a.take<float>(mx * rp) : 0, o_itX = it ? a.take<float>(mx) : 0;
   if (h->base) {
     char* b = h->base;
     h->Wt = (float*)(b + o_Wt); h->WtT = (float*)(b + o_WtT);
@@ -201,6 +218,10 @@ size_t layout(nq_lbadmm* h) {
     h->s1c = (float*)(b + o_s1c); h->s2c = (float*)(b + o_s2c);
     h->SU = (int8_t*)(b + o_SU); h->SV = (int8_t*)(b + o_SV);
     h->rhs_part = (float*)(b + o_rp);
+    if (it) {
+      h->itG = (float*)(b + o_itG); h->itD = (float*)(b + o_itD);
+      h->itQ = (float*)(b + o_itQ); h->itDelta = (float*)(b + o_itX);
+    }
   }
   return a.off;
 }
@@ -275,8 +296,58 @@ nq_status run_svid(nq_lbadmm* h, const Half& x, hipStream_t vs) {
 //        until the next half of its own factor (later on this stream) to
 //        finish.
 // Without overlap every kernel goes to s in the same order.
+// The iterative form of a half (NQ_FLAG_SOLVE_CG / _GD): the Gram reduced to
+// G = other^T other + rho I on s, the RHS GEMM on gemm_s beside it (on the
+// whole chip: there is no chain), then on s, from the factor's current value
+// u: g = u G - R (the GEMM with the RHS epilogue, rho = -1), d = -g, and
+// per step the GEMM d G and the row-local step; finally out^T.
+nq_status run_half_iterative(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t s,
+                             bool overlap) {
+  const int rp = h->rp;
+  hipStream_t gs = overlap ? h->gemm_s : s;
+  long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
+  HIPCHK(launch_gram_partial(x.otherT, x.K, x.K, rp, x.gp, h->gpart, s,
+                             overlap ? h->ev_gram : nullptr));
+  if (overlap) HIPCHK(hipStreamWaitEvent(h->gemm_s, h->ev_gram, 0));
+  GemmArgs g{};
+  g.A = x.Wside; g.lda = x.K; g.B = x.otherT; g.ldb = x.K; g.C = h->R; g.ldc = rp;
+  g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
+  long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, gs);
+  HIPCHK(launch_gemm(g, kEpiRhs, gs));
+  prof_end(h, pr, gs);
+  if (overlap) HIPCHK(hipEventRecord(h->ev_rhs, gs));
+  HIPCHK(launch_gram_reduce(h->gpart, x.K, rp, x.gp, h->d.rho, true, h->G, rp, s));
+  prof_end(h, pc, s);
+  if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
+  const bool cg = (h->d.flags & NQ_FLAG_SOLVE_CG) != 0;
+  const int steps = h->d.solve_steps;
+  long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
+  // g = out G - R (G symmetric: its own transposed operand)
+  GemmArgs r{};
+  r.A = x.out; r.lda = rp; r.B = h->G; r.ldb = rp; r.C = h->itG; r.ldc = rp;
+  r.P = h->R; r.rho = -1.0f; r.M = x.M; r.N = rp; r.K = rp;
+  HIPCHK(launch_gemm(r, kEpiRhs, s));
+  HIPCHK(launch_itsolve_init(h->itG, h->itD, h->itDelta, x.M, rp, s));
+  GemmArgs q{};
+  q.A = h->itD; q.lda = rp; q.B = h->G; q.ldb = rp; q.C = h->itQ; q.ldc = rp;
+  q.M = x.M; q.N = rp; q.K = rp;
+  for (int k = 0; k < steps; ++k) {
+    HIPCHK(launch_gemm(q, kEpiPlain, s));
+    HIPCHK(launch_itsolve_step(h->itQ, h->itD, x.out, h->itG, h->itDelta, x.M, rp, cg,
+                               k == steps - 1, s));
+  }
+  HIPCHK(launch_transpose(x.out, x.M, rp, rp, x.outT, x.M, s));
+  prof_end(h, ps, s);
+  if (pending) {
+    nq_status st = run_svid(h, *pending, overlap ? gs : s);
+    if (st != NQ_OK) return st;
+  }
+  return NQ_OK;
+}
+
 nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t s,
                    bool overlap) {
+  if (iterative(h)) return run_half_iterative(h, x, pending, s, overlap);
   const int rp = h->rp;
   hipStream_t gs = overlap ? h->gemm_s : s;
   long pc = prof_begin(h, NQ_PHASE_CHAIN, s);
@@ -420,7 +491,7 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
   {
     int ncu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      h->pin = ncu == kPinGrid && cholesky_pinnable(h->rp, false);
+      h->pin = ncu == kPinGrid && cholesky_pinnable(h->rp, false) && !iterative(h);
     if (const char* y = std::getenv("NQ_PIN")) h->pin = h->pin && std::atoi(y) != 0;
     bool rr = false;
     if (h->pin && xcd_round_robin_ok(&rr) == hipSuccess) h->pin = rr;

@@ -39,8 +39,9 @@ def test_struct_layouts_match_header(tmp_path):
     src = tmp_path / "sz.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "nq.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu\\n\", sizeof(nq_lbadmm_desc),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(nq_lbadmm_desc),"
         " offsetof(nq_lbadmm_desc, seed), offsetof(nq_lbadmm_desc, flags),"
+        " offsetof(nq_lbadmm_desc, solve_steps),"
         " sizeof(nq_lbadmm_stats), offsetof(nq_lbadmm_stats, potrf_info),"
         " offsetof(nq_lbadmm_stats, elapsed_ms)); return 0;}\n")
     exe = tmp_path / "sz"
@@ -48,6 +49,7 @@ def test_struct_layouts_match_header(tmp_path):
                            "-o", str(exe)])
     vals = [int(v) for v in subprocess.check_output([str(exe)]).split()]
     assert vals == [C.sizeof(L.Desc), L.Desc.seed.offset, L.Desc.flags.offset,
+                    L.Desc.solve_steps.offset,
                     C.sizeof(L.Stats), L.Stats.potrf_info.offset, L.Stats.elapsed_ms.offset]
 
 
@@ -59,7 +61,7 @@ def test_status_strings_and_version(lib):
 
 
 def _desc(**kw):
-    d = dict(m=256, n=512, r=128, rho=1.0, iters=2, svid_steps=5, seed=0, flags=0)
+    d = dict(m=256, n=512, r=128, rho=1.0, iters=2, svid_steps=5, seed=0, flags=0, solve_steps=0)
     d.update(kw)
     return L.Desc(**d)
 
@@ -67,6 +69,8 @@ def _desc(**kw):
 @pytest.mark.parametrize("bad", [dict(m=0), dict(n=-1), dict(r=0), dict(rho=0.0),
                                  dict(rho=float("nan")), dict(rho=float("inf")), dict(iters=-1),
                                  dict(svid_steps=0), dict(flags=0x100), dict(r=1 << 17),
+                                 dict(flags=0xC0, solve_steps=3), dict(flags=0x40),
+                                 dict(flags=0x80, solve_steps=10001), dict(solve_steps=2),
                                  dict(r=(1 << 13) + 1), dict(m=(1 << 21) - 255),
                                  dict(n=(1 << 21) - 255)])
 def test_create_rejects_bad_desc_before_device_work(lib, bad):

@@ -139,6 +139,35 @@ def test_one_iteration_full_size(gpu, name):
     assert sign_agreement(st["V"], ref.V) >= 0.999
 
 
+@pytest.mark.parametrize("method, steps", [("cg", 8), ("gd", 4)])
+def test_iterative_solve_full_size_sampled(gpu, method, steps):
+    """4096 x 4096, r = 2048 with the iterative solve: the first U-half's rows
+    are independent systems u G = r, so sampled rows of the GPU's U after one
+    iteration are compared with oracle.iterative_solve on those rows (G and R
+    built from the inputs by the oracle's routines, warm start U0)."""
+    import sub_bit_weight_lb_amd as nq
+    L = make_layer(ATTN)
+    wl = L.workload
+    print(f"case {ATTN}: one iteration, {method} x{steps}", flush=True)
+    h = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=1, svid_steps=wl.svid_steps,
+                  solver=(method, steps))
+    h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+    U = H(h.state()["U"])
+    h.close()
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    s0 = O.init_scale(Wt, wl.r)
+    U0 = s0 * L.EU.astype(np.float64)
+    V0 = s0 * L.EV.astype(np.float64)
+    ZU0, _, _ = O.svid(U0, wl.svid_steps)
+    rows = np.random.default_rng(8).choice(wl.m, 16, replace=False)
+    G = O.gram(V0, wl.rho)
+    R = O.rhs(Wt[rows], V0, ZU0[rows], np.zeros((len(rows), wl.r)), wl.rho)
+    ref = O.iterative_solve(R, G, U0[rows], steps, method)
+    e = relerr(U[rows], ref)
+    print(f"  sampled rows {e:.2e}", flush=True)
+    assert e < 1e-4
+
+
 @pytest.mark.parametrize("name", [ATTN, MLP] + BLOCK_ALL)
 def test_full_run_vs_stored_oracle(gpu, name):
     g = load_golden(name)

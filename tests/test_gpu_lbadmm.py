@@ -241,3 +241,44 @@ def test_finish_matches_oracle_on_gpu_state(gpu):
     np.testing.assert_array_equal(H(res.V_bits).view(np.uint32), vb)
     assert abs(res.stats["rel_err_wtilde"] - e_wt) < 1e-5
     assert abs(res.stats["rel_err_w"] - e_w) < 1e-5
+
+
+@pytest.mark.parametrize("method, steps, shape", [("cg", 5, (256, 512, 128)),
+                                                  ("gd", 3, (300, 200, 70)),
+                                                  ("cg", 1, (64, 48, 8)),
+                                                  ("cg", 12, (256, 384, 96)),
+                                                  ("gd", 8, (1, 1, 1))])
+def test_iterative_solve_iterations(gpu, method, steps, shape):
+    """NQ_FLAG_SOLVE_CG / _GD: one and two iterations with the iterative solve
+    against oracle.iterate with the same solver, warm start and step count."""
+    import sub_bit_weight_lb_amd as nq
+    m, n, r = shape
+    L = make_tiny(m, n, r, seed=31 + m)
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    for iters in (1, 2):
+        print(f"case {method} x{steps} {shape} iters={iters}", flush=True)
+        h = nq.LBADMM(m, n, r, iters=iters, balance=False, solver=(method, steps))
+        h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
+        st = {k: H(v) for k, v in h.state().items()}
+        h.close()
+        ref = O.init_state(Wt, r, 5, EU=L.EU, EV=L.EV)
+        ref = O.iterate(Wt, ref, 1.0, 5, iters, solver=(method, steps))
+        assert relerr(st["U"], ref.U) < 1e-4, relerr(st["U"], ref.U)
+        assert relerr(st["V"], ref.V) < 1e-4, relerr(st["V"], ref.V)
+        for k, Xk in (("Z_U", ref.Lam_U + ref.Z_U), ("Lam_U", ref.Lam_U + ref.Z_U),
+                      ("Z_V", ref.Lam_V + ref.Z_V), ("Lam_V", ref.Lam_V + ref.Z_V)):
+            assert masked_rel(st[k], getattr(ref, k), Xk) < 1e-4, k
+        assert sign_agreement(st["U"], ref.U) >= 0.999
+
+
+def test_iterative_solve_rejects_bad_desc(gpu):
+    import sub_bit_weight_lb_amd as nq
+    with pytest.raises(ValueError):
+        nq.LBADMM(64, 48, 8, solver=("sor", 3))
+    with pytest.raises(nq.NQError):
+        nq.LBADMM(64, 48, 8, solver=("cg", 0))
+    with pytest.raises(nq.NQError):
+        nq.lbadmm_create(64, 48, 8, flags=nq.NQ_FLAG_SOLVE_CG | nq.NQ_FLAG_SOLVE_GD,
+                         solve_steps=3)
+    with pytest.raises(nq.NQError):
+        nq.lbadmm_create(64, 48, 8, solve_steps=3)
