@@ -197,6 +197,59 @@ def cpu_baseline(layers, budget_s=10.0, budget_fp32_s=6.0, max_halves=24):
     }
 
 
+def lw_bench(nq, torch, dev, p=4096, chunk=16384, reps=3):
+    """The Ledoit-Wolf preconditioner of one layer side: the pages'
+    calibration set (128 x 2048 tokens) of p-feature activations, resident in
+    HBM as chunk-row pieces (seeded on the device with the feature profile of
+    synth.activations), accumulated chunk by chunk and finalised. Algorithmic
+    work: the second moment's Gram, N p^2 flops (symmetric count); HBM bytes:
+    the samples read twice (staging and row norms), 8 N p."""
+    import numpy as np
+    from synth.activations import CALIB_TOKENS, feature_profile
+    N = CALIB_TOKENS
+    scale, mean, _ = feature_profile(p, 0)
+    sc = torch.from_numpy(scale.astype(np.float32)).to(dev)
+    mu = torch.from_numpy(mean.astype(np.float32)).to(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    chunks = [torch.randn(chunk, p, generator=g, device=dev) * sc + mu for _ in range(N // chunk)]
+    torch.cuda.synchronize()
+    lw = nq.LedoitWolf(p, chunk)
+    res = {"p": p, "tokens": N, "chunk_rows": chunk}
+    times = []
+    for rep in range(reps + 1):
+        lw.reset()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c in chunks:
+            lw.accumulate(c)
+        d, s = lw.finalize()
+        e1.record()
+        torch.cuda.synchronize()
+        if rep:
+            times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    flops = float(N) * p * p
+    res.update({"ms": round(ms, 3), "tokens_per_s": round(N / (ms * 1e-3), 1),
+                "gram_flops": flops, "whole_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "whole_frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+                "shrinkage": s, "d_min": float(d.min()), "d_max": float(d.max())})
+    lw.close()
+    return res
+
+
+def lw_cpu_baseline(p=4096, tokens=128):
+    """The oracle (oracle/precond.py) on a bounded sample of the same
+    workload: `tokens` tokens of p features; tokens/s."""
+    from oracle import precond as P
+    from synth.activations import make_activations
+    Z = make_activations(tokens, p, 0)
+    t0 = time.perf_counter()
+    P.diag_preconditioner(Z)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "kind": "oracle",
+            "sample": f"{tokens} tokens x {p} features, NumPy float64, {dt:.1f} s"}
+
+
 def binary_bench(nq, torch, dev, reps=20, replays=5):
     """nq_binary_matmul (Y = X W^T for W = diag(s1) S_U S_V^T diag(s2)) on the
     factorised-layer shapes. Random sign words on the device. Calls are
@@ -283,6 +336,9 @@ def main():
                     help="METHOD:STEPS, an iterative solve of each half's system instead of the "
                          "Cholesky factor: cg (conjugate gradients) or gd (steepest descent), "
                          "STEPS steps per half, e.g. cg:8")
+    ap.add_argument("--lw", action="store_true",
+                    help="only time the Ledoit-Wolf diagonal preconditioner (nq_lw_*) on the "
+                         "calibration set's 128 x 2048 tokens of 4096 features")
     ap.add_argument("--binary", action="store_true",
                     help="only time the binary-layer product (nq_binary_matmul) on the layer "
                          "shapes, warm and with its sign bits rotated through > 256 MB")
@@ -332,6 +388,12 @@ def main():
         return
     if args.binary:
         print(json.dumps({"binary_matmul": binary_bench(nq, torch, dev)}), flush=True)
+        return
+    if args.lw:
+        out = {"ledoit_wolf": lw_bench(nq, torch, dev)}
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = lw_cpu_baseline()
+        print(json.dumps(out), flush=True)
         return
     names = workload_layers(args.workload)
     if args.hbm:

@@ -257,6 +257,44 @@ nq_status nq_binary_matmul_noalloc(const uint32_t* U_bits, int64_t ldu, const ui
                                    const float* s1, const float* s2, const float* X, int64_t B,
                                    int64_t ldx, float* Y, int64_t ldy, void* stream);
 
+/* ---- diagonal preconditioners from activation samples ----
+ * The digest's first stage (方法步骤详情, stage 1) collects statistics z_in
+ * and z_out of each linear layer's activations and builds robust diagonal
+ * preconditioners D_in and D_out with Ledoit-Wolf shrinkage (a simplified
+ * diagonal K-FAC, 前置知识). The formulas implemented (the pages give none):
+ * for a sample Z (N tokens x p features), S = Z^T Z / N (uncentered),
+ * m = tr(S) / p, Ledoit & Wolf's (J. Multivariate Anal. 88, 2004) intensity
+ * shrinkage = min(b2bar, d2) / d2 with d2 = ||S - m I||^2 and
+ * b2bar = N^-2 sum_k ||z_k z_k^T - S||^2 (||A||^2 = tr(A A^T) / p), and
+ * D_jj = sqrt((1 - shrinkage) S_jj + shrinkage m). D_in comes from the
+ * layer's input sample, D_out from its output-side sample; they are the
+ * d_in, d_out of nq_lbadmm_run. */
+typedef struct nq_lw* nq_lw_t;
+
+/* Handle for one feature dimension p (1 .. 16384) taking chunks of at most
+ * max_rows rows (1 .. 2^20, p * max_rows <= 2^30). Allocates its device
+ * workspace on the current device (about 8 p^2 bytes for S in fp64, 12 p^2
+ * for the Gram, 4 p max_rows for a staged chunk). NQ_ERR_INVALID_ARG for bad
+ * sizes, NQ_ERR_UNSUPPORTED without a gfx950 device. */
+nq_status nq_lw_create(int64_t p, int64_t max_rows, nq_lw_t* out);
+
+/* Add the samples Z (device, rows x p floats, row stride ldz >= p; rows
+ * above max_rows are taken in pieces) to the running statistics, on
+ * `stream`. Asynchronous; Z must stay valid until the stream reaches the
+ * call. Calls on one handle must be ordered on one stream. rows == 0 is a
+ * no-op. */
+nq_status nq_lw_accumulate(nq_lw_t h, const float* Z, int64_t rows, int64_t ldz, void* stream);
+
+/* d (device, p floats) = the diagonal of D over all samples added since
+ * creation or the last reset. If shrinkage (host) is non-NULL it receives
+ * the intensity and the call waits for `stream`. NQ_ERR_INVALID_ARG when no
+ * sample was added. The statistics are kept: more chunks may follow. */
+nq_status nq_lw_finalize(nq_lw_t h, float* d, double* shrinkage, void* stream);
+
+/* Forget the samples (no device work; the next accumulate clears). */
+nq_status nq_lw_reset(nq_lw_t h);
+nq_status nq_lw_destroy(nq_lw_t h);
+
 /* ---- building blocks (the same kernels the run uses; for tests and tools) ----
  * These take caller buffers of any shape, copy into zero-padded temporaries
  * (hipMalloc, freed before the call returns), run the kernels on `stream`,

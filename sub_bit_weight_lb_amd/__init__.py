@@ -9,7 +9,7 @@ loudly when libnq.so or the GPU is missing. There is no CPU fallback.
 Functions mirror the C names without the ``nq_`` prefix:
     lbadmm_create / lbadmm_run / lbadmm_query / lbadmm_get_state /
     lbadmm_destroy / lbadmm_workspace_bytes / pack_signs /
-    transpose_signs / binary_matmul / binary_matmul_noalloc /
+    transpose_signs / binary_matmul / binary_matmul_noalloc / lw_* (LedoitWolf) /
     op_precondition / op_gram / op_gemm_rhs / op_cholesky_inverse / op_svid
 plus the conveniences ``LBADMM`` (a handle object) and ``lbadmm`` (one call).
 """
@@ -27,7 +27,8 @@ from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
     "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "transpose_signs",
-    "binary_matmul", "binary_matmul_noalloc", "op_precondition", "op_gram",
+    "binary_matmul", "binary_matmul_noalloc", "LedoitWolf", "ledoit_wolf_diag",
+    "preconditioners", "op_precondition", "op_gram",
     "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
 ]
@@ -295,6 +296,73 @@ def _binmm_out(Y, B, m, vec, device):
         raise ValueError(f"Y must be 2-D with unit column stride and at least {B} x {m}, "
                          f"got {tuple(Y.shape)}")
     return Y2
+
+
+class LedoitWolf:
+    """Running Ledoit-Wolf statistics of activation samples with p features
+    (nq_lw_*): accumulate() chunks of tokens x p float32 samples, then
+    finalize() -> (d, shrinkage), d the diagonal of the preconditioner
+    sqrt(diag(shrunk second moment)) as a float32 device vector."""
+
+    def __init__(self, p, max_rows=16384):
+        h = C.c_void_p(0)
+        _check(_lib.load().nq_lw_create(int(p), int(max_rows), C.byref(h)), "nq_lw_create")
+        self.handle, self.p = h.value, int(p)
+
+    def accumulate(self, Z, stream=None):
+        torch = _torch()
+        if Z.dim() != 2 or Z.shape[1] != self.p or Z.stride(1) != 1:
+            raise ValueError(f"Z must be rows x {self.p} with unit column stride")
+        _check(_lib.load().nq_lw_accumulate(
+            C.c_void_p(self.handle), _ptr(Z, "Z", torch.float32, 2, need_contig=False),
+            Z.shape[0], Z.stride(0), _stream(stream)), "nq_lw_accumulate")
+
+    def finalize(self, d=None, stream=None):
+        torch = _torch()
+        if d is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+            d = torch.empty(self.p, dtype=torch.float32, device=dev)
+        elif d.numel() != self.p:
+            raise ValueError(f"d must hold {self.p} values")
+        shrink = C.c_double(0.0)
+        _check(_lib.load().nq_lw_finalize(C.c_void_p(self.handle), _ptr(d, "d", torch.float32),
+                                          C.byref(shrink), _stream(stream)), "nq_lw_finalize")
+        return d, shrink.value
+
+    def reset(self):
+        _check(_lib.load().nq_lw_reset(C.c_void_p(self.handle)), "nq_lw_reset")
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _lib.load().nq_lw_destroy(C.c_void_p(self.handle))
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ledoit_wolf_diag(Z, max_rows=16384, stream=None):
+    """(d, shrinkage) for one sample matrix Z (device, tokens x p float32)."""
+    with LedoitWolf(Z.shape[1], min(max_rows, max(1, Z.shape[0]))) as lw:
+        lw.accumulate(Z, stream)
+        return lw.finalize(stream=stream)
+
+
+def preconditioners(X_in, Z_out, max_rows=16384, stream=None):
+    """(d_out, d_in) of a layer from its input-side sample X_in (N x n) and
+    output-side sample Z_out (N x m), ready for nq_lbadmm_run."""
+    d_in, _ = ledoit_wolf_diag(X_in, max_rows, stream)
+    d_out, _ = ledoit_wolf_diag(Z_out, max_rows, stream)
+    return d_out, d_in
 
 
 def op_precondition(W, d_out, d_in, stream=None):

@@ -61,6 +61,11 @@ SIGNATURES = {
     "nq_transpose_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_binary_matmul": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P, P]),
     "nq_binary_matmul_noalloc": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P]),
+    "nq_lw_create": (ST, [I64, I64, C.POINTER(P)]),
+    "nq_lw_accumulate": (ST, [P, P, I64, I64, P]),
+    "nq_lw_finalize": (ST, [P, P, C.POINTER(C.c_double), P]),
+    "nq_lw_reset": (ST, [P]),
+    "nq_lw_destroy": (ST, [P]),
     "nq_op_precondition": (ST, [P, I64, I64, I64, P, P, P, I64, P]),
     "nq_op_gram": (ST, [P, I64, I64, I64, F32, P, I64, P]),
     "nq_op_gemm_rhs": (ST, [P, I64, P, I64, P, I64, F32, P, I64, I64, I64, I64, P]),

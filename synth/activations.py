@@ -15,15 +15,22 @@ import numpy as np
 CALIB_TOKENS = 128 * 2048
 
 
-def make_activations(N: int, p: int, seed: int, outlier_frac: float = 0.01,
-                     dtype=np.float32) -> np.ndarray:
-    """N tokens x p features."""
+def feature_profile(p: int, seed: int, outlier_frac: float = 0.01):
+    """(scale, mean) per feature, float64, and the generator to draw tokens
+    with afterwards."""
     rng = np.random.default_rng(seed)
     scale = rng.lognormal(0.0, 1.0, p)
     k = int(round(outlier_frac * p))
     if k:
         scale[rng.choice(p, k, replace=False)] *= 20.0
     mean = 0.3 * rng.standard_normal(p) * scale
+    return scale, mean, rng
+
+
+def make_activations(N: int, p: int, seed: int, outlier_frac: float = 0.01,
+                     dtype=np.float32) -> np.ndarray:
+    """N tokens x p features."""
+    scale, mean, rng = feature_profile(p, seed, outlier_frac)
     Z = rng.standard_normal((N, p), dtype=np.float32)
     Z *= scale.astype(np.float32)
     Z += mean.astype(np.float32)

@@ -180,6 +180,22 @@ def test_binary_layer_argument_checks(lib):
     assert call_na(r=1 << 19, ldu=1 << 14, B=2) == L.NQ_ERR_INVALID_ARG
 
 
+def test_ledoit_wolf_argument_checks(lib):
+    h = C.c_void_p(0)
+    assert lib.nq_lw_create(0, 16, C.byref(h)) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_create(16385, 16, C.byref(h)) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_create(8, 0, C.byref(h)) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_create(8, (1 << 20) + 1, C.byref(h)) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_create(16384, 1 << 17, C.byref(h)) == L.NQ_ERR_INVALID_ARG  # > 2^30 staged
+    assert h.value is None
+    f = C.c_void_p(0x1000)
+    d = C.c_double(0)
+    assert lib.nq_lw_accumulate(None, f, 4, 8, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_finalize(None, f, C.byref(d), None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_reset(None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_lw_destroy(None) == 0
+
+
 def test_ops_argument_checks(lib):
     f = C.c_void_p(0x1000)
     info = C.c_int64(0)
