@@ -3,4 +3,4 @@
 Only the test-suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg
 of ``bench.py`` import this package. The GPU library never does.
 """
-from . import binary, brute, lbadmm, precond  # noqa: F401
+from . import binary, brute, lbadmm, precond, ste  # noqa: F401
