@@ -250,6 +250,93 @@ def lw_cpu_baseline(p=4096, tokens=128):
             "sample": f"{tokens} tokens x {p} features, NumPy float64, {dt:.1f} s"}
 
 
+def ste_bench(nq, torch, dev, samples=128, seq=2048, batch=4, epochs=8, admm_iters=50):
+    """STE refinement of the 4096 x 4096, r = 2048 layer with the pages'
+    settings: the calibration set (128 samples x 2048 tokens) of activations
+    seeded on the device (feature profile of synth.activations), targets
+    Y = X W^T, 8 epochs of shuffled batches of 4 samples (8192 tokens), lr
+    1e-4 -> 1e-6 on the cosine schedule, from the factors of an LB-ADMM run.
+    Algorithmic work per step: six sign products, 6 T r (m + n) flops."""
+    import numpy as np
+    from synth import make_layer
+    from synth.activations import feature_profile
+    L = make_layer(WORKLOAD)
+    wl = L.workload
+    m, n, r = wl.m, wl.n, wl.r
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    W = t(L.W)
+    with nq.LBADMM(m, n, r, rho=wl.rho, iters=admm_iters, svid_steps=wl.svid_steps) as h:
+        res = h.run(W, t(L.d_out), t(L.d_in), t(L.EU), t(L.EV))
+    N = samples * seq
+    scale, mean, _ = feature_profile(n, 0)
+    sc = torch.from_numpy(scale.astype(np.float32)).to(dev)
+    mu = torch.from_numpy(mean.astype(np.float32)).to(dev)
+    g = torch.Generator(device=dev).manual_seed(0)
+    X = torch.randn(N, n, generator=g, device=dev) * sc + mu
+    Y = X @ W.T
+    rng = np.random.default_rng(0)
+    batches = []
+    for _ in range(epochs):
+        order = rng.permutation(samples)
+        for b in range(0, samples, batch):
+            idx = (order[b:b + batch, None] * seq + np.arange(seq)[None, :]).reshape(-1)
+            batches.append(torch.from_numpy(idx.astype(np.int32)).to(dev))
+    T = batch * seq
+    out = {"m": m, "n": n, "r": r, "tokens_per_step": T, "steps": len(batches),
+           "epochs": epochs, "schedule": "cosine 1e-4 -> 1e-6, Adam"}
+    with nq.STERefiner(m, n, r, T) as ste:
+        # untimed: the loss of every step (each read waits for the GPU)
+        ste.set_params(res.U, res.V, res.s1, res.s2)
+        losses = ste.refine(X, Y, batches)
+        out["loss_first"] = losses[0]
+        out["loss_last"] = losses[-1]
+        out["loss_epoch_means"] = [round(float(np.mean(losses[e * len(batches) // epochs:
+                                                            (e + 1) * len(batches) // epochs])), 6)
+                                   for e in range(epochs)]
+        # timed: the same schedule from the same start, no reads
+        ste.set_params(res.U, res.V, res.s1, res.s2)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ste.refine(X, Y, batches, losses=False, check_rows=False)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+    flops = 6.0 * T * r * (m + n)
+    step_ms = ms / len(batches)
+    out.update({"ms_total": round(ms, 2), "ms_per_step": round(step_ms, 3),
+                "steps_per_s": round(1e3 / step_ms, 2), "tokens_per_s": round(T * 1e3 / step_ms, 1),
+                "flops_per_step": flops, "tflops": round(flops / (step_ms * 1e-3) / 1e12, 2),
+                "frac_of_fp32_peak": round(flops / (step_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)})
+    return out
+
+
+def ste_cpu_baseline(tokens=2048):
+    """The oracle (oracle/ste.py) on a bounded sample of the same workload:
+    one step (gradients + Adam) on `tokens` tokens of the 4096 x 4096,
+    r = 2048 layer from a random start, scaled to 8192-token steps."""
+    import numpy as np
+    from oracle import ste as S
+    from synth.activations import make_activations
+    rng = np.random.default_rng(0)
+    m = n = 4096
+    r = 2048
+    W = 0.02 * rng.standard_normal((m, n))
+    X = make_activations(tokens, n, 0).astype(np.float64)
+    Y = X @ W.T
+    U, V = rng.standard_normal((m, r)), rng.standard_normal((n, r))
+    s1, s2 = np.full(m, 0.02), np.full(n, 0.02)
+    t0 = time.perf_counter()
+    st = S.adam_init([U, V, s1, s2])
+    S.adam_step([U, V, s1, s2], S.grads(X, Y, U, V, s1, s2), st, 1e-4)
+    dt = time.perf_counter() - t0
+    return {"value": 1.0 / (dt * 8192 / tokens), "unit": "steps/s (8192-token steps)",
+            "kind": "oracle", "sample": f"one step on {tokens} tokens, NumPy float64, {dt:.1f} s"}
+
+
 def binary_bench(nq, torch, dev, reps=20, replays=5):
     """nq_binary_matmul (Y = X W^T for W = diag(s1) S_U S_V^T diag(s2)) on the
     factorised-layer shapes. Random sign words on the device. Calls are
@@ -336,6 +423,9 @@ def main():
                     help="METHOD:STEPS, an iterative solve of each half's system instead of the "
                          "Cholesky factor: cg (conjugate gradients) or gd (steepest descent), "
                          "STEPS steps per half, e.g. cg:8")
+    ap.add_argument("--ste", action="store_true",
+                    help="only time the STE refinement (nq_ste_*) of the 4096 x 4096, r = 2048 "
+                         "layer: 8 epochs of 4-sample batches over 128 x 2048 tokens")
     ap.add_argument("--lw", action="store_true",
                     help="only time the Ledoit-Wolf diagonal preconditioner (nq_lw_*) on the "
                          "calibration set's 128 x 2048 tokens of 4096 features")
@@ -388,6 +478,12 @@ def main():
         return
     if args.binary:
         print(json.dumps({"binary_matmul": binary_bench(nq, torch, dev)}), flush=True)
+        return
+    if args.ste:
+        out = {"ste_refinement": ste_bench(nq, torch, dev)}
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = ste_cpu_baseline()
+        print(json.dumps(out), flush=True)
         return
     if args.lw:
         out = {"ledoit_wolf": lw_bench(nq, torch, dev)}

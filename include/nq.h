@@ -295,6 +295,47 @@ nq_status nq_lw_finalize(nq_lw_t h, float* d, double* shrinkage, void* stream);
 nq_status nq_lw_reset(nq_lw_t h);
 nq_status nq_lw_destroy(nq_lw_t h);
 
+/* ---- STE refinement of a factorised layer ----
+ * The digest's stage 2 step (3) (方法步骤详情) refines the continuous latents
+ * U, V and the scales s1, s2 of each layer jointly with a straight-through
+ * estimator against the MSE of the quantised output, then takes the signs;
+ * its reproduction settings (复现评估) use lr 1e-4 -> 1e-6 with a cosine
+ * schedule, batches of 1-4 samples, 8 epochs. The formulas implemented (the
+ * pages give none): for a batch X (T x n) and target Y = X W^T (T x m),
+ * Yq = X diag(s2) sign(V) sign(U)^T diag(s1), loss = mean((Yq - Y)^2) over
+ * T x m; sign(x >= 0) = +1 and d sign / dx taken as 1; one Adam step
+ * (beta1 0.9, beta2 0.999, eps 1e-8, bias-corrected) on U, V, s1, s2 per
+ * batch. The caller owns the schedule and passes each step's lr. */
+typedef struct nq_ste* nq_ste_t;
+
+/* Handle for a layer m x n of rank r and batches of up to max_tokens tokens
+ * (all >= 1; m, n, max_tokens <= 2^21 - 256, r <= 2^13). Allocates every
+ * buffer on the current device; steps allocate nothing. */
+nq_status nq_ste_create(int64_t m, int64_t n, int64_t r, int64_t max_tokens, nq_ste_t* out);
+
+/* Start from U (m x r), V (n x r), s1 (m), s2 (n), device, contiguous (the
+ * outputs of nq_lbadmm_run); clears the Adam state. */
+nq_status nq_ste_set_params(nq_ste_t h, const float* U, const float* V, const float* s1,
+                            const float* s2, void* stream);
+
+/* One step on T tokens (1 .. max_tokens): rows t of the batch are
+ * X[rows[t]] and Y[rows[t]] (rows: device int32, or NULL for rows 0 .. T-1);
+ * X (row stride ldx >= n) and Y (ldy >= m) device float32. Computes the loss
+ * of the current parameters on the batch (kept for nq_ste_last_loss) and
+ * takes one Adam step with learning rate lr (finite, >= 0). Asynchronous on
+ * `stream`; calls on one handle must be ordered on one stream. */
+nq_status nq_ste_step(nq_ste_t h, const float* X, int64_t ldx, const float* Y, int64_t ldy,
+                      const int32_t* rows, int64_t T, float lr, void* stream);
+
+/* The loss of the last step's batch before its update (host double); waits
+ * for `stream`. */
+nq_status nq_ste_last_loss(nq_ste_t h, double* loss, void* stream);
+
+/* Copy the current parameters out (device, contiguous; any may be NULL).
+ * Their signs packed by nq_pack_signs are the refined binary factors. */
+nq_status nq_ste_get_params(nq_ste_t h, float* U, float* V, float* s1, float* s2, void* stream);
+nq_status nq_ste_destroy(nq_ste_t h);
+
 /* ---- building blocks (the same kernels the run uses; for tests and tools) ----
  * These take caller buffers of any shape, copy into zero-padded temporaries
  * (hipMalloc, freed before the call returns), run the kernels on `stream`,

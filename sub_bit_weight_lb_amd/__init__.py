@@ -10,6 +10,7 @@ Functions mirror the C names without the ``nq_`` prefix:
     lbadmm_create / lbadmm_run / lbadmm_query / lbadmm_get_state /
     lbadmm_destroy / lbadmm_workspace_bytes / pack_signs /
     transpose_signs / binary_matmul / binary_matmul_noalloc / lw_* (LedoitWolf) /
+    ste_* (STERefiner) /
     op_precondition / op_gram / op_gemm_rhs / op_cholesky_inverse / op_svid
 plus the conveniences ``LBADMM`` (a handle object) and ``lbadmm`` (one call).
 """
@@ -28,7 +29,7 @@ __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
     "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "transpose_signs",
     "binary_matmul", "binary_matmul_noalloc", "LedoitWolf", "ledoit_wolf_diag",
-    "preconditioners", "op_precondition", "op_gram",
+    "preconditioners", "STERefiner", "cosine_lr", "op_precondition", "op_gram",
     "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
 ]
@@ -363,6 +364,111 @@ def preconditioners(X_in, Z_out, max_rows=16384, stream=None):
     d_in, _ = ledoit_wolf_diag(X_in, max_rows, stream)
     d_out, _ = ledoit_wolf_diag(Z_out, max_rows, stream)
     return d_out, d_in
+
+
+def cosine_lr(t, K, lr_max=1e-4, lr_min=1e-6):
+    """Learning rate of step t (0-based) of K on the cosine schedule."""
+    import math
+    return lr_min + (lr_max - lr_min) * (1.0 + math.cos(math.pi * t / K)) / 2.0
+
+
+class STERefiner:
+    """STE refinement of one factorised layer (nq_ste_*): set_params() from
+    a run's U, V, s1, s2, then step() per batch (X, Y = X W^T device float32;
+    rows: an int32 device index vector or None), or refine() over a list of
+    batches with the cosine schedule."""
+
+    def __init__(self, m, n, r, max_tokens):
+        h = C.c_void_p(0)
+        _check(_lib.load().nq_ste_create(int(m), int(n), int(r), int(max_tokens), C.byref(h)),
+               "nq_ste_create")
+        self.handle, self.m, self.n, self.r = h.value, int(m), int(n), int(r)
+        self.max_tokens = int(max_tokens)
+
+    def set_params(self, U, V, s1, s2, stream=None):
+        torch = _torch()
+        f32 = torch.float32
+        if (tuple(U.shape) != (self.m, self.r) or tuple(V.shape) != (self.n, self.r)
+                or s1.numel() != self.m or s2.numel() != self.n):
+            raise ValueError("U, V, s1, s2 must be m x r, n x r, m and n")
+        _check(_lib.load().nq_ste_set_params(
+            C.c_void_p(self.handle), _ptr(U, "U", f32, 2), _ptr(V, "V", f32, 2),
+            _ptr(s1, "s1", f32), _ptr(s2, "s2", f32), _stream(stream)), "nq_ste_set_params")
+
+    def step(self, X, Y, lr, rows=None, stream=None, check_rows=True):
+        """check_rows: verify on the host that every index is a row of X
+        (a device read and a wait; the library cannot see X's length)."""
+        torch = _torch()
+        f32 = torch.float32
+        if X.dim() != 2 or X.shape[1] != self.n or X.stride(1) != 1:
+            raise ValueError(f"X must be tokens x {self.n} with unit column stride")
+        if Y.dim() != 2 or Y.shape[1] != self.m or Y.stride(1) != 1 or Y.shape[0] != X.shape[0]:
+            raise ValueError(f"Y must be tokens x {self.m}, as many rows as X")
+        if rows is None:
+            T = X.shape[0]
+            rp = None
+        else:
+            if rows.dtype != torch.int32 or rows.dim() != 1:
+                raise ValueError("rows must be a 1-D int32 tensor")
+            T = rows.numel()
+            rp = _ptr(rows, "rows", torch.int32)
+            if check_rows and T and (int(rows.min()) < 0 or int(rows.max()) >= X.shape[0]):
+                raise ValueError("rows holds an index outside X")
+        if not 1 <= T <= self.max_tokens:
+            raise ValueError(f"a batch holds 1 .. {self.max_tokens} tokens")
+        _check(_lib.load().nq_ste_step(
+            C.c_void_p(self.handle), _ptr(X, "X", f32, 2, need_contig=False), X.stride(0),
+            _ptr(Y, "Y", f32, 2, need_contig=False), Y.stride(0), rp, T, float(lr),
+            _stream(stream)), "nq_ste_step")
+
+    def last_loss(self, stream=None):
+        out = C.c_double(0.0)
+        _check(_lib.load().nq_ste_last_loss(C.c_void_p(self.handle), C.byref(out),
+                                            _stream(stream)), "nq_ste_last_loss")
+        return out.value
+
+    def params(self, stream=None):
+        torch = _torch()
+        dev = torch.device("cuda", torch.cuda.current_device())
+        f32 = torch.float32
+        U = torch.empty((self.m, self.r), dtype=f32, device=dev)
+        V = torch.empty((self.n, self.r), dtype=f32, device=dev)
+        s1 = torch.empty(self.m, dtype=f32, device=dev)
+        s2 = torch.empty(self.n, dtype=f32, device=dev)
+        _check(_lib.load().nq_ste_get_params(
+            C.c_void_p(self.handle), _ptr(U, "U", f32), _ptr(V, "V", f32), _ptr(s1, "s1", f32),
+            _ptr(s2, "s2", f32), _stream(stream)), "nq_ste_get_params")
+        return U, V, s1, s2
+
+    def refine(self, X, Y, batches, lr_max=1e-4, lr_min=1e-6, losses=True, stream=None,
+               check_rows=True):
+        """One step per batch (int32 device index vectors) on the cosine
+        schedule from lr_max to lr_min; returns the per-step losses (each
+        read back, which waits for the stream) or None."""
+        out = [] if losses else None
+        K = len(batches)
+        for t, rows in enumerate(batches):
+            self.step(X, Y, cosine_lr(t, K, lr_max, lr_min), rows, stream, check_rows)
+            if losses:
+                out.append(self.last_loss(stream))
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _lib.load().nq_ste_destroy(C.c_void_p(self.handle))
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def op_precondition(W, d_out, d_in, stream=None):

@@ -66,6 +66,12 @@ SIGNATURES = {
     "nq_lw_finalize": (ST, [P, P, C.POINTER(C.c_double), P]),
     "nq_lw_reset": (ST, [P]),
     "nq_lw_destroy": (ST, [P]),
+    "nq_ste_create": (ST, [I64, I64, I64, I64, C.POINTER(P)]),
+    "nq_ste_set_params": (ST, [P, P, P, P, P, P]),
+    "nq_ste_step": (ST, [P, P, I64, P, I64, P, I64, C.c_float, P]),
+    "nq_ste_last_loss": (ST, [P, C.POINTER(C.c_double), P]),
+    "nq_ste_get_params": (ST, [P, P, P, P, P, P]),
+    "nq_ste_destroy": (ST, [P]),
     "nq_op_precondition": (ST, [P, I64, I64, I64, P, P, P, I64, P]),
     "nq_op_gram": (ST, [P, I64, I64, I64, F32, P, I64, P]),
     "nq_op_gemm_rhs": (ST, [P, I64, P, I64, P, I64, F32, P, I64, I64, I64, I64, P]),
