@@ -104,6 +104,7 @@ def hbm_bench(nq, torch, dev, L, reps=20):
 
     W, d_out, d_in, EU, EV = t(L.W), t(L.d_out), t(L.d_in), t(L.EU), t(L.EV)
     h = nq.LBADMM(m, n, r, rho=wl.rho, iters=1, svid_steps=wl.svid_steps, compute_error=True,
+                  init_draws=True,
                   profile=True)
     out = h.alloc_outputs(dev)
     h.run(W, d_out, d_in, EU, EV, out=out, want_stats=False)
@@ -268,7 +269,8 @@ def ste_bench(nq, torch, dev, samples=128, seq=2048, batch=4, epochs=8, admm_ite
         return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
 
     W = t(L.W)
-    with nq.LBADMM(m, n, r, rho=wl.rho, iters=admm_iters, svid_steps=wl.svid_steps) as h:
+    with nq.LBADMM(m, n, r, rho=wl.rho, iters=admm_iters, svid_steps=wl.svid_steps,
+                   init_draws=True) as h:
         res = h.run(W, t(L.d_out), t(L.d_in), t(L.EU), t(L.EV))
     N = samples * seq
     scale, mean, _ = feature_profile(n, 0)
@@ -541,6 +543,7 @@ def measure(nq, torch, dev, args, layers, solver=None):
     for wl, iters, ins in runs:
         hp = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
                        compute_error=True, single_stream=args.single_stream, profile=True,
+                       init_draws=True,
                        solver=solver)
         out = hp.alloc_outputs(dev)
         hp.run(*ins, out=out, want_stats=False)
@@ -553,6 +556,7 @@ def measure(nq, torch, dev, args, layers, solver=None):
     for wl, iters, ins in runs:
         h = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
                       compute_error=True, single_stream=args.single_stream, profile="rhs",
+                      init_draws=True,
                       solver=solver)
         handles.append((h, h.alloc_outputs(dev)))
 

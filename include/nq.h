@@ -62,8 +62,9 @@ typedef enum nq_status {
 
 /* Flags of nq_lbadmm_desc.flags. */
 #define NQ_FLAG_COMPUTE_ERROR 0x1u  /* compute rel. reconstruction errors into stats     */
-#define NQ_FLAG_INIT_EXACT    0x2u  /* U0/V0 are the starting latents themselves, not
-                                       standard-normal draws to be scaled by sigma0      */
+#define NQ_FLAG_INIT_DRAWS    0x2u  /* U0/V0 are standard-normal draws that the run
+                                       scales by sigma0 (without it they are the starting
+                                       latents themselves, e.g. a warm start)            */
 #define NQ_FLAG_NO_BALANCE    0x4u  /* skip magnitude balancing (U, V, scales and bits
                                        then come from the raw latents)                   */
 #define NQ_FLAG_SINGLE_STREAM 0x8u  /* no internal second stream: the r x r chain runs
@@ -141,9 +142,10 @@ nq_status nq_lbadmm_workspace_bytes(const nq_lbadmm_desc* desc, size_t* bytes);
  *   precondition -> init -> `iters` ADMM iterations -> balance -> scales ->
  *   sign packing (-> errors if NQ_FLAG_COMPUTE_ERROR).
  * Inputs (device): W m x n (ld ldw >= n), d_out (m), d_in (n), all > 0.
- *   U0 (m x r, ld r) and V0 (n x r, ld r): standard-normal draws scaled by
- *   sigma0 on device, or with NQ_FLAG_INIT_EXACT the starting latents as is.
- *   Both NULL: draws come from the built-in Philox generator and desc.seed.
+ *   U0 (m x r, ld r) and V0 (n x r, ld r): the starting latents as given, or
+ *   with NQ_FLAG_INIT_DRAWS standard-normal draws that the run scales by
+ *   sigma0. Both NULL: sigma0 times normals from the built-in Philox
+ *   generator and desc.seed.
  *   Exactly one NULL is NQ_ERR_INVALID_ARG.
  * Outputs (device, caller-owned, contiguous):
  *   U (m x r) and V (n x r): the balanced latents;

@@ -21,7 +21,7 @@ from dataclasses import dataclass
 from typing import Optional
 
 from . import _lib
-from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_EXACT, NQ_FLAG_NO_BALANCE,  # noqa: F401
+from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_DRAWS, NQ_FLAG_NO_BALANCE,  # noqa: F401
                    NQ_FLAG_PROFILE, NQ_FLAG_PROFILE_RHS_ONLY, NQ_FLAG_SINGLE_STREAM,
                    NQ_FLAG_SOLVE_CG, NQ_FLAG_SOLVE_GD, NQ_OK, PHASES, Desc, Stats)
 
@@ -568,9 +568,11 @@ class LBADMM:
     """One handle for one layer shape; reusable across runs of that shape."""
 
     def __init__(self, m, n, r, rho=1.0, iters=50, svid_steps=5, seed=0, compute_error=True,
-                 init_exact=False, balance=True, single_stream=False, profile=False,
+                 init_draws=False, balance=True, single_stream=False, profile=False,
                  solver=None):
-        """profile: False, True (every phase) or "rhs" (only the RHS GEMM).
+        """init_draws: U0/V0 passed to run() are standard-normal draws that
+        the run scales by sigma0 (default: they are the starting latents).
+        profile: False, True (every phase) or "rhs" (only the RHS GEMM).
         solver: None (the Cholesky solve) or (method, steps) with method "cg"
         (conjugate gradients) or "gd" (steepest descent): an iterative solve
         of each half's system, warm-started from the factor's previous value."""
@@ -583,7 +585,7 @@ class LBADMM:
         flags |= NQ_FLAG_PROFILE if profile else 0
         flags |= NQ_FLAG_PROFILE_RHS_ONLY if profile == "rhs" else 0
         flags |= NQ_FLAG_COMPUTE_ERROR if compute_error else 0
-        flags |= NQ_FLAG_INIT_EXACT if init_exact else 0
+        flags |= NQ_FLAG_INIT_DRAWS if init_draws else 0
         flags |= 0 if balance else NQ_FLAG_NO_BALANCE
         flags |= NQ_FLAG_SINGLE_STREAM if single_stream else 0
         self.m, self.n, self.r = int(m), int(n), int(r)
@@ -642,10 +644,10 @@ class LBADMM:
 
 
 def lbadmm(W, d_out, d_in, r, rho=1.0, iters=50, svid_steps=5, U0=None, V0=None, seed=0,
-           compute_error=True, init_exact=False, balance=True, single_stream=False,
+           compute_error=True, init_draws=False, balance=True, single_stream=False,
            solver=None) -> Result:
     """Factorise one layer: W ~ diag(s1) sign(U) sign(V)^T diag(s2)."""
     m, n = W.shape
-    with LBADMM(m, n, r, rho, iters, svid_steps, seed, compute_error, init_exact, balance,
+    with LBADMM(m, n, r, rho, iters, svid_steps, seed, compute_error, init_draws, balance,
                 single_stream, solver=solver) as h:
         return h.run(W, d_out, d_in, U0, V0)

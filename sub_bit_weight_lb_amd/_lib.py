@@ -17,7 +17,7 @@ NQ_ERR_NONFINITE = 6
 NQ_ERR_BAD_PRECONDITIONER = 7
 
 NQ_FLAG_COMPUTE_ERROR = 0x1
-NQ_FLAG_INIT_EXACT = 0x2
+NQ_FLAG_INIT_DRAWS = 0x2
 NQ_FLAG_NO_BALANCE = 0x4
 NQ_FLAG_SINGLE_STREAM = 0x8
 NQ_FLAG_PROFILE = 0x10

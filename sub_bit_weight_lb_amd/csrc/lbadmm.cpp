@@ -37,7 +37,7 @@ nq_status hip_fail(hipError_t e, const char* what) { return hip_error(e, what); 
 
 #define HIPCHK(expr) NQ_HIPCHK(expr)
 
-constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_EXACT |
+constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_DRAWS |
                                   NQ_FLAG_NO_BALANCE | NQ_FLAG_SINGLE_STREAM | NQ_FLAG_PROFILE |
                                   NQ_FLAG_PROFILE_RHS_ONLY | NQ_FLAG_SOLVE_CG | NQ_FLAG_SOLVE_GD;
 constexpr int kProfileRuns = 8;
@@ -552,8 +552,8 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
   if (ldw < h->d.n) return fail(NQ_ERR_INVALID_ARG, "ldw < n");
   if ((U0 == nullptr) != (V0 == nullptr))
     return fail(NQ_ERR_INVALID_ARG, "U0 and V0 must be both given or both NULL");
-  if ((h->d.flags & NQ_FLAG_INIT_EXACT) && !U0)
-    return fail(NQ_ERR_INVALID_ARG, "NQ_FLAG_INIT_EXACT needs U0 and V0");
+  if ((h->d.flags & NQ_FLAG_INIT_DRAWS) && !U0)
+    return fail(NQ_ERR_INVALID_ARG, "NQ_FLAG_INIT_DRAWS needs U0 and V0");
   int cur = 0;
   HIPCHK(hipGetDevice(&cur));
   if (cur != h->device) return fail(NQ_ERR_INVALID_ARG, "handle belongs to another device");
@@ -577,7 +577,7 @@ nq_status nq_lbadmm_run(nq_lbadmm_t h, const float* W, int64_t ldw, const float*
                                d.r, h->st, s));
   // init: U0 (the latent) into U, and X = U0 into the Lam buffer for SVID
   if (U0) {
-    const bool scale = !(d.flags & NQ_FLAG_INIT_EXACT);
+    const bool scale = (d.flags & NQ_FLAG_INIT_DRAWS) != 0;
     HIPCHK(launch_init_copy(U0, d.m, d.r, d.r, h->U, h->LamU, mp, rp, scale, h->st, s));
     HIPCHK(launch_init_copy(V0, d.n, d.r, d.r, h->V, h->LamV, np_, rp, scale, h->st, s));
   } else {

@@ -115,7 +115,7 @@ def test_binary_matmul_on_a_factorised_layer(gpu):
     import sub_bit_weight_lb_amd as nq
     L = make_tiny(192, 160, 40, seed=8, iters=4)
     m, n = L.W.shape
-    res = nq.LBADMM(m, n, 40, iters=4).run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu),
+    res = nq.LBADMM(m, n, 40, iters=4, init_draws=True).run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu),
                                           T(L.EU, gpu), T(L.EV, gpu))
     Vt = nq.transpose_signs(res.V_bits, n, 40)
     X = np.random.default_rng(2).standard_normal((4, n)).astype(np.float32)

@@ -72,7 +72,7 @@ def bench_run(L, iters, dev):
     wl = L.workload
     m, n = L.W.shape
     h = nq.LBADMM(m, n, wl.r, rho=wl.rho, iters=iters, svid_steps=wl.svid_steps,
-                  compute_error=True, profile=True)
+                  compute_error=True, profile=True, init_draws=True)
     res = h.run(T(L.W, dev), T(L.d_out, dev), T(L.d_in, dev), T(L.EU, dev), T(L.EV, dev))
     st = {k: H(v) for k, v in h.state().items()}
     h.close()
@@ -150,7 +150,7 @@ def test_iterative_solve_full_size_sampled(gpu, method, steps):
     wl = L.workload
     print(f"case {ATTN}: one iteration, {method} x{steps}", flush=True)
     h = nq.LBADMM(wl.m, wl.n, wl.r, rho=wl.rho, iters=1, svid_steps=wl.svid_steps,
-                  solver=(method, steps))
+                  solver=(method, steps), init_draws=True)
     h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
     U = H(h.state()["U"])
     h.close()

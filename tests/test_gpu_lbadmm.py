@@ -27,7 +27,7 @@ def run_gpu(L, r, iters, dev, rho=1.0, T_=5, balance=True, init_exact=False, U0=
     import sub_bit_weight_lb_amd as nq
     m, n = L.W.shape
     h = nq.LBADMM(m, n, r, rho=rho, iters=iters, svid_steps=T_, balance=balance,
-                  init_exact=init_exact)
+                  init_draws=not init_exact)
     U0 = L.EU if U0 is None else U0
     V0 = L.EV if V0 is None else V0
     res = h.run(T(L.W, dev), T(L.d_out, dev), T(L.d_in, dev), T(U0, dev), T(V0, dev))
@@ -118,7 +118,7 @@ def test_planted_fixed_point(gpu):
 def test_deterministic_rerun(gpu):
     import sub_bit_weight_lb_amd as nq
     L = make_tiny(300, 260, 70, seed=4, iters=3)
-    h = nq.LBADMM(300, 260, 70, iters=3)
+    h = nq.LBADMM(300, 260, 70, iters=3, init_draws=True)
     a = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
     b = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
     h.close()
@@ -146,7 +146,7 @@ def test_profile_phases(gpu, profile):
     RHS GEMM (one interval per half-iteration). Results do not depend on it."""
     import sub_bit_weight_lb_amd as nq
     L = make_tiny(300, 260, 70, seed=4, iters=3)
-    h = nq.LBADMM(300, 260, 70, iters=3, profile=profile)
+    h = nq.LBADMM(300, 260, 70, iters=3, profile=profile, init_draws=True)
     res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
     prof = h.profile(reset=True)
     h.close()
@@ -175,7 +175,7 @@ def test_launch_layouts_agree(gpu, shape, monkeypatch):
             monkeypatch.delenv("NQ_PIN", raising=False)
         else:
             monkeypatch.setenv("NQ_PIN", env)
-        h = nq.LBADMM(m, n, r, iters=2, single_stream=single)
+        h = nq.LBADMM(m, n, r, iters=2, single_stream=single, init_draws=True)
         res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
         outs[name] = {k: H(v) for k, v in h.state().items()}
         h.close()
@@ -225,7 +225,7 @@ def test_finish_matches_oracle_on_gpu_state(gpu):
     L = make_tiny(300, 260, 70, seed=9, iters=3)
     m, n = L.W.shape
     r = 70
-    h = nq.LBADMM(m, n, r, iters=3)
+    h = nq.LBADMM(m, n, r, iters=3, init_draws=True)
     res = h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
     st = {k: H(v).astype(np.float64) for k, v in h.state().items()}
     h.close()
@@ -257,7 +257,8 @@ def test_iterative_solve_iterations(gpu, method, steps, shape):
     Wt = O.precondition(L.W, L.d_out, L.d_in)
     for iters in (1, 2):
         print(f"case {method} x{steps} {shape} iters={iters}", flush=True)
-        h = nq.LBADMM(m, n, r, iters=iters, balance=False, solver=(method, steps))
+        h = nq.LBADMM(m, n, r, iters=iters, balance=False, solver=(method, steps),
+                      init_draws=True)
         h.run(T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(L.EU, gpu), T(L.EV, gpu))
         st = {k: H(v) for k, v in h.state().items()}
         h.close()
@@ -282,3 +283,33 @@ def test_iterative_solve_rejects_bad_desc(gpu):
                          solve_steps=3)
     with pytest.raises(nq.NQError):
         nq.lbadmm_create(64, 48, 8, solve_steps=3)
+
+
+def test_warm_start_is_taken_as_given(gpu):
+    """Without NQ_FLAG_INIT_DRAWS, U0 and V0 are the starting latents: at
+    iters = 0 the state holds them bit for bit and Z = SVID(U0), SVID(V0);
+    with the flag the same arrays are draws scaled by sigma0."""
+    import sub_bit_weight_lb_amd as nq
+    m, n, r = 200, 150, 40
+    L = make_tiny(m, n, r, seed=17)
+    rng = np.random.default_rng(5)
+    U0 = (0.05 * rng.standard_normal((m, r))).astype(np.float32)
+    V0 = (0.05 * rng.standard_normal((n, r))).astype(np.float32)
+    args = (T(L.W, gpu), T(L.d_out, gpu), T(L.d_in, gpu), T(U0, gpu), T(V0, gpu))
+    Wt = O.precondition(L.W, L.d_out, L.d_in)
+    for draws in (False, True):
+        h = nq.LBADMM(m, n, r, iters=0, balance=False, init_draws=draws)
+        res = h.run(*args)
+        st = {k: H(v) for k, v in h.state().items()}
+        h.close()
+        if draws:
+            s0 = np.float32(res.stats["sigma0"])
+            np.testing.assert_array_equal(st["U"], s0 * U0)
+            np.testing.assert_array_equal(st["V"], s0 * V0)
+            ref = O.init_state(Wt, r, 5, EU=U0, EV=V0)
+        else:
+            np.testing.assert_array_equal(st["U"], U0)
+            np.testing.assert_array_equal(st["V"], V0)
+            ref = O.init_state(Wt, r, 5, U0=U0, V0=V0)
+        for k, X in (("Z_U", ref.U), ("Z_V", ref.V)):
+            assert masked_rel(st[k], getattr(ref, k), X) < 1e-4, (draws, k)

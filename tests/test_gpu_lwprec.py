@@ -115,7 +115,7 @@ def test_lw_feeds_the_factorisation(gpu):
     np.testing.assert_allclose(H(d_in), di_ref, rtol=1e-5)
     EU = rng.standard_normal((m, r)).astype(np.float32)
     EV = rng.standard_normal((n, r)).astype(np.float32)
-    h = nq.LBADMM(m, n, r, iters=1, balance=False)
+    h = nq.LBADMM(m, n, r, iters=1, balance=False, init_draws=True)
     h.run(T(W, gpu), d_out, d_in, T(EU, gpu), T(EV, gpu))
     st = {k: H(v) for k, v in h.state().items()}
     h.close()
