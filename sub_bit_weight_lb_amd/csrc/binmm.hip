@@ -219,6 +219,19 @@ __global__ __launch_bounds__(256) void bin_mfma_kernel(
   }
 }
 
+// part[e] = part[e] + part[e + stride] + ... (nsum slots, added in slot
+// order, the order the second product's staging would add them), for the
+// n = B r elements of the first slot, in place
+__global__ void bin_sum_partials_kernel(float* __restrict__ part, int nsum, int64_t stride,
+                                        int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    float y = part[e];
+    for (int z = 1; z < nsum; ++z) y += part[e + z * stride];
+    part[e] = y;
+  }
+}
+
 // out (cols x ld_out words) bit (c, i) = in bit (i, c), in holding rows x cols
 // signs (rows x ld_in words). Wave (row block of 64, input word cw): lane l
 // reads the word of row 64 q + l; the ballot of bit j over the lanes is
@@ -336,7 +349,15 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
     int64_t sp = std::min<int64_t>((1024 + wgs - 1) / wgs, kBinSplit);
     sp = std::max<int64_t>(1, std::min<int64_t>(sp, ((n + 31) / 32 + 7) / 8));
     rowdot_mfma<1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, (int)sp, B, s);
-    rowdot_mfma<kBinSplit>(su, ldu, m, r, T, r, (int)sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
+    // the partials summed once (in slot order) rather than by every row
+    // block of the second product while it stages its input
+    if (sp > 1) {
+      const int64_t ne = B * r;
+      hipLaunchKernelGGL(bin_sum_partials_kernel,
+                         dim3((unsigned)std::min<int64_t>((ne + 255) / 256, 4096)), dim3(256), 0, s,
+                         T, (int)sp, ne, ne);
+    }
+    rowdot_mfma<1>(su, ldu, m, r, T, r, 1, 0, nullptr, s1, Y, ldy, 0, 1, B, s);
     return hipGetLastError();
   }
   // (below 4096 rows and for one or two inputs, 16 rows per workgroup: 64
@@ -349,11 +370,20 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
     rowdot_any<kRpw2, 1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, sp, B, s);
   // Y = s1 * (T S_U^T): the m rows of S_U against the sum of the partials
   // (more than two inputs: 64 rows per workgroup, so each table serves more
-  // rows; one or two: 16, for a wider grid)
-  if (B > 2)
-    rowdot_any<kRpw1, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
-  else
+  // rows; one or two: 16, for a wider grid). With more than two inputs the
+  // partials are summed once first (in slot order, as the staging would):
+  // each of the m / 64 row blocks would otherwise load all of them.
+  if (B > 2) {
+    if (sp > 1) {
+      const int64_t ne = B * r;
+      hipLaunchKernelGGL(bin_sum_partials_kernel,
+                         dim3((unsigned)std::min<int64_t>((ne + 255) / 256, 4096)), dim3(256), 0, s,
+                         T, sp, ne, ne);
+    }
+    rowdot_any<kRpw1, 1>(su, ldu, m, r, T, r, 1, 0, nullptr, s1, Y, ldy, 0, 1, B, s);
+  } else {
     rowdot_any<kRpw2, kBinSplit>(su, ldu, m, r, T, r, sp, B * r, nullptr, s1, Y, ldy, 0, 1, B, s);
+  }
   return hipGetLastError();
 }
 
