@@ -156,21 +156,29 @@ __global__ __launch_bounds__(256) void bin_rowdot_kernel(
 // out[b][n] = sum_k v[b][k] sign(n, k), i.e. a (B x K) x (K x N) product
 // whose right operand is +-1, exact in fp32. v_mfma_f32_16x16x4f32 takes
 // A[b][k] for b = lane % 16, k = lane / 16 (from the inputs staged in LDS)
-// and B[k][n] for n = lane % 16 (+-1 from bit k of row n's word, one word
-// load per 8 MFMA steps); lane l ends with out[4 (l / 16) + v][n]. Four waves,
-// 16 rows (n) each; inputs staged 256 columns at a time (the sum of nsum
-// partial vectors, times pre). Sums run in a fixed order.
-template <int NS>
+// and B[k][n] for n = lane % 16 (+-1 from bit k of row n's word); lane l
+// ends with out[4 (l / 16) + v][n]. Inputs are staged 256 columns at a time
+// (the sum of nsum partial vectors, times pre). Two layouts:
+//   SPLITW: a workgroup takes 16 rows and its four waves split each stage's
+//     8 words (two each), so a wave's chain of dependent matrix steps is a
+//     quarter of the row's; the waves' partial tiles are added through LDS
+//     in wave order at the end (for grids that would otherwise be small);
+//   otherwise: 64 rows, 16 per wave, each wave taking every word (each
+//     staged input serves four times the rows; for wide grids).
+// Sums run in a fixed order.
+template <int NS, bool SPLITW>
 __global__ __launch_bounds__(256) void bin_mfma_kernel(
     const uint32_t* __restrict__ bits, int64_t ldw, int64_t rows, int64_t cols,
     const float* __restrict__ v, int64_t ldv, int nsum, int64_t vstride,
     const float* __restrict__ pre, const float* __restrict__ post, float* __restrict__ out,
     int64_t ldo, int64_t ostride, int64_t wsplit, int64_t B) {
   constexpr int KC = 256;                 // input columns per stage
+  constexpr int WPW = SPLITW ? KC / 32 / 4 : KC / 32;  // words per wave per stage
   __shared__ float zs[16][KC + 4];
+  __shared__ f32x4 red[3][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t b0 = (int64_t)blockIdx.y * 16;
-  const int64_t n = ((int64_t)blockIdx.x * 4 + wave) * 16 + (lane & 15);
+  const int64_t n = (SPLITW ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + wave) * 16 + (lane & 15);
   const int64_t nw = (cols + 31) / 32;
   const int64_t w_lo = (int64_t)blockIdx.z * wsplit;
   const int64_t w_hi = min(nw, w_lo + wsplit);
@@ -197,10 +205,13 @@ __global__ __launch_bounds__(256) void bin_mfma_kernel(
       zs[bb][k] = y;
     }
     __syncthreads();
-    const int64_t wend = min(w_hi, wc + KC / 32);
-    for (int64_t w = wc; w < wend; ++w) {
+#pragma unroll
+    for (int u = 0; u < WPW; ++u) {
+      const int wi = SPLITW ? WPW * wave + u : u;   // word within the stage
+      const int64_t w = wc + wi;
+      if (w >= w_hi) break;
       const uint32_t word = n < rows ? bits[n * ldw + w] : 0u;
-      const int kb = (int)(w - wc) * 32;
+      const int kb = wi * 32;
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8) {
         const int k = 4 * s8 + kq;
@@ -210,7 +221,12 @@ __global__ __launch_bounds__(256) void bin_mfma_kernel(
       }
     }
   }
-  if (n < rows) {
+  if (SPLITW) {
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) acc = ((acc + red[0][lane]) + red[1][lane]) + red[2][lane];
+  }
+  if ((!SPLITW || wave == 0) && n < rows) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t b = b0 + 4 * kq + q;
@@ -287,9 +303,18 @@ void rowdot_mfma(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, 
                  float* out, int64_t ldo, int64_t ostride, int split, int64_t B, hipStream_t s) {
   const int64_t nw = (cols + 31) / 32;
   const int64_t wsplit = ((nw + split - 1) / split + 7) / 8 * 8;
-  const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((B + 15) / 16), (unsigned)split);
-  hipLaunchKernelGGL((bin_mfma_kernel<NS>), grid, dim3(256), 0, s, bits, ldw, rows, cols, v, ldv,
-                     nsum, vstride, pre, post, out, ldo, ostride, wsplit, B);
+  // 16-row workgroups with the words split over the waves when 64-row ones
+  // would leave the chip under-filled (fewer than 512 workgroups)
+  const int64_t g64 = ((rows + 63) / 64) * ((B + 15) / 16) * split;
+  if (g64 < 512) {
+    const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((B + 15) / 16), (unsigned)split);
+    hipLaunchKernelGGL((bin_mfma_kernel<NS, true>), grid, dim3(256), 0, s, bits, ldw, rows, cols, v,
+                       ldv, nsum, vstride, pre, post, out, ldo, ostride, wsplit, B);
+  } else {
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((B + 15) / 16), (unsigned)split);
+    hipLaunchKernelGGL((bin_mfma_kernel<NS, false>), grid, dim3(256), 0, s, bits, ldw, rows, cols,
+                       v, ldv, nsum, vstride, pre, post, out, ldo, ostride, wsplit, B);
+  }
 }
 
 template <int RPW, int NS>
@@ -344,7 +369,7 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
   if (B >= 9) {
     // nine or more inputs: the matrix-core form, 16 inputs per pass (one
     // pass costs about what four passes of two inputs through the tables
-    // cost); the first product split as below, over 64-row workgroups
+    // cost); the first product split as below, counted in 64-row blocks
     const int64_t wgs = ((r + 63) / 64) * ((B + 15) / 16);
     int64_t sp = std::min<int64_t>((1024 + wgs - 1) / wgs, kBinSplit);
     sp = std::max<int64_t>(1, std::min<int64_t>(sp, ((n + 31) / 32 + 7) / 8));
