@@ -321,7 +321,8 @@ nq_status nq_ste_set_params(nq_ste_t h, const float* U, const float* V, const fl
                             const float* s2, void* stream);
 
 /* One step on T tokens (1 .. max_tokens): rows t of the batch are
- * X[rows[t]] and Y[rows[t]] (rows: device int32, or NULL for rows 0 .. T-1);
+ * X[rows[t]] and Y[rows[t]] (rows: device int32, or NULL for rows 0 .. T-1;
+ * every index must be a row of X and Y: the library cannot check it);
  * X (row stride ldx >= n) and Y (ldy >= m) device float32. Computes the loss
  * of the current parameters on the batch (kept for nq_ste_last_loss) and
  * takes one Adam step with learning rate lr (finite, >= 0). Asynchronous on

@@ -145,3 +145,26 @@ def test_lw_full_size_chunked(gpu):
     _, s_sk = ledoit_wolf(Z64, assume_centered=True)
     print(f"  shrinkage gpu {s:.8f} sklearn {s_sk:.8f}", flush=True)
     assert abs(s - s_sk) <= 1e-5 + 1e-4 * s_sk
+
+
+def test_lw_wide_features(gpu):
+    """11008 features (the output width of a Llama-2-7B MLP projection, past
+    the ADMM path's largest rank), 640 tokens in chunks of 256 (the last
+    ragged): the estimator's form with exact S_jj, and the intensity
+    against scikit-learn."""
+    from sklearn.covariance import ledoit_wolf
+    import sub_bit_weight_lb_amd as nq
+    N, p = 640, 11008
+    Z = make_activations(N, p, seed=21)
+    print(f"case N={N} p={p}", flush=True)
+    with nq.LedoitWolf(p, 256) as lw:
+        lw.accumulate(T(Z, gpu))
+        d, s = lw.finalize()
+    d = H(d).astype(np.float64)
+    Z64 = Z.astype(np.float64)
+    Sjj = np.einsum("kj,kj->j", Z64, Z64) / N
+    m = Sjj.mean()
+    np.testing.assert_allclose(d ** 2, (1 - s) * Sjj + s * m, rtol=2e-5)
+    _, s_sk = ledoit_wolf(Z64, assume_centered=True)
+    print(f"  shrinkage gpu {s:.8f} sklearn {s_sk:.8f}", flush=True)
+    assert abs(s - s_sk) <= 1e-5 + 1e-4 * s_sk
