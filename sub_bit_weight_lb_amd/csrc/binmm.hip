@@ -39,6 +39,9 @@ namespace {
 
 constexpr int CW = 64;   // words per column chunk, one per lane
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ inline float wave_sum64(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -235,6 +238,172 @@ __global__ __launch_bounds__(256) void bin_mfma_kernel(
   }
 }
 
+// The same row dots for up to 16 inputs at once on the bf16 matrix cores,
+// exactly: +-1 is exact in bf16, and each input x is split into three bf16
+// terms x = h + m + l by truncation (h = the top 16 bits of x, m the top 16
+// bits of x - h, l = x - h - m, which has at most 8 significant bits), so
+// every product is exact and only the fp32 accumulation rounds.
+// v_mfma_f32_16x16x32_bf16 takes A[b][k] from lane b + 16 (k / 8), element
+// k % 8, B[k][n] from lane n + 16 (k / 8), and leaves D[4 (l / 16) + v][l % 16]
+// in lane l, element v. The order of k within a product is free, so lane
+// group g (lanes 16 g .. 16 g + 15) of wave w takes word 4 g + w of the
+// stage and, in step s (0..3), its bits 4 s + d and 4 s + d + 16 (d = 0..3)
+// as elements 2 d and 2 d + 1. Both land at bits 15 and 31 of one dword with
+// a single shift, and (w << (15 - 4 s - d)) & 0x80008000 | 0x3F803F80 is
+// the pair (-+1, -+1) in bf16: bit 1 gives -1, so the accumulator holds
+// minus the row dot and is negated at the end (exact). The inputs are
+// staged in LDS in the same pair order: dword j (< 16) of a word holds
+// (x[32 w + j], x[32 w + j + 16]) as bf16, one array per term.
+//
+// A workgroup takes RT row tiles of 16 rows; a stage is 16 words (512
+// columns), of which each wave takes four, for all RT tiles; the waves'
+// partial tiles are added through LDS in wave order at the end. The next
+// stage's inputs and sign words are fetched into registers while the
+// current one computes. Loads go through buffer descriptors: an element
+// outside the inputs, the rows or the workgroup's words gets an offset past
+// the descriptor's range and reads 0, so no load needs a branch.
+// Sums run in a fixed order.
+constexpr int kBfWords = 16;                   // words per stage
+constexpr int kBfRow = kBfWords * 16 + 4;      // dwords per staged input row (+ pad)
+constexpr uint32_t kBfOut = 0x80000000u;       // an offset past every descriptor's range
+constexpr int kBufFlags = 0x00020000;          // raw buffer, 32-bit data
+
+template <int RT, bool PRE>
+__global__ __launch_bounds__(256) void bin_bf16_kernel(
+    const uint32_t* __restrict__ bits, int64_t ldw, int64_t rows, int64_t cols,
+    const float* __restrict__ v, int64_t ldv, const float* __restrict__ pre,
+    const float* __restrict__ post, float* __restrict__ out, int64_t ldo, int64_t ostride,
+    int64_t wsplit, int64_t B) {
+  __shared__ __align__(16) uint32_t zs[3][16][kBfRow];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+  const int64_t b0 = (int64_t)blockIdx.y * 16;
+  const int64_t row0 = (int64_t)blockIdx.x * (16 * RT);
+  const int64_t nw = (cols + 31) / 32;
+  const int64_t w_lo = (int64_t)blockIdx.z * wsplit;
+  const int64_t w_hi = min(nw, w_lo + wsplit);
+  out += (int64_t)blockIdx.z * ostride;
+  // inputs b0 .. b0 + nb - 1, columns < cols: the descriptor ends after the
+  // last one (rows past nb start beyond it, as ldv >= cols)
+  const int64_t nb = min<int64_t>(16, B - b0);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(v + b0 * ldv), (short)0, (int)(((nb - 1) * ldv + cols) * 4), kBufFlags);
+  // rows row0 .. min(rows, row0 + 16 RT) - 1, every word of each
+  const int64_t nr = min<int64_t>(16 * RT, rows - row0);
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(bits + row0 * ldw), (short)0, (int)(((nr - 1) * ldw + nw) * 4), kBufFlags);
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(PRE ? pre : v), (short)0, PRE ? (int)(cols * 4) : 0, kBufFlags);
+  // staging map: thread t takes pair j = t % 16 of word t / 16 for each of
+  // the 16 inputs. Byte offsets are 32-bit: a valid one is below 2^31, an
+  // invalid one has bit 31 set, and no sum passes 2^32 (the host bounds the
+  // strides).
+  const int sj = threadIdx.x & 15, sw = threadIdx.x >> 4;
+  const uint32_t bro = (uint32_t)(li * ldw * 4);   // this lane's row in a tile
+  float xa[16], xb[16], pa = 1.0f, pb = 1.0f;   // raw inputs and their scales
+  uint32_t bw[RT];
+  auto fetch = [&](int64_t wst) {
+    const int64_t w = wst + sw;
+    const int64_t ca = w * 32 + sj, cb = ca + 16;
+    const bool okw = w < w_hi;
+    const uint32_t oa = (uint32_t)(ca * 4) | (okw && ca < cols ? 0u : kBfOut);
+    const uint32_t ob = (uint32_t)(cb * 4) | (okw && cb < cols ? 0u : kBfOut);
+    if (PRE) {
+      pa = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, oa, 0, 0));
+      pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(pr, ob, 0, 0));
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t ro = (uint32_t)(u * ldv * 4);
+      const float ya = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, oa + ro, 0, 0));
+      const float yb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vr, ob + ro, 0, 0));
+      xa[u] = ya;
+      xb[u] = yb;
+    }
+    const int64_t w2 = wst + 4 * g + wave;   // this lane's word
+    const uint32_t wo = (uint32_t)(w2 * 4) | (w2 < w_hi ? 0u : kBfOut);
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+      bw[t] = __builtin_amdgcn_raw_buffer_load_b32(br, bro + (uint32_t)(16 * t * ldw * 4) + wo, 0, 0);
+  };
+  // the sign masks held in registers, so that each dword of signs takes a
+  // shift and one and-or
+  uint32_t smask = 0x80008000u, sone = 0x3F803F80u;
+  asm volatile("" : "+v"(smask), "+v"(sone));
+  f32x4 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (w_lo < w_hi) fetch(w_lo);
+  for (int64_t wst = w_lo; wst < w_hi; wst += kBfWords) {
+    __syncthreads();  // the previous stage's terms are consumed
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float xu = PRE ? xa[u] * pa : xa[u], yu = PRE ? xb[u] * pb : xb[u];
+      const uint32_t ua = __float_as_uint(xu), ub = __float_as_uint(yu);
+      const float ra = xu - __uint_as_float(ua & 0xffff0000u);
+      const float rb = yu - __uint_as_float(ub & 0xffff0000u);
+      const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
+      const float la = ra - __uint_as_float(va & 0xffff0000u);
+      const float lb = rb - __uint_as_float(vb & 0xffff0000u);
+      const uint32_t wa = __float_as_uint(la), wb = __float_as_uint(lb);
+      uint32_t* z = &zs[0][u][sw * 16 + sj];
+      z[0] = (ua >> 16) | (ub & 0xffff0000u);
+      z[16 * kBfRow] = (va >> 16) | (vb & 0xffff0000u);
+      z[32 * kBfRow] = (wa >> 16) | (wb & 0xffff0000u);
+    }
+    __syncthreads();
+    uint32_t bc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) bc[t] = bw[t];
+    if (wst + kBfWords < w_hi) fetch(wst + kBfWords);
+    const int wl = 4 * g + wave;   // this lane's word in the stage
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int off = li * kBfRow + wl * 16 + 4 * s;
+      const bf16x8 ah = __builtin_bit_cast(bf16x8, *(const u32x4*)&zs[0][0][off]);
+      const bf16x8 am = __builtin_bit_cast(bf16x8, *(const u32x4*)&zs[1][0][off]);
+      const bf16x8 al = __builtin_bit_cast(bf16x8, *(const u32x4*)&zs[2][0][off]);
+      bf16x8 bs[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        u32x4 sg;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) sg[d] = ((bc[t] << (15 - 4 * s - d)) & smask) | sone;
+        bs[t] = __builtin_bit_cast(bf16x8, sg);
+      }
+      // the terms in order h, m, l for every tile; consecutive products
+      // are independent
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bs[t], acc[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am, bs[t], acc[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bs[t], acc[t], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with the staged terms
+  f32x4* red = (f32x4*)&zs[0][0][0];   // [wave][t][lane]
+#pragma unroll
+  for (int t = 0; t < RT; ++t) red[(wave * RT + t) * 64 + lane] = acc[t];
+  __syncthreads();
+  // wave w finishes tiles w, w + 4, ...: the four partials in wave order
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    if ((t & 3) != wave) continue;
+    const f32x4 a = ((red[(0 * RT + t) * 64 + lane] + red[(1 * RT + t) * 64 + lane]) +
+                     red[(2 * RT + t) * 64 + lane]) +
+                    red[(3 * RT + t) * 64 + lane];
+    const int64_t n = row0 + 16 * t + li;
+    if (n >= rows) continue;
+    const float pn = post ? post[n] : 1.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = b0 + 4 * g + q;
+      if (b < B) out[b * ldo + n] = post ? -a[q] * pn : -a[q];
+    }
+  }
+}
+
 // part[e] = part[e] + part[e + stride] + ... (nsum slots, added in slot
 // order, the order the second product's staging would add them), for the
 // n = B r elements of the first slot, in place
@@ -317,6 +486,49 @@ void rowdot_mfma(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, 
   }
 }
 
+// The bf16 matrix-core row dots: workgroups of RT row tiles whose waves
+// split the words, RT as large as leaves at least kBfMinWgs workgroups (one
+// tile when even that does not). More rows per workgroup share each staged
+// (and split) input among more tiles; more workgroups fill the chip.
+constexpr int64_t kBfMinWgs = 512;
+
+template <int RT, bool PRE>
+void launch_bf16(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
+                 int64_t ldv, const float* pre, const float* post, float* out, int64_t ldo,
+                 int64_t ostride, int split, int64_t wsplit, int64_t B, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 16 * RT - 1) / (16 * RT)), (unsigned)((B + 15) / 16),
+                  (unsigned)split);
+  hipLaunchKernelGGL((bin_bf16_kernel<RT, PRE>), grid, dim3(256), 0, s, bits, ldw, rows, cols, v,
+                     ldv, pre, post, out, ldo, ostride, wsplit, B);
+}
+
+template <bool PRE>
+void rowdot_bf16_t(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
+                   int64_t ldv, const float* pre, const float* post, float* out, int64_t ldo,
+                   int64_t ostride, int split, int64_t B, hipStream_t s) {
+  const int64_t nw = (cols + 31) / 32;
+  const int64_t wsplit = ((nw + split - 1) / split + kBfWords - 1) / kBfWords * kBfWords;
+  const int64_t bt = (B + 15) / 16;
+  auto wgs = [&](int rt) { return (rows + 16 * rt - 1) / (16 * rt) * bt * split; };
+  if (wgs(8) >= kBfMinWgs)
+    launch_bf16<8, PRE>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, ostride, split, wsplit, B, s);
+  else if (wgs(4) >= kBfMinWgs)
+    launch_bf16<4, PRE>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, ostride, split, wsplit, B, s);
+  else if (wgs(2) >= kBfMinWgs)
+    launch_bf16<2, PRE>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, ostride, split, wsplit, B, s);
+  else
+    launch_bf16<1, PRE>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, ostride, split, wsplit, B, s);
+}
+
+void rowdot_bf16(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
+                 int64_t ldv, const float* pre, const float* post, float* out, int64_t ldo,
+                 int64_t ostride, int split, int64_t B, hipStream_t s) {
+  if (pre)
+    rowdot_bf16_t<true>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, ostride, split, B, s);
+  else
+    rowdot_bf16_t<false>(bits, ldw, rows, cols, v, ldv, pre, post, out, ldo, ostride, split, B, s);
+}
+
 template <int RPW, int NS>
 void rowdot_any(const uint32_t* bits, int64_t ldw, int64_t rows, int64_t cols, const float* v,
                 int64_t ldv, int nsum, int64_t vstride, const float* pre, const float* post,
@@ -362,7 +574,14 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
                                 float* Y, int64_t ldy, float* T, hipStream_t s) {
   if (m <= 0 || n <= 0 || r <= 0 || B <= 0) return hipSuccess;
   if ((r + 4 * kRpw2 - 1) / (4 * kRpw2) > 0x7fffffff || (m + 4 * kRpw2 - 1) / (4 * kRpw2) > 0x7fffffff ||
-      (B + 15) / 16 > 65535)
+      (B + 15) / 16 > 65535 || n > 0x7fffffff || r > 0x7fffffff)
+    return hipErrorInvalidValue;
+  // the matrix-core kernel's 32-bit byte offsets: 16 rows of an input plus
+  // a stage past its width, or 128 rows of signs plus a row's words, stay
+  // below 2^31 bytes
+  if (B >= 9 && (16 * std::max(ldx, r) + std::max(n, r) + 1024) * 4 >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  if (B >= 9 && (128 * std::max(ldu, ldvt) + std::max(ldu, ldvt)) * 4 >= (int64_t(1) << 31))
     return hipErrorInvalidValue;
   // T = (X * s2) S_V: the r rows of S_V^T against x, their words split over
   // sp workgroups, each writing a partial T (sp x B x r)
@@ -372,8 +591,8 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
     // cost); the first product split as below, counted in 64-row blocks
     const int64_t wgs = ((r + 63) / 64) * ((B + 15) / 16);
     int64_t sp = std::min<int64_t>((1024 + wgs - 1) / wgs, kBinSplit);
-    sp = std::max<int64_t>(1, std::min<int64_t>(sp, ((n + 31) / 32 + 7) / 8));
-    rowdot_mfma<1>(svt, ldvt, r, n, X, ldx, 1, 0, s2, nullptr, T, r, B * r, (int)sp, B, s);
+    sp = std::max<int64_t>(1, std::min<int64_t>(sp, ((n + 31) / 32 + kBfWords - 1) / kBfWords));
+    rowdot_bf16(svt, ldvt, r, n, X, ldx, s2, nullptr, T, r, B * r, (int)sp, B, s);
     // the partials summed once (in slot order) rather than by every row
     // block of the second product while it stages its input
     if (sp > 1) {
@@ -382,7 +601,7 @@ hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t*
                          dim3((unsigned)std::min<int64_t>((ne + 255) / 256, 4096)), dim3(256), 0, s,
                          T, (int)sp, ne, ne);
     }
-    rowdot_mfma<1>(su, ldu, m, r, T, r, 1, 0, nullptr, s1, Y, ldy, 0, 1, B, s);
+    rowdot_bf16(su, ldu, m, r, T, r, nullptr, s1, Y, ldy, 0, 1, B, s);
     return hipGetLastError();
   }
   // (below 4096 rows and for one or two inputs, 16 rows per workgroup: 64
