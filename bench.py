@@ -362,7 +362,7 @@ def binary_bench(nq, torch, dev, reps=20, replays=5):
         for B in (1, 8, 16):
             X = torch.randn(B, n, generator=g).to(dev)
             Y = torch.empty(B, m, device=dev)
-            work = torch.empty(8 * B * r, device=dev)
+            work = torch.empty(nq.binary_matmul_work_floats(B, n, r), device=dev)
             nq.binary_matmul(U[0], Vt[0], s1, s2, X, r, Y=Y, work=work)
             ref = Y.clone()
             res = {"m": m, "n": n, "r": r, "B": B}

@@ -232,23 +232,32 @@ nq_status nq_transpose_signs(const uint32_t* in, int64_t rows, int64_t cols, int
  *   Vt_bits r x ldvt words (ldvt >= ceil(n/32)): S_V^T (nq_transpose_signs of V_bits);
  *   s1 (m), s2 (n) float32; X: B x n float32, row stride ldx >= n;
  *   Y: B x m float32, row stride ldy >= m (written, not read);
- *   work: 8 * B * r float32 of caller scratch (partial sums of the r
- *         projections per input).
- * Two launches on `stream`, no allocation, no host synchronisation. Sums run
- * in a fixed order, so results are bit-reproducible. m == 0 or B == 0 is a
- * no-op; otherwise n, r >= 1. NQ_ERR_INVALID_ARG for bad sizes or strides. */
+ *   work: nq_binary_matmul_work_floats(B, n, r) float32 of caller scratch
+ *         (partial sums of the r projections per input, then the inputs
+ *         as bf16 terms), 16-byte aligned.
+ * One input: two launches (lookup tables). Two or more: four (the inputs
+ * split into exact bf16 terms, the matrix-core product, the same for the
+ * projections). All on `stream`, no allocation, no host synchronisation.
+ * Sums run in a fixed order, so results are bit-reproducible. m == 0 or
+ * B == 0 is a no-op; otherwise n, r >= 1. NQ_ERR_INVALID_ARG for bad sizes
+ * or strides. */
 nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits,
                            int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
                            const float* s2, const float* X, int64_t B, int64_t ldx, float* Y,
                            int64_t ldy, float* work, void* stream);
 
+/* Floats of `work` that nq_binary_matmul needs for B inputs of width n and
+ * rank r: 8 B r (rounded up to 64) + 3072 ceil(B / 16) ceil(max(n, r) / 128).
+ * Host only; -1 for negative sizes. */
+int64_t nq_binary_matmul_work_floats(int64_t B, int64_t n, int64_t r);
+
 /* nq_binary_matmul for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses
  * that forbid allocation. The same arguments and result (bit for bit) as
- * nq_binary_matmul without `work`: the partial sums go to a fixed scratch
- * array of 2^22 float32 (16 MiB) in the library, one per GPU, taken on the
- * first call on a device (the current device) and held until the process
- * ends. Limit: B * r <= 2^19 (8 B r floats must fit), else
+ * nq_binary_matmul without `work`: the workspace is a fixed scratch array
+ * of 2^23 float32 (32 MiB) in the library, one per GPU, taken on the first
+ * call on a device (the current device) and held until the process ends.
+ * Limit: nq_binary_matmul_work_floats(B, n, r) <= 2^23, else
  * NQ_ERR_INVALID_ARG before any device work. Calls no allocating routine.
  * Every call on one GPU uses that GPU's one array: calls whose device work
  * overlaps (other streams, other threads) race and give wrong results; calls

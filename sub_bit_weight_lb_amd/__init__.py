@@ -28,7 +28,7 @@ from ._lib import (NQ_FLAG_COMPUTE_ERROR, NQ_FLAG_INIT_DRAWS, NQ_FLAG_NO_BALANCE
 __all__ = [
     "NQError", "lbadmm_create", "lbadmm_run", "lbadmm_query", "lbadmm_get_state",
     "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "transpose_signs",
-    "binary_matmul", "binary_matmul_noalloc", "LedoitWolf", "ledoit_wolf_diag",
+    "binary_matmul", "binary_matmul_noalloc", "binary_matmul_work_floats", "LedoitWolf", "ledoit_wolf_diag",
     "preconditioners", "STERefiner", "cosine_lr", "op_precondition", "op_gram",
     "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
@@ -210,11 +210,24 @@ def transpose_signs(bits, rows, cols, out=None, stream=None):
     return out
 
 
+def binary_matmul_work_floats(B, n, r):
+    """Floats of workspace binary_matmul needs for B inputs of width n and
+    rank r: the formula of nq_binary_matmul_work_floats (8 partial sums per
+    input and rank, rounded up to 64 floats, then the inputs' bf16 terms,
+    3072 floats per 16 inputs and 128 columns of the wider product),
+    computed here so that buffer checks need no library call."""
+    B, n, r = int(B), int(n), int(r)
+    if B < 0 or n < 0 or r < 0:
+        return -1
+    return -(-8 * B * r // 64) * 64 + 3072 * (-(-B // 16)) * (-(-max(n, r) // 128))
+
+
 def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None):
     """Y = X W^T for the factorised layer W = diag(s1) S_U S_V^T diag(s2):
     U_bits (m x ceil(r/32) int32), Vt_bits (r x ceil(n/32) int32, from
     transpose_signs of the run's V_bits), s1 (m), s2 (n), X (B x n float32,
-    or a vector of length n); work, if given, holds 8 B r float32. Returns Y
+    or a vector of length n); work, if given, holds
+    binary_matmul_work_floats(B, n, r) float32 (16-byte aligned). Returns Y
     (B x m, or length m)."""
     torch = _torch()
     vec = X.dim() == 1
@@ -224,10 +237,13 @@ def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None)
     B, n = X2.shape
     m = _check_binmm_shapes(U_bits, Vt_bits, s1, s2, n, r)
     Y2 = _binmm_out(Y, B, m, vec, X.device)
+    need = binary_matmul_work_floats(B, n, r)
     if work is None:
-        work = torch.empty((max(8 * B * r, 1),), dtype=torch.float32, device=X.device)
-    elif work.numel() < 8 * B * r:
-        raise ValueError(f"work holds {work.numel()} floats, needs 8 * B * r = {8 * B * r}")
+        work = torch.empty((max(need, 1),), dtype=torch.float32, device=X.device)
+    elif work.numel() < need:
+        raise ValueError(f"work holds {work.numel()} floats, needs {need}")
+    elif work.data_ptr() % 16:
+        raise ValueError("work must be 16-byte aligned")
     _check(_lib.load().nq_binary_matmul(
         _ptr(U_bits, "U_bits", torch.int32, 2, need_contig=False), U_bits.stride(0),
         _ptr(Vt_bits, "Vt_bits", torch.int32, 2, need_contig=False), Vt_bits.stride(0),
@@ -238,16 +254,17 @@ def binary_matmul(U_bits, Vt_bits, s1, s2, X, r, Y=None, work=None, stream=None)
     return Y2[0] if vec else Y2
 
 
-# B * r limit of binary_matmul_noalloc: its fixed scratch holds 2^22 floats,
-# eight partial sums per input and rank
-NOALLOC_MAX_BR = 1 << 19
+# Workspace limit of binary_matmul_noalloc: its fixed scratch holds 2^23
+# floats, so binary_matmul_work_floats(B, n, r) must not exceed that
+NOALLOC_MAX_FLOATS = 1 << 23
 
 
 def binary_matmul_noalloc(U_bits, Vt_bits, s1, s2, X, r, Y, stream=None):
     """binary_matmul into a caller-given Y with no device allocation: the
-    library's fixed per-GPU scratch holds the partial sums, so B * r must not
-    exceed NOALLOC_MAX_BR. Calls that overlap on one GPU race; calls ordered
-    on one stream do not. Returns Y."""
+    library's fixed per-GPU scratch is the workspace, so
+    binary_matmul_work_floats(B, n, r) must not exceed NOALLOC_MAX_FLOATS.
+    Calls that overlap on one GPU race; calls ordered on one stream do not.
+    Returns Y."""
     torch = _torch()
     vec = X.dim() == 1
     X2 = X.unsqueeze(0) if vec else X
@@ -258,8 +275,10 @@ def binary_matmul_noalloc(U_bits, Vt_bits, s1, s2, X, r, Y, stream=None):
     if Y is None:
         raise ValueError("Y is required: this entry point allocates nothing")
     Y2 = _binmm_out(Y, B, m, vec, X.device)
-    if B * r > NOALLOC_MAX_BR:
-        raise ValueError(f"B * r = {B * r} exceeds the fixed scratch ({NOALLOC_MAX_BR})")
+    need = binary_matmul_work_floats(B, n, r)
+    if need > NOALLOC_MAX_FLOATS:
+        raise ValueError(f"the call needs {need} floats of workspace, more than the fixed "
+                         f"scratch ({NOALLOC_MAX_FLOATS})")
     _check(_lib.load().nq_binary_matmul_noalloc(
         _ptr(U_bits, "U_bits", torch.int32, 2, need_contig=False), U_bits.stride(0),
         _ptr(Vt_bits, "Vt_bits", torch.int32, 2, need_contig=False), Vt_bits.stride(0),

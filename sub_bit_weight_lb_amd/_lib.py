@@ -59,6 +59,7 @@ SIGNATURES = {
     "nq_lbadmm_time_svid": (ST, [P, C.c_int32, C.c_int32, P, C.POINTER(C.c_double)]),
     "nq_pack_signs": (ST, [P, I64, I64, I64, P, I64, P]),
     "nq_transpose_signs": (ST, [P, I64, I64, I64, P, I64, P]),
+    "nq_binary_matmul_work_floats": (I64, [I64, I64, I64]),
     "nq_binary_matmul": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P, P]),
     "nq_binary_matmul_noalloc": (ST, [P, I64, P, I64, I64, I64, I64, P, P, P, I64, I64, P, I64, P]),
     "nq_lw_create": (ST, [I64, I64, C.POINTER(P)]),

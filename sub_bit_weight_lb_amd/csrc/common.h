@@ -266,16 +266,18 @@ hipError_t launch_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t
 hipError_t launch_transpose_bits(const uint32_t* in, int64_t rows, int64_t cols, int64_t ld_in,
                                  uint32_t* out, int64_t ld_out, hipStream_t s);
 // Y (B x m, ld ldy) = s1 * ((X * s2) S_V S_U^T) from S_U bits (m x r, ld ldu
-// words) and S_V^T bits (r x n, ld ldvt words); X B x n (ld ldx); T:
-// kBinSplit B r floats of scratch (partial projections).
+// words) and S_V^T bits (r x n, ld ldvt words); X B x n (ld ldx); work:
+// binmm_work_floats(B, n, r) floats of scratch (kBinSplit B r partial
+// projections, then the inputs' bf16 terms).
 constexpr int kBinSplit = 8;
+int64_t binmm_work_floats(int64_t B, int64_t n, int64_t r);
 hipError_t launch_binary_matmul(const uint32_t* su, int64_t ldu, const uint32_t* svt,
                                 int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
                                 const float* s2, const float* X, int64_t B, int64_t ldx,
-                                float* Y, int64_t ldy, float* T, hipStream_t s);
-// Floats in the fixed scratch array of binmm.hip (16 MiB per GPU): room for
-// kBinSplit B r partials while B r <= 2^19.
-constexpr int64_t kBinScratchFloats = int64_t(1) << 22;
+                                float* Y, int64_t ldy, float* work, hipStream_t s);
+// Floats in the fixed scratch array of binmm.hip (32 MiB per GPU): calls
+// with binmm_work_floats(B, n, r) up to this fit.
+constexpr int64_t kBinScratchFloats = int64_t(1) << 23;
 // *out = this GPU's copy of that array (the current device's), its address
 // looked up on first use on each device.
 hipError_t binmm_fixed_scratch(float** out);

@@ -85,6 +85,11 @@ nq_status nq_transpose_signs(const uint32_t* in, int64_t rows, int64_t cols, int
   return NQ_OK;
 }
 
+int64_t nq_binary_matmul_work_floats(int64_t B, int64_t n, int64_t r) {
+  if (B < 0 || n < 0 || r < 0) return -1;
+  return binmm_work_floats(B, n, r);
+}
+
 nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* Vt_bits,
                            int64_t ldvt, int64_t m, int64_t n, int64_t r, const float* s1,
                            const float* s2, const float* X, int64_t B, int64_t ldx, float* Y,
@@ -105,9 +110,10 @@ nq_status nq_binary_matmul_noalloc(const uint32_t* U_bits, int64_t ldu, const ui
   bool noop = false;
   nq_status st = check_binmm(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy, &noop);
   if (st != NQ_OK || noop) return st;
-  if (B > kBinScratchFloats / kBinSplit / r)
+  if (binmm_work_floats(B, n, r) > kBinScratchFloats)
     return set_error(NQ_ERR_INVALID_ARG,
-                     "B * r exceeds the fixed scratch (B * r <= 2^19 for nq_binary_matmul_noalloc)");
+                     "the call's workspace exceeds the fixed scratch "
+                     "(nq_binary_matmul_work_floats(B, n, r) <= 2^23 for nq_binary_matmul_noalloc)");
   float* work = nullptr;
   NQ_HIPCHK(binmm_fixed_scratch(&work));
   NQ_HIPCHK(launch_binary_matmul(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy,

@@ -168,7 +168,24 @@ def test_binary_layer_argument_checks(lib):
     assert call(r=0) == L.NQ_ERR_INVALID_ARG
     assert call(n=-1) == L.NQ_ERR_INVALID_ARG
 
-    # the fixed-scratch variant: the same checks, and B * r <= 2^19
+    # the workspace size: 8 B r partial sums (rounded up to 64 floats), then
+    # the bf16 terms, 3072 floats per 16 inputs and 128 columns of the wider
+    # of the two products
+    ws = lib.nq_binary_matmul_work_floats
+    assert ws(2, 70, 40) == 640 + 3072
+    assert ws(16, 28672, 6144) == 8 * 16 * 6144 + 3072 * 224
+    assert ws(17, 100, 300) == 40832 + 3072 * 2 * 3   # 8 * 17 * 300 = 40800, rounded up to 64
+    assert ws(1, 1, 1) == 64 + 3072
+    assert ws(-1, 4, 4) == -1
+    # the binding's copy of the formula (it checks buffers without calling
+    # the library) agrees with the library's
+    import sub_bit_weight_lb_amd as nq
+    for B, n, r in ((1, 1, 1), (2, 70, 40), (9, 4100, 2049), (33, 1000, 33), (128, 2048, 6656),
+                    (16, 28672, 6144), (0, 5, 5), (3, 0, 7)):
+        assert nq.binary_matmul_work_floats(B, n, r) == ws(B, n, r), (B, n, r)
+
+    # the fixed-scratch variant: the same checks, and the workspace must fit
+    # its 2^23 floats
     def call_na(**kw):
         a = dict(args, **kw)
         return lib.nq_binary_matmul_noalloc(f, a["ldu"], f, a["ldvt"], a["m"], a["n"], a["r"],
@@ -176,8 +193,10 @@ def test_binary_layer_argument_checks(lib):
     assert call_na(m=0) == 0 and call_na(B=0) == 0
     assert call_na(ldu=1) == L.NQ_ERR_INVALID_ARG
     assert call_na(ldy=9) == L.NQ_ERR_INVALID_ARG
-    assert call_na(r=4096, ldu=128, B=129) == L.NQ_ERR_INVALID_ARG
-    assert call_na(r=1 << 19, ldu=1 << 14, B=2) == L.NQ_ERR_INVALID_ARG
+    assert ws(129, 70, 8192) > 1 << 23
+    assert call_na(r=8192, ldu=256, B=129) == L.NQ_ERR_INVALID_ARG
+    assert ws(2, 1 << 22, 40) > 1 << 23
+    assert call_na(n=1 << 22, ldvt=1 << 17, ldx=1 << 22) == L.NQ_ERR_INVALID_ARG
 
 
 def test_ledoit_wolf_argument_checks(lib):

@@ -25,7 +25,7 @@ def operands(m=40, n=70, r=33, B=3):
 
 
 @pytest.mark.parametrize("change, what", [
-    (dict(work=torch.zeros(8 * 3 * 33 - 1)), "work"),
+    (dict(work=torch.zeros(nq.binary_matmul_work_floats(3, 70, 33) - 1)), "work"),
     (dict(Y=torch.zeros((2, 40))), "Y"),
     (dict(Y=torch.zeros((3, 39))), "Y"),
     (dict(Y=torch.zeros((3, 80))[:, ::2]), "Y"),     # column stride 2

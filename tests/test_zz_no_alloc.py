@@ -55,7 +55,7 @@ def run_both(nq, ops, r, dev):
     return H(Y), H(Y_ref)
 
 
-# (m, n, r, B): nine or more inputs take the matrix-core kernels, fewer the
+# (m, n, r, B): two or more inputs take the matrix-core kernels, one the
 # lookup-table kernels; each second case is smaller than its first
 PAIRS = [
     ((1000, 2000, 512, 16), (300, 500, 100, 3)),
@@ -77,11 +77,13 @@ def test_noalloc_matches_workspace_entry_point_twice(gpu, first, second):
 
 
 def test_noalloc_at_its_limit_then_vector(gpu):
-    """B * r at the limit (2^19), then a one-input call into a strided Y."""
+    """A workspace near the limit (2^23 floats: 512 more columns of rank
+    would pass it), then a one-input call into a strided Y."""
     import torch
     import sub_bit_weight_lb_amd as nq
-    m, n, r, B = 1024, 2048, 4096, 128
-    assert B * r == nq.NOALLOC_MAX_BR
+    m, n, r, B = 1024, 2048, 6656, 128
+    assert nq.binary_matmul_work_floats(B, n, r) <= nq.NOALLOC_MAX_FLOATS
+    assert nq.binary_matmul_work_floats(B, n, r + 512) > nq.NOALLOC_MAX_FLOATS
     print(f"noalloc at limit: m={m} n={n} r={r} B={B}", flush=True)
     ops, ref_args = operands(7, m, n, r, B, gpu)
     Y, Y_ref = run_both(nq, ops, r, gpu)
@@ -105,20 +107,21 @@ def test_noalloc_rejects_beyond_the_limit_without_touching_Y(gpu):
     import torch
     import sub_bit_weight_lb_amd as nq
     from sub_bit_weight_lb_amd import _lib
-    m, n, r, B = 64, 64, 4096, 129
+    m, n, r, B = 64, 64, 8192, 129
+    assert nq.binary_matmul_work_floats(B, n, r) > nq.NOALLOC_MAX_FLOATS
     Y = torch.full((B, m), 5.0, dtype=torch.float32, device=gpu)
-    with pytest.raises(ValueError, match="B \\* r"):
-        nq.binary_matmul_noalloc(torch.zeros((m, 128), dtype=torch.int32, device=gpu),
+    with pytest.raises(ValueError, match="more than the fixed scratch"):
+        nq.binary_matmul_noalloc(torch.zeros((m, 256), dtype=torch.int32, device=gpu),
                                  torch.zeros((r, 2), dtype=torch.int32, device=gpu),
                                  torch.ones(m, device=gpu), torch.ones(n, device=gpu),
                                  torch.zeros((B, n), device=gpu), r, Y)
     # the C entry point refuses it too, before any device work
-    ub = torch.zeros((m, 128), dtype=torch.int32, device=gpu)
+    ub = torch.zeros((m, 256), dtype=torch.int32, device=gpu)
     vt = torch.zeros((r, 2), dtype=torch.int32, device=gpu)
     s = torch.ones(m, device=gpu)
     X = torch.zeros((B, n), device=gpu)
     p = lambda t: C.c_void_p(t.data_ptr())  # noqa: E731
-    st = _lib.load().nq_binary_matmul_noalloc(p(ub), 128, p(vt), 2, m, n, r, p(s), p(s), p(X),
+    st = _lib.load().nq_binary_matmul_noalloc(p(ub), 256, p(vt), 2, m, n, r, p(s), p(s), p(X),
                                               B, n, p(Y), m, None)
     assert st == _lib.NQ_ERR_INVALID_ARG
     torch.cuda.synchronize()
