@@ -1,7 +1,7 @@
 """GPU parity of the binary-layer product (nq_binary_matmul) and the sign
-transpose (nq_transpose_signs) against the CPU oracle. Up to eight inputs
-run the lookup-table kernel, nine or more the matrix-core kernel; the
-shapes below cover both.
+transpose (nq_transpose_signs) against the CPU oracle. One input runs the
+lookup-table kernel, two or more the bf16 matrix-core kernel; the shapes
+below cover both.
 
 The transpose is bit-exact against oracle.lbadmm.pack_signs of the
 transposed sign matrix. The product is compared with oracle.binary in
@@ -76,6 +76,27 @@ def test_binary_matmul_matches_oracle(gpu, m, n, r, B):
     e = relerr(Y, ref)
     print(f"  rel err {e:.2e}", flush=True)
     assert e < 1e-5
+
+
+def test_bf16_terms_are_exact(gpu):
+    """Two or more inputs run on the bf16 matrix cores with each input split
+    into three bf16 terms, which is exact: only the fp32 accumulation
+    rounds. Over 4096 columns and 2048 ranks that keeps the product within
+    about 5e-7 of the float64 oracle. Keeping only the first two terms
+    would leave ~1e-5, only the first ~3e-3 (fp32 accumulation of the
+    truncated terms, 32 columns per step, simulated in float64 on these
+    sizes), so a 2e-6 bound tells them apart where the general 1e-5
+    tolerance would not."""
+    import sub_bit_weight_lb_amd as nq
+    m, n, r, B = 1024, 4096, 2048, 16
+    rng = np.random.default_rng(11)
+    SU, SV, s1, s2 = layer(rng, m, n, r)
+    X = rng.standard_normal((B, n)).astype(np.float32)
+    print(f"case bf16 exactness m={m} n={n} r={r} B={B}", flush=True)
+    Vt = nq.transpose_signs(bits_dev(SV, gpu), n, r)
+    Y = H(nq.binary_matmul(bits_dev(SU, gpu), Vt, T(s1, gpu), T(s2, gpu), T(X, gpu), r))
+    ref = OB.binary_matmul(X, O.pack_signs(SU), O.pack_signs(SV), r, s1, s2)
+    assert relerr(Y, ref) < 2e-6
 
 
 def test_binary_matmul_strided_vector_and_repeatable(gpu):
