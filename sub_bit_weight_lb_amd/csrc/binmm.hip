@@ -184,9 +184,10 @@ constexpr int kPlaneFloats = 3 * 4 * 4 * 16 * 4;   // dwords per (tile, word gro
 constexpr uint32_t kBfOut = 0x80000000u;            // an offset past every descriptor's range
 constexpr int kBufFlags = 0x00020000;               // raw buffer, 32-bit data
 
-// planes <- the terms of v (B x cols, ld ldv): the sum of nsum partial
-// vectors v + z vstride (added in slot order), times pre if given; ngw word
-// groups per tile. One thread per dword of each term.
+// planes <- the terms of v (B x cols, ld ldv): the sum of nsum (at most
+// NS) partial vectors v + z vstride (added in slot order), times pre
+// if given; ngw word groups per tile. One thread per dword of each term.
+template <int NS>
 __global__ __launch_bounds__(256) void bin_split_kernel(const float* __restrict__ v, int64_t ldv,
                                                         int64_t B, int64_t cols, int nsum,
                                                         int64_t vstride,
@@ -202,18 +203,26 @@ __global__ __launch_bounds__(256) void bin_split_kernel(const float* __restrict_
     const int d = o & 3, i = (o >> 2) & 15, g = (o >> 6) & 3, st = o >> 8;
     const int64_t b = bt * 16 + i;
     const int64_t ca = (q * 4 + g) * 32 + 4 * st + d, cb = ca + 16;
-    float x[2] = {0.0f, 0.0f};
-    if (b < B) {
-      const float* vp = v + b * ldv;
+    // every load is issued before any add (clamped indices, no branches
+    // around loads); the slots are then added in order
+    float x[2], t[2][NS];
+    bool ok[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t c = h ? cb : ca;
-        if (c < cols) {
-          float y = vp[c];
-          for (int z = 1; z < nsum; ++z) y += vp[c + z * vstride];
-          x[h] = pre ? y * pre[c] : y;
-        }
-      }
+    for (int h = 0; h < 2; ++h) {
+      const int64_t c = h ? cb : ca;
+      ok[h] = b < B && c < cols;
+      const float* vp = v + (ok[h] ? b * ldv + c : 0);
+#pragma unroll
+      for (int z = 0; z < NS; ++z) t[h][z] = vp[(z < nsum ? z : 0) * vstride];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float y = t[h][0];
+#pragma unroll
+      for (int z = 1; z < NS; ++z)
+        if (z < nsum) y += t[h][z];
+      if (pre) y *= pre[ok[h] ? (h ? cb : ca) : 0];
+      x[h] = ok[h] ? y : 0.0f;
     }
     const uint32_t ua = __float_as_uint(x[0]), ub = __float_as_uint(x[1]);
     const float ra = x[0] - __uint_as_float(ua & 0xffff0000u);
@@ -425,8 +434,13 @@ hipError_t split_terms(const float* v, int64_t ldv, int64_t B, int64_t cols, int
   const int64_t ngw = (cols + 127) / 128;
   const int64_t total = (B + 15) / 16 * ngw * 1024;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(bin_split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, v, ldv, B, cols,
-                     nsum, vstride, pre, planes, ngw);
+  if (nsum < 1 || nsum > kBinSplit) return hipErrorInvalidValue;
+  if (nsum == 1)
+    hipLaunchKernelGGL(bin_split_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, v, ldv, B,
+                       cols, nsum, vstride, pre, planes, ngw);
+  else
+    hipLaunchKernelGGL(bin_split_kernel<kBinSplit>, dim3((unsigned)blocks), dim3(256), 0, s, v,
+                       ldv, B, cols, nsum, vstride, pre, planes, ngw);
   return hipGetLastError();
 }
 
