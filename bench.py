@@ -45,6 +45,7 @@ WORKLOAD = "llama2-7b-attn-4096x4096-r2048"
 BLOCK = "llama2-7b-block"
 METRIC = "LB-ADMM iters/s on 4096x4096 r=2048 fp32 layer; % of fp32 MFMA peak"
 FP32_MFMA_PEAK_TFLOPS = 157.3
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemm_rhs_4096x4096_r2048_counters.md")
 GEMM_SRC = os.path.join(ROOT, "sub_bit_weight_lb_amd", "csrc", "gemm.hip")
@@ -257,7 +258,10 @@ def ste_bench(nq, torch, dev, samples=128, seq=2048, batch=4, epochs=8, admm_ite
     seeded on the device (feature profile of synth.activations), targets
     Y = X W^T, 8 epochs of shuffled batches of 4 samples (8192 tokens), lr
     1e-4 -> 1e-6 on the cosine schedule, from the factors of an LB-ADMM run.
-    Algorithmic work per step: six sign products, 6 T r (m + n) flops."""
+    Algorithmic work per step: six products, 6 T r (m + n) flops. Four have
+    a +-1 factor and run on the bf16 matrix cores with the other factor as
+    three exact bf16 terms (3x the flops there), two on the fp32 ones; the
+    step's roofline is the time both sets would take at their peaks."""
     import numpy as np
     from synth import make_layer
     from synth.activations import feature_profile
@@ -308,11 +312,16 @@ def ste_bench(nq, torch, dev, samples=128, seq=2048, batch=4, epochs=8, admm_ite
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
     flops = 6.0 * T * r * (m + n)
+    sign_flops = 4.0 * T * r * (m + n)          # P, Q, dP, dA
+    fp32_flops = flops - sign_flops             # dU, dV
+    # the step at both peaks: 3 bf16 products per sign product
+    t_roof = 3.0 * sign_flops / (BF16_MFMA_PEAK_TFLOPS * 1e12) + fp32_flops / (FP32_MFMA_PEAK_TFLOPS * 1e12)
     step_ms = ms / len(batches)
     out.update({"ms_total": round(ms, 2), "ms_per_step": round(step_ms, 3),
                 "steps_per_s": round(1e3 / step_ms, 2), "tokens_per_s": round(T * 1e3 / step_ms, 1),
                 "flops_per_step": flops, "tflops": round(flops / (step_ms * 1e-3) / 1e12, 2),
-                "frac_of_fp32_peak": round(flops / (step_ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4)})
+                "roofline_ms_per_step": round(t_roof * 1e3, 3),
+                "frac_of_roofline": round(t_roof * 1e3 / step_ms, 4)})
     return out
 
 

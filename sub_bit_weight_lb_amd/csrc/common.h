@@ -257,6 +257,15 @@ hipError_t launch_itsolve_init(const float* g, float* d, float* delta, int rows,
                                hipStream_t s);
 hipError_t launch_itsolve_step(const float* Q, float* d, float* u, float* g, float* delta,
                                int rows, int rp, bool cg, bool last, hipStream_t s);
+// ---------------------------------------------------------------- sign products (signmm.hip)
+// C (M x N, ld ldc) = A S^T for A (M x K, ld lda) and S (N x K, ld lds) whose
+// entries are +-1 (stored as fp32), on the bf16 matrix cores with A split
+// into three exact bf16 terms; Ct (N x M, ld ldct), if given, receives C^T.
+// M, N % 128 == 0, K % 64 == 0, lds and ldct multiples of 4, A, S, Ct
+// 16-byte aligned (else hipErrorInvalidValue, nothing launched).
+hipError_t launch_sign_gemm(const float* A, int64_t lda, const float* S, int64_t lds, float* C,
+                            int64_t ldc, float* Ct, int64_t ldct, int M, int N, int K,
+                            hipStream_t s);
 // ---------------------------------------------------------------- packing
 hipError_t launch_pack_signs(const float* X, int64_t rows, int64_t cols, int64_t ldx,
                              uint32_t* bits, int64_t ld_words, hipStream_t s);

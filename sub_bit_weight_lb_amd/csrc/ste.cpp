@@ -171,16 +171,18 @@ nq_status nq_ste_step(nq_ste_t h, const float* X, int64_t ldx, const float* Y, i
   const int64_t mp = h->mp, np_ = h->np_, rp = h->rp, tp = round_up(T, 256);
   // forward
   NQ_HIPCHK(launch_ste_stage(X, ldx, rows, T, h->n, h->s2, np_, tp, h->A, h->At, s));
-  NQ_HIPCHK(gemm(h->A, np_, h->SVt, np_, h->P, rp, tp, rp, np_, h->Pt, tp, s));
-  NQ_HIPCHK(gemm(h->P, rp, h->SU, rp, h->Q, mp, tp, mp, rp, nullptr, 0, s));
+  // (the four products with a sign factor run on the bf16 matrix cores,
+  // exactly: launch_sign_gemm)
+  NQ_HIPCHK(launch_sign_gemm(h->A, np_, h->SVt, np_, h->P, rp, h->Pt, tp, (int)tp, (int)rp, (int)np_, s));
+  NQ_HIPCHK(launch_sign_gemm(h->P, rp, h->SU, rp, h->Q, mp, nullptr, 0, (int)tp, (int)mp, (int)rp, s));
   // loss, dL/dYq, ds1, dQ
   NQ_HIPCHK(launch_ste_loss(h->Q, Y, ldy, rows, T, h->m, h->s1, mp, tp, h->dQ, h->dQt, h->ds1p,
                             h->lossp, h->ds1, h->loss, s));
   // backward through the two sign products
   NQ_HIPCHK(gemm(h->dQt, tp, h->Pt, tp, h->dU, rp, mp, rp, tp, nullptr, 0, s));
-  NQ_HIPCHK(gemm(h->dQ, mp, h->SUt, mp, h->dP, rp, tp, rp, mp, h->dPt, tp, s));
+  NQ_HIPCHK(launch_sign_gemm(h->dQ, mp, h->SUt, mp, h->dP, rp, h->dPt, tp, (int)tp, (int)rp, (int)mp, s));
   NQ_HIPCHK(gemm(h->At, tp, h->dPt, tp, h->dV, rp, np_, rp, tp, nullptr, 0, s));
-  NQ_HIPCHK(gemm(h->dP, rp, h->SV, rp, h->dA, np_, tp, np_, rp, nullptr, 0, s));
+  NQ_HIPCHK(launch_sign_gemm(h->dP, rp, h->SV, rp, h->dA, np_, nullptr, 0, (int)tp, (int)np_, (int)rp, s));
   NQ_HIPCHK(launch_ste_ds2(h->dA, X, ldx, rows, T, h->n, np_, tp, h->ds2p, h->ds2, s));
   // Adam, then the signs of the moved latents
   h->t += 1;

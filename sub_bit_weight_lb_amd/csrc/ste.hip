@@ -5,21 +5,24 @@
 //
 // One step on a batch X (T tokens x n), target Y = X W^T (T x m):
 //   A = X diag(s2) (and A^T)          ste_stage_kernel (rows gathered by index)
-//   P = A S_V (and P^T)               tiled GEMM, solve epilogue (C and C^T)
-//   Q = P S_U^T                       tiled GEMM
+//   P = A S_V (and P^T)               sign GEMM (signmm.hip), C and C^T
+//   Q = P S_U^T                       sign GEMM
 //   E = Q diag(s1) - Y, G = 2E/(T m)  ste_loss_kernel: loss and ds1 partials,
 //   dQ = G diag(s1) (and dQ^T)          dQ and dQ^T
-//   dU = dQ^T P                       tiled GEMM
-//   dP = dQ S_U (and dP^T)            tiled GEMM, solve epilogue
-//   dV = A^T dP                       tiled GEMM
-//   dA = dP S_V^T                     tiled GEMM
+//   dU = dQ^T P                       fp32 tiled GEMM
+//   dP = dQ S_U (and dP^T)            sign GEMM, C and C^T
+//   dV = A^T dP                       fp32 tiled GEMM
+//   dA = dP S_V^T                     sign GEMM
 //   ds2_j = sum_t dA_tj X_tj          ste_ds2_kernel (partials)
 //   column partial sums -> ds1, ds2   ste_colsum_kernel (fixed order)
 //   Adam on U, V, s1, s2              ste_adam_kernel
 //   S_U, S_U^T, S_V, S_V^T            ste_signs_kernel (sign(x >= 0) = +1,
 //                                     zero in the padding)
-// The sign matrices are exact +-1 in fp32, so the products are the fp32
-// matrix-core GEMM of the ADMM path; every reduction runs in a fixed order.
+// The sign matrices are exact +-1 (stored in fp32): the four products with
+// one run on the bf16 matrix cores with the other factor split into three
+// exact bf16 terms (every product exact, fp32 accumulation), the two
+// without on the fp32 matrix-core GEMM of the ADMM path. Every reduction
+// runs in a fixed order.
 #include "common.h"
 
 #include <algorithm>
