@@ -372,6 +372,15 @@ nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ld
                          float* C, int64_t ldc,
                          int64_t rows, int64_t cols, int64_t k, void* stream);
 
+/* C = A S^T for A rows x k (lda) and S cols x k (lds) with entries +-1: the
+ * products of the STE step through the sign matrices ("方法步骤详情", stage 2
+ * step (3)), on the bf16 matrix cores with A split into three exact bf16
+ * terms (entries of S other than +-1 and 0 are cut to bf16). C rows x cols
+ * (ldc); Ct (nullable) cols x rows (ldct) receives C^T. */
+nq_status nq_op_sign_gemm(const float* A, int64_t lda, const float* S, int64_t lds,
+                          float* C, int64_t ldc, float* Ct, int64_t ldct,
+                          int64_t rows, int64_t cols, int64_t k, void* stream);
+
 /* Cholesky factorisation G = L L^T of an SPD r x r matrix (lower triangle of
  * G read) and the inverse Ginv = L^-T L^-1 (full symmetric; formed, as in the
  * run, as the Gram product M^T M of M = L^-1). Ginv (device, nullable)

@@ -30,7 +30,7 @@ __all__ = [
     "lbadmm_destroy", "lbadmm_profile", "lbadmm_workspace_bytes", "pack_signs", "transpose_signs",
     "binary_matmul", "binary_matmul_noalloc", "binary_matmul_work_floats", "LedoitWolf", "ledoit_wolf_diag",
     "preconditioners", "STERefiner", "cosine_lr", "op_precondition", "op_gram",
-    "op_gemm_rhs", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
+    "op_gemm_rhs", "op_sign_gemm", "op_cholesky_inverse", "op_svid", "LBADMM", "lbadmm", "Result",
     "status_string", "version",
 ]
 
@@ -523,6 +523,23 @@ def op_gemm_rhs(A, B, P=None, rho=0.0, stream=None):
         _ptr(A, "A", f32, 2), k, _ptr(B, "B", f32, 2), cols, _ptr(P, "P", f32, 2, True), cols,
         float(rho), _ptr(Cm, "C", f32, 2), cols, rows, cols, k, _stream(stream)), "nq_op_gemm_rhs")
     return Cm
+
+
+def op_sign_gemm(A, S, transposed=False, stream=None):
+    """C = A S^T for A (rows x k) and a +-1 matrix S (cols x k), on the bf16
+    matrix cores; with transposed=True returns (C, C^T from the kernel)."""
+    torch = _torch()
+    rows, k = A.shape
+    cols, k2 = S.shape
+    if k2 != k:
+        raise ValueError("A and S must have the same number of columns")
+    f32 = torch.float32
+    Cm = torch.empty((rows, cols), dtype=f32, device=A.device)
+    Ct = torch.empty((cols, rows), dtype=f32, device=A.device) if transposed else None
+    _check(_lib.load().nq_op_sign_gemm(
+        _ptr(A, "A", f32, 2), k, _ptr(S, "S", f32, 2), k, _ptr(Cm, "C", f32, 2), cols,
+        _ptr(Ct, "Ct", f32, 2, True), rows, rows, cols, k, _stream(stream)), "nq_op_sign_gemm")
+    return (Cm, Ct) if transposed else Cm
 
 
 def op_cholesky_inverse(G, stream=None):

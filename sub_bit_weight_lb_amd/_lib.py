@@ -76,6 +76,7 @@ SIGNATURES = {
     "nq_op_precondition": (ST, [P, I64, I64, I64, P, P, P, I64, P]),
     "nq_op_gram": (ST, [P, I64, I64, I64, F32, P, I64, P]),
     "nq_op_gemm_rhs": (ST, [P, I64, P, I64, P, I64, F32, P, I64, I64, I64, I64, P]),
+    "nq_op_sign_gemm": (ST, [P, I64, P, I64, P, I64, P, I64, I64, I64, I64, P]),
     "nq_op_cholesky_inverse": (ST, [P, I64, I64, P, I64, P, I64, C.POINTER(I64), P]),
     "nq_op_svid": (ST, [P, I64, I64, I64, C.c_int32, P, I64, P, P, P]),
     "nq_op_svid_dual": (ST, [P, P, I64, I64, I64, C.c_int32, P, P, I64, P, P, P]),

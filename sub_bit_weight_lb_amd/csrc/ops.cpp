@@ -190,6 +190,31 @@ nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ld
   return NQ_OK;
 }
 
+nq_status nq_op_sign_gemm(const float* A, int64_t lda, const float* S, int64_t lds, float* C,
+                          int64_t ldc, float* Ct, int64_t ldct, int64_t rows, int64_t cols,
+                          int64_t k, void* stream) {
+  if (rows < 1 || cols < 1 || k < 1 || !A || !S || !C || lda < k || lds < k || ldc < cols ||
+      (Ct && ldct < rows))
+    return set_error(NQ_ERR_INVALID_ARG, "bad sign gemm arguments");
+  if (rows > (1 << 24) || cols > (1 << 24) || k > (1 << 24))
+    return set_error(NQ_ERR_INVALID_ARG, "rows, cols and k must be <= 2^24");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t Mp = round_up(rows, 128), Np = round_up(cols, 128), Kp = round_up(k, 64);
+  DevBuf a, b, c, ct;
+  NQ_HIPCHK(a.alloc(sizeof(float) * Mp * Kp));
+  NQ_HIPCHK(b.alloc(sizeof(float) * Np * Kp));
+  NQ_HIPCHK(c.alloc(sizeof(float) * Mp * Np));
+  if (Ct) NQ_HIPCHK(ct.alloc(sizeof(float) * Np * Mp));
+  NQ_HIPCHK(stage_in(A, rows, k, lda, a.f(), Mp, Kp, s));
+  NQ_HIPCHK(stage_in(S, cols, k, lds, b.f(), Np, Kp, s));
+  NQ_HIPCHK(launch_sign_gemm(a.f(), Kp, b.f(), Kp, c.f(), Np, Ct ? ct.f() : nullptr, Mp,
+                             (int)Mp, (int)Np, (int)Kp, s));
+  NQ_HIPCHK(stage_out(c.f(), Np, C, ldc, rows, cols, s));
+  if (Ct) NQ_HIPCHK(stage_out(ct.f(), Mp, Ct, ldct, cols, rows, s));
+  NQ_HIPCHK(hipStreamSynchronize(s));
+  return NQ_OK;
+}
+
 nq_status nq_op_cholesky_inverse(const float* G, int64_t r, int64_t ldg, float* L, int64_t ldl,
                                  float* Ginv, int64_t ldgi, int64_t* info, void* stream) {
   if (r < 1 || ldg < r || !G || !info || (L && ldl < r) || (Ginv && ldgi < r))

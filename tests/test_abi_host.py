@@ -224,6 +224,12 @@ def test_ops_argument_checks(lib):
     assert lib.nq_op_cholesky_inverse(f, 4, 3, f, 4, f, 4, C.byref(info), None) == \
         L.NQ_ERR_INVALID_ARG
     assert lib.nq_op_svid(f, 4, 4, 4, 0, f, 4, None, None, None) == L.NQ_ERR_INVALID_ARG
+    # sign gemm: lda < k, lds < k, ldc < cols, ldct < rows, a missing operand
+    assert lib.nq_op_sign_gemm(f, 4, f, 5, f, 6, None, 0, 3, 6, 5, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_sign_gemm(f, 5, f, 4, f, 6, None, 0, 3, 6, 5, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_sign_gemm(f, 5, f, 5, f, 5, None, 0, 3, 6, 5, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_sign_gemm(f, 5, f, 5, f, 6, f, 2, 3, 6, 5, None) == L.NQ_ERR_INVALID_ARG
+    assert lib.nq_op_sign_gemm(None, 5, f, 5, f, 6, None, 0, 3, 6, 5, None) == L.NQ_ERR_INVALID_ARG
 
 
 def test_binding_imports_and_missing_library_fails_loudly(tmp_path):

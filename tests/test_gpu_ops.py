@@ -34,6 +34,27 @@ def test_precondition_bit_exact(gpu, m, n):
     np.testing.assert_array_equal(got, O.precondition(W, do, di, np.float32))
 
 
+@pytest.mark.parametrize("rows,k,cols", [(128, 64, 128), (300, 70, 90), (1000, 517, 260),
+                                         (512, 4096, 256), (8192, 2048, 384)])
+def test_sign_gemm_is_exact(gpu, rows, k, cols):
+    """C = A S^T with S = +-1 (the STE step's products through the sign
+    matrices) against the float64 product. A is split into three exact bf16
+    terms, so only the fp32 accumulation rounds: at K = 4096 the error is
+    ~3e-7, where keeping two terms would leave ~1e-5 and one ~3e-3 (the
+    same sums as the binary product's exactness test). C^T is the same
+    numbers, transposed."""
+    import sub_bit_weight_lb_amd as nq
+    rng = np.random.default_rng(rows + 3 * k + 7 * cols)
+    A = rng.standard_normal((rows, k)).astype(np.float32)
+    S = np.where(rng.random((cols, k)) < 0.5, -1.0, 1.0).astype(np.float32)
+    print(f"case sign gemm rows={rows} k={k} cols={cols}", flush=True)
+    C, Ct = nq.op_sign_gemm(T(A, gpu), T(S, gpu), transposed=True)
+    C, Ct = H(C), H(Ct)
+    ref = A.astype(np.float64) @ S.astype(np.float64).T
+    assert relerr(C, ref) < 2e-6
+    np.testing.assert_array_equal(Ct, C.T)
+
+
 @pytest.mark.parametrize("rows,k,cols", [(256, 32, 128), (300, 70, 90), (1000, 517, 260),
                                          (512, 4096, 256)])
 def test_gemm_rhs(gpu, rows, k, cols):
