@@ -62,7 +62,9 @@ def test_transpose_signs_bit_exact(gpu, rows, cols):
 @pytest.mark.parametrize("m,n,r,B", [(1, 1, 1, 1), (64, 48, 8, 1), (300, 200, 70, 3), (257, 1000, 33, 2),
                                      (100, 4100, 2049, 5), (4096, 4096, 2048, 1), (4096, 4096, 2048, 8),
                                      (11008, 4096, 1536, 4), (300, 200, 70, 9), (257, 1000, 33, 33),
-                                     (65, 4100, 2049, 16), (4096, 4096, 2048, 24)])
+                                     (65, 4100, 2049, 16), (4096, 4096, 2048, 24),
+                                     (1, 1, 1, 2), (3, 5, 2, 17), (64, 33, 31, 100),
+                                     (129, 129, 129, 31)])
 def test_binary_matmul_matches_oracle(gpu, m, n, r, B):
     import sub_bit_weight_lb_amd as nq
     rng = np.random.default_rng(m + 3 * n + 7 * r + B)
