@@ -98,6 +98,7 @@ nq_status nq_binary_matmul(const uint32_t* U_bits, int64_t ldu, const uint32_t* 
   nq_status st = check_binmm(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy, &noop);
   if (st != NQ_OK || noop) return st;
   if (!work) return set_error(NQ_ERR_INVALID_ARG, "work is required");
+  if ((uintptr_t)work % 16) return set_error(NQ_ERR_INVALID_ARG, "work must be 16-byte aligned");
   NQ_HIPCHK(launch_binary_matmul(U_bits, ldu, Vt_bits, ldvt, m, n, r, s1, s2, X, B, ldx, Y, ldy,
                                  work, (hipStream_t)stream));
   return NQ_OK;

@@ -161,6 +161,7 @@ def test_binary_layer_argument_checks(lib):
                                     a["B"], a["ldx"], f, a["ldy"], work, None)
     assert call(m=0) == 0 and call(B=0) == 0
     assert call(work=None) == L.NQ_ERR_INVALID_ARG
+    assert call(work=C.c_void_p(0x1004)) == L.NQ_ERR_INVALID_ARG   # not 16-byte aligned
     assert call(ldu=1) == L.NQ_ERR_INVALID_ARG          # < ceil(40/32)
     assert call(ldvt=2) == L.NQ_ERR_INVALID_ARG         # < ceil(70/32)
     assert call(ldx=69) == L.NQ_ERR_INVALID_ARG
