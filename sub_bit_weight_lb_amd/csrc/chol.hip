@@ -536,13 +536,13 @@ __device__ __forceinline__ void diag_step(const float* A, int rp, int k, float* 
 //   [k < R]  1 diagonal (writes M_kk), R-1-k panel tiles, k inverse-row tiles;
 //   [k >= 1] 1 with want_L (writes L_{k-1,k-1}), n(n+1)/2 trailing tiles
 //            (n = R-1-k), n k partial sums.
-// With pin (a 256-workgroup grid: 32 workgroups on each of the 8 XCDs), the
-// ndiag workgroups that factor a diagonal tile are those on XCD 7, one per
-// CU, and the update workgroups those on XCDs 0-6; the others exit. A GEMM
-// that leaves XCD 7 free (GemmArgs::free_xcd7) then never shares a CU with
-// the diagonal work. The XCD comes from the hardware register: consecutive
-// workgroups go to consecutive XCDs, but the first one's XCD depends on the
-// queue's history.
+// With pin = px > 0 (a 256-workgroup grid: 32 workgroups on each of the 8
+// XCDs), the ndiag workgroups that factor a diagonal tile are on the last px
+// XCDs, one per CU, and the update workgroups on the others; the rest exit.
+// A GEMM that leaves those XCDs free (GemmArgs::free_xcds = px) then never
+// shares a CU with the diagonal work. The XCD comes from the hardware
+// register: consecutive workgroups go to consecutive XCDs, but the first
+// one's XCD depends on the queue's history.
 __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, int rp,
                                                        int k, int r_real, int want_L,
                                                        int upd_blocks, DevStats* st, int pin,
@@ -559,18 +559,19 @@ __global__ __launch_bounds__(NT) void chol_step_kernel(float* A, float* M, int r
   if (k != 0) g.part = nullptr;
   int b = blockIdx.x;
   // update tiles [t_lo, t_hi) with stride t_step for this workgroup (pinned:
-  // the XCD 7 workgroups take the first dtiles after their diagonal work,
-  // which runs alone on that XCD, and the others the rest)
+  // the workgroups of the last pin XCDs take the first dtiles after their
+  // diagonal work, which runs alone on those XCDs, and the others the rest)
   int t_lo = -1, t_hi = INT_MAX, t_step = upd_blocks;
   if (pin) {
-    const int x = xcd_id(), i = b >> 3;
-    if (x == 7) {
-      t_lo = i;
+    const int x = xcd_id(), i = b >> 3, x0 = 8 - pin;
+    if (x >= x0) {
+      const int di = i * pin + (x - x0);
+      t_lo = di;
       t_hi = dtiles;
-      t_step = kPinDiagSlots;
-      b = i < ndiag ? i : INT_MAX;
+      t_step = kPinXcdCus * pin;
+      b = di < ndiag ? di : INT_MAX;
     } else {
-      const int u = i * 7 + x;
+      const int u = i * x0 + x;
       if (u >= upd_blocks) return;
       t_lo = dtiles + u;
       b = INT_MAX;
@@ -701,26 +702,35 @@ __global__ void zero_upper_kernel(float* A, int rp) {
 
 }  // namespace
 
-// Update tiles per launch that the XCD 7 workgroups take after their
-// diagonal work (pinned mode); NQ_PIN_DIAG_TILES overrides it.
-int pin_diag_tiles() {
+// Update tiles per launch that the workgroups of the diagonal XCDs take
+// after their diagonal work (pinned mode), measured best: with one XCD the
+// first 64 (the other XCDs, beside the GEMM, take the rest); with two, all
+// of them (the chain keeps to its two XCDs, the GEMM has the other six to
+// itself). NQ_PIN_DIAG_TILES overrides it.
+int pin_diag_tiles(int px) {
   static const int d = [] {
     const char* e = std::getenv("NQ_PIN_DIAG_TILES");
-    return e ? std::max(0, std::atoi(e)) : 64;
+    return e ? std::max(0, std::atoi(e)) : -1;
   }();
-  return d;
+  return d >= 0 ? d : px == 1 ? 64 : INT_MAX;
 }
 
-bool cholesky_pinnable(int rp, bool want_L) {
-  return rp % NB == 0 && rp / NB + (want_L ? 1 : 0) <= kPinDiagSlots;
+int cholesky_pin_xcds(int rp, bool want_L) {
+  if (rp % NB) return 0;
+  const int ndiag = rp / NB + (want_L ? 1 : 0);
+  for (int px = 1; px <= kPinMaxXcds; ++px)
+    if (ndiag <= kPinXcdCus * px) return px;
+  return 0;
 }
 
 hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
-                                   bool pin, float* Mt, GramSrc src) {
+                                   int pin, float* Mt, GramSrc src) {
   if (rp % NB) return hipErrorInvalidValue;
   if (src.part && (want_L || rp % 128 || src.L <= 0)) return hipErrorInvalidValue;
-  if (pin && !cholesky_pinnable(rp, want_L)) return hipErrorInvalidValue;
+  if (pin < 0 || pin > kPinMaxXcds) return hipErrorInvalidValue;
+  if (pin && (cholesky_pin_xcds(rp, want_L) == 0 || cholesky_pin_xcds(rp, want_L) > pin))
+    return hipErrorInvalidValue;
   const int R = rp / NB;
   if (zero_m) {
     hipError_t e = launch_zero(M, (size_t)rp * rp, s);
@@ -731,14 +741,14 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
     int nb = k < R ? 1 + n + k : 0;  // diagonal, panel and inverse-row workgroups
     int upd = 0, upd_tiles = 0;
     // launch 0 with src: the update workgroups reduce the Gram tiles the
-    // diagonal and panel ones do not (XCD 7, busy with those, takes none)
+    // diagonal and panel ones do not (the diagonal XCDs, busy with those, take none)
     const bool red = k == 0 && src.part;
     if (k >= 1 || red) {
       nb += k >= 1 && want_L ? 1 : 0;
       const int tiles = red ? 1 + (R - 1) * R / 2 : n > 0 ? n * (n + 1) / 2 + n * k : 0;
       upd = upd_tiles = tiles;
       if (pin) {
-        upd = std::min(tiles, kPinUpdSlots);
+        upd = std::min(tiles, kPinGrid - kPinXcdCus * pin);
       } else {
         const int cap = chol_launch_cap();
         if (cap > 0 && nb + upd > cap)
@@ -749,7 +759,7 @@ hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
     if (nb + upd > 0)
       hipLaunchKernelGGL(chol_step_kernel, dim3(pin ? kPinGrid : nb + upd), dim3(NT), 0, s, A, M,
                          rp, k, r_real, want_L ? 1 : 0, std::max(upd, 1), st,
-                         pin ? 1 : 0, nb, pin && !red ? std::min(upd_tiles, pin_diag_tiles()) : 0,
+                         pin, nb, pin && !red ? std::min(upd_tiles, pin_diag_tiles(pin)) : 0,
                          Mt, src);
   }
   if (!want_L) return hipGetLastError();

@@ -43,10 +43,12 @@ struct DevStats {
   uint32_t to_src, to_src_prog;  // the workgroup it waited for, and its progress word then
 };
 
-// Launch layout of the pinned overlap (MI355X: 8 XCDs x 32 CUs).
-constexpr int kPinGrid = 256;      // workgroups of a pinned launch, 32 per XCD
-constexpr int kPinDiagSlots = 32;  // XCD 7
-constexpr int kPinUpdSlots = 224;  // XCDs 0-6
+// Launch layout of the pinned overlap (MI355X: 8 XCDs x 32 CUs): the chain's
+// diagonal work takes the last px XCDs (px = 1 or 2), the RHS GEMM the
+// others.
+constexpr int kPinGrid = 256;     // workgroups of a pinned launch, 32 per XCD
+constexpr int kPinXcdCus = 32;    // workgroups of a pinned launch on one XCD
+constexpr int kPinMaxXcds = 2;    // at most two XCDs for the diagonal work
 
 // ---------------------------------------------------------------- GEMM
 enum GemmEpilogue : int {
@@ -65,19 +67,20 @@ struct GemmArgs {
   int M, N, K;
   int yield;                     // s_sleep units per K step (0: none), to leave
                                  // issue cycles to a kernel running beside it
-  int free_xcd7;                 // kEpiRhs: run on XCDs 0-6 only (XCD 7 left to a
-                                 // pinned Cholesky chain); part is then required
-  float* part;                   // kPinUpdSlots x 256 x 128 floats of partial tiles
+  int free_xcds;                 // kEpiRhs: 0, or 1-2 to run on XCDs 0 .. 7 - free_xcds
+                                 // only (the others left to a pinned Cholesky
+                                 // chain); part is then required
+  float* part;                   // up to 224 x 256 x 128 floats of partial tiles
 };
 // M % 256 == 0, N % 128 == 0, K % 32 == 0; every ld a multiple of 4 and every
 // pointer 16-byte aligned (else hipErrorInvalidValue, nothing launched).
-// With free_xcd7, the 256 x 128 tiles go to the 224 workgroups of XCDs 0-6:
-// each takes whole tiles, and the tiles left over are split along K into
-// partial tiles (in part) that a second kernel adds up, with rho P, in a
-// fixed order.
+// With free_xcds = f, the 256 x 128 tiles go to the 32 (8 - f) workgroups of
+// XCDs 0 .. 7 - f: each takes whole tiles, and the tiles left over are split
+// along K into partial tiles (in part) that a second kernel adds up, with
+// rho P, in a fixed order.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
-// Floats of `part` a free_xcd7 launch of this shape needs (0 if none).
-size_t rhs_part_floats(int M, int N, int K);
+// Floats of `part` a launch of this shape with free_xcds = f needs (0 if none).
+size_t rhs_part_floats(int M, int N, int K, int f);
 
 // ---------------------------------------------------------------- Gram
 // K steps (of 32) of the lower 128 x 128 tiles of a Gram product, tile
@@ -136,10 +139,12 @@ constexpr int kNB = 64;  // block size of the blocked Cholesky
 // zeros above their diagonal); M's other tiles are not written, and with
 // zero_m M is zeroed first so that they read as zero.
 // st->potrf_info gets min(1 + failing column).
-// pin: place the diagonal work on XCD 7 (one workgroup per CU) and the
-// update tiles on XCDs 0-6, for a run beside a GEMM that leaves XCD 7 free;
-// needs cholesky_pinnable (at most kPinDiagSlots diagonal workgroups).
-bool cholesky_pinnable(int rp, bool want_L);
+// pin = px > 0: place the diagonal work on the last px XCDs (one workgroup
+// per CU) and the update tiles on the others, for a run beside a GEMM with
+// free_xcds = px; needs at most 32 px diagonal workgroups per launch.
+// cholesky_pin_xcds gives the fewest XCDs that hold them (0: more than
+// kPinMaxXcds would be needed).
+int cholesky_pin_xcds(int rp, bool want_L);
 // Mt (nullable): the upper block triangle of M^T (the lower blocks are never
 // written and must read as zero), the operand of G^-1 = M^T M
 // (launch_gram_partial with a triangular plan).
@@ -150,7 +155,7 @@ bool cholesky_pinnable(int rp, bool want_L);
 // triangle and diagonal 64 x 64 blocks). Not with want_L.
 hipError_t launch_cholesky_inverse(float* A, float* M, int rp, int r_real,
                                    DevStats* st, bool want_L, bool zero_m, hipStream_t s,
-                                   bool pin = false, float* Mt = nullptr,
+                                   int pin = 0, float* Mt = nullptr,
                                    GramSrc src = GramSrc{nullptr, GramSteps{0, 0}, 1, 0.0f});
 
 // ---------------------------------------------------------------- SVID

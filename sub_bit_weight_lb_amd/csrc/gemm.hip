@@ -290,16 +290,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) float lds[Tile<256>::LDS_FLOATS];
   const int tiles = (p.M / 256) * (p.N / TN);
   const int ksteps = p.K / BK;
-  if (!p.free_xcd7) {
+  if (!p.free_xcds) {
     gemm_tile<EPI>(p, xcd_tile(blockIdx.x, tiles), 0, ksteps, nullptr, lds);
     return;
   }
   // consecutive workgroups go to consecutive XCDs (the first one's XCD
   // depends on the queue's history): with 32 per XCD, blockIdx / 8 numbers
-  // the workgroups of one XCD. XCD 7 is left to the chain.
-  const int x = xcd_id(), i = blockIdx.x >> 3;
-  if (x == 7) return;
-  const int per = gridDim.x / 8, nwg = 7 * per, w = i * 7 + x;
+  // the workgroups of one XCD. XCDs nx .. 7 are left to the chain.
+  const int x = xcd_id(), i = blockIdx.x >> 3, nx = 8 - p.free_xcds;
+  if (x >= nx) return;
+  const int per = gridDim.x / 8, nwg = nx * per, w = i * nx + x;
   int F, E, C;
   tile_split(tiles, nwg, ksteps, F, E, C);
   for (int f = 0; f < F; ++f) {
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
   }
 }
 
-// The leftover tiles of a free_xcd7 launch: C = sum of the C partial tiles
+// The leftover tiles of a launch with free_xcds: C = sum of the C partial tiles
 // in chunk order, + rho P. Block (e, y) covers rows 8 y .. 8 y + 7 of tile e.
 __global__ __launch_bounds__(256) void rhs_fixup_kernel(GemmArgs p, int F, int nwg, int C) {
   const int e = blockIdx.x;
@@ -404,10 +404,13 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   if ((int64_t)256 * a.lda * 4 >= (int64_t)1 << 31 || (int64_t)TN * a.ldb * 4 >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   const int nt = (a.M / 256) * (a.N / TN);
-  if (a.free_xcd7) {
-    if (epi != kEpiRhs || !a.part || !aligned16(a.part)) return hipErrorInvalidValue;
-    constexpr int kGrid = kPinGrid, kWgs = kPinUpdSlots;  // 8 XCDs x 32; XCDs 0-6
-    hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, dim3(kGrid), dim3(NT), 0, s, a);
+  if (a.free_xcds) {
+    if (epi != kEpiRhs || !a.part || !aligned16(a.part) || a.free_xcds < 0 ||
+        a.free_xcds > kPinMaxXcds)
+      return hipErrorInvalidValue;
+    // 8 XCDs x 32 workgroups; those of XCDs 0 .. 7 - free_xcds work
+    const int kWgs = kPinGrid - kPinXcdCus * a.free_xcds;
+    hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, dim3(kPinGrid), dim3(NT), 0, s, a);
     int F, E, C;
     tile_split(nt, kWgs, a.K / BK, F, E, C);
     if (E > 0)
@@ -423,10 +426,11 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t rhs_part_floats(int M, int N, int K) {
-  if (M % 256 || N % TN || K % BK || M <= 0 || N <= 0 || K <= 0) return 0;
+size_t rhs_part_floats(int M, int N, int K, int f) {
+  if (M % 256 || N % TN || K % BK || M <= 0 || N <= 0 || K <= 0 || f <= 0 || f > kPinMaxXcds)
+    return 0;
   int F, E, C;
-  tile_split((M / 256) * (N / TN), kPinUpdSlots, K / BK, F, E, C);
+  tile_split((M / 256) * (N / TN), kPinGrid - kPinXcdCus * f, K / BK, F, E, C);
   return (size_t)E * C * 256 * TN;
 }
 

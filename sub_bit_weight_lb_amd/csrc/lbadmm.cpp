@@ -23,6 +23,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -43,7 +44,10 @@ constexpr uint32_t kKnownFlags = NQ_FLAG_COMPUTE_ERROR | NQ_FLAG_INIT_DRAWS |
 constexpr int kProfileRuns = 8;
 constexpr int64_t kMaxMN = (1 << 21) - 256;
 constexpr int64_t kMaxR = 1 << 13;
-constexpr int kRhsYield = 8;
+// s_sleep units per K step of the RHS GEMM beside the chain (measured best):
+// 8 when chain update tiles share its CUs (one diagonal XCD or none), 0 when
+// the chain keeps to two XCDs of its own
+constexpr int kRhsYield = 8, kRhsYieldTwoXcds = 0;
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
@@ -95,6 +99,31 @@ struct Arena {
   }
 };
 
+
+// The side stream of a device (the RHS GEMM and the SVIDs of every handle on
+// it), created with the first handle and kept until the process ends.
+// HIP maps streams onto a few hardware queues (four by default), sharing
+// queues round-robin once they run out; a side stream per handle made the
+// seventh handle's land on its caller's queue, where it runs after the
+// chain rather than beside it (that layer took 1.5x as long). Handles used
+// at the same time from different caller streams share it too: their RHS
+// GEMMs and SVIDs then run in the order they were enqueued.
+hipError_t side_stream(int dev, hipStream_t* out) {
+  static std::mutex mu;
+  static std::vector<hipStream_t> streams;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0) return hipErrorInvalidDevice;
+  if ((size_t)dev >= streams.size()) streams.resize(dev + 1, nullptr);
+  if (!streams[dev]) {
+    hipStream_t st = nullptr;
+    const hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    streams[dev] = st;
+  }
+  *out = streams[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace nq {
@@ -125,12 +154,12 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
-  float* rhs_part;  // partial tiles of the RHS GEMM when it leaves XCD 7 free
+  float* rhs_part;  // partial tiles of the RHS GEMM when it leaves XCDs to the chain
   // iterative solve (NQ_FLAG_SOLVE_CG / _GD): gradient, direction and its
   // product with G (max(mp, np) x rp each) and the per-row g.g
   float *itG = nullptr, *itD = nullptr, *itQ = nullptr, *itDelta = nullptr;
   // gemm_s: the RHS GEMM and the SVIDs, beside the caller's stream (see
-  // run_half)
+  // run_half); the device's side stream, shared by its handles
   hipStream_t gemm_s = nullptr;
   hipEvent_t ev_fork = nullptr, ev_gram = nullptr, ev_rhs = nullptr, ev_t0 = nullptr,
             ev_t1 = nullptr;
@@ -138,14 +167,17 @@ struct nq_lbadmm {
   bool has_run = false;
   bool stats_valid = false;  // the stats block describes the last run (not a time_svid call)
   // s_sleep units (~64 cycles each) per K step of the RHS GEMM while it runs
-  // beside the chain: the chain is the critical path and a wave sharing a
-  // SIMD with an MFMA-bound wave gets little issue time; the RHS has slack.
-  // NQ_RHS_YIELD overrides it.
+  // beside the chain: where chain waves share its CUs, a wave sharing a SIMD
+  // with an MFMA-bound wave gets little issue time and the RHS has slack
+  // (kRhsYield); with two diagonal XCDs nothing of the chain shares its CUs
+  // (kRhsYieldTwoXcds). NQ_RHS_YIELD overrides it.
   int rhs_yield = kRhsYield;
-  // Pinned overlap: the chain's diagonal work on XCD 7 (one workgroup per CU),
-  // the RHS GEMM on XCDs 0-6. Needs 8 x 32 CUs and at most 32 diagonal
-  // workgroups per launch (r_p <= 2048); NQ_PIN=0 turns it off.
-  bool pin = false;
+  // Pinned overlap: the chain's diagonal work on the last `pin` XCDs (one
+  // workgroup per CU), the RHS GEMM on the others. Needs 8 x 32 CUs and at
+  // most 32 diagonal workgroups per launch and XCD: pin = 1 for r_p <= 2048,
+  // 2 for r_p <= 4096, 0 (unpinned) above. NQ_PIN=0 turns it off; NQ_PIN=2
+  // asks for two XCDs where one would do.
+  int pin = 0;
   int svid_g = 256;  // workgroups of an SVID launch (svid_grid())
   // NQ_FLAG_PROFILE: ring of (start, end) event pairs and per-phase totals
   std::vector<hipEvent_t> prof_ev;
@@ -189,8 +221,11 @@ size_t layout(nq_lbadmm* h) {
   size_t o_s1c = a.take<float>(mp), o_s2c = a.take<float>(np_);
   size_t o_SU = a.take<int8_t>(mp * rp), o_SV = a.take<int8_t>(np_ * rp);
   size_t o_st = a.take<DevStats>(1);
-  size_t o_rp = a.take<float>(std::max(rhs_part_floats((int)mp, (int)rp, (int)np_),
-                                        rhs_part_floats((int)np_, (int)rp, (int)mp)));
+  size_t part_floats = 0;
+  for (int f = 1; f <= kPinMaxXcds; ++f)
+    part_floats = std::max({part_floats, rhs_part_floats((int)mp, (int)rp, (int)np_, f),
+                            rhs_part_floats((int)np_, (int)rp, (int)mp, f)});
+  size_t o_rp = a.take<float>(part_floats);
   const bool it = iterative(h);
   size_t o_itG = it ? a.take<float>(mx * rp) : 0, o_itD = it ? a.take<float>(mx * rp) : 0;
   size_t o_itQ = it ? a.take<float>(mx * rp) : 0, o_itX = it ? a.take<float>(mx) : 0;
@@ -366,7 +401,7 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   g.A = x.Wside; g.lda = x.K; g.B = x.otherT; g.ldb = x.K; g.C = h->R; g.ldc = rp;
   g.P = x.P; g.rho = h->d.rho; g.M = x.M; g.N = rp; g.K = x.K;
   g.yield = overlap ? h->rhs_yield : 0;
-  g.free_xcd7 = overlap && h->pin ? 1 : 0;
+  g.free_xcds = overlap ? h->pin : 0;
   g.part = h->rhs_part;
   long pr = prof_begin(h, NQ_PHASE_GEMM_RHS, gs);
   HIPCHK(launch_gemm(g, kEpiRhs, gs));
@@ -378,7 +413,7 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   // reduces the Gram segments into G itself (its update workgroups are
   // otherwise idle): G has no reduction launch of its own.
   HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, false,
-                                 s, overlap && h->pin, h->Mt,
+                                 s, overlap ? h->pin : 0, h->Mt,
                                  GramSrc{h->gpart, GramSteps{x.K / 32, 0}, x.gp.steps, h->d.rho}));
   HIPCHK(launch_gram_partial(h->Mt, rp, rp, rp, h->gI, h->gpart, s));
   HIPCHK(launch_gram_reduce(h->gpart, rp, rp, h->gI, 0.0f, true, h->Ginv, rp, s));
@@ -487,17 +522,21 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
     return hip_fail(e, "hipMalloc(workspace)");
   }
   layout(h);
-  if (const char* y = std::getenv("NQ_RHS_YIELD")) h->rhs_yield = std::max(0, std::atoi(y));
   {
     int ncu = 0;
-    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-      h->pin = ncu == kPinGrid && cholesky_pinnable(h->rp, false) && !iterative(h);
-    if (const char* y = std::getenv("NQ_PIN")) h->pin = h->pin && std::atoi(y) != 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        ncu == kPinGrid && !iterative(h))
+      h->pin = cholesky_pin_xcds((int)h->rp, false);
+    if (const char* y = std::getenv("NQ_PIN")) {
+      const int want = std::atoi(y);
+      h->pin = want <= 0 ? 0 : h->pin ? std::max(h->pin, std::min(want, kPinMaxXcds)) : 0;
+    }
     bool rr = false;
-    if (h->pin && xcd_round_robin_ok(&rr) == hipSuccess) h->pin = rr;
-    else h->pin = false;
+    if (h->pin && !(xcd_round_robin_ok(&rr) == hipSuccess && rr)) h->pin = 0;
   }
-  e = hipStreamCreateWithFlags(&h->gemm_s, hipStreamNonBlocking);
+  h->rhs_yield = h->pin == 2 ? kRhsYieldTwoXcds : kRhsYield;
+  if (const char* y = std::getenv("NQ_RHS_YIELD")) h->rhs_yield = std::max(0, std::atoi(y));
+  e = side_stream(dev, &h->gemm_s);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_gram, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_rhs, hipEventDisableTiming);
@@ -537,7 +576,6 @@ void nq_lbadmm_destroy(nq_lbadmm_t h) {
   if (h->ev_t1) (void)hipEventDestroy(h->ev_t1);
   for (hipEvent_t ev : h->prof_ev)
     if (ev) (void)hipEventDestroy(ev);
-  if (h->gemm_s) (void)hipStreamDestroy(h->gemm_s);
   if (h->base) (void)hipFree(h->base);
   if (cur != h->device) (void)hipSetDevice(cur);
   delete h;

@@ -8,7 +8,7 @@ events and the error computation on).
   tests/golden/make_lbadmm_final.py, which calls only oracle/).
 - The seven layers of one Llama-2-7B-shaped block (q, k, v, o at 4096 x 4096,
   r = 2048; gate and up at 11008 x 4096 and down at 4096 x 11008, r = 2970,
-  which pads to 3072 and so runs the unpinned overlap): one iteration of q,
+  which pads to 3072 and so pins the chain to two XCDs): one iteration of q,
   gate and down against the oracle, and the 40-iteration run of every layer
   against its stored end-of-run figures.
 - 8192 x 28672, r = 6144: the oracle cannot run an iteration in seconds here,

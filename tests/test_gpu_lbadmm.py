@@ -160,17 +160,19 @@ def test_profile_phases(gpu, profile):
     np.testing.assert_array_equal(H(res.U), H(plain.U))
 
 
-@pytest.mark.parametrize("shape", [(512, 384, 1100), (768, 640, 300)])
+@pytest.mark.parametrize("shape", [(512, 384, 1100), (768, 640, 300), (512, 384, 2100)])
 def test_launch_layouts_agree(gpu, shape, monkeypatch):
-    """The pinned overlap (the chain's diagonal work on one XCD, the RHS GEMM
-    on the others with leftover tiles split along K), the unpinned overlap
-    and the single-stream order compute the same iteration."""
+    """The pinned overlap (the chain's diagonal work on the last one or two
+    XCDs, the RHS GEMM on the others with leftover tiles split along K), the
+    unpinned overlap and the single-stream order compute the same iteration.
+    r = 2100 pads to 2176 (34 diagonal workgroups per launch), which takes two
+    XCDs by default; NQ_PIN=2 asks for two where one would do."""
     import sub_bit_weight_lb_amd as nq
     m, n, r = shape
     L = make_tiny(m, n, r, seed=21 + r, iters=2)
     outs = {}
-    for name, env, single in (("default", None, False), ("unpinned", "0", False),
-                              ("single", None, True)):
+    for name, env, single in (("default", None, False), ("two-xcds", "2", False),
+                              ("unpinned", "0", False), ("single", None, True)):
         if env is None:
             monkeypatch.delenv("NQ_PIN", raising=False)
         else:
