@@ -70,17 +70,20 @@ struct GemmArgs {
   int free_xcds;                 // kEpiRhs: 0, or 1-2 to run on XCDs 0 .. 7 - free_xcds
                                  // only (the others left to a pinned Cholesky
                                  // chain); part is then required
-  float* part;                   // up to 224 x 256 x 128 floats of partial tiles
+  float* part;                   // nullable: up to 256 x 256 x 128 floats of partial
+                                 // tiles (gemm_part_floats)
 };
 // M % 256 == 0, N % 128 == 0, K % 32 == 0; every ld a multiple of 4 and every
 // pointer 16-byte aligned (else hipErrorInvalidValue, nothing launched).
 // With free_xcds = f, the 256 x 128 tiles go to the 32 (8 - f) workgroups of
 // XCDs 0 .. 7 - f: each takes whole tiles, and the tiles left over are split
 // along K into partial tiles (in part) that a second kernel adds up, with
-// rho P, in a fixed order.
+// the epilogue, in a fixed order. With part and free_xcds = 0, a launch of
+// more than 256 tiles that do not fill whole rounds of 256 runs the same way
+// on all 8 XCDs; otherwise one workgroup per tile.
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s);
 // Floats of `part` a launch of this shape with free_xcds = f needs (0 if none).
-size_t rhs_part_floats(int M, int N, int K, int f);
+size_t gemm_part_floats(int M, int N, int K, int f);
 
 // ---------------------------------------------------------------- Gram
 // K steps (of 32) of the lower 128 x 128 tiles of a Gram product, tile
@@ -113,10 +116,12 @@ struct GramSrc {
 // Work split of a Gram product (GramSteps over R = rp / 128 tile rows) into
 // equal ranges of `steps` steps, one per workgroup (`wgs` of them); a tile's
 // segments go to at most `slots` partial buffers of rp x rp.
+// xcds = px > 0: the workgroups run on the last px XCDs only (two per CU),
+// for a Gram that follows a chain pinned there while a GEMM holds the others.
 struct GramPlan {
-  int steps, wgs, slots, tri;
+  int steps, wgs, slots, tri, xcds;
 };
-GramPlan gram_plan(int K, int rp, bool tri = false);
+GramPlan gram_plan(int K, int rp, bool tri = false, int xcds = 0);
 // Partial Gram tiles of A^T A for A (K x rp) given as At = A^T (rp x K, ld
 // ldat) into part (p.slots buffers of rp x rp, ld rp; lower tiles only).
 // rp % 128 == 0, K a multiple of 32; with p.tri, K == rp and A upper

@@ -285,19 +285,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int t, int ks, int 
     }
 }
 
+// nx = 0: one workgroup per tile. nx > 0: 256 workgroups (32 per XCD), those
+// of XCDs 0 .. nx - 1 working; each takes whole tiles, and the tiles left
+// over are split along K into partial tiles that gemm_fixup_kernel adds up.
 template <int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
+__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p, int nx) {
   __shared__ __attribute__((aligned(1024))) float lds[Tile<256>::LDS_FLOATS];
   const int tiles = (p.M / 256) * (p.N / TN);
   const int ksteps = p.K / BK;
-  if (!p.free_xcds) {
+  if (!nx) {
     gemm_tile<EPI>(p, xcd_tile(blockIdx.x, tiles), 0, ksteps, nullptr, lds);
     return;
   }
   // consecutive workgroups go to consecutive XCDs (the first one's XCD
   // depends on the queue's history): with 32 per XCD, blockIdx / 8 numbers
-  // the workgroups of one XCD. XCDs nx .. 7 are left to the chain.
-  const int x = xcd_id(), i = blockIdx.x >> 3, nx = 8 - p.free_xcds;
+  // the workgroups of one XCD. XCDs nx .. 7 are left to a pinned chain.
+  const int x = xcd_id(), i = blockIdx.x >> 3;
   if (x >= nx) return;
   const int per = gridDim.x / 8, nwg = nx * per, w = i * nx + x;
   int F, E, C;
@@ -320,9 +323,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p) {
   }
 }
 
-// The leftover tiles of a launch with free_xcds: C = sum of the C partial tiles
-// in chunk order, + rho P. Block (e, y) covers rows 8 y .. 8 y + 7 of tile e.
-__global__ __launch_bounds__(256) void rhs_fixup_kernel(GemmArgs p, int F, int nwg, int C) {
+// The leftover tiles of a split launch: the sum of the C partial tiles in
+// chunk order, then the epilogue (+ rho P; C^T beside C). Block (e, y) covers
+// rows 8 y .. 8 y + 7 of tile e.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs p, int F, int nwg, int C) {
   const int e = blockIdx.x;
   const int r = blockIdx.y * 8 + (threadIdx.x >> 5), c4 = (threadIdx.x & 31) * 4;
   const int tilesN = p.N / TN;
@@ -331,8 +336,14 @@ __global__ __launch_bounds__(256) void rhs_fixup_kernel(GemmArgs p, int F, int n
   const float* src = p.part + (int64_t)e * C * 256 * TN + r * TN + c4;
   f32x4 sum = *(const f32x4*)src;
   for (int cc = 1; cc < C; ++cc) sum += *(const f32x4*)(src + (int64_t)cc * 256 * TN);
-  const int64_t idx = (int64_t)(tm * 256 + r) * p.ldc + tn * TN + c4;
-  *(f32x4*)&p.C[idx] = sum + p.rho * *(const f32x4*)&p.P[idx];
+  const int64_t row = (int64_t)tm * 256 + r, col = (int64_t)tn * TN + c4;
+  const int64_t idx = row * p.ldc + col;
+  if (EPI == kEpiRhs) sum += p.rho * *(const f32x4*)&p.P[idx];
+  *(f32x4*)&p.C[idx] = sum;
+  if (EPI == kEpiSolve && p.Ct) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p.Ct[(col + j) * p.ldct + row] = sum[j];
+  }
 }
 
 // Partial Gram tiles, stream-K: the K steps of 32 of the lower tiles (tile
@@ -344,12 +355,22 @@ __global__ __launch_bounds__(256) void rhs_fixup_kernel(GemmArgs p, int F, int n
 // workgroup that touches tile t.
 __global__ __launch_bounds__(NT, 2) void gram_nt_kernel(const float* __restrict__ At,
                                                         int64_t ldat, int rp, GramSteps gs,
-                                                        int L, int64_t S, int W,
+                                                        int L, int64_t S, int W, int px,
                                                         float* __restrict__ part) {
   constexpr int TM = 128;
   using T_ = Tile<TM>;
   __shared__ __attribute__((aligned(1024))) float lds[T_::LDS_FLOATS];
-  const int w = xcd_tile(blockIdx.x, W);
+  int w;
+  if (px) {
+    // only the last px XCDs work, each on a contiguous run of ranges; the
+    // workgroups that land elsewhere exit (each fits beside a GEMM
+    // workgroup: 64 + 96 KB of LDS)
+    const int x = xcd_id(), x0 = 8 - px;
+    if (x < x0) return;
+    w = (x - x0) * (int)(gridDim.x / 8) + (int)(blockIdx.x >> 3);
+  } else {
+    w = xcd_tile(blockIdx.x, W);
+  }
   int64_t s0 = (int64_t)w * L;
   const int64_t s1 = min(S, s0 + L);
   const int wave = threadIdx.x >> 6;
@@ -404,49 +425,63 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
   if ((int64_t)256 * a.lda * 4 >= (int64_t)1 << 31 || (int64_t)TN * a.ldb * 4 >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
   const int nt = (a.M / 256) * (a.N / TN);
-  if (a.free_xcds) {
-    if (epi != kEpiRhs || !a.part || !aligned16(a.part) || a.free_xcds < 0 ||
-        a.free_xcds > kPinMaxXcds)
-      return hipErrorInvalidValue;
-    // 8 XCDs x 32 workgroups; those of XCDs 0 .. 7 - free_xcds work
-    const int kWgs = kPinGrid - kPinXcdCus * a.free_xcds;
-    hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, dim3(kPinGrid), dim3(NT), 0, s, a);
-    int F, E, C;
-    tile_split(nt, kWgs, a.K / BK, F, E, C);
-    if (E > 0)
-      hipLaunchKernelGGL(rhs_fixup_kernel, dim3(E, 256 / 8), dim3(256), 0, s, a, F, kWgs, C);
-    return hipGetLastError();
-  }
-  dim3 grid(nt), block(NT);
+  if (a.free_xcds && (epi != kEpiRhs || !a.part || a.free_xcds < 0 || a.free_xcds > kPinMaxXcds))
+    return hipErrorInvalidValue;
+  if (a.part && !aligned16(a.part)) return hipErrorInvalidValue;
+  // Split launches: with free_xcds, on XCDs 0 .. 7 - free_xcds; with part
+  // alone, on the whole chip when the tiles are more than one per CU and do
+  // not fill whole rounds (one workgroup per tile would leave most CUs idle
+  // in the last round).
+  const int nx = a.free_xcds ? 8 - a.free_xcds
+                 : (a.part && nt > kPinGrid && nt % kPinGrid) ? 8 : 0;
+  dim3 grid(nx ? kPinGrid : nt), block(NT);
   switch (epi) {
-    case kEpiRhs: hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, grid, block, 0, s, a); break;
-    case kEpiSolve: hipLaunchKernelGGL(gemm_nt_kernel<kEpiSolve>, grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL(gemm_nt_kernel<kEpiPlain>, grid, block, 0, s, a); break;
+    case kEpiRhs: hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, grid, block, 0, s, a, nx); break;
+    case kEpiSolve: hipLaunchKernelGGL(gemm_nt_kernel<kEpiSolve>, grid, block, 0, s, a, nx); break;
+    default: hipLaunchKernelGGL(gemm_nt_kernel<kEpiPlain>, grid, block, 0, s, a, nx); break;
+  }
+  if (nx) {
+    const int nwg = kPinXcdCus * nx;
+    int F, E, C;
+    tile_split(nt, nwg, a.K / BK, F, E, C);
+    const dim3 fg(E, 256 / 8);
+    if (E > 0) {
+      switch (epi) {
+        case kEpiRhs: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiRhs>, fg, dim3(256), 0, s, a, F, nwg, C); break;
+        case kEpiSolve: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiSolve>, fg, dim3(256), 0, s, a, F, nwg, C); break;
+        default: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiPlain>, fg, dim3(256), 0, s, a, F, nwg, C); break;
+      }
+    }
   }
   return hipGetLastError();
 }
 
-size_t rhs_part_floats(int M, int N, int K, int f) {
-  if (M % 256 || N % TN || K % BK || M <= 0 || N <= 0 || K <= 0 || f <= 0 || f > kPinMaxXcds)
+size_t gemm_part_floats(int M, int N, int K, int f) {
+  if (M % 256 || N % TN || K % BK || M <= 0 || N <= 0 || K <= 0 || f < 0 || f > kPinMaxXcds)
     return 0;
+  const int nt = (M / 256) * (N / TN);
+  if (f == 0 && (nt <= kPinGrid || nt % kPinGrid == 0)) return 0;
   int F, E, C;
-  tile_split((M / 256) * (N / TN), kPinGrid - kPinXcdCus * f, K / BK, F, E, C);
+  tile_split(nt, kPinGrid - kPinXcdCus * f, K / BK, F, E, C);
   return (size_t)E * C * 256 * TN;
 }
 
-GramPlan gram_plan(int K, int rp, bool tri) {
+GramPlan gram_plan(int K, int rp, bool tri, int xcds) {
   GramPlan p{};
   const int R = rp / 128;
   const int T = K / BK;
   const GramSteps gs{T, tri ? 1 : 0};
   const int64_t S = gs.row_start(R);
-  // two workgroups per CU; a tile gets at most 8 segments
-  int64_t L = std::max<int64_t>((S + 511) / 512, (T + 6) / 7);
+  // two workgroups per CU (of the whole chip, or of the last xcds XCDs); a
+  // tile gets at most 8 segments
+  const int64_t cap = xcds > 0 ? (int64_t)2 * kPinXcdCus * xcds : 512;
+  int64_t L = std::max<int64_t>((S + cap - 1) / cap, (T + 6) / 7);
   L = std::max<int64_t>(L, 1);
   p.steps = (int)L;
   p.wgs = (int)((S + L - 1) / L);
   p.slots = (int)((T + L - 1) / L) + 1;
   p.tri = tri ? 1 : 0;
+  p.xcds = xcds > 0 ? std::min(xcds, kPinMaxXcds) : 0;
   return p;
 }
 
@@ -461,8 +496,13 @@ hipError_t launch_gram_partial(const float* At, int64_t ldat, int K, int rp, con
   const int64_t S = gs.row_start(R);
   // `done` is recorded by the kernel's own completion (no marker of its own
   // between this kernel and the next one on s)
-  hipExtLaunchKernelGGL(gram_nt_kernel, dim3(p.wgs), dim3(NT), 0, s, nullptr, done, 0u, At, ldat,
-                        rp, gs, p.steps, S, p.wgs, part);
+  // with p.xcds: two workgroups per CU of all 8 XCDs, those of the last
+  // p.xcds working (p.wgs <= 64 p.xcds)
+  if (p.xcds < 0 || p.xcds > kPinMaxXcds || (p.xcds && p.wgs > 2 * kPinXcdCus * p.xcds))
+    return hipErrorInvalidValue;
+  const unsigned grid = p.xcds ? 2u * kPinGrid : (unsigned)p.wgs;
+  hipExtLaunchKernelGGL(gram_nt_kernel, dim3(grid), dim3(NT), 0, s, nullptr, done, 0u, At, ldat,
+                        rp, gs, p.steps, S, p.wgs, p.xcds, part);
   return hipGetLastError();
 }
 

@@ -143,6 +143,7 @@ struct nq_lbadmm {
   int mp = 0, np_ = 0, rp = 0;
   GramPlan gU{}, gV{};  // Gram work splits of the U-half (K = n) and V-half (K = m)
   GramPlan gI{};        // G^-1 = M^T M from M^T (triangular, K = rp)
+  GramPlan gIp{};       // the same on the chain's two XCDs (pin == 2, overlap)
   char* base = nullptr;
   size_t bytes = 0;
   float *Wt, *WtT, *U, *V, *UT, *VT, *LamU, *PU, *LamV, *PV, *R, *G, *Minv, *Ginv, *gpart;
@@ -154,7 +155,7 @@ struct nq_lbadmm {
   float *colpartU, *colpartV, *cbal, *s1w, *s2w, *s1c, *s2c;
   int8_t *SU, *SV;
   DevStats* st;
-  float* rhs_part;  // partial tiles of the RHS GEMM when it leaves XCDs to the chain
+  float* rhs_part;  // partial tiles of the split RHS and solve GEMM launches
   // iterative solve (NQ_FLAG_SOLVE_CG / _GD): gradient, direction and its
   // product with G (max(mp, np) x rp each) and the per-row g.g
   float *itG = nullptr, *itD = nullptr, *itQ = nullptr, *itDelta = nullptr;
@@ -221,10 +222,14 @@ size_t layout(nq_lbadmm* h) {
   size_t o_s1c = a.take<float>(mp), o_s2c = a.take<float>(np_);
   size_t o_SU = a.take<int8_t>(mp * rp), o_SV = a.take<int8_t>(np_ * rp);
   size_t o_st = a.take<DevStats>(1);
+  // partial tiles of the split GEMM launches: the RHS GEMMs on the whole
+  // chip or beside a pinned chain, and the solves (never at the same time)
   size_t part_floats = 0;
-  for (int f = 1; f <= kPinMaxXcds; ++f)
-    part_floats = std::max({part_floats, rhs_part_floats((int)mp, (int)rp, (int)np_, f),
-                            rhs_part_floats((int)np_, (int)rp, (int)mp, f)});
+  for (int f = 0; f <= kPinMaxXcds; ++f)
+    part_floats = std::max({part_floats, gemm_part_floats((int)mp, (int)rp, (int)np_, f),
+                            gemm_part_floats((int)np_, (int)rp, (int)mp, f),
+                            gemm_part_floats((int)mp, (int)rp, (int)rp, f),
+                            gemm_part_floats((int)np_, (int)rp, (int)rp, f)});
   size_t o_rp = a.take<float>(part_floats);
   const bool it = iterative(h);
   size_t o_itG = it ? a.take<float>(mx * rp) : 0, o_itD = it ? a.take<float>(mx * rp) : 0;
@@ -415,8 +420,11 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   HIPCHK(launch_cholesky_inverse(h->G, h->Minv, rp, (int)h->d.r, h->st, false, false,
                                  s, overlap ? h->pin : 0, h->Mt,
                                  GramSrc{h->gpart, GramSteps{x.K / 32, 0}, x.gp.steps, h->d.rho}));
-  HIPCHK(launch_gram_partial(h->Mt, rp, rp, rp, h->gI, h->gpart, s));
-  HIPCHK(launch_gram_reduce(h->gpart, rp, rp, h->gI, 0.0f, true, h->Ginv, rp, s));
+  // With the chain on two XCDs of its own, G^-1's Gram stays there too: the
+  // RHS GEMM on the other six is still running and is the longer side.
+  const GramPlan& gi = overlap && h->pin == 2 ? h->gIp : h->gI;
+  HIPCHK(launch_gram_partial(h->Mt, rp, rp, rp, gi, h->gpart, s));
+  HIPCHK(launch_gram_reduce(h->gpart, rp, rp, gi, 0.0f, true, h->Ginv, rp, s));
   prof_end(h, pc, s);
   if (overlap) HIPCHK(hipStreamWaitEvent(s, h->ev_rhs, 0));
   // out = R G^-1 (G^-1 symmetric, so it is its own transposed operand),
@@ -424,6 +432,9 @@ nq_status run_half(nq_lbadmm* h, const Half& x, const Half* pending, hipStream_t
   GemmArgs q{};
   q.A = h->R; q.lda = rp; q.B = h->Ginv; q.ldb = rp; q.C = x.out; q.ldc = rp;
   q.Ct = x.outT; q.ldct = x.M; q.M = x.M; q.N = rp; q.K = rp;
+  // leftover tiles split along K (the RHS GEMM and its fix-up, the only
+  // other users of part, have ended: this stream waited for ev_rhs)
+  q.part = h->rhs_part;
   long ps = prof_begin(h, NQ_PHASE_GEMM_SOLVE, s);
   HIPCHK(launch_gemm(q, kEpiSolve, s));
   prof_end(h, ps, s);
@@ -535,6 +546,10 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
     if (h->pin && !(xcd_round_robin_ok(&rr) == hipSuccess && rr)) h->pin = 0;
   }
   h->rhs_yield = h->pin == 2 ? kRhsYieldTwoXcds : kRhsYield;
+  // (fewer workgroups, so longer ranges and no more partial slots than the
+  // workspace holds for gI)
+  h->gIp = h->pin == 2 ? gram_plan((int)h->rp, (int)h->rp, true, 2) : h->gI;
+  if (h->gIp.slots > h->gI.slots) h->gIp = h->gI;
   if (const char* y = std::getenv("NQ_RHS_YIELD")) h->rhs_yield = std::max(0, std::atoi(y));
   e = side_stream(dev, &h->gemm_s);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming);

@@ -185,6 +185,13 @@ nq_status nq_op_gemm_rhs(const float* A, int64_t lda, const float* B, int64_t ld
   GemmArgs g{};
   g.A = a.f(); g.lda = Kp; g.B = bt.f(); g.ldb = Kp; g.C = c.f(); g.ldc = Np;
   g.P = p.f(); g.rho = rho; g.M = (int)Mp; g.N = (int)Np; g.K = (int)Kp;
+  // more tiles than CUs, not in whole rounds: the leftover tiles split along
+  // K, as in the layer's RHS GEMM and solve
+  DevBuf part;
+  if (const size_t pf = gemm_part_floats((int)Mp, (int)Np, (int)Kp, 0)) {
+    NQ_HIPCHK(part.alloc(sizeof(float) * pf));
+    g.part = part.f();
+  }
   NQ_HIPCHK(launch_gemm(g, kEpiRhs, s));
   NQ_HIPCHK(stage_out(c.f(), Np, C, ldc, rows, cols, s));
   NQ_HIPCHK(hipStreamSynchronize(s));
