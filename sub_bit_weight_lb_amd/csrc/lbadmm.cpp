@@ -45,9 +45,21 @@ constexpr int kProfileRuns = 8;
 constexpr int64_t kMaxMN = (1 << 21) - 256;
 constexpr int64_t kMaxR = 1 << 13;
 // s_sleep units per K step of the RHS GEMM beside the chain (measured best):
-// 8 when chain update tiles share its CUs (one diagonal XCD or none), 0 when
-// the chain keeps to two XCDs of its own
-constexpr int kRhsYield = 8, kRhsYieldTwoXcds = 0;
+// 8 where chain update tiles share its CUs and the chain is about as long as
+// the GEMM; 0 where the GEMM is clearly the longer side (it has nothing to
+// give) or the chain keeps to two XCDs of its own.
+constexpr int kRhsYield = 8;
+
+// Whether the chain is about as long as the RHS GEMM beside it: r_p / 64
+// launches of ~20 us against 2 m n r_p flops at ~105 TFLOP/s (the GEMM on 7
+// XCDs). Measured: 4096 x 4096, r 2048 (chain ~640 us, GEMM ~650 us): yield
+// 8 best (415 against 400 it/s at 0); 11008 x 4096, r 1536 (~480 against
+// ~1320 us): yield 0 best (265.8 against 256.9 it/s).
+bool chain_balances_rhs(int64_t mp, int64_t np_, int64_t rp) {
+  const double chain_us = (double)(rp / 64) * 20.0;
+  const double rhs_us = 2.0 * (double)mp * (double)np_ * (double)rp / 105e6;
+  return chain_us >= 0.67 * rhs_us;
+}
 
 nq_status check_desc(const nq_lbadmm_desc* d) {
   if (!d) return fail(NQ_ERR_INVALID_ARG, "desc is NULL");
@@ -169,9 +181,9 @@ struct nq_lbadmm {
   bool stats_valid = false;  // the stats block describes the last run (not a time_svid call)
   // s_sleep units (~64 cycles each) per K step of the RHS GEMM while it runs
   // beside the chain: where chain waves share its CUs, a wave sharing a SIMD
-  // with an MFMA-bound wave gets little issue time and the RHS has slack
-  // (kRhsYield); with two diagonal XCDs nothing of the chain shares its CUs
-  // (kRhsYieldTwoXcds). NQ_RHS_YIELD overrides it.
+  // with an MFMA-bound wave gets little issue time, so the RHS gives way
+  // (kRhsYield) when it has slack (chain_balances_rhs); with two diagonal
+  // XCDs nothing of the chain shares its CUs. NQ_RHS_YIELD overrides it.
   int rhs_yield = kRhsYield;
   // Pinned overlap: the chain's diagonal work on the last `pin` XCDs (one
   // workgroup per CU), the RHS GEMM on the others. Needs 8 x 32 CUs and at
@@ -545,7 +557,7 @@ nq_status nq_lbadmm_create(const nq_lbadmm_desc* desc, nq_lbadmm_t* out) {
     bool rr = false;
     if (h->pin && !(xcd_round_robin_ok(&rr) == hipSuccess && rr)) h->pin = 0;
   }
-  h->rhs_yield = h->pin == 2 ? kRhsYieldTwoXcds : kRhsYield;
+  h->rhs_yield = h->pin != 2 && chain_balances_rhs(h->mp, h->np_, h->rp) ? kRhsYield : 0;
   // (fewer workgroups, so longer ranges and no more partial slots than the
   // workspace holds for gI)
   h->gIp = h->pin == 2 ? gram_plan((int)h->rp, (int)h->rp, true, 2) : h->gI;
