@@ -28,8 +28,11 @@
 // - K order inside a chunk of 8: lane half h (lanes 32..63 are h = 1) feeds
 //   k = 4 h + s to MFMA step s = 0..3, the same for both operands.
 // - Tile order is XCD-aware: workgroup b runs on XCD b % 8, and each XCD gets
-//   a contiguous range of tiles, so row and column panels are shared in its
-//   L2.
+//   a contiguous range of tile indices, so row and column panels are shared
+//   in its L2. Indices run down bands of 4 tile rows (tile_rc), so the 32
+//   tiles an XCD holds at once form a 4 x 8 block: 4 row panels and 8
+//   column panels per K step instead of 2 and 16 in row-major order, a fifth
+//   fewer bytes through the XCD's L2.
 #include "common.h"
 
 #include <hip/hip_ext.h>
@@ -193,6 +196,21 @@ __device__ __forceinline__ int xcd_tile(int b, int nt) {
   return (nt % 8 == 0) ? (b % 8) * (nt / 8) + b / 8 : b;
 }
 
+// Tile index -> (tile row, tile column) of a tilesM x tilesN grid: indices
+// run down bands of kBand tile rows, column by column (the last band may be
+// shorter), so any 32 consecutive indices that start on a multiple of 32
+// inside a band of 16 or more columns form a kBand x 8 block. A bijection, so
+// every tile is still computed exactly once and in the same way.
+constexpr int kBand = 4;
+__host__ __device__ inline void tile_rc(int t, int tilesM, int tilesN, int& tm, int& tn) {
+  const int band = t / (kBand * tilesN);
+  const int rest = tilesM - band * kBand;
+  const int bh = rest < kBand ? rest : kBand;
+  const int idx = t - band * kBand * tilesN;
+  tm = band * kBand + idx % bh;
+  tn = idx / bh;
+}
+
 // Epilogue for one 32 x 32 accumulator block through a per-wave LDS block:
 // lane l, register v holds row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32;
 // it is written in that layout, read back row-major as float4, and stored
@@ -233,8 +251,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int t, int ks, int 
                                           float* lds) {
   constexpr int TM = 256;
   using T = Tile<TM>;
-  const int tilesN = p.N / TN;
-  const int tm = t / tilesN, tn = t % tilesN;
+  int tm, tn;
+  tile_rc(t, p.M / TM, p.N / TN, tm, tn);
   f32x16 acc[T::MI][2];
   nt_mainloop<TM>(p.A + (int64_t)tm * TM * p.lda, (int)p.lda, p.B + (int64_t)tn * TN * p.ldb,
                   (int)p.ldb, ks * BK, ke - ks, lds, acc, p.yield);
@@ -330,9 +348,8 @@ template <int EPI>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs p, int F, int nwg, int C) {
   const int e = blockIdx.x;
   const int r = blockIdx.y * 8 + (threadIdx.x >> 5), c4 = (threadIdx.x & 31) * 4;
-  const int tilesN = p.N / TN;
-  const int t = F * nwg + e;
-  const int tm = t / tilesN, tn = t % tilesN;
+  int tm, tn;
+  tile_rc(F * nwg + e, p.M / 256, p.N / TN, tm, tn);
   const float* src = p.part + (int64_t)e * C * 256 * TN + r * TN + c4;
   f32x4 sum = *(const f32x4*)src;
   for (int cc = 1; cc < C; ++cc) sum += *(const f32x4*)(src + (int64_t)cc * 256 * TN);
