@@ -75,6 +75,13 @@ __global__ __launch_bounds__(256) void apply_finish_kernel(
 // Sign-product error: P = S_U S_V^T exactly with the int8 MFMA (|P| <= r, int32
 // accumulate), E = s1w_i s2w_j P_ij, squared errors in Wt and W space summed
 // per 128 x 128 tile in double.
+// K runs in chunks of 32 (v_mfma_i32_32x32x32_i8, 16 bytes of one row per
+// lane), four chunks per round: a round's 16 fragment loads all go out
+// before the previous round's 16 MFMAs, so each round waits on one load
+// latency at most. Lane half h of chunk u holds bytes 32 u + 16 h of the
+// round's 128 for its row of S_U or S_V; both operands use the same map, so
+// the products sum over every k exactly once. rp % 128 == 0.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(256) void error_kernel(
     const int8_t* __restrict__ SU, const int8_t* __restrict__ SV, int np_, int rp,
     const float* __restrict__ s1w, const float* __restrict__ s2w, const float* __restrict__ Wt,
@@ -93,19 +100,37 @@ __global__ __launch_bounds__(256) void error_kernel(
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0;
-  const int8_t* ua = SU + (int64_t)(ti * 128 + wm * 64 + l32) * rp + 8 * half;
-  const int8_t* vb = SV + (int64_t)(tj * 128 + wn * 64 + l32) * rp + 8 * half;
-  for (int k0 = 0; k0 < rp; k0 += 16) {
-    long af[2], bf[2];
+  const int8_t* ua = SU + (int64_t)(ti * 128 + wm * 64 + l32) * rp + 16 * half;
+  const int8_t* vb = SV + (int64_t)(tj * 128 + wn * 64 + l32) * rp + 16 * half;
+  constexpr int U = 4;
+  i32x4 af[U][2], bf[U][2];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a) af[a] = *(const long*)(ua + (int64_t)a * 32 * rp + k0);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) bf[b] = *(const long*)(vb + (int64_t)b * 32 * rp + k0);
+      for (int a = 0; a < 2; ++a) {
+        af[u][a] = *(const i32x4*)(ua + (int64_t)a * 32 * rp + k0 + 32 * u);
+        bf[u][a] = *(const i32x4*)(vb + (int64_t)a * 32 * rp + k0 + 32 * u);
+      }
+  };
+  load(0);
+  for (int k0 = 0; k0 < rp; k0 += 32 * U) {
+    i32x4 ca[U][2], cb[U][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x16_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
+      for (int a = 0; a < 2; ++a) {
+        ca[u][a] = af[u][a];
+        cb[u][a] = bf[u][a];
+      }
+    if (k0 + 32 * U < rp) load(k0 + 32 * U);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ca[u][a], cb[u][b], acc[a][b], 0, 0, 0);
   }
   double e_wt = 0.0, e_w = 0.0;
 #pragma unroll
@@ -212,7 +237,7 @@ hipError_t launch_error(const int8_t* SU, const int8_t* SV, int mp, int np_, int
                         const float* s1w, const float* s2w, const float* Wt, const float* W,
                         int64_t ldw, int64_t m, int64_t n, const float* s1, const float* s2,
                         double* parts, DevStats* st, hipStream_t s) {
-  if (mp % 128 || np_ % 128 || rp % 16) return hipErrorInvalidValue;
+  if (mp % 128 || np_ % 128 || rp % 128 || rp <= 0) return hipErrorInvalidValue;
   const int nb = error_nparts(mp, np_);
   hipLaunchKernelGGL(error_kernel, dim3(nb), dim3(256), 0, s, SU, SV, np_, rp, s1w, s2w, Wt, W,
                      ldw, m, n, s1, s2, parts);
