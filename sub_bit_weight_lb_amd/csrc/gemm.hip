@@ -351,11 +351,24 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs p, int F, int 
   int tm, tn;
   tile_rc(F * nwg + e, p.M / 256, p.N / TN, tm, tn);
   const float* src = p.part + (int64_t)e * C * 256 * TN + r * TN + c4;
-  f32x4 sum = *(const f32x4*)src;
-  for (int cc = 1; cc < C; ++cc) sum += *(const f32x4*)(src + (int64_t)cc * 256 * TN);
   const int64_t row = (int64_t)tm * 256 + r, col = (int64_t)tn * TN + c4;
   const int64_t idx = row * p.ldc + col;
-  if (EPI == kEpiRhs) sum += p.rho * *(const f32x4*)&p.P[idx];
+  f32x4 pv = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (EPI == kEpiRhs) pv = *(const f32x4*)&p.P[idx];
+  // every chunk of a batch of 8 is loaded before any is added (a loop over a
+  // run-time count would wait on each load in turn); the sum runs in chunk
+  // order all the same
+  f32x4 sum = *(const f32x4*)src;
+  for (int c0 = 1; c0 < C; c0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < C) v[j] = *(const f32x4*)(src + (int64_t)(c0 + j) * 256 * TN);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < C) sum += v[j];
+  }
+  if (EPI == kEpiRhs) sum += p.rho * pv;
   *(f32x4*)&p.C[idx] = sum;
   if (EPI == kEpiSolve && p.Ct) {
 #pragma unroll
