@@ -234,14 +234,48 @@ __device__ __forceinline__ void stage_block(const f32x16& a, float* stage, F&& s
   __builtin_amdgcn_wave_barrier();
 }
 
-// Work split of the 256 x 128 tiles over nwg workgroups: F whole tiles each,
-// then the E tiles left over cut along K into C chunks (E C <= nwg).
-__host__ __device__ inline void tile_split(int tiles, int nwg, int ksteps, int& F, int& E,
-                                           int& C) {
-  F = tiles / nwg;
-  E = tiles - F * nwg;
-  C = E > 0 ? nwg / E : 0;
-  if (C > ksteps) C = ksteps;
+// Work split of the 256 x 128 tiles over nwg workgroups: F whole tiles
+// each, then the E tiles left over cut along K into C chunks each, q
+// consecutive chunks per workgroup (workgroup w takes chunks [w q, w q + q)
+// of the E C, chunk c of tile e being c - e C; the chunks of one tile that a
+// workgroup holds are one K range). The largest share of a workgroup is
+// F + q / C tiles; C is the smallest count (at most 64, at least one K step
+// per chunk) whose share is within 2 % of the best: 32 tiles over 224
+// workgroups give C = 7, q = 1; 192 tiles C = 7, q = 6 (6/7 of a tile each,
+// where one workgroup per tile left 32 idle). Tile e's chunks are held by
+// workgroups w0(e) = e C / q .. w1(e) = (e C + C - 1) / q, whose partial
+// tiles go to slots 0 .. w1 - w0 of the tile (S slots per tile at most).
+struct TileSplit {
+  int F, E, C, q, S;
+};
+__host__ __device__ inline TileSplit tile_split(int tiles, int nwg, int ksteps) {
+  TileSplit t{};
+  t.F = tiles / nwg;
+  t.E = tiles - t.F * nwg;
+  if (t.E == 0) return t;
+  const int cmax = ksteps < 64 ? ksteps : 64;
+  // share(C) = F + ceil(E C / nwg) / C = (F C + q) / C, compared as fractions
+  int bc = 1, bq = (t.E + nwg - 1) / nwg;
+  for (int c = 2; c <= cmax; ++c) {
+    const int q = (t.E * c + nwg - 1) / nwg;
+    if ((int64_t)(t.F * c + q) * bc < (int64_t)(t.F * bc + bq) * c) { bc = c; bq = q; }
+  }
+  for (int c = 1; c <= cmax; ++c) {  // the smallest C within 2 % of the best
+    const int q = (t.E * c + nwg - 1) / nwg;
+    if ((int64_t)100 * (t.F * c + q) * bc <= (int64_t)102 * (t.F * bc + bq) * c) {
+      bc = c;
+      bq = q;
+      break;
+    }
+  }
+  t.C = bc;
+  t.q = bq;
+  t.S = 0;
+  for (int e = 0; e < t.E; ++e) {
+    const int n = (e * t.C + t.C - 1) / t.q - (e * t.C) / t.q + 1;
+    t.S = n > t.S ? n : t.S;
+  }
+  return t;
 }
 
 // One 256 x 128 tile: K steps [ks, ke) into acc, then either the full
@@ -307,7 +341,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& p, int t, int ks, int 
 // of XCDs 0 .. nx - 1 working; each takes whole tiles, and the tiles left
 // over are split along K into partial tiles that gemm_fixup_kernel adds up.
 template <int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p, int nx) {
+__global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p, int nx, TileSplit sp) {
   __shared__ __attribute__((aligned(1024))) float lds[Tile<256>::LDS_FLOATS];
   const int tiles = (p.M / 256) * (p.N / TN);
   const int ksteps = p.K / BK;
@@ -321,42 +355,51 @@ __global__ __launch_bounds__(NT, 1) void gemm_nt_kernel(GemmArgs p, int nx) {
   const int x = xcd_id(), i = blockIdx.x >> 3;
   if (x >= nx) return;
   const int per = gridDim.x / 8, nwg = nx * per, w = i * nx + x;
-  int F, E, C;
-  tile_split(tiles, nwg, ksteps, F, E, C);
-  for (int f = 0; f < F; ++f) {
-    if (f > 0) {  // the next tile's copies overwrite the LDS the epilogue staged in
+  bool first = true;
+  for (int f = 0; f < sp.F; ++f) {
+    if (!first) {  // the next tile's copies overwrite the LDS the epilogue staged in
       __builtin_amdgcn_s_waitcnt(0xc07f);
       asm volatile("s_barrier" ::: "memory");
     }
+    first = false;
     gemm_tile<EPI>(p, f * nwg + x * per + i, 0, ksteps, nullptr, lds);
   }
-  if (w < E * C) {
-    if (F > 0) {
+  // this workgroup's chunks [c0, c1) of the leftover tiles, one K range per
+  // tile they touch
+  const int total = sp.E * sp.C;
+  const int c0 = w * sp.q, c1 = c0 + sp.q < total ? c0 + sp.q : total;
+  for (int c = c0; c < c1;) {
+    const int e = c / sp.C, ce = (e + 1) * sp.C < c1 ? (e + 1) * sp.C : c1;
+    if (!first) {
       __builtin_amdgcn_s_waitcnt(0xc07f);
       asm volatile("s_barrier" ::: "memory");
     }
-    const int e = w / C, c = w % C;
-    gemm_tile<EPI>(p, F * nwg + e, c * ksteps / C, (c + 1) * ksteps / C,
-                   p.part + (int64_t)(e * C + c) * 256 * TN, lds);
+    first = false;
+    const int slot = w - (e * sp.C) / sp.q;
+    gemm_tile<EPI>(p, sp.F * nwg + e, (c - e * sp.C) * ksteps / sp.C,
+                   (ce - e * sp.C) * ksteps / sp.C,
+                   p.part + ((int64_t)e * sp.S + slot) * 256 * TN, lds);
+    c = ce;
   }
 }
 
-// The leftover tiles of a split launch: the sum of the C partial tiles in
-// chunk order, then the epilogue (+ rho P; C^T beside C). Block (e, y) covers
-// rows 8 y .. 8 y + 7 of tile e.
+// The leftover tiles of a split launch: the sum of each tile's partial
+// tiles in slot (workgroup) order, then the epilogue (+ rho P; C^T beside
+// C). Block (e, y) covers rows 8 y .. 8 y + 7 of tile e.
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs p, int F, int nwg, int C) {
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs p, int nwg, TileSplit sp) {
   const int e = blockIdx.x;
   const int r = blockIdx.y * 8 + (threadIdx.x >> 5), c4 = (threadIdx.x & 31) * 4;
   int tm, tn;
-  tile_rc(F * nwg + e, p.M / 256, p.N / TN, tm, tn);
-  const float* src = p.part + (int64_t)e * C * 256 * TN + r * TN + c4;
+  tile_rc(sp.F * nwg + e, p.M / 256, p.N / TN, tm, tn);
+  const int C = (e * sp.C + sp.C - 1) / sp.q - (e * sp.C) / sp.q + 1;  // slots of tile e
+  const float* src = p.part + (int64_t)e * sp.S * 256 * TN + r * TN + c4;
   const int64_t row = (int64_t)tm * 256 + r, col = (int64_t)tn * TN + c4;
   const int64_t idx = row * p.ldc + col;
   f32x4 pv = {0.0f, 0.0f, 0.0f, 0.0f};
   if (EPI == kEpiRhs) pv = *(const f32x4*)&p.P[idx];
-  // every chunk of a batch of 8 is loaded before any is added (a loop over a
-  // run-time count would wait on each load in turn); the sum runs in chunk
+  // every slot of a batch of 8 is loaded before any is added (a loop over a
+  // run-time count would wait on each load in turn); the sum runs in slot
   // order all the same
   f32x4 sum = *(const f32x4*)src;
   for (int c0 = 1; c0 < C; c0 += 8) {
@@ -441,6 +484,12 @@ __global__ __launch_bounds__(NT, 2) void gram_nt_kernel(const float* __restrict_
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Whether a whole-chip launch with a partial buffer splits its tiles (see
+// launch_gemm).
+bool whole_chip_split(int nt, int ksteps) {
+  return (nt > kPinGrid && nt % kPinGrid) || (nt >= kPinGrid / 4 && nt < kPinGrid && ksteps >= 32);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
@@ -459,28 +508,25 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t s) {
     return hipErrorInvalidValue;
   if (a.part && !aligned16(a.part)) return hipErrorInvalidValue;
   // Split launches: with free_xcds, on XCDs 0 .. 7 - free_xcds; with part
-  // alone, on the whole chip when the tiles are more than one per CU and do
-  // not fill whole rounds (one workgroup per tile would leave most CUs idle
-  // in the last round).
-  const int nx = a.free_xcds ? 8 - a.free_xcds
-                 : (a.part && nt > kPinGrid && nt % kPinGrid) ? 8 : 0;
+  // alone, on the whole chip when one workgroup per tile would leave CUs
+  // idle: more tiles than CUs, not in whole rounds, or fewer tiles than
+  // CUs but at least a quarter of them, with K long enough to cut.
+  const int ksteps = a.K / BK;
+  const int nx = a.free_xcds ? 8 - a.free_xcds : (a.part && whole_chip_split(nt, ksteps)) ? 8 : 0;
+  const int nwg = kPinXcdCus * nx;
+  const TileSplit sp = nx ? tile_split(nt, nwg, ksteps) : TileSplit{};
   dim3 grid(nx ? kPinGrid : nt), block(NT);
   switch (epi) {
-    case kEpiRhs: hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, grid, block, 0, s, a, nx); break;
-    case kEpiSolve: hipLaunchKernelGGL(gemm_nt_kernel<kEpiSolve>, grid, block, 0, s, a, nx); break;
-    default: hipLaunchKernelGGL(gemm_nt_kernel<kEpiPlain>, grid, block, 0, s, a, nx); break;
+    case kEpiRhs: hipLaunchKernelGGL(gemm_nt_kernel<kEpiRhs>, grid, block, 0, s, a, nx, sp); break;
+    case kEpiSolve: hipLaunchKernelGGL(gemm_nt_kernel<kEpiSolve>, grid, block, 0, s, a, nx, sp); break;
+    default: hipLaunchKernelGGL(gemm_nt_kernel<kEpiPlain>, grid, block, 0, s, a, nx, sp); break;
   }
-  if (nx) {
-    const int nwg = kPinXcdCus * nx;
-    int F, E, C;
-    tile_split(nt, nwg, a.K / BK, F, E, C);
-    const dim3 fg(E, 256 / 8);
-    if (E > 0) {
-      switch (epi) {
-        case kEpiRhs: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiRhs>, fg, dim3(256), 0, s, a, F, nwg, C); break;
-        case kEpiSolve: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiSolve>, fg, dim3(256), 0, s, a, F, nwg, C); break;
-        default: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiPlain>, fg, dim3(256), 0, s, a, F, nwg, C); break;
-      }
+  if (nx && sp.E > 0) {
+    const dim3 fg(sp.E, 256 / 8);
+    switch (epi) {
+      case kEpiRhs: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiRhs>, fg, dim3(256), 0, s, a, nwg, sp); break;
+      case kEpiSolve: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiSolve>, fg, dim3(256), 0, s, a, nwg, sp); break;
+      default: hipLaunchKernelGGL(gemm_fixup_kernel<kEpiPlain>, fg, dim3(256), 0, s, a, nwg, sp); break;
     }
   }
   return hipGetLastError();
@@ -490,10 +536,9 @@ size_t gemm_part_floats(int M, int N, int K, int f) {
   if (M % 256 || N % TN || K % BK || M <= 0 || N <= 0 || K <= 0 || f < 0 || f > kPinMaxXcds)
     return 0;
   const int nt = (M / 256) * (N / TN);
-  if (f == 0 && (nt <= kPinGrid || nt % kPinGrid == 0)) return 0;
-  int F, E, C;
-  tile_split(nt, kPinGrid - kPinXcdCus * f, K / BK, F, E, C);
-  return (size_t)E * C * 256 * TN;
+  if (f == 0 && !whole_chip_split(nt, K / BK)) return 0;
+  const TileSplit sp = tile_split(nt, kPinGrid - kPinXcdCus * f, K / BK);
+  return (size_t)sp.E * sp.S * 256 * TN;
 }
 
 GramPlan gram_plan(int K, int rp, bool tri, int xcds) {

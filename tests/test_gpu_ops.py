@@ -57,9 +57,13 @@ def test_sign_gemm_is_exact(gpu, rows, k, cols):
 
 # (4608, 512, 2048): 288 tiles of 256 x 128, one round of 256 and 32 tiles
 # split 8 ways along K; (5000, 100, 1700): 280 tiles padded from a ragged
-# shape, 24 split 4 ways (one K step each)
+# shape, 24 split 4 ways (one K step each); (4096, 2048, 1536): 192 tiles,
+# fewer than the 256 CUs, cut into 4 chunks of 16 K steps, 3 chunks per
+# workgroup, so most tiles sum partials from two workgroups; (2000, 1111,
+# 1000): 64 tiles from a ragged shape, 4 chunks each over 256 workgroups
 @pytest.mark.parametrize("rows,k,cols", [(256, 32, 128), (300, 70, 90), (1000, 517, 260),
-                                         (512, 4096, 256), (4608, 512, 2048), (5000, 100, 1700)])
+                                         (512, 4096, 256), (4608, 512, 2048), (5000, 100, 1700),
+                                         (4096, 2048, 1536), (2000, 1111, 1000)])
 def test_gemm_rhs(gpu, rows, k, cols):
     import sub_bit_weight_lb_amd as nq
     rng = np.random.default_rng(rows + k + cols)
